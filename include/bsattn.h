@@ -1,0 +1,216 @@
+/*
+ * libbsattn -- block-sparse flash attention forward for AMD Instinct MI355X
+ * (gfx950 / CDNA4).  C ABI: plain structs, plain pointers, status codes.
+ *
+ * The operation (forward only):
+ *   For every batch b, query head h and query q, with hk = h / (H / Hkv):
+ *     A(q)  = { k : allowed(h, q, k) }                 (the sparse layout)
+ *     s_k   = scale * dot(Q[b,h,q,:], K[b,hk,k,:])      k in A(q)
+ *     O[b,h,q,:] = sum_k softmax(s)_k * V[b,hk,k,:]
+ *     LSE[b,h,q] = log(sum_k exp(s_k))                  (natural log)
+ *   An empty A(q) gives O = 0 and LSE = -inf.
+ *   Sources: the attention formula softmax(QK^T / sqrt(d_k)) V, section "The
+ *   Mechanics: How Flash MSA Sparse Attention Works Under the Hood" of the page
+ *   "Flash MSA Sparse Attention vs Full Attention"; the five-step block-sparse
+ *   procedure (tile the sequence, block-level mask, fetch only active K/V
+ *   blocks, flash tiling over them, online-softmax accumulation), section "How
+ *   Does Flash-MSA Sparse Attention Work?" of "How Do Sparse Attention Kernels
+ *   Work in GPU Clusters?"; the (batch, heads, seq_len, d_head) inputs and a
+ *   mask given as bits or as block indices, section "The Architecture of Flash
+ *   MSA Sparse Attention Kernels" of "Flash MSA Sparse Attention Kernels
+ *   Explained".  The score matrix is never materialised.  The log-sum-exp
+ *   output is this library's addition: merging partial results by online
+ *   softmax and a backward pass both need it.
+ *
+ * Layout predicate (which (q, k) pairs are allowed), with u = units of the
+ * window/global fields (tokens: q, k; blocks: q / block, k / block):
+ *   allowed = causal_ok && (bitmap ? bitmap[hl][q/bs][k/bs]
+ *                                  : in_window || key_global || query_global)
+ *   causal_ok    = !causal || k <= q                (always token-exact)
+ *   in_window    = (wl < 0 || qu - ku <= wl) && (wr < 0 || ku - qu <= wr)
+ *   key_global   = ku < global_keys
+ *   query_global = qu < global_queries
+ * Sliding window |i - j| <= W and the causal window: section "The Mechanics"
+ * of "Flash MSA Sparse Attention vs Full Attention"; global tokens that both
+ * see and are seen by every position: "Global Tokens" under "Sparse Patterns
+ * Beyond Sliding Windows" on the same page; a window counted in blocks plus
+ * a few global blocks: "The Real Deal: Block-Sparse FlashAttention" of "The
+ * Only Guide You Need for Sparse Attention Kernels in Long-Context LLMs".
+ *
+ * Threading: calls on different plans may run concurrently; a plan may be
+ * used by several streams at once (bsa_forward only reads it).  The last
+ * error string is thread-local.
+ */
+#ifndef BSATTN_H
+#define BSATTN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BSA_ABI_VERSION 1
+
+/* Status codes.  Every entry point that can fail returns one; no exception
+ * crosses the ABI.  Out-parameters are written only on BSA_OK. */
+typedef int32_t bsa_status_t;
+#define BSA_OK                   0
+#define BSA_ERR_INVALID_ARGUMENT 1  /* bad shape, pointer, field or plan state */
+#define BSA_ERR_UNSUPPORTED      2  /* valid but not built: (dtype, head_dim, block) */
+#define BSA_ERR_OUT_OF_MEMORY    3  /* host or device allocation failed */
+#define BSA_ERR_DEVICE           4  /* HIP runtime error (launch, copy, device) */
+
+/* Element type of Q, K, V and O.  LSE is always float32. */
+#define BSA_F32  0
+#define BSA_BF16 1
+
+/* Units of the window/global fields of bsa_layout_t. */
+#define BSA_UNIT_TOKENS 0
+#define BSA_UNIT_BLOCKS 1
+
+/* Work-order policy for the plan (which workgroup runs which q-block). */
+#define BSA_SCHEDULE_DEFAULT  0  /* = BSA_SCHEDULE_XCD */
+#define BSA_SCHEDULE_XCD      1  /* locality runs per XCD, cost-balanced, LPT tail */
+#define BSA_SCHEDULE_LPT      2  /* global longest-first */
+#define BSA_SCHEDULE_ROWMAJOR 3  /* (b, h, q-block) order */
+
+/* The attention problem a plan is prepared for.
+ *   batch >= 0, num_heads >= 1, num_kv_heads >= 1, num_heads % num_kv_heads == 0
+ *     (query head h reads KV head h / (num_heads / num_kv_heads)).
+ *   seq_len >= 0 and a multiple of block_size (the FAQ of "The Only Guide You
+ *     Need for Sparse Attention Kernels in Long-Context LLMs" answers the
+ *     variable-length question by padding to the block size).
+ *   block_size: layout block = kernel tile height and width.
+ *   Supported (dtype, head_dim, block_size):
+ *     BSA_BF16: (128, 128)                    -- MFMA kernel
+ *     BSA_F32 : (64 | 128, 64 | 128)          -- exact fp32 kernel
+ *   scale: 0 means 1/sqrt(head_dim); otherwise finite and > 0.
+ *   schedule: one of BSA_SCHEDULE_*.
+ */
+typedef struct {
+  int32_t batch;
+  int32_t num_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int64_t seq_len;
+  int32_t block_size;
+  int32_t dtype;
+  float   scale;
+  int32_t schedule;
+} bsa_problem_t;
+
+/* Which (q, k) pairs are allowed (see the predicate above).
+ *   causal: 0 or 1.  unit: BSA_UNIT_TOKENS or BSA_UNIT_BLOCKS.
+ *   window_left, window_right >= -1 (-1 = unbounded), inclusive distances.
+ *   global_keys, global_queries >= 0.
+ *   bitmap: NULL, or a HOST array uint8 [bitmap_heads][nb][nb] (nb =
+ *     seq_len / block_size), nonzero = block active, row = q-block, column =
+ *     k-block; it replaces window/global (causal still applies).  The plan
+ *     copies what it needs; the caller keeps ownership.  bitmap_heads is 1
+ *     (shared by every head) or num_heads (one layout per query head); the
+ *     bitmap is shared across the batch.
+ */
+typedef struct {
+  int32_t causal;
+  int32_t unit;
+  int64_t window_left;
+  int64_t window_right;
+  int64_t global_keys;
+  int64_t global_queries;
+  const uint8_t* bitmap;
+  int32_t bitmap_heads;
+} bsa_layout_t;
+
+/* Opaque plan: owns its host CSR arrays and, when built by bsa_plan, their
+ * device copy on the HIP device that was current at creation. */
+typedef struct bsa_plan* bsa_plan_t;
+
+/* Summary of a plan (all counts exact). */
+typedef struct {
+  int32_t layout_heads;      /* 1 or num_heads */
+  int32_t num_blocks;        /* nb = seq_len / block_size */
+  int64_t nnz;               /* CSR entries over all layout heads */
+  int64_t nnz_partial;       /* of which PARTIAL (token mask applied) */
+  int64_t active_blocks;     /* sum over (b, h) of the row lengths: tiles computed per forward */
+  int64_t allowed_pairs;     /* sum over (b, h) of allowed (q, k) pairs */
+  int64_t work_items;        /* batch * num_heads * nb */
+  int64_t launch_slots;      /* workgroups launched (>= work_items; idle slots exit) */
+  int32_t max_row_entries;   /* longest q-block row */
+  int32_t on_device;         /* 1 if the plan has a device copy */
+} bsa_plan_info_t;
+
+/* Build a plan: validate the problem and layout, turn the layout into a
+ * per-q-block CSR list of key blocks (ascending, each flagged FULL or PARTIAL
+ * from its exact allowed-pair count), build the work order, and upload it to
+ * the current HIP device (synchronous hipMalloc + hipMemcpy).
+ * Per-query-block lists of key blocks: step three of "How Does Flash-MSA
+ * Sparse Attention Work?" (each query block fetches only its active K/V
+ * blocks) and the precomputed block offsets recommended in the FAQ entry on
+ * sparse kernels slower than dense, both on "How Do Sparse Attention Kernels
+ * Work in GPU Clusters?".
+ * Errors: INVALID_ARGUMENT (NULL pointers, bad fields), UNSUPPORTED,
+ * OUT_OF_MEMORY, DEVICE.  *out_plan is written only on BSA_OK. */
+bsa_status_t bsa_plan(const bsa_problem_t* problem, const bsa_layout_t* layout,
+                      bsa_plan_t* out_plan);
+
+/* Same as bsa_plan but host-only: no HIP call is made, so it works without a
+ * GPU.  Such a plan can be inspected but not passed to bsa_forward. */
+bsa_status_t bsa_plan_host(const bsa_problem_t* problem, const bsa_layout_t* layout,
+                           bsa_plan_t* out_plan);
+
+/* Free a plan and its device copy.  NULL is ignored.  The caller must make
+ * sure no forward using the plan is still running (synchronise first). */
+void bsa_plan_destroy(bsa_plan_t plan);
+
+/* The CSR of one layout head: row_ptr [nb + 1] (head-local offsets), col_idx
+ * [nnz] ascending within each row, flags [nnz] (0 = FULL, 1 = PARTIAL).  The
+ * pointers are owned by the plan and valid until bsa_plan_destroy.
+ * Errors: INVALID_ARGUMENT for a NULL plan/out pointer or a layout_head out
+ * of range. */
+bsa_status_t bsa_plan_csr(bsa_plan_t plan, int32_t layout_head, const int32_t** row_ptr,
+                          const int32_t** col_idx, const uint8_t** flags, int64_t* nnz);
+
+/* Plan summary.  Errors: INVALID_ARGUMENT for NULL pointers. */
+bsa_status_t bsa_plan_get_info(bsa_plan_t plan, bsa_plan_info_t* info);
+
+/* The launch order: slot s of the grid runs item work[s] = (b * H + h) * nb + i,
+ * or -1 for an idle slot.  Owned by the plan.  Errors: INVALID_ARGUMENT. */
+bsa_status_t bsa_plan_work(bsa_plan_t plan, const int32_t** work, int64_t* slots);
+
+/* Sum over (b, h) of CSR entries: the tiles one forward computes (the
+ * numerator of the active-block FLOP count 4 * block^2 * head_dim per tile).
+ * Returns -1 for a NULL plan. */
+int64_t bsa_plan_active_blocks(bsa_plan_t plan);
+
+/* Run the forward pass asynchronously on `stream` (a hipStream_t; NULL = the
+ * default stream) of the plan's device.
+ *   q   : device, [batch][num_heads][seq_len][head_dim], contiguous, dtype
+ *   k, v: device, [batch][num_kv_heads][seq_len][head_dim], contiguous, dtype
+ *   out : device, [batch][num_heads][seq_len][head_dim], contiguous, dtype
+ *         (bf16 rounded to nearest even from float32 accumulators)
+ *   lse : device, float32 [batch][num_heads][seq_len]; natural log of the sum
+ *         of exp(scaled scores) over the allowed keys; -inf for empty rows
+ * All buffers are caller-owned; out and lse must not alias the inputs.  Every
+ * element of out and lse is written.  Nothing is allocated or freed.
+ * Errors (returned before anything is launched): INVALID_ARGUMENT for NULL
+ * pointers, a host-only plan, or a plan made on another device; DEVICE if
+ * the launch fails.  Faults during execution surface at the caller's next
+ * synchronisation.  A problem with no work items returns BSA_OK at once. */
+bsa_status_t bsa_forward(const void* q, const void* k, const void* v, bsa_plan_t plan,
+                         void* out, float* lse, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* bsa_status_string(bsa_status_t status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* bsa_last_error(void);
+
+/* BSA_ABI_VERSION of the built library. */
+int32_t bsa_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSATTN_H */

@@ -1,0 +1,10 @@
+"""Test-infrastructure oracle for block-sparse flash attention (CPU, float64).
+
+Only tests, the smoke check and the benchmark's CPU-baseline leg use this
+package.  The product package never imports it.
+"""
+from .bsa_oracle import (FULL, PARTIAL, allowed_count, allowed_keys, attend_row,
+                         forward, plan, tile_counts)
+
+__all__ = ["FULL", "PARTIAL", "allowed_count", "allowed_keys", "attend_row",
+           "forward", "plan", "tile_counts"]

@@ -1,0 +1,298 @@
+"""Reference oracle for block-sparse flash attention (forward).
+
+TEST INFRASTRUCTURE ONLY.  This module is a plain, slow, obviously-correct CPU
+implementation used to check the HIP path.  Only the test suite, the smoke
+check and the benchmark's CPU-baseline leg may import it; the product path
+(`block_sparse_flash_bsa_amd`) never does, and it shares no code with it.
+
+What it computes (all arithmetic in float64 with numpy):
+
+* `allowed_keys(layout, N, bs, h, q)` -- the set A(q) of keys query q of head h
+  may attend to.  The layout is either a window/global/causal spec or a block
+  bitmap.  Sources: section "How Does Flash-MSA Sparse Attention Work?" of
+  "How Do Sparse Attention Kernels Work in GPU Clusters?" (a boolean mask of
+  shape (N_blocks, N_blocks); whole blocks are in or out); the sliding-window
+  mask |i-j| <= W and the causal window in "The Mechanics", and global tokens
+  that both see and are seen by every position in "Global Tokens" under
+  "Sparse Patterns Beyond Sliding Windows", both on "Flash MSA Sparse
+  Attention vs Full Attention".
+  Readings where the pages are silent or disagree (inclusive window distances,
+  token vs block units, global keys and global queries as separate knobs,
+  causal always token-exact) are listed in the design notes.
+
+* `forward(Q, K, V, layout, block_size)` -- masked softmax attention written
+  as its definition: for every (b, h, q), s_k = scale * <Q[q], K[k]> over
+  k in A(q), m = max s_k, l = sum exp(s_k - m), O = sum exp(s_k - m) V[k] / l,
+  LSE = m + ln l.  Attention formula: softmax(QK^T / sqrt(d_k)) V ("The
+  Mechanics", Flash MSA Sparse Attention vs Full Attention; the naive masked
+  version in "How Sparse Attention Kernels Actually Speed Up Inference" on
+  "Sparse Attention Kernels vs Full Attention Performance").  The flash/online
+  formulation on the pages reaches exactly this result (it only avoids
+  materialising the scores), so the oracle is the definition, not the tiled
+  algorithm.  An empty A(q) gives O = 0 and LSE = -inf (log of an empty sum).
+  GQA: query head h reads KV head h // (H / Hkv).
+
+* `plan(layout, N, bs)` -- the per-query-block list of key blocks (step three
+  of "How Does Flash-MSA Sparse Attention Work?": a query block fetches only
+  its active key blocks; a mask given as block indices in "The Architecture
+  of Flash MSA Sparse Attention Kernels" on "Flash MSA Sparse Attention
+  Kernels Explained"): for each
+  (layout head, q-block i) the ascending key blocks j whose tile holds at
+  least one allowed (q, k) pair, each flagged FULL when every pair of the tile
+  is allowed and PARTIAL otherwise.  Counts are exact: brute force over the
+  tile for small problems, per-query interval overlap otherwise.
+
+Layout dictionary (plain Python, no dependency on the product package):
+    causal          bool   -- token-exact k <= q
+    unit            "tokens" | "blocks"  (units of the four fields below)
+    window_left     int    -- q - k <= window_left  (-1: unbounded)
+    window_right    int    -- k - q <= window_right (-1: unbounded)
+    global_keys     int    -- keys  < global_keys  are visible to every query
+    global_queries  int    -- queries < global_queries see every key
+    bitmap          None or uint8/bool array [layout_heads, nb, nb]; when set
+                    it replaces window/global (causal still applies)
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional, Tuple
+
+import numpy as np
+
+FULL = 0
+PARTIAL = 1
+
+
+# --------------------------------------------------------------------------
+# Layout predicate
+# --------------------------------------------------------------------------
+def _num_layout_heads(layout) -> int:
+    bm = layout.get("bitmap")
+    return 1 if bm is None else int(np.asarray(bm).shape[0])
+
+
+def _layout_head(layout, h: int) -> int:
+    """Layout head used by query head h: a shared layout or one per head."""
+    return 0 if _num_layout_heads(layout) == 1 else h
+
+
+def _token_pieces(layout, N: int, q: int):
+    """Allowed keys of query q for a token-unit spec as closed intervals.
+
+    The allowed set is (window(q) U globals) n causal(q), returned as the two
+    (possibly overlapping, possibly empty) intervals W n C and G n C, or the
+    single interval C for a global query.  lo > hi means empty.
+    """
+    wl = layout["window_left"]
+    wr = layout["window_right"]
+    hi_c = q if layout["causal"] else N - 1          # causal: k <= q
+    if q < layout["global_queries"]:                 # global query: every key
+        return [(0, hi_c)]
+    w_lo = 0 if wl < 0 else max(0, q - wl)
+    w_hi = N - 1 if wr < 0 else min(N - 1, q + wr)
+    return [(w_lo, min(w_hi, hi_c)), (0, min(layout["global_keys"] - 1, hi_c))]
+
+
+def _intervals_tokens(layout, N: int, q: int):
+    """Signed intervals whose overlap counts sum to |A(q) n block|.
+
+    Inclusion-exclusion over the two pieces keeps every term an interval:
+    |W u G| = |W| + |G| - |W n G|.  Returns (lo, hi, sign) triples.
+    """
+    pieces = _token_pieces(layout, N, q)
+    if len(pieces) == 1:
+        return [(pieces[0][0], pieces[0][1], 1)]
+    (a0, b0), (a1, b1) = pieces
+    return [(a0, b0, 1), (a1, b1, 1), (max(a0, a1), min(b0, b1), -1)]
+
+
+def _block_active(layout, lh: int, i: int, j: int) -> bool:
+    """Block-level part of the predicate for block-unit specs and bitmaps."""
+    bm = layout.get("bitmap")
+    if bm is not None:
+        return bool(np.asarray(bm)[lh, i, j])
+    wl = layout["window_left"]
+    wr = layout["window_right"]
+    in_w = (wl < 0 or i - j <= wl) and (wr < 0 or j - i <= wr)
+    return in_w or j < layout["global_keys"] or i < layout["global_queries"]
+
+
+def allowed_keys(layout, N: int, bs: int, h: int, q: int) -> np.ndarray:
+    """Sorted int64 array of the keys query q of head h may attend to."""
+    if layout.get("bitmap") is None and layout["unit"] == "tokens":
+        parts = [np.arange(lo, hi + 1) for lo, hi in _token_pieces(layout, N, q) if lo <= hi]
+        if not parts:
+            return np.zeros(0, dtype=np.int64)
+        return np.unique(np.concatenate(parts)).astype(np.int64)
+    lh = _layout_head(layout, h)
+    nb = N // bs
+    i = q // bs
+    blocks = [j for j in range(nb) if _block_active(layout, lh, i, j)]
+    if not blocks:
+        return np.zeros(0, dtype=np.int64)
+    keys = np.concatenate([np.arange(j * bs, (j + 1) * bs) for j in blocks])
+    if layout["causal"]:
+        keys = keys[keys <= q]
+    return keys.astype(np.int64)
+
+
+def allowed_count(layout, N: int, bs: int, h: int, q: int) -> int:
+    return int(allowed_keys(layout, N, bs, h, q).size)
+
+
+# --------------------------------------------------------------------------
+# Forward: masked softmax attention, per query over its allowed keys
+# --------------------------------------------------------------------------
+def _f64(x) -> np.ndarray:
+    """Exact upcast of a torch tensor (any float dtype) or array to float64."""
+    try:
+        import torch  # local import: the oracle also works on numpy inputs
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
+
+
+def attend_row(q_vec: np.ndarray, K_rows: np.ndarray, V_rows: np.ndarray,
+               scale: float) -> Tuple[np.ndarray, float]:
+    """One query against its allowed keys (already gathered), float64.
+
+    Returns (o, lse).  With no keys: o = 0, lse = -inf.
+    """
+    D = V_rows.shape[1] if V_rows.ndim == 2 else q_vec.shape[0]
+    if K_rows.shape[0] == 0:
+        return np.zeros(D), -math.inf
+    s = scale * (K_rows @ q_vec)
+    m = s.max()
+    w = np.exp(s - m)
+    l = w.sum()
+    o = (w @ V_rows) / l
+    return o, float(m + math.log(l))
+
+
+def forward(Q, K, V, layout, block_size: int, scale: Optional[float] = None,
+            rows: Optional[Iterable[Tuple[int, int, int]]] = None):
+    """Oracle forward.
+
+    Q: [B, H, N, D]; K, V: [B, Hkv, N, D]; numpy arrays or CPU torch tensors of
+    any float dtype (upcast exactly to float64).
+    rows: optional iterable of (b, h, q) to evaluate; default every row.  With
+    rows given only the rows and keys they touch are upcast, so full-size
+    inputs can be checked on a sample.
+    Returns (O, LSE) as float64 arrays: [B,H,N,D] / [B,H,N] when rows is None,
+    otherwise [R, D] / [R] in the order of `rows`.
+    """
+    B, H, N, D = (int(x) for x in Q.shape)
+    Hkv = int(K.shape[1])
+    assert H % Hkv == 0, "query heads must be a multiple of KV heads"
+    group = H // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    if rows is None:
+        Qd, Kd, Vd = _f64(Q), _f64(K), _f64(V)
+        O = np.zeros((B, H, N, D))
+        L = np.full((B, H, N), -math.inf)
+        for b in range(B):
+            for h in range(H):
+                hk = h // group
+                for q in range(N):
+                    keys = allowed_keys(layout, N, block_size, h, q)
+                    O[b, h, q], L[b, h, q] = attend_row(
+                        Qd[b, h, q], Kd[b, hk, keys], Vd[b, hk, keys], scale)
+        return O, L
+    rows = list(rows)
+    O = np.zeros((len(rows), D))
+    L = np.full(len(rows), -math.inf)
+    for r, (b, h, q) in enumerate(rows):
+        hk = h // group
+        keys = allowed_keys(layout, N, block_size, h, q)
+        O[r], L[r] = attend_row(_f64(Q[b, h, q]), _f64(K[b, hk][keys]),
+                                _f64(V[b, hk][keys]), scale)
+    return O, L
+
+
+# --------------------------------------------------------------------------
+# Plan oracle: per-q-block CSR list of key blocks with FULL/PARTIAL flags
+# --------------------------------------------------------------------------
+def _tile_counts_bruteforce(layout, N: int, bs: int, h: int, i: int) -> np.ndarray:
+    """Allowed-pair count of every tile (i, j) by enumerating A(q)."""
+    nb = N // bs
+    counts = np.zeros(nb, dtype=np.int64)
+    for q in range(i * bs, (i + 1) * bs):
+        keys = allowed_keys(layout, N, bs, h, q)
+        counts += np.bincount(keys // bs, minlength=nb)
+    return counts
+
+
+def _tile_counts_intervals(layout, N: int, bs: int, i: int) -> np.ndarray:
+    """Same counts for a token-unit spec, by interval overlap per query."""
+    nb = N // bs
+    counts = np.zeros(nb, dtype=np.int64)
+    full_mid = np.zeros(nb + 1, dtype=np.int64)      # difference array of whole-block runs
+    for q in range(i * bs, (i + 1) * bs):
+        for lo, hi, sign in _intervals_tokens(layout, N, q):
+            if lo > hi:
+                continue
+            ja, jb = lo // bs, hi // bs
+            if ja == jb:
+                counts[ja] += sign * (hi - lo + 1)
+                continue
+            counts[ja] += sign * ((ja + 1) * bs - lo)
+            counts[jb] += sign * (hi - jb * bs + 1)
+            if jb > ja + 1:
+                full_mid[ja + 1] += sign * bs
+                full_mid[jb] -= sign * bs
+    counts += np.cumsum(full_mid)[:nb]
+    return counts
+
+
+def _tile_counts_blocks(layout, N: int, bs: int, h: int, i: int) -> np.ndarray:
+    """Counts for block-unit specs and bitmaps: whole tiles, causal cuts the diagonal."""
+    nb = N // bs
+    lh = _layout_head(layout, h)
+    counts = np.zeros(nb, dtype=np.int64)
+    for j in range(nb):
+        if not _block_active(layout, lh, i, j):
+            continue
+        if not layout["causal"] or j < i:
+            counts[j] = bs * bs
+        elif j == i:
+            counts[j] = bs * (bs + 1) // 2           # pairs with k <= q inside the tile
+    return counts
+
+
+def tile_counts(layout, N: int, bs: int, h: int, i: int, brute: bool = False) -> np.ndarray:
+    if brute:
+        return _tile_counts_bruteforce(layout, N, bs, h, i)
+    if layout.get("bitmap") is None and layout["unit"] == "tokens":
+        return _tile_counts_intervals(layout, N, bs, i)
+    return _tile_counts_blocks(layout, N, bs, h, i)
+
+
+def plan(layout, N: int, bs: int, brute: Optional[bool] = None):
+    """CSR plan per layout head.
+
+    Returns a list (one per layout head) of dicts with int32 `row_ptr` [nb+1],
+    int32 `col_idx` [nnz] and uint8 `flags` [nnz] (0 = FULL, 1 = PARTIAL).
+    """
+    assert N % bs == 0, "sequence length must be a multiple of the block size"
+    nb = N // bs
+    if brute is None:
+        brute = N <= 1024
+    out = []
+    for lh in range(_num_layout_heads(layout)):
+        row_ptr = [0]
+        cols, flags = [], []
+        for i in range(nb):
+            c = tile_counts(layout, N, bs, lh, i, brute=brute)
+            js = np.flatnonzero(c > 0)
+            cols.extend(int(j) for j in js)
+            flags.extend(FULL if c[j] == bs * bs else PARTIAL for j in js)
+            row_ptr.append(len(cols))
+        out.append({
+            "row_ptr": np.asarray(row_ptr, dtype=np.int32),
+            "col_idx": np.asarray(cols, dtype=np.int32),
+            "flags": np.asarray(flags, dtype=np.uint8),
+        })
+    return out
