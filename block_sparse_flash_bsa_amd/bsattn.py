@@ -1,0 +1,244 @@
+"""ctypes binding over libbsattn (include/bsattn.h).
+
+Argument marshalling only: every step of the forward runs in the library's
+HIP kernels; PyTorch provides device memory and the current stream.
+
+    p = plan(batch=1, num_heads=32, num_kv_heads=32, seq_len=16384, head_dim=128,
+             block_size=128, dtype=torch.bfloat16,
+             layout=dict(causal=True, unit="tokens", window_left=511, window_right=0,
+                         global_keys=0, global_queries=0, bitmap=None))
+    out, lse = forward(q, k, v, p)
+
+The library is loaded on first use; if it has not been built the call raises
+(there is no fallback path).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from ctypes import POINTER, c_char_p, c_float, c_int32, c_int64, c_uint8, c_void_p
+from typing import Dict, Optional
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsattn.so")
+
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_OUT_OF_MEMORY, ERR_DEVICE = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+UNIT_TOKENS, UNIT_BLOCKS = 0, 1
+SCHEDULE_DEFAULT, SCHEDULE_XCD, SCHEDULE_LPT, SCHEDULE_ROWMAJOR = 0, 1, 2, 3
+
+# Every entry point include/bsattn.h declares.
+EXPORTS = ("bsa_plan", "bsa_plan_host", "bsa_plan_destroy", "bsa_plan_csr", "bsa_plan_get_info",
+           "bsa_plan_work", "bsa_plan_active_blocks", "bsa_forward", "bsa_status_string",
+           "bsa_last_error", "bsa_abi_version")
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("batch", c_int32), ("num_heads", c_int32), ("num_kv_heads", c_int32),
+                ("head_dim", c_int32), ("seq_len", c_int64), ("block_size", c_int32),
+                ("dtype", c_int32), ("scale", c_float), ("schedule", c_int32)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("causal", c_int32), ("unit", c_int32), ("window_left", c_int64),
+                ("window_right", c_int64), ("global_keys", c_int64), ("global_queries", c_int64),
+                ("bitmap", POINTER(c_uint8)), ("bitmap_heads", c_int32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("layout_heads", c_int32), ("num_blocks", c_int32), ("nnz", c_int64),
+                ("nnz_partial", c_int64), ("active_blocks", c_int64), ("allowed_pairs", c_int64),
+                ("work_items", c_int64), ("launch_slots", c_int64), ("max_row_entries", c_int32),
+                ("on_device", c_int32)]
+
+
+class BsaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.detail = detail
+        super().__init__(f"{_status_name(status)}: {detail}")
+
+
+_lib = None
+
+
+def lib():
+    """Load libbsattn.so once; raise if it is missing (no fallback)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libbsattn.so is not built ({LIB_PATH}); run "
+                           "`python -m block_sparse_flash_bsa_amd.build` or __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    P = c_void_p
+    L.bsa_plan.argtypes = [POINTER(Problem), POINTER(Layout), POINTER(P)]
+    L.bsa_plan_host.argtypes = [POINTER(Problem), POINTER(Layout), POINTER(P)]
+    L.bsa_plan_destroy.argtypes = [P]
+    L.bsa_plan_destroy.restype = None
+    L.bsa_plan_csr.argtypes = [P, c_int32, POINTER(POINTER(c_int32)), POINTER(POINTER(c_int32)),
+                               POINTER(POINTER(c_uint8)), POINTER(c_int64)]
+    L.bsa_plan_get_info.argtypes = [P, POINTER(PlanInfo)]
+    L.bsa_plan_work.argtypes = [P, POINTER(POINTER(c_int32)), POINTER(c_int64)]
+    L.bsa_plan_active_blocks.argtypes = [P]
+    L.bsa_plan_active_blocks.restype = c_int64
+    L.bsa_forward.argtypes = [c_void_p, c_void_p, c_void_p, P, c_void_p, c_void_p, c_void_p]
+    L.bsa_status_string.argtypes = [c_int32]
+    L.bsa_status_string.restype = c_char_p
+    L.bsa_last_error.argtypes = []
+    L.bsa_last_error.restype = c_char_p
+    L.bsa_abi_version.restype = c_int32
+    for name in ("bsa_plan", "bsa_plan_host", "bsa_plan_csr", "bsa_plan_get_info", "bsa_plan_work",
+                 "bsa_forward"):
+        getattr(L, name).restype = c_int32
+    _lib = L
+    return L
+
+
+def _status_name(status: int) -> str:
+    try:
+        return lib().bsa_status_string(status).decode()
+    except Exception:  # pragma: no cover - library not loadable
+        return f"status {status}"
+
+
+def _check(status: int):
+    if status != OK:
+        raise BsaError(status, lib().bsa_last_error().decode())
+
+
+def _dtype_code(dtype) -> int:
+    import torch
+    if dtype in (torch.bfloat16, "bf16", BF16):
+        return BF16
+    if dtype in (torch.float32, "f32", F32):
+        return F32
+    raise ValueError(f"unsupported dtype {dtype}")
+
+
+def make_layout(layout: Dict):
+    """Layout dict -> (ctypes Layout, keep-alive bitmap array)."""
+    bm = layout.get("bitmap")
+    arr = None
+    lay = Layout()
+    lay.causal = 1 if layout["causal"] else 0
+    lay.unit = {"tokens": UNIT_TOKENS, "blocks": UNIT_BLOCKS}[layout["unit"]]
+    lay.window_left = int(layout["window_left"])
+    lay.window_right = int(layout["window_right"])
+    lay.global_keys = int(layout["global_keys"])
+    lay.global_queries = int(layout["global_queries"])
+    if bm is not None:
+        if hasattr(bm, "numpy"):
+            bm = bm.detach().cpu().numpy()
+        arr = np.ascontiguousarray(np.asarray(bm) != 0, dtype=np.uint8)
+        if arr.ndim != 3:
+            raise ValueError("bitmap must have shape [bitmap_heads, nb, nb]")
+        lay.bitmap = arr.ctypes.data_as(POINTER(c_uint8))
+        lay.bitmap_heads = arr.shape[0]
+    else:
+        lay.bitmap = None
+        lay.bitmap_heads = 0
+    return lay, arr
+
+
+class Plan:
+    """Owns a bsa_plan_t; freed on close() or garbage collection."""
+
+    def __init__(self, handle: int, problem: Problem, host_only: bool):
+        self._h = c_void_p(handle)
+        self.problem = problem
+        self.host_only = host_only
+        info = PlanInfo()
+        _check(lib().bsa_plan_get_info(self._h, ctypes.byref(info)))
+        self.info = {name: getattr(info, name) for name, _ in PlanInfo._fields_}
+
+    @property
+    def handle(self):
+        if self._h is None or not self._h.value:
+            raise RuntimeError("plan has been destroyed")
+        return self._h
+
+    def csr(self, layout_head: int = 0):
+        rp, ci, fl = POINTER(c_int32)(), POINTER(c_int32)(), POINTER(c_uint8)()
+        nnz = c_int64()
+        _check(lib().bsa_plan_csr(self.handle, layout_head, ctypes.byref(rp), ctypes.byref(ci),
+                                  ctypes.byref(fl), ctypes.byref(nnz)))
+        nb = self.info["num_blocks"]
+        n = nnz.value
+        return {"row_ptr": np.ctypeslib.as_array(rp, (nb + 1,)).copy(),
+                "col_idx": np.ctypeslib.as_array(ci, (n,)).copy() if n else np.zeros(0, np.int32),
+                "flags": np.ctypeslib.as_array(fl, (n,)).copy() if n else np.zeros(0, np.uint8)}
+
+    def work(self):
+        w = POINTER(c_int32)()
+        n = c_int64()
+        _check(lib().bsa_plan_work(self.handle, ctypes.byref(w), ctypes.byref(n)))
+        return np.ctypeslib.as_array(w, (n.value,)).copy() if n.value else np.zeros(0, np.int32)
+
+    def active_blocks(self) -> int:
+        return int(lib().bsa_plan_active_blocks(self.handle))
+
+    def flops(self) -> float:
+        """Active-tile FLOPs of one forward: 2 GEMMs of block^2 x head_dim per tile."""
+        p = self.problem
+        return 4.0 * p.block_size * p.block_size * p.head_dim * self.active_blocks()
+
+    def close(self):
+        if self._h is not None and self._h.value:
+            lib().bsa_plan_destroy(self._h)
+        self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def make_problem(batch, num_heads, num_kv_heads, seq_len, head_dim, block_size, dtype,
+                 scale=0.0, schedule=SCHEDULE_DEFAULT) -> Problem:
+    pr = Problem()
+    pr.batch, pr.num_heads, pr.num_kv_heads, pr.head_dim = batch, num_heads, num_kv_heads, head_dim
+    pr.seq_len, pr.block_size, pr.dtype = seq_len, block_size, _dtype_code(dtype)
+    pr.scale, pr.schedule = float(scale), int(schedule)
+    return pr
+
+
+def plan(batch: int, num_heads: int, num_kv_heads: int, seq_len: int, head_dim: int,
+         block_size: int, dtype, layout: Dict, scale: float = 0.0,
+         schedule: int = SCHEDULE_DEFAULT, host_only: bool = False) -> Plan:
+    """bsa_plan (or bsa_plan_host) on the current HIP device."""
+    pr = make_problem(batch, num_heads, num_kv_heads, seq_len, head_dim, block_size, dtype,
+                      scale, schedule)
+    lay, keep = make_layout(layout)
+    h = c_void_p()
+    fn = lib().bsa_plan_host if host_only else lib().bsa_plan
+    _check(fn(ctypes.byref(pr), ctypes.byref(lay), ctypes.byref(h)))
+    del keep
+    return Plan(h.value, pr, host_only)
+
+
+def forward(q, k, v, p: Plan, out=None, lse=None):
+    """bsa_forward on torch.cuda.current_stream(); returns (out, lse)."""
+    import torch
+    pr = p.problem
+    B, H, Hk, N, D = pr.batch, pr.num_heads, pr.num_kv_heads, pr.seq_len, pr.head_dim
+    dt = torch.bfloat16 if pr.dtype == BF16 else torch.float32
+    for name, t, shape in (("q", q, (B, H, N, D)), ("k", k, (B, Hk, N, D)), ("v", v, (B, Hk, N, D))):
+        if not t.is_cuda or t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} CUDA tensor of shape {shape}, got "
+                             f"{tuple(t.shape)} {t.dtype} on {t.device}")
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=dt, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if tuple(out.shape) != (B, H, N, D) or out.dtype != dt or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError("out has the wrong shape, dtype or layout")
+    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
+        raise ValueError("lse must be a contiguous float32 CUDA tensor of shape (B, H, N)")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+        _check(lib().bsa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), p.handle,
+                                 out.data_ptr(), lse.data_ptr(), c_void_p(stream)))
+    return out, lse

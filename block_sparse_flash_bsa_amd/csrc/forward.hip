@@ -1,0 +1,428 @@
+// Block-sparse flash attention forward kernels for gfx950 (CDNA4) and the
+// bsa_forward launcher.
+//
+// One workgroup owns one (batch, head, q-block) item of the plan's launch
+// order and walks that q-block's CSR list of key blocks: fetch K/V block j,
+// scores on the tile, online-softmax update, accumulate P.V; finally write
+// O = acc / l and LSE = m + ln l.  That is the block-sparse FlashAttention
+// procedure of "How Does Flash-MSA Sparse Attention Work?" (How Do Sparse
+// Attention Kernels Work in GPU Clusters?) with the running max / running sum
+// recurrence of "The Mechanics" (Flash MSA Sparse Attention vs Full
+// Attention); only the active tiles are ever computed and no score matrix is
+// stored.  Token masks are evaluated only in tiles the plan flags PARTIAL.
+//
+// bf16 kernel (head_dim 128, block 128): 4 waves x 32 query rows.  Scores are
+// computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16, so that
+// each lane holds one query row: the row max and row sum are in-lane plus a
+// single exchange between lanes l and l + 32.  O^T = V^T P^T keeps that
+// layout, so the per-row rescale is a per-lane scalar.  K is staged in LDS
+// row-major; V is staged transposed (V^T), with the key order inside each
+// 16-key chunk permuted so that every MFMA operand is one 16-byte LDS read.
+// The softmax runs in the exp2 domain with a lazily updated reference max
+// (the accumulator is rescaled only when a row max grows by more than 2^8).
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "internal.h"
+
+namespace bsa {
+namespace {
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const RowDesc* rows;
+  const int32_t* entries;
+  const int32_t* work;
+  int64_t N;
+  int32_t H, Hkv, group, nb, per_head_layout;
+  float sl2;  // scale * log2(e)
+  int32_t causal, token_rule;
+  int64_t wl, wr, gk, gq;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Token-level predicate inside a PARTIAL tile.  With token_rule == 0 the
+// window/global part is uniform over the tile and already true for every
+// planned tile, so only causality remains.
+__device__ __forceinline__ bool allowed(const FwdParams& p, int64_t q, int64_t k) {
+  if (p.causal && k > q) return false;
+  if (!p.token_rule) return true;
+  const bool in_w = (p.wl < 0 || q - k <= p.wl) && (p.wr < 0 || k - q <= p.wr);
+  return in_w || k < p.gk || q < p.gq;
+}
+
+__device__ __forceinline__ void decode(const FwdParams& p, int item, int& b, int& h, int& i) {
+  i = item % p.nb;
+  const int bh = item / p.nb;
+  h = bh % p.H;
+  b = bh / p.H;
+}
+
+// ---------------------------------------------------------------------------
+// bf16, head_dim 128, block 128: MFMA kernel
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBM = 128;        // query rows per workgroup (= layout block)
+constexpr int kBN = 128;        // keys per CSR entry (= layout block)
+constexpr int kD = 128;         // head dim
+constexpr int kThreads = 256;   // 4 waves of 64
+constexpr int kKS = kD + 8;     // K row stride in LDS (elements): 272 B, conflict-free 16 B reads
+constexpr int kVS = kBN + 8;    // V^T row stride in LDS (elements)
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * kKS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[kD * kVS];
+
+  const int item = p.work[blockIdx.x];
+  if (item < 0) return;
+  int b, h, i;
+  decode(p, item, b, h, i);
+  const int hk = h / p.group;
+  const RowDesc row = p.rows[(p.per_head_layout ? h : 0) * p.nb + i];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63, r32 = lane & 31, hf = lane >> 5;
+  const int qrow = wave * 32 + r32;                       // row within the q-block
+  const int64_t qg = int64_t(i) * kBM + qrow;             // global query index
+
+  const uint16_t* __restrict__ Qp =
+      static_cast<const uint16_t*>(p.q) + ((int64_t(b) * p.H + h) * p.N + qg) * kD;
+  const uint16_t* __restrict__ Kb =
+      static_cast<const uint16_t*>(p.k) + (int64_t(b) * p.Hkv + hk) * p.N * kD;
+  const uint16_t* __restrict__ Vb =
+      static_cast<const uint16_t*>(p.v) + (int64_t(b) * p.Hkv + hk) * p.N * kD;
+
+  // Q^T operand: lane (row r32, half hf) holds d = 16c + 8hf .. +7 for c = 0..7.
+  bf16x8 qf[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(Qp + c * 16 + hf * 8);
+
+  // K/V staging registers.  K: thread loads rows (tid>>4) + 16u, 16 B column tid&15.
+  // V: thread loads key quads (tid>>4) and (tid>>4) + 16, 4 rows each, same column.
+  u32x4 kr[8], vr[8];
+  const int col8 = (tid & 15) * 8;
+  auto load_kv = [&](int j) {
+    const uint16_t* kp = Kb + int64_t(j) * kBN * kD;
+    const uint16_t* vp = Vb + int64_t(j) * kBN * kD;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      kr[u] = *reinterpret_cast<const u32x4*>(kp + ((tid >> 4) + 16 * u) * kD + col8);
+#pragma unroll
+    for (int qd = 0; qd < 2; ++qd)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        vr[qd * 4 + r] =
+            *reinterpret_cast<const u32x4*>(vp + (4 * ((tid >> 4) + 16 * qd) + r) * kD + col8);
+  };
+  auto store_kv = [&]() {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      *reinterpret_cast<u32x4*>(Ks + ((tid >> 4) + 16 * u) * kKS + col8) = kr[u];
+#pragma unroll
+    for (int qd = 0; qd < 2; ++qd) {
+      // Keys 4*quad .. 4*quad+3 go to positions pos .. pos+3 of their 16-key
+      // chunk; quads 0,1,2,3 of a chunk land at offsets 0, 8, 4, 12.
+      const int quad = (tid >> 4) + 16 * qd;
+      const int pos = 16 * (quad >> 2) + ((quad & 1) << 3) + ((quad & 2) << 1);
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const uint32_t w0 = vr[qd * 4 + 0][dd >> 1], w1 = vr[qd * 4 + 1][dd >> 1];
+        const uint32_t w2 = vr[qd * 4 + 2][dd >> 1], w3 = vr[qd * 4 + 3][dd >> 1];
+        u32x2 pk;
+        if (dd & 1) {
+          pk[0] = (w0 >> 16) | (w1 & 0xffff0000u);
+          pk[1] = (w2 >> 16) | (w3 & 0xffff0000u);
+        } else {
+          pk[0] = (w0 & 0xffffu) | (w1 << 16);
+          pk[1] = (w2 & 0xffffu) | (w3 << 16);
+        }
+        *reinterpret_cast<u32x2*>(Vt + (col8 + dd) * kVS + pos) = pk;
+      }
+    }
+  };
+
+  f32x16 o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
+  float m_ref = -INFINITY;   // reference max (log2 domain, scaled)
+  float l_part = 0.f;        // this lane's share of the row sum
+  const float c = p.sl2;
+
+  const int e0 = row.start, ne = row.count;
+  if (ne > 0) load_kv(p.entries[e0] >> 1);
+  for (int e = 0; e < ne; ++e) {
+    const int ent = p.entries[e0 + e];
+    const int j = ent >> 1;
+    const bool partial = ent & 1;
+    __syncthreads();           // every wave is done with the previous tile
+    store_kv();
+    __syncthreads();
+    if (e + 1 < ne) load_kv(p.entries[e0 + e + 1] >> 1);
+
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // S^T for 64 keys: two 32x32 tiles; lane holds row r32, keys
+      // 32*kt + 8*(r/4) + 4*hf + r%4 for accumulator register r.
+      f32x16 s[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        s[t] = f32x16{};
+        const int kt = half * 2 + t;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (kt * 32 + r32) * kKS + cc * 16 + hf * 8);
+          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], s[t], 0, 0, 0);
+        }
+      }
+      if (partial) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int64_t kg = int64_t(j) * kBN + (half * 2 + t) * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (!allowed(p, qg, kg)) s[t][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = mx * c;
+      if (__any(m_new > m_ref + 8.f)) {
+        const float m_t = fmaxf(m_ref, m_new);
+        const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_t);
+        l_part *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+        m_ref = m_t;
+      }
+      const float msub = (m_ref == -INFINITY) ? 0.f : m_ref;
+      // P in bf16.  Accumulator registers 8q .. 8q+7 of tile t are exactly the
+      // 8 keys this lane supplies for 16-key chunk 2t + q of the P.V product.
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+          for (int ii = 0; ii < 8; ++ii) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[t][q2 * 8 + ii], c, -msub));
+            l_part += pv;
+            pb[t][q2][ii] = static_cast<__bf16>(pv);
+          }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2) {
+            const int c16 = (half * 2 + t) * 2 + q2;
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vt + (dt * 32 + r32) * kVS + c16 * 16 + hf * 8);
+            o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t][q2], o[dt], 0, 0, 0);
+          }
+    }
+  }
+
+  // Epilogue: O = acc / l (0 for an empty row), LSE = ln2 * (m_ref + log2 l).
+  const float l = l_part + __shfl_xor(l_part, 32);
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  uint16_t* Op = static_cast<uint16_t*>(p.o) + ((int64_t(b) * p.H + h) * p.N + qg) * kD;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 pk;
+      pk[0] = uint32_t(bf16_bits(o[dt][4 * g + 0] * inv)) | (uint32_t(bf16_bits(o[dt][4 * g + 1] * inv)) << 16);
+      pk[1] = uint32_t(bf16_bits(o[dt][4 * g + 2] * inv)) | (uint32_t(bf16_bits(o[dt][4 * g + 3] * inv)) << 16);
+      *reinterpret_cast<u32x2*>(Op + dt * 32 + 8 * g + 4 * hf) = pk;
+    }
+  if (hf == 0)
+    p.lse[(int64_t(b) * p.H + h) * p.N + qg] = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
+}
+
+// ---------------------------------------------------------------------------
+// float32 kernel (head_dim 64/128, block 64/128): exact fp32 FMA on the VALU.
+// One thread per query row; K/V tiles staged through LDS in 64-key stages.
+// ---------------------------------------------------------------------------
+template <int D, int BS>
+__global__ __launch_bounds__(BS) void fwd_f32(FwdParams p) {
+  constexpr int KT = BS < 64 ? BS : 64;  // keys per LDS stage
+  constexpr int QS = D + 1;              // padded Q row stride (conflict-free per-thread rows)
+  extern __shared__ float smem[];
+  float* Qs = smem;                      // [BS][QS]
+  float* Ks = Qs + BS * QS;              // [KT][D]
+  float* Vs = Ks + KT * D;               // [KT][D]
+
+  const int item = p.work[blockIdx.x];
+  if (item < 0) return;
+  int b, h, i;
+  decode(p, item, b, h, i);
+  const int hk = h / p.group;
+  const RowDesc row = p.rows[(p.per_head_layout ? h : 0) * p.nb + i];
+  const int t = threadIdx.x;
+  const int64_t q0 = int64_t(i) * BS;
+  const int64_t qg = q0 + t;
+
+  const float* Qp = static_cast<const float*>(p.q) + ((int64_t(b) * p.H + h) * p.N + q0) * D;
+  const float* Kb = static_cast<const float*>(p.k) + (int64_t(b) * p.Hkv + hk) * p.N * D;
+  const float* Vb = static_cast<const float*>(p.v) + (int64_t(b) * p.Hkv + hk) * p.N * D;
+  for (int x = t; x < BS * D; x += BS) Qs[(x / D) * QS + (x % D)] = Qp[x];
+
+  float acc[D];
+#pragma unroll
+  for (int d = 0; d < D; ++d) acc[d] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const float c = p.sl2;
+  const float* qr = Qs + t * QS;
+
+  for (int e = 0; e < row.count; ++e) {
+    const int ent = p.entries[row.start + e];
+    const int j = ent >> 1;
+    const bool partial = ent & 1;
+    for (int st = 0; st < BS / KT; ++st) {
+      const int64_t k0 = int64_t(j) * BS + st * KT;
+      __syncthreads();
+      for (int x = t; x < KT * D; x += BS) {
+        Ks[x] = Kb[k0 * D + x];
+        Vs[x] = Vb[k0 * D + x];
+      }
+      __syncthreads();
+      for (int kc = 0; kc < KT; kc += 16) {
+        float s[16];
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          const float* kr = Ks + (kc + kk) * D;
+          float a = 0.f;
+#pragma unroll 16
+          for (int d = 0; d < D; ++d) a = fmaf(qr[d], kr[d], a);
+          s[kk] = (partial && !allowed(p, qg, k0 + kc + kk)) ? -INFINITY : a * c;
+        }
+        float mx = m;
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) mx = fmaxf(mx, s[kk]);
+        if (mx > m) {
+          const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mx);
+          l *= alpha;
+#pragma unroll
+          for (int d = 0; d < D; ++d) acc[d] *= alpha;
+          m = mx;
+        }
+        const float msub = (m == -INFINITY) ? 0.f : m;
+#pragma unroll
+        for (int kk = 0; kk < 16; ++kk) {
+          const float pv = __builtin_amdgcn_exp2f(s[kk] - msub);
+          l += pv;
+          const float* vr = Vs + (kc + kk) * D;
+#pragma unroll
+          for (int d = 0; d < D; ++d) acc[d] = fmaf(pv, vr[d], acc[d]);
+        }
+      }
+    }
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  float* Op = static_cast<float*>(p.o) + ((int64_t(b) * p.H + h) * p.N + qg) * D;
+#pragma unroll
+  for (int d = 0; d < D; ++d) Op[d] = acc[d] * inv;
+  p.lse[(int64_t(b) * p.H + h) * p.N + qg] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+}
+
+template <int D, int BS>
+constexpr size_t f32_smem_bytes() {
+  return size_t(BS * (D + 1) + 2 * (BS < 64 ? BS : 64) * D) * sizeof(float);
+}
+
+template <int D, int BS>
+hipError_t launch_f32(const FwdParams& prm, int64_t slots, hipStream_t stream) {
+  constexpr size_t smem = f32_smem_bytes<D, BS>();
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_f32<D, BS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((fwd_f32<D, BS>), dim3(unsigned(slots)), dim3(BS), smem, stream, prm);
+  return hipGetLastError();
+}
+
+}  // namespace
+}  // namespace bsa
+
+extern "C" bsa_status_t bsa_forward(const void* q, const void* k, const void* v, bsa_plan_t plan,
+                                    void* out, float* lse, void* stream) {
+  using namespace bsa;
+  clear_error();
+  if (!plan) return fail(BSA_ERR_INVALID_ARGUMENT, "plan must not be NULL");
+  if (!plan->info.on_device)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "plan was built by bsa_plan_host and has no device copy");
+  const int64_t slots = plan->info.launch_slots;
+  if (plan->info.work_items == 0) return BSA_OK;
+  if (!q || !k || !v || !out || !lse)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v, out and lse must all be non-NULL");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(BSA_ERR_DEVICE, "hipGetDevice failed");
+  if (dev != plan->device)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "plan was built on device %d but device %d is current",
+                plan->device, dev);
+  const bsa_problem_t& pr = plan->prob;
+  FwdParams prm;
+  prm.q = q;
+  prm.k = k;
+  prm.v = v;
+  prm.o = out;
+  prm.lse = lse;
+  prm.rows = plan->d_rows;
+  prm.entries = plan->d_entries;
+  prm.work = plan->d_work;
+  prm.N = pr.seq_len;
+  prm.H = pr.num_heads;
+  prm.Hkv = pr.num_kv_heads;
+  prm.group = pr.num_heads / pr.num_kv_heads;
+  prm.nb = plan->nb;
+  prm.per_head_layout = plan->layout_heads > 1 ? 1 : 0;
+  prm.sl2 = pr.scale * kLog2e;
+  prm.causal = plan->causal;
+  prm.token_rule = plan->token_rule;
+  prm.wl = plan->wl;
+  prm.wr = plan->wr;
+  prm.gk = plan->gk;
+  prm.gq = plan->gq;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t err = hipSuccess;
+  if (pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128) {
+    hipLaunchKernelGGL(fwd_bf16_d128, dim3(unsigned(slots)), dim3(kThreads), 0, s, prm);
+    err = hipGetLastError();
+  } else if (pr.dtype == BSA_F32 && pr.head_dim == 64 && pr.block_size == 64) {
+    err = launch_f32<64, 64>(prm, slots, s);
+  } else if (pr.dtype == BSA_F32 && pr.head_dim == 64 && pr.block_size == 128) {
+    err = launch_f32<64, 128>(prm, slots, s);
+  } else if (pr.dtype == BSA_F32 && pr.head_dim == 128 && pr.block_size == 64) {
+    err = launch_f32<128, 64>(prm, slots, s);
+  } else if (pr.dtype == BSA_F32 && pr.head_dim == 128 && pr.block_size == 128) {
+    err = launch_f32<128, 128>(prm, slots, s);
+  } else {
+    return fail(BSA_ERR_UNSUPPORTED, "no kernel for this (dtype, head_dim, block_size)");
+  }
+  if (err != hipSuccess) return fail(BSA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
+  return BSA_OK;
+}

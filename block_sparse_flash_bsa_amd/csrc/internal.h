@@ -1,0 +1,56 @@
+// Internal definitions shared by the host planner and the forward launcher.
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "bsattn.h"
+
+namespace bsa {
+
+// Device row descriptor: entries [start, start + count) of the entry array.
+struct RowDesc {
+  int32_t start;
+  int32_t count;
+};
+
+// Entry encoding in device memory: (key block << 1) | partial.
+inline int32_t encode_entry(int32_t j, bool partial) { return (j << 1) | (partial ? 1 : 0); }
+
+// Record a failure detail for bsa_last_error() and return `status`.
+bsa_status_t fail(bsa_status_t status, const char* fmt, ...);
+void clear_error();
+
+// Supported kernel instantiations (dtype, head_dim, block_size).
+bool kernel_supported(int32_t dtype, int32_t head_dim, int32_t block_size);
+
+}  // namespace bsa
+
+struct bsa_plan {
+  bsa_problem_t prob{};        // scale resolved to its effective value
+  // Token-level mask parameters for PARTIAL tiles.  When token_rule is 0 the
+  // window/global part of the predicate is uniform over every tile (block
+  // units or a bitmap), so only the causal cut is applied inside a tile.
+  int32_t causal = 0;
+  int32_t token_rule = 0;
+  int64_t wl = -1, wr = -1, gk = 0, gq = 0;
+  int32_t layout_heads = 1;
+  int32_t nb = 0;
+  std::vector<std::vector<int32_t>> row_ptr;   // [layout_heads][nb + 1]
+  std::vector<std::vector<int32_t>> col_idx;   // [layout_heads][nnz_h]
+  std::vector<std::vector<uint8_t>> flags;     // [layout_heads][nnz_h]
+  std::vector<int32_t> work;                   // [launch slots], -1 = idle
+  bsa_plan_info_t info{};
+  // Device copy (bsa_plan only).
+  int device = -1;
+  void* dev_mem = nullptr;
+  const bsa::RowDesc* d_rows = nullptr;        // [layout_heads * nb]
+  const int32_t* d_entries = nullptr;          // [nnz]
+  const int32_t* d_work = nullptr;             // [launch slots]
+};
+
+namespace bsa {
+// The C function bsa_plan() hides the struct tag in C++; use this alias.
+using Plan = struct ::bsa_plan;
+}  // namespace bsa

@@ -1,0 +1,416 @@
+// Host planner: layout spec or block bitmap -> per-q-block CSR of key blocks
+// with exact FULL/PARTIAL flags, plus the workgroup launch order.
+//
+// A query block walks only the key blocks its layout admits (step three of
+// "How Does Flash-MSA Sparse Attention Work?", How Do Sparse Attention Kernels
+// Work in GPU Clusters?).  The lists are built once on the host so the kernel
+// never evaluates the layout per element except inside PARTIAL tiles (the
+// precomputed-offsets advice in the FAQ of the same page).  Uneven row lengths
+// make the forward a load-balancing problem (section "Distributed Training and
+// Sparse Attention" of Flash MSA Sparse Attention Kernels Explained; "When
+// Sparse Kernels Break" of the GPU-clusters page suggests grouping queries by
+// how much work they have): the work order below balances cost per XCD.
+#include <hip/hip_runtime_api.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <numeric>
+
+#include "internal.h"
+
+namespace bsa {
+
+static thread_local std::string g_last_error;
+
+bsa_status_t fail(bsa_status_t status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+void clear_error() { g_last_error.clear(); }
+
+bool kernel_supported(int32_t dtype, int32_t head_dim, int32_t block_size) {
+  if (dtype == BSA_BF16) return head_dim == 128 && block_size == 128;
+  if (dtype == BSA_F32)
+    return (head_dim == 64 || head_dim == 128) && (block_size == 64 || block_size == 128);
+  return false;
+}
+
+namespace {
+
+constexpr int kNumXcd = 8;  // MI355X: 8 XCDs; workgroup w is dispatched to XCD w % 8
+
+struct TokenRule {
+  bool causal;
+  int64_t N, wl, wr, gk, gq;
+
+  // |A(q) n [k0, k1]| for one query, by inclusion-exclusion over the window
+  // interval W and the global-key prefix G, both cut by causality.
+  int64_t count(int64_t q, int64_t k0, int64_t k1) const {
+    const int64_t hi = causal ? std::min(q, k1) : k1;
+    if (hi < k0) return 0;
+    if (q < gq) return hi - k0 + 1;
+    const int64_t w_lo = std::max(k0, wl < 0 ? int64_t(0) : q - wl);
+    const int64_t w_hi = std::min(hi, wr < 0 ? N - 1 : q + wr);
+    const int64_t g_hi = std::min(hi, gk - 1);
+    auto len = [](int64_t a, int64_t b) { return b >= a ? b - a + 1 : int64_t(0); };
+    return len(w_lo, w_hi) + len(k0, g_hi) - len(w_lo, std::min(w_hi, g_hi));
+  }
+};
+
+// Pair count of tile (i, j) for a token-unit spec.  O(1) when the tile is
+// wholly inside the allowed region, else one interval count per query.
+int64_t tile_count_tokens(const TokenRule& r, int64_t bs, int64_t i, int64_t j) {
+  const int64_t q0 = i * bs, q1 = q0 + bs - 1, k0 = j * bs, k1 = k0 + bs - 1;
+  const bool causal_full = !r.causal || k1 <= q0;
+  if (causal_full) {
+    const bool win_full = (r.wl < 0 || q1 - k0 <= r.wl) && (r.wr < 0 || k1 - q0 <= r.wr);
+    if (win_full || k1 < r.gk || q1 < r.gq) return bs * bs;
+  }
+  int64_t c = 0;
+  for (int64_t q = q0; q <= q1; ++q) c += r.count(q, k0, k1);
+  return c;
+}
+
+bool block_rule(const bsa_layout_t& L, int64_t i, int64_t j) {
+  const bool in_w = (L.window_left < 0 || i - j <= L.window_left) &&
+                    (L.window_right < 0 || j - i <= L.window_right);
+  return in_w || j < L.global_keys || i < L.global_queries;
+}
+
+bsa_status_t validate(const bsa_problem_t* p, const bsa_layout_t* L) {
+  if (!p || !L) return fail(BSA_ERR_INVALID_ARGUMENT, "problem and layout must not be NULL");
+  if (p->batch < 0) return fail(BSA_ERR_INVALID_ARGUMENT, "batch must be >= 0 (got %d)", p->batch);
+  if (p->num_heads < 1 || p->num_kv_heads < 1)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "num_heads and num_kv_heads must be >= 1 (got %d, %d)",
+                p->num_heads, p->num_kv_heads);
+  if (p->num_heads % p->num_kv_heads != 0)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "num_heads (%d) must be a multiple of num_kv_heads (%d)",
+                p->num_heads, p->num_kv_heads);
+  if (p->dtype != BSA_F32 && p->dtype != BSA_BF16)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "dtype must be BSA_F32 or BSA_BF16 (got %d)", p->dtype);
+  if (p->head_dim < 1 || p->block_size < 1)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "head_dim and block_size must be >= 1 (got %d, %d)",
+                p->head_dim, p->block_size);
+  if (p->seq_len < 0 || p->seq_len % p->block_size != 0)
+    return fail(BSA_ERR_INVALID_ARGUMENT,
+                "seq_len (%lld) must be >= 0 and a multiple of block_size (%d); pad the sequence",
+                (long long)p->seq_len, p->block_size);
+  if (!(std::isfinite(p->scale) && p->scale >= 0.f))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "scale must be 0 (default) or finite and > 0");
+  if (p->schedule < BSA_SCHEDULE_DEFAULT || p->schedule > BSA_SCHEDULE_ROWMAJOR)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "unknown schedule %d", p->schedule);
+  if (L->causal != 0 && L->causal != 1)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "causal must be 0 or 1 (got %d)", L->causal);
+  if (L->unit != BSA_UNIT_TOKENS && L->unit != BSA_UNIT_BLOCKS)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "unit must be BSA_UNIT_TOKENS or BSA_UNIT_BLOCKS");
+  if (L->window_left < -1 || L->window_right < -1)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "window_left/right must be >= -1");
+  if (L->global_keys < 0 || L->global_queries < 0)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "global_keys/global_queries must be >= 0");
+  if (L->bitmap && L->bitmap_heads != 1 && L->bitmap_heads != p->num_heads)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "bitmap_heads must be 1 or num_heads (%d), got %d",
+                p->num_heads, L->bitmap_heads);
+  const int64_t nb = p->seq_len / p->block_size;
+  const int64_t items = int64_t(p->batch) * p->num_heads * nb;
+  if (items > INT32_MAX / 2 || nb > (INT32_MAX >> 2))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "problem too large: %lld work items", (long long)items);
+  if (!kernel_supported(p->dtype, p->head_dim, p->block_size))
+    return fail(BSA_ERR_UNSUPPORTED,
+                "no kernel for dtype=%s head_dim=%d block_size=%d (bf16: 128/128; f32: 64|128 / 64|128)",
+                p->dtype == BSA_BF16 ? "bf16" : "f32", p->head_dim, p->block_size);
+  return BSA_OK;
+}
+
+void build_csr(Plan& P, const bsa_layout_t& L) {
+  const int64_t bs = P.prob.block_size, nb = P.nb;
+  const TokenRule rule{L.causal != 0, P.prob.seq_len, L.window_left, L.window_right,
+                       L.global_keys, L.global_queries};
+  const bool tokens = !L.bitmap && L.unit == BSA_UNIT_TOKENS;
+  const int64_t full = bs * bs, diag = bs * (bs + 1) / 2;
+  P.row_ptr.assign(P.layout_heads, std::vector<int32_t>(nb + 1, 0));
+  P.col_idx.assign(P.layout_heads, {});
+  P.flags.assign(P.layout_heads, {});
+  P.info.allowed_pairs = 0;
+  int64_t pairs_per_layout_head_sum = 0;
+  std::vector<int64_t> cand;
+  for (int lh = 0; lh < P.layout_heads; ++lh) {
+    auto& cols = P.col_idx[lh];
+    auto& flg = P.flags[lh];
+    const uint8_t* bm = L.bitmap ? L.bitmap + size_t(lh) * nb * nb : nullptr;
+    int64_t pairs = 0;
+    for (int64_t i = 0; i < nb; ++i) {
+      if (tokens) {
+        // Candidate key blocks: window span, global-key prefix, or all for a
+        // global query row; causality caps them at the diagonal.
+        cand.clear();
+        const int64_t jmax = L.causal ? i : nb - 1;
+        if (i * bs < L.global_queries) {
+          for (int64_t j = 0; j <= jmax; ++j) cand.push_back(j);
+        } else {
+          const int64_t klo = L.window_left < 0 ? 0 : std::max<int64_t>(0, i * bs - L.window_left);
+          const int64_t khi = L.window_right < 0 ? P.prob.seq_len - 1
+                                                 : std::min(P.prob.seq_len - 1, (i + 1) * bs - 1 + L.window_right);
+          const int64_t gblocks = (L.global_keys + bs - 1) / bs;
+          for (int64_t j = 0; j < std::min(gblocks, nb); ++j) cand.push_back(j);
+          for (int64_t j = klo / bs; j <= khi / bs; ++j) cand.push_back(j);
+          std::sort(cand.begin(), cand.end());
+          cand.erase(std::unique(cand.begin(), cand.end()), cand.end());
+          while (!cand.empty() && cand.back() > jmax) cand.pop_back();
+        }
+        for (int64_t j : cand) {
+          const int64_t c = tile_count_tokens(rule, bs, i, j);
+          if (c == 0) continue;
+          cols.push_back(int32_t(j));
+          flg.push_back(c == full ? 0 : 1);
+          pairs += c;
+        }
+      } else {
+        for (int64_t j = 0; j < nb; ++j) {
+          const bool on = bm ? bm[i * nb + j] != 0 : block_rule(L, i, j);
+          if (!on) continue;
+          const int64_t c = (!L.causal || j < i) ? full : (j == i ? diag : 0);
+          if (c == 0) continue;
+          cols.push_back(int32_t(j));
+          flg.push_back(c == full ? 0 : 1);
+          pairs += c;
+        }
+      }
+      P.row_ptr[lh][i + 1] = int32_t(cols.size());
+    }
+    pairs_per_layout_head_sum += pairs;
+  }
+  int64_t nnz = 0, npart = 0, row_max = 0;
+  for (int lh = 0; lh < P.layout_heads; ++lh) {
+    nnz += int64_t(P.col_idx[lh].size());
+    for (uint8_t f : P.flags[lh]) npart += f;
+    for (int64_t i = 0; i < nb; ++i)
+      row_max = std::max<int64_t>(row_max, P.row_ptr[lh][i + 1] - P.row_ptr[lh][i]);
+  }
+  // Every query head uses layout head 0 when the layout is shared.
+  const int64_t head_mult = P.layout_heads == 1 ? P.prob.num_heads : 1;
+  P.info.layout_heads = P.layout_heads;
+  P.info.num_blocks = int32_t(nb);
+  P.info.nnz = nnz;
+  P.info.nnz_partial = npart;
+  P.info.active_blocks = int64_t(P.prob.batch) * head_mult * nnz;
+  P.info.allowed_pairs = int64_t(P.prob.batch) * head_mult * pairs_per_layout_head_sum;
+  P.info.max_row_entries = int32_t(row_max);
+}
+
+// Launch order.  Item id = (b * H + h) * nb + i; cost = row length + 1.
+void build_work(Plan& P) {
+  const int64_t B = P.prob.batch, H = P.prob.num_heads, nb = P.nb;
+  const int64_t group = P.prob.num_heads / P.prob.num_kv_heads;
+  const int64_t items = B * H * nb;
+  auto cost = [&](int64_t item) -> int64_t {
+    const int64_t i = item % nb, h = (item / nb) % H;
+    const auto& rp = P.row_ptr[P.layout_heads == 1 ? 0 : h];
+    return int64_t(rp[i + 1] - rp[i]) + 1;
+  };
+  P.work.clear();
+  int schedule = P.prob.schedule == BSA_SCHEDULE_DEFAULT ? BSA_SCHEDULE_XCD : P.prob.schedule;
+  if (schedule == BSA_SCHEDULE_ROWMAJOR || items == 0) {
+    P.work.resize(items);
+    std::iota(P.work.begin(), P.work.end(), 0);
+  } else if (schedule == BSA_SCHEDULE_LPT) {
+    std::vector<int32_t> order(items);
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int32_t a, int32_t b) { return cost(a) > cost(b); });
+    P.work = std::move(order);
+  } else {
+    // Locality order: heads sharing a KV head and neighbouring q-blocks are
+    // adjacent, so the workgroups running together on one XCD read the same
+    // K/V blocks through that XCD's L2.
+    std::vector<int32_t> loc;
+    loc.reserve(items);
+    for (int64_t b = 0; b < B; ++b)
+      for (int64_t hk = 0; hk < H / group; ++hk)
+        for (int64_t i = 0; i < nb; ++i)
+          for (int64_t g = 0; g < group; ++g) loc.push_back(int32_t((b * H + hk * group + g) * nb + i));
+    // Cut it into one contiguous run per XCD with equal total cost.
+    int64_t total = 0;
+    for (int32_t it : loc) total += cost(it);
+    std::vector<std::vector<int32_t>> seg(kNumXcd);
+    int64_t acc = 0;
+    for (int32_t it : loc) {
+      const int64_t x = std::min<int64_t>(kNumXcd - 1, (acc * kNumXcd) / std::max<int64_t>(total, 1));
+      seg[x].push_back(it);
+      acc += cost(it);
+    }
+    size_t longest = 0;
+    for (auto& s : seg) longest = std::max(longest, s.size());
+    // Slot s = kNumXcd * r + x runs the r-th item of XCD x's run.
+    P.work.assign(longest * kNumXcd, -1);
+    for (int x = 0; x < kNumXcd; ++x)
+      for (size_t r = 0; r < seg[x].size(); ++r) P.work[r * kNumXcd + x] = seg[x][r];
+  }
+  P.info.work_items = items;
+  P.info.launch_slots = int64_t(P.work.size());
+}
+
+bsa_status_t upload(Plan& P) {
+  if (hipGetDevice(&P.device) != hipSuccess)
+    return fail(BSA_ERR_DEVICE, "hipGetDevice failed: no usable HIP device");
+  const size_t rows = size_t(P.layout_heads) * P.nb;
+  const size_t nnz = size_t(P.info.nnz);
+  const size_t slots = P.work.size();
+  const size_t off_entries = rows * sizeof(bsa::RowDesc);
+  const size_t off_work = (off_entries + nnz * sizeof(int32_t) + 255) & ~size_t(255);
+  const size_t bytes = off_work + slots * sizeof(int32_t) + 16;
+  std::vector<unsigned char> host(bytes, 0);
+  auto* rd = reinterpret_cast<bsa::RowDesc*>(host.data());
+  auto* en = reinterpret_cast<int32_t*>(host.data() + off_entries);
+  int32_t start = 0;
+  for (int lh = 0; lh < P.layout_heads; ++lh) {
+    for (int64_t i = 0; i < P.nb; ++i) {
+      const int32_t a = P.row_ptr[lh][i], b = P.row_ptr[lh][i + 1];
+      rd[size_t(lh) * P.nb + i] = {start + a, b - a};
+    }
+    for (size_t e = 0; e < P.col_idx[lh].size(); ++e)
+      en[start + e] = bsa::encode_entry(P.col_idx[lh][e], P.flags[lh][e] != 0);
+    start += int32_t(P.col_idx[lh].size());
+  }
+  if (slots) std::memcpy(host.data() + off_work, P.work.data(), slots * sizeof(int32_t));
+  hipError_t err = hipMalloc(&P.dev_mem, bytes);
+  if (err != hipSuccess) {
+    P.dev_mem = nullptr;
+    return fail(err == hipErrorOutOfMemory ? BSA_ERR_OUT_OF_MEMORY : BSA_ERR_DEVICE,
+                "hipMalloc(%zu) for the plan failed: %s", bytes, hipGetErrorString(err));
+  }
+  err = hipMemcpy(P.dev_mem, host.data(), bytes, hipMemcpyHostToDevice);
+  if (err != hipSuccess) {
+    (void)hipFree(P.dev_mem);
+    P.dev_mem = nullptr;
+    return fail(BSA_ERR_DEVICE, "plan upload failed: %s", hipGetErrorString(err));
+  }
+  auto* base = static_cast<unsigned char*>(P.dev_mem);
+  P.d_rows = reinterpret_cast<const bsa::RowDesc*>(base);
+  P.d_entries = reinterpret_cast<const int32_t*>(base + off_entries);
+  P.d_work = reinterpret_cast<const int32_t*>(base + off_work);
+  P.info.on_device = 1;
+  return BSA_OK;
+}
+
+bsa_status_t make_plan(const bsa_problem_t* problem, const bsa_layout_t* layout, bool dev,
+                       bsa_plan_t* out) {
+  bsa::clear_error();
+  if (!out) return fail(BSA_ERR_INVALID_ARGUMENT, "out_plan must not be NULL");
+  bsa_status_t st = validate(problem, layout);
+  if (st != BSA_OK) return st;
+  Plan* P = new (std::nothrow) Plan();
+  if (!P) return fail(BSA_ERR_OUT_OF_MEMORY, "host allocation of the plan failed");
+  try {
+    P->prob = *problem;
+    if (P->prob.scale == 0.f) P->prob.scale = 1.0f / std::sqrt(float(problem->head_dim));
+    P->nb = int32_t(problem->seq_len / problem->block_size);
+    P->layout_heads = layout->bitmap ? layout->bitmap_heads : 1;
+    P->causal = layout->causal;
+    P->token_rule = (!layout->bitmap && layout->unit == BSA_UNIT_TOKENS) ? 1 : 0;
+    if (P->token_rule) {
+      P->wl = layout->window_left;
+      P->wr = layout->window_right;
+      P->gk = layout->global_keys;
+      P->gq = layout->global_queries;
+    }
+    build_csr(*P, *layout);
+    build_work(*P);
+  } catch (const std::bad_alloc&) {
+    delete P;
+    return fail(BSA_ERR_OUT_OF_MEMORY, "host allocation while building the plan failed");
+  }
+  if (dev) {
+    st = upload(*P);
+    if (st != BSA_OK) {
+      delete P;
+      return st;
+    }
+  }
+  *out = P;
+  return BSA_OK;
+}
+
+}  // namespace
+}  // namespace bsa
+
+extern "C" {
+
+bsa_status_t bsa_plan(const bsa_problem_t* problem, const bsa_layout_t* layout, bsa_plan_t* out_plan) {
+  return bsa::make_plan(problem, layout, true, out_plan);
+}
+
+bsa_status_t bsa_plan_host(const bsa_problem_t* problem, const bsa_layout_t* layout,
+                           bsa_plan_t* out_plan) {
+  return bsa::make_plan(problem, layout, false, out_plan);
+}
+
+void bsa_plan_destroy(bsa_plan_t plan) {
+  if (!plan) return;
+  if (plan->dev_mem) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != plan->device) (void)hipSetDevice(plan->device);
+    (void)hipFree(plan->dev_mem);
+    if (cur != plan->device && cur >= 0) (void)hipSetDevice(cur);
+  }
+  delete plan;
+}
+
+bsa_status_t bsa_plan_csr(bsa_plan_t plan, int32_t layout_head, const int32_t** row_ptr,
+                          const int32_t** col_idx, const uint8_t** flags, int64_t* nnz) {
+  bsa::clear_error();
+  if (!plan || !row_ptr || !col_idx || !flags || !nnz)
+    return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "NULL argument to bsa_plan_csr");
+  if (layout_head < 0 || layout_head >= plan->layout_heads)
+    return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "layout_head %d out of range [0, %d)", layout_head,
+                     plan->layout_heads);
+  *row_ptr = plan->row_ptr[layout_head].data();
+  *col_idx = plan->col_idx[layout_head].data();
+  *flags = plan->flags[layout_head].data();
+  *nnz = int64_t(plan->col_idx[layout_head].size());
+  return BSA_OK;
+}
+
+bsa_status_t bsa_plan_get_info(bsa_plan_t plan, bsa_plan_info_t* info) {
+  bsa::clear_error();
+  if (!plan || !info) return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "NULL argument to bsa_plan_get_info");
+  *info = plan->info;
+  return BSA_OK;
+}
+
+bsa_status_t bsa_plan_work(bsa_plan_t plan, const int32_t** work, int64_t* slots) {
+  bsa::clear_error();
+  if (!plan || !work || !slots) return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "NULL argument to bsa_plan_work");
+  *work = plan->work.data();
+  *slots = int64_t(plan->work.size());
+  return BSA_OK;
+}
+
+int64_t bsa_plan_active_blocks(bsa_plan_t plan) { return plan ? plan->info.active_blocks : -1; }
+
+const char* bsa_status_string(bsa_status_t s) {
+  switch (s) {
+    case BSA_OK: return "BSA_OK";
+    case BSA_ERR_INVALID_ARGUMENT: return "BSA_ERR_INVALID_ARGUMENT";
+    case BSA_ERR_UNSUPPORTED: return "BSA_ERR_UNSUPPORTED";
+    case BSA_ERR_OUT_OF_MEMORY: return "BSA_ERR_OUT_OF_MEMORY";
+    case BSA_ERR_DEVICE: return "BSA_ERR_DEVICE";
+    default: return "BSA_ERR_UNKNOWN";
+  }
+}
+
+const char* bsa_last_error(void) { return bsa::g_last_error.c_str(); }
+
+int32_t bsa_abi_version(void) { return BSA_ABI_VERSION; }
+
+}  // extern "C"

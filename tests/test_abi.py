@@ -1,0 +1,233 @@
+"""CPU tests of the C-ABI library: symbol exports, the host planner against
+the oracle's plan (bit-exact), the work order, and every error path that can
+be reached without a GPU (bsa_plan_host makes no HIP call)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_flash_bsa_amd import bsattn
+from block_sparse_flash_bsa_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsattn.h")
+
+
+def spec(causal, unit, w_left=-1, w_right=-1, gk=0, gq=0, bitmap=None):
+    return dict(causal=causal, unit=unit, window_left=w_left, window_right=w_right,
+                global_keys=gk, global_queries=gq, bitmap=bitmap)
+
+
+def host_plan(w, layout=None, **kw):
+    return bsattn.plan(w.batch, w.heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.dtype,
+                       layout if layout is not None else wl.layout_of(w), host_only=True, **kw)
+
+
+# ------------------------------------------------------------------ exports
+def test_library_exports_every_declared_symbol():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(bsa_\w+)\s*\(", text))
+    assert declared == set(bsattn.EXPORTS)
+    L = ctypes.CDLL(bsattn.LIB_PATH)
+    for name in declared:
+        assert hasattr(L, name), name
+    assert bsattn.lib().bsa_abi_version() == int(re.search(r"BSA_ABI_VERSION (\d+)", text).group(1))
+
+
+def test_status_strings():
+    L = bsattn.lib()
+    assert L.bsa_status_string(0) == b"BSA_OK"
+    assert L.bsa_status_string(2) == b"BSA_ERR_UNSUPPORTED"
+    assert L.bsa_status_string(99) == b"BSA_ERR_UNKNOWN"
+
+
+def test_struct_layouts_match_header():
+    assert ctypes.sizeof(bsattn.Problem) == 40
+    assert ctypes.sizeof(bsattn.Layout) == 56
+    assert bsattn.Layout.bitmap.offset == 40
+
+
+# --------------------------------------------------------- plan bit-exactness
+def assert_same_plan(p, ref):
+    assert len(ref) == p.info["layout_heads"]
+    for lh, r in enumerate(ref):
+        got = p.csr(lh)
+        for key in ("row_ptr", "col_idx", "flags"):
+            np.testing.assert_array_equal(got[key], r[key], err_msg=f"{key} head {lh}")
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "window16k", "winglobal128k", "random32k", "gqa256k",
+                                  "dense256k"])
+def test_plan_matches_oracle_full_size(name):
+    w = wl.WORKLOADS[name]
+    lay = wl.layout_of(w)
+    p = host_plan(w, lay)
+    assert_same_plan(p, oracle.plan(lay, w.seq_len, w.block))
+
+
+def test_plan_matches_oracle_bruteforce_random_specs():
+    rng = np.random.default_rng(21)
+    for _ in range(120):
+        bs = 64 if rng.random() < 0.5 else 128
+        nb = int(rng.integers(1, 9))
+        N = bs * nb
+        unit = "tokens" if rng.random() < 0.6 else "blocks"
+        lim = N if unit == "tokens" else nb
+        lay = spec(bool(rng.integers(0, 2)), unit, int(rng.integers(-1, lim + 2)),
+                   int(rng.integers(-1, lim + 2)), int(rng.integers(0, lim + 1)),
+                   int(rng.integers(0, lim + 1)))
+        p = bsattn.plan(1, 2, 1, N, 64, bs, torch.float32, lay, host_only=True)
+        assert_same_plan(p, oracle.plan(lay, N, bs, brute=True))
+
+
+def test_plan_bitmap_per_head_and_causal_cut():
+    rng = np.random.default_rng(22)
+    nb, bs = 12, 64
+    bm = (rng.random((3, nb, nb)) < 0.4).astype(np.uint8)
+    bm[1, 5, :] = 0
+    for causal in (False, True):
+        lay = spec(causal, "blocks", bitmap=bm)
+        p = bsattn.plan(2, 3, 3, nb * bs, 64, bs, torch.float32, lay, host_only=True)
+        assert_same_plan(p, oracle.plan(lay, nb * bs, bs, brute=True))
+        assert p.info["active_blocks"] == 2 * sum(len(x["col_idx"]) for x in oracle.plan(lay, nb * bs, bs))
+
+
+def test_plan_info_counts():
+    w = wl.WORKLOADS["gqa256k"]
+    p = host_plan(w)
+    i = p.info
+    assert (i["nnz"], i["nnz_partial"], i["active_blocks"], i["max_row_entries"]) == (69071, 6079, 2210272, 34)
+    q = np.arange(w.seq_len)
+    from tests.closed_forms import count
+    assert i["allowed_pairs"] == 32 * int(count("gqa256k", q, w.seq_len).sum())
+    assert p.flops() == 4.0 * 128 * 128 * 128 * 2210272
+
+
+# ---------------------------------------------------------------- work order
+@pytest.mark.parametrize("schedule", [0, 1, 2, 3])
+@pytest.mark.parametrize("name", ["winglobal128k", "random32k", "gqa256k"])
+def test_work_order_is_a_permutation(name, schedule):
+    w = wl.WORKLOADS[name]
+    p = host_plan(w, schedule=schedule)
+    work = p.work()
+    items = work[work >= 0]
+    n = w.batch * w.heads * w.num_blocks
+    assert p.info["work_items"] == n and p.info["launch_slots"] == len(work)
+    np.testing.assert_array_equal(np.sort(items), np.arange(n))
+
+
+def test_xcd_schedule_runs_are_local_and_balanced():
+    w = wl.WORKLOADS["gqa256k"]
+    p = host_plan(w, schedule=bsattn.SCHEDULE_XCD)
+    work = p.work()
+    nb, H, group = w.num_blocks, w.heads, w.heads // w.kv_heads
+    lens = np.diff(p.csr(0)["row_ptr"])
+    costs = []
+    for x in range(8):
+        run = work[x::8]
+        run = run[run >= 0]
+        i, h = run % nb, (run // nb) % H
+        # within a run: KV head major, then q-block, then the heads of the group
+        key = (h // group) * nb * group + i * group + h % group
+        assert np.all(np.diff(key) > 0)
+        costs.append(int((lens[i] + 1).sum()))
+    assert max(costs) - min(costs) <= lens.max() + 1
+
+
+def test_lpt_schedule_is_longest_first():
+    w = wl.WORKLOADS["random32k"]
+    p = host_plan(w, schedule=bsattn.SCHEDULE_LPT)
+    work = p.work()
+    nb, H = w.num_blocks, w.heads
+    lens = [np.diff(p.csr(h)["row_ptr"]) for h in range(H)]
+    c = np.array([lens[(it // nb) % H][it % nb] for it in work])
+    assert np.all(np.diff(c) <= 0)
+
+
+# ------------------------------------------------------------------- errors
+def expect_error(status, **over):
+    args = dict(batch=1, num_heads=4, num_kv_heads=2, seq_len=1024, head_dim=128, block_size=128,
+                dtype=torch.bfloat16, layout=spec(True, "tokens", 100, 0))
+    args.update(over)
+    with pytest.raises(bsattn.BsaError) as ei:
+        bsattn.plan(host_only=True, **args)
+    assert ei.value.status == status, ei.value
+    assert ei.value.detail  # bsa_last_error() explains it
+
+
+def test_invalid_arguments():
+    E = bsattn.ERR_INVALID_ARGUMENT
+    expect_error(E, seq_len=1000)                        # not a multiple of the block
+    expect_error(E, seq_len=-128)
+    expect_error(E, num_heads=3, num_kv_heads=2)
+    expect_error(E, num_kv_heads=0)
+    expect_error(E, batch=-1)
+    expect_error(E, scale=float("nan"))
+    expect_error(E, scale=-1.0)
+    expect_error(E, schedule=9)
+    expect_error(E, layout=spec(True, "tokens", -2, 0))
+    expect_error(E, layout=spec(True, "tokens", 4, 0, gk=-1))
+    expect_error(E, layout=spec(True, "blocks", bitmap=np.ones((3, 8, 8), np.uint8)))
+    with pytest.raises(bsattn.BsaError) as ei:
+        pr = bsattn.make_problem(1, 4, 2, 1024, 128, 128, torch.bfloat16)
+        lay, _ = bsattn.make_layout(spec(True, "tokens"))
+        lay.causal = 2
+        h = ctypes.c_void_p()
+        bsattn._check(bsattn.lib().bsa_plan_host(ctypes.byref(pr), ctypes.byref(lay), ctypes.byref(h)))
+    assert ei.value.status == E
+
+
+def test_null_arguments():
+    L = bsattn.lib()
+    h = ctypes.c_void_p()
+    assert L.bsa_plan_host(None, None, ctypes.byref(h)) == bsattn.ERR_INVALID_ARGUMENT
+    pr = bsattn.make_problem(1, 1, 1, 128, 128, 128, torch.bfloat16)
+    lay, _ = bsattn.make_layout(spec(False, "tokens"))
+    assert L.bsa_plan_host(ctypes.byref(pr), ctypes.byref(lay), None) == bsattn.ERR_INVALID_ARGUMENT
+    assert L.bsa_plan_get_info(None, None) == bsattn.ERR_INVALID_ARGUMENT
+    assert L.bsa_plan_active_blocks(None) == -1
+    L.bsa_plan_destroy(None)
+
+
+def test_unsupported_shapes():
+    U = bsattn.ERR_UNSUPPORTED
+    expect_error(U, head_dim=96, seq_len=1152)
+    expect_error(U, head_dim=64)                          # bf16 kernel is head_dim 128
+    expect_error(U, block_size=64, seq_len=1024)          # bf16 kernel is block 128
+    expect_error(U, dtype=torch.float32, head_dim=256)
+
+
+def test_host_plan_cannot_run_forward():
+    p = bsattn.plan(1, 1, 1, 128, 128, 128, torch.bfloat16, spec(False, "tokens"), host_only=True)
+    st = bsattn.lib().bsa_forward(None, None, None, p.handle, None, None, None)
+    assert st == bsattn.ERR_INVALID_ARGUMENT
+    assert b"bsa_plan_host" in bsattn.lib().bsa_last_error()
+
+
+def test_csr_head_out_of_range():
+    p = bsattn.plan(1, 2, 2, 256, 128, 128, torch.bfloat16, spec(False, "tokens"), host_only=True)
+    with pytest.raises(bsattn.BsaError):
+        p.csr(1)
+
+
+def test_empty_problems():
+    p = bsattn.plan(0, 2, 2, 256, 128, 128, torch.bfloat16, spec(True, "tokens"), host_only=True)
+    assert p.info["work_items"] == 0 and p.info["active_blocks"] == 0
+    p = bsattn.plan(1, 2, 2, 0, 128, 128, torch.bfloat16, spec(True, "tokens"), host_only=True)
+    assert p.info["num_blocks"] == 0 and p.info["nnz"] == 0 and p.work().size == 0
+
+
+def test_empty_rows_have_no_entries():
+    bm = np.zeros((1, 4, 4), np.uint8)
+    bm[0, 1, 2] = 1
+    p = bsattn.plan(1, 1, 1, 512, 128, 128, torch.bfloat16, spec(False, "blocks", bitmap=bm),
+                    host_only=True)
+    np.testing.assert_array_equal(p.csr(0)["row_ptr"], [0, 0, 1, 1, 1])
+    # causal removes the only block above the diagonal
+    p = bsattn.plan(1, 1, 1, 512, 128, 128, torch.bfloat16, spec(True, "blocks", bitmap=bm),
+                    host_only=True)
+    assert p.info["nnz"] == 0

@@ -1,0 +1,321 @@
+"""GPU parity of bsa_forward against the CPU oracle, through the C ABI.
+
+* every row of each workload's rule at a size the oracle finishes in seconds
+  (several tiles, the ramp of short rows, partial tiles);
+* full-size workloads in the benchmark's launch configuration (default plan):
+  sampled rows against the oracle, plus exact whole-tensor properties --
+  Q = 0 makes every weight exactly 1, so exp(LSE) must equal |A(q)| for every
+  row, and with V[k, d] = [k mod 128 == d] the output counts, per residue,
+  which keys each row saw (a one-key shift of a window edge changes it);
+* invariants (weights sum to one, single-key rows, empty rows), determinism,
+  no unwritten outputs, schedule independence, non-default streams.
+Tolerances (max abs error over all compared elements): fp32 inputs 1e-5 on
+O and LSE; bf16 inputs 2e-2 on O and 1e-3 on LSE.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_flash_bsa_amd import bsattn
+from block_sparse_flash_bsa_amd import workloads as wl
+from tests.closed_forms import count as closed_count
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: (1e-5, 1e-5), torch.bfloat16: (2e-2, 1e-3)}
+
+SMALL = {
+    "tiny_f32": wl.WORKLOADS["tiny_f32"],
+    "window16k": wl.small_variant(wl.WORKLOADS["window16k"], 4096, heads=2, kv_heads=2),
+    "winglobal128k": wl.small_variant(wl.WORKLOADS["winglobal128k"], 10240, heads=2, kv_heads=2),
+    "random32k": wl.small_variant(wl.WORKLOADS["random32k"], 4096, heads=4, kv_heads=4, batch=2),
+    "gqa256k": wl.small_variant(wl.WORKLOADS["gqa256k"], 6144, heads=4, kv_heads=1),
+    "dense256k": wl.small_variant(wl.WORKLOADS["dense256k"], 2048, heads=4, kv_heads=1),
+}
+FULL = ["window16k", "winglobal128k", "random32k", "gqa256k"]
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bsattn.lib()      # raises if the library is missing: no fallback
+    torch.cuda.set_device(0)
+
+
+def gpu_plan(w, layout, **kw):
+    return bsattn.plan(w.batch, w.heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.dtype,
+                       layout, **kw)
+
+
+def run(p, q, k, v, out=None, lse=None):
+    out, lse = bsattn.forward(q, k, v, p, out, lse)
+    torch.cuda.synchronize()
+    return out, lse
+
+
+def check(O, L, O_ref, L_ref, dtype, what=""):
+    to, tl = TOL[dtype]
+    O = np.asarray(O, dtype=np.float64)
+    L = np.asarray(L, dtype=np.float64)
+    assert not np.isnan(O).any() and not np.isnan(L).any(), what
+    fin = np.isfinite(L_ref)
+    assert np.array_equal(np.isfinite(L), fin), f"{what}: empty-row pattern differs"
+    eo = float(np.abs(O - O_ref).max()) if O.size else 0.0
+    el = float(np.abs(L[fin] - L_ref[fin]).max()) if fin.any() else 0.0
+    say(f"  {what}: max|dO| = {eo:.3e} (tol {to}), max|dLSE| = {el:.3e} (tol {tl})")
+    assert eo <= to, f"{what}: O error {eo} > {to}"
+    assert el <= tl, f"{what}: LSE error {el} > {tl}"
+    assert np.all(O[~fin] == 0), f"{what}: empty rows must give O = 0"
+
+
+# ------------------------------------------------------- every row, small sizes
+@pytest.mark.parametrize("name", list(SMALL))
+def test_parity_all_rows_small(name):
+    w = SMALL[name]
+    say(f"[parity-small] {w.name} B={w.batch} H={w.heads}/{w.kv_heads} N={w.seq_len}")
+    lay = wl.layout_of(w)
+    q, k, v = wl.make_qkv(w, "cpu")
+    p = gpu_plan(w, lay)
+    out, lse = run(p, q.cuda(), k.cuda(), v.cuda())
+    O_ref, L_ref = oracle.forward(q, k, v, lay, w.block)
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref, w.dtype, w.name)
+
+
+# ------------------------------------------------------------ full size, sampled
+def sample_rows(w, n_random=96, seed=0):
+    rng = np.random.default_rng(seed)
+    N, H, B = w.seq_len, w.heads, w.batch
+    qs = [0, 1, 127, 128, 129, 511, 512, 4095, 4096, 4103, 4104, 8191, 8192, 8320, N // 2, N - 129,
+          N - 128, N - 1]
+    rows = []
+    for qq in qs:
+        if qq < N:
+            rows.append((int(rng.integers(0, B)), int(rng.integers(0, H)), qq))
+    for _ in range(n_random):
+        rows.append((int(rng.integers(0, B)), int(rng.integers(0, H)), int(rng.integers(0, N))))
+    rows += [(B - 1, H - 1, N - 1), (0, 0, 0)]
+    return rows
+
+
+def oracle_sampled(w, lay, q, k, v, rows):
+    """Oracle on sampled rows; only the needed K/V heads are copied to the host."""
+    group = w.heads // w.kv_heads
+    need = sorted({(b, h // group) for b, h, _ in rows})
+    Kc = {key: k[key[0], key[1]].cpu() for key in need}
+    Vc = {key: v[key[0], key[1]].cpu() for key in need}
+    O = np.zeros((len(rows), w.head_dim))
+    L = np.zeros(len(rows))
+    for r, (b, h, qq) in enumerate(rows):
+        keys = oracle.allowed_keys(lay, w.seq_len, w.block, h, qq)
+        kk = torch.from_numpy(keys)
+        O[r], L[r] = oracle.attend_row(q[b, h, qq].double().cpu().numpy(),
+                                       Kc[(b, h // group)][kk].double().numpy(),
+                                       Vc[(b, h // group)][kk].double().numpy(),
+                                       1.0 / math.sqrt(w.head_dim))
+    return O, L
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_parity_full_size_sampled(name):
+    w = wl.WORKLOADS[name]
+    say(f"[parity-full] {w.name} B={w.batch} H={w.heads}/{w.kv_heads} N={w.seq_len}")
+    lay = wl.layout_of(w)
+    q, k, v = wl.make_qkv(w, "cuda")
+    p = gpu_plan(w, lay)
+    out, lse = run(p, q, k, v)
+    rows = sample_rows(w)
+    idx = tuple(torch.tensor(x) for x in zip(*rows))
+    O = out[idx].float().cpu().numpy()
+    L = lse[idx].cpu().numpy()
+    O_ref, L_ref = oracle_sampled(w, lay, q, k, v, rows)
+    check(O, L, O_ref, L_ref, w.dtype, f"{w.name} ({len(rows)} sampled rows)")
+
+
+def expected_counts(w, lay):
+    """|A(q)| per (layout head, q) from the closed forms."""
+    q = np.arange(w.seq_len)
+    if lay.get("bitmap") is not None:
+        bm = lay["bitmap"].numpy()
+        return np.stack([closed_count(w.name, q, w.seq_len, bm[h].sum(1)) for h in range(bm.shape[0])])
+    return closed_count(w.name, q, w.seq_len)[None]
+
+
+@pytest.mark.parametrize("name", FULL + ["tiny_f32"])
+def test_count_probe_full_size(name):
+    """Q = 0: every weight is exactly 1, so exp(LSE) = |A(q)| on every row."""
+    w = wl.WORKLOADS[name]
+    say(f"[count-probe] {w.name}")
+    lay = wl.layout_of(w)
+    _, k, v = wl.make_qkv(w, "cuda")
+    q = torch.zeros((w.batch, w.heads, w.seq_len, w.head_dim), dtype=w.dtype, device="cuda")
+    p = gpu_plan(w, lay)
+    _, lse = run(p, q, k, v)
+    got = np.rint(np.exp(lse.double().cpu().numpy()))
+    exp = expected_counts(w, lay)
+    exp = np.broadcast_to(exp[None] if exp.shape[0] == w.heads else exp[None, :1], (w.batch,) + got.shape[1:2] + exp.shape[1:]) \
+        if exp.shape[0] == w.heads else np.broadcast_to(exp[None], got.shape)
+    bad = np.argwhere(got != exp)
+    assert bad.size == 0, f"{len(bad)} rows with a wrong key count, first {bad[:5].tolist()}"
+
+
+@pytest.mark.parametrize("name", FULL + ["tiny_f32"])
+def test_residue_probe_full_size(name):
+    """Q = 0 and V[k, d] = [k mod D == d]: O[q, d] = #{k in A(q): k = d mod D} / |A(q)|."""
+    w = wl.WORKLOADS[name]
+    say(f"[residue-probe] {w.name}")
+    lay = wl.layout_of(w)
+    D = w.head_dim
+    q = torch.zeros((w.batch, w.heads, w.seq_len, D), dtype=w.dtype, device="cuda")
+    k = torch.randn((w.batch, w.kv_heads, w.seq_len, D), dtype=torch.float32, device="cuda").to(w.dtype)
+    kk = torch.arange(w.seq_len, device="cuda")
+    v1 = (kk[:, None] % D == torch.arange(D, device="cuda")[None]).to(w.dtype)
+    v = v1.expand(w.batch, w.kv_heads, w.seq_len, D).contiguous()
+    p = gpu_plan(w, lay)
+    out, _ = run(p, q, k, v)
+    rows = sample_rows(w, n_random=200, seed=1)
+    rel = 2.0 ** -8 if w.dtype == torch.bfloat16 else 1e-6
+    for b, h, qq in rows:
+        keys = oracle.allowed_keys(lay, w.seq_len, w.block, h, qq)
+        cnt = np.bincount(keys % D, minlength=D) / max(len(keys), 1)
+        got = out[b, h, qq].double().cpu().numpy()
+        assert np.all(np.abs(got - cnt) <= rel * cnt + 1e-7), (b, h, qq)
+
+
+# ------------------------------------------------------------------ invariants
+def small_case(B=1, H=4, Hk=2, N=2048, D=128, bs=128, dtype=torch.bfloat16, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    mk = lambda hh: torch.randn(B, hh, N, D, generator=g).to(dtype)
+    return mk(H), mk(Hk), mk(Hk)
+
+
+def spec(causal, unit, w_left=-1, w_right=-1, gk=0, gq=0, bitmap=None):
+    return dict(causal=causal, unit=unit, window_left=w_left, window_right=w_right,
+                global_keys=gk, global_queries=gq, bitmap=bitmap)
+
+
+def plan_for(q, k, lay, dtype=torch.bfloat16, **kw):
+    B, H, N, D = q.shape
+    bs = kw.pop("bs", 128)
+    return bsattn.plan(B, H, k.shape[1], N, D, bs, dtype, lay, **kw)
+
+
+def test_weights_sum_to_one():
+    q, k, _ = small_case(N=4096)
+    v = torch.ones_like(k)
+    lay = spec(True, "tokens", 700, 0, gk=5)
+    out, lse = run(plan_for(q, k, lay), q.cuda(), k.cuda(), v.cuda())
+    assert torch.isfinite(lse).all()
+    assert (out.float() - 1).abs().max().item() <= 2 ** -8
+
+
+def test_single_allowed_key_returns_its_value_row():
+    q, k, v = small_case(N=1024, H=2, Hk=2)
+    out, lse = run(plan_for(q, k, spec(True, "tokens", 0, 0)), q.cuda(), k.cuda(), v.cuda())
+    assert torch.equal(out.cpu(), v)
+    s = (q.double() * k.double()).sum(-1) / math.sqrt(128)
+    assert (lse.double().cpu() - s).abs().max().item() <= 1e-3
+
+
+def test_empty_rows_give_zero_and_minus_inf():
+    q, k, v = small_case(N=1024, H=2, Hk=2)
+    nb = 8
+    bm = (np.random.default_rng(3).random((2, nb, nb)) < 0.5).astype(np.uint8)
+    bm[0, 3, :] = 0                         # empty q-block row, head 0
+    bm[1, 0, :] = 0
+    bm[1, 0, 5] = 1                         # only a block above the diagonal: empty once causal
+    lay = spec(True, "blocks", bitmap=bm)
+    out, lse = run(plan_for(q, k, lay), q.cuda(), k.cuda(), v.cuda())
+    O_ref, L_ref = oracle.forward(q, k, v, lay, 128)
+    assert np.isneginf(L_ref[0, 0, 384:512]).all() and np.isneginf(L_ref[0, 1, 0:128]).all()
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref, torch.bfloat16, "empty rows")
+
+
+def test_no_unwritten_outputs_and_deterministic():
+    w = SMALL["gqa256k"]
+    lay = wl.layout_of(w)
+    q, k, v = (x.cuda() for x in wl.make_qkv(w, "cpu"))
+    p = gpu_plan(w, lay)
+    res = []
+    for _ in range(2):
+        out = torch.full((w.batch, w.heads, w.seq_len, w.head_dim), float("nan"), dtype=w.dtype, device="cuda")
+        lse = torch.full((w.batch, w.heads, w.seq_len), float("nan"), device="cuda")
+        run(p, q, k, v, out, lse)
+        assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+        res.append((out.clone(), lse.clone()))
+    assert torch.equal(res[0][0], res[1][0]) and torch.equal(res[0][1], res[1][1])
+
+
+def test_schedules_give_identical_results():
+    w = SMALL["random32k"]
+    lay = wl.layout_of(w)
+    q, k, v = (x.cuda() for x in wl.make_qkv(w, "cpu"))
+    outs = [run(gpu_plan(w, lay, schedule=s), q, k, v) for s in (1, 2, 3)]
+    for o, l in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
+
+
+def test_non_default_stream():
+    q, k, v = (x.cuda() for x in small_case(N=2048))
+    lay = spec(True, "tokens", 300, 0, gk=3)
+    p = plan_for(q, k, lay)
+    ref = run(p, q, k, v)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out, lse = bsattn.forward(q, k, v, p)
+    s.synchronize()
+    assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1])
+
+
+@pytest.mark.parametrize("D,bs", [(64, 64), (64, 128), (128, 64), (128, 128)])
+def test_f32_kernels(D, bs):
+    q, k, v = small_case(B=2, H=4, Hk=2, N=8 * bs, D=D, dtype=torch.float32, seed=D + bs)
+    lay = spec(True, "tokens", 3 * bs - 7, 2, gk=5, gq=3)
+    out, lse = run(plan_for(q, k, lay, dtype=torch.float32, bs=bs), q.cuda(), k.cuda(), v.cuda())
+    O_ref, L_ref = oracle.forward(q, k, v, lay, bs)
+    check(out.cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref, torch.float32, f"f32 D={D} bs={bs}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_token_rule_both_sides_and_gqa(causal):
+    q, k, v = small_case(B=2, H=6, Hk=3, N=3072, seed=7)
+    lay = spec(causal, "tokens", 333, 200, gk=130, gq=260)
+    out, lse = run(plan_for(q, k, lay), q.cuda(), k.cuda(), v.cuda())
+    O_ref, L_ref = oracle.forward(q, k, v, lay, 128)
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref, torch.bfloat16, "token rule")
+
+
+def test_custom_scale():
+    q, k, v = small_case(N=1024, H=2, Hk=1, seed=9)
+    lay = spec(False, "tokens", 200, 200)
+    out, lse = run(plan_for(q, k, lay, scale=0.05), q.cuda(), k.cuda(), v.cuda())
+    O_ref, L_ref = oracle.forward(q, k, v, lay, 128, scale=0.05)
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref, torch.bfloat16, "scale 0.05")
+
+
+def test_large_magnitude_scores_stay_finite():
+    """Scores up to ~1e3: the online softmax must not overflow or produce NaN."""
+    q, k, v = small_case(N=2048, H=2, Hk=2, seed=10)
+    q = (q.float() * 30).to(torch.bfloat16)
+    lay = spec(True, "tokens", 900, 0, gk=2)
+    out, lse = run(plan_for(q, k, lay), q.cuda(), k.cuda(), v.cuda())
+    O_ref, L_ref = oracle.forward(q, k, v, lay, 128)
+    assert torch.isfinite(out.float()).all()
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref, torch.bfloat16, "large scores")
+
+
+def test_forward_rejects_wrong_device_pointers():
+    q, k, v = small_case(N=256, H=1, Hk=1)
+    p = plan_for(q, k, spec(False, "tokens"))
+    st = bsattn.lib().bsa_forward(None, None, None, p.handle, None, None, None)
+    assert st == bsattn.ERR_INVALID_ARGUMENT
+    with pytest.raises(ValueError):
+        bsattn.forward(q, k, v, p)          # host tensors are refused by the binding
