@@ -64,42 +64,82 @@ def plan_for(w, lay, **kw):
 _CPU = {}
 
 
-def _cpu_worker(rows):
-    import oracle  # the oracle is test infrastructure; only this baseline leg uses it
+def _cpu_init(path, lay, bs):
+    """Worker start-up (spawned process): memory-map one head's Q/K/V."""
+    os.environ["OMP_NUM_THREADS"] = "1"
+    import oracle  # test infrastructure: only this baseline leg of the benchmark uses it
+    _CPU.update(oracle=oracle, lay=lay, bs=bs,
+                q=np.load(path + "_q.npy", mmap_mode="r"), k=np.load(path + "_k.npy", mmap_mode="r"),
+                v=np.load(path + "_v.npy", mmap_mode="r"))
+
+
+def _cpu_worker(args):
+    """Run the oracle row by row on random queries for `seconds`; return (rows, elapsed)."""
+    seed, seconds = args
     d = _CPU
-    t = time.perf_counter()
-    oracle.forward(d["q"], d["k"], d["v"], d["lay"], d["bs"], rows=rows)
-    return time.perf_counter() - t
+    N = d["q"].shape[2]
+    rng = np.random.default_rng(seed)
+    done, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        d["oracle"].forward(d["q"], d["k"], d["v"], d["lay"], d["bs"],
+                            rows=[(0, 0, int(rng.integers(0, N)))])
+        done += 1
+    return done, time.perf_counter() - t0
 
 
-def cpu_baseline(w, lay, q, k, v, flops, target_s=15.0):
-    """Time the oracle on a bounded sample of rows and scale to the full job."""
+def cpu_baseline(w, lay, q, k, v, flops, seconds=15.0):
+    """The oracle, as it is, on a bounded sample of the workload's rows.
+
+    One head's Q/K/V (exact float32 copies of the bf16 inputs) is written to
+    /tmp and memory-mapped by spawned worker processes (one thread each); each
+    worker evaluates random query rows for `seconds`.  The full-job time is
+    extrapolated from the measured rows per second."""
+    import tempfile
     B, H, N = w.batch, w.heads, w.seq_len
     group = w.heads // w.kv_heads
-    rng = np.random.default_rng(0)
-    b0, h0 = 0, int(rng.integers(0, H))
-    _CPU.update(q=q[b0:b0 + 1, h0:h0 + 1].cpu(), k=k[b0:b0 + 1, h0 // group:h0 // group + 1].cpu(),
-                v=v[b0:b0 + 1, h0 // group:h0 // group + 1].cpu(), bs=w.block,
-                lay=dict(lay, bitmap=None if lay.get("bitmap") is None else lay["bitmap"][h0:h0 + 1]))
-    # Rows spread over the whole sequence so short and long rows are both sampled.
-    probe = [(0, 0, int(x)) for x in rng.integers(0, N, 32)]
-    t_row = _cpu_worker(probe) / len(probe)
+    h0 = H // 2
+    tmp = tempfile.mkdtemp(prefix="bsa_cpu_")
+    path = os.path.join(tmp, "head")
+    np.save(path + "_q.npy", q[0:1, h0:h0 + 1].float().cpu().numpy())
+    np.save(path + "_k.npy", k[0:1, h0 // group:h0 // group + 1].float().cpu().numpy())
+    np.save(path + "_v.npy", v[0:1, h0 // group:h0 // group + 1].float().cpu().numpy())
+    lay1 = dict(lay)
+    if lay.get("bitmap") is not None:
+        lay1["bitmap"] = np.asarray(lay["bitmap"][h0:h0 + 1])
     cores = max(1, min(16, os.cpu_count() or 1))
-    n_rows = max(cores, int(target_s * cores / max(t_row, 1e-6)))
-    rows = [(0, 0, int(x)) for x in rng.integers(0, N, n_rows)]
-    chunks = [rows[c::cores] for c in range(cores)]
-    os.environ.setdefault("OMP_NUM_THREADS", "1")
-    ctx = mp.get_context("fork")
-    t0 = time.perf_counter()
-    with ctx.Pool(cores) as pool:
-        pool.map(_cpu_worker, chunks)
-    wall = time.perf_counter() - t0
-    full_s = wall * (B * H * N) / n_rows
+    ctx = mp.get_context("spawn")
+    try:
+        with ctx.Pool(cores, initializer=_cpu_init, initargs=(path, lay1, w.block)) as pool:
+            pool.map(_cpu_worker, [(s, 0.5) for s in range(cores)])       # warm-up
+            t0 = time.perf_counter()
+            res = []
+            for r in pool.imap_unordered(_cpu_worker, [(100 + s, seconds) for s in range(cores)]):
+                res.append(r)
+                log(f"[bench] cpu worker done: {r[0]} rows in {r[1]:.1f} s")
+            wall = time.perf_counter() - t0
+    finally:
+        for suffix in ("_q.npy", "_k.npy", "_v.npy"):
+            if os.path.exists(path + suffix):
+                os.remove(path + suffix)
+        os.rmdir(tmp)
+    rows = sum(r[0] for r in res)
+    full_s = wall * (B * H * N) / rows
     return {"value": flops / full_s / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_rows} random query rows of one head (b={b0}, h={h0}) of {w.name}, "
-                      f"{wall:.1f} s wall on {cores} processes; full-job time extrapolated as "
-                      f"wall x {B * H * N} rows / {n_rows} = {full_s:.0f} s",
-            "extrapolated_full_s": full_s}
+            "sample": f"{rows} random query rows of head {h0} of {w.name}, evaluated one by one by "
+                      f"the float64 oracle in {cores} single-threaded processes over {wall:.1f} s; "
+                      f"full-job time extrapolated to {B * H * N} rows = {full_s:.0f} s",
+            "extrapolated_full_s": round(full_s, 1)}
+
+
+def calibrate_copy(mib):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    x = torch.ones(mib * 2 ** 18, dtype=torch.float32, device="cuda")
+    y = torch.empty_like(x)
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": x.numel() * 4, "copy_bytes_written": y.numel() * 4,
+                      "launches": 3}), flush=True)
 
 
 def main():
@@ -112,6 +152,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
+                    help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -123,6 +165,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     bsattn.lib()
 
     w = wl.WORKLOADS[args.workload]
@@ -191,7 +236,7 @@ def main():
                                               ctx["gqa256k"]["ms_per_forward"], 2)
         result["context"] = ctx
     if not args.no_cpu_baseline:
-        if "q" not in dir() or q.shape[2] != w.seq_len:
+        if q.shape[2] != w.seq_len or q.shape[1] != w.heads:
             q, k, v = wl.make_qkv(w, "cuda")
         log("[bench] timing the CPU oracle on a sample ...")
         result["cpu_baseline"] = cpu_baseline(w, lay, q, k, v, flops, args.cpu_seconds)

@@ -122,7 +122,9 @@ bsa_status_t validate(const bsa_problem_t* p, const bsa_layout_t* L) {
                 p->num_heads, L->bitmap_heads);
   const int64_t nb = p->seq_len / p->block_size;
   const int64_t items = int64_t(p->batch) * p->num_heads * nb;
-  if (items > INT32_MAX / 2 || nb > (INT32_MAX >> 2))
+  if (p->seq_len > (int64_t(1) << 30))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "seq_len %lld exceeds 2^30", (long long)p->seq_len);
+  if (items > INT32_MAX / 2)
     return fail(BSA_ERR_INVALID_ARGUMENT, "problem too large: %lld work items", (long long)items);
   if (!kernel_supported(p->dtype, p->head_dim, p->block_size))
     return fail(BSA_ERR_UNSUPPORTED,

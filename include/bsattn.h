@@ -78,7 +78,7 @@ typedef int32_t bsa_status_t;
 /* The attention problem a plan is prepared for.
  *   batch >= 0, num_heads >= 1, num_kv_heads >= 1, num_heads % num_kv_heads == 0
  *     (query head h reads KV head h / (num_heads / num_kv_heads)).
- *   seq_len >= 0 and a multiple of block_size (the FAQ of "The Only Guide You
+ *   seq_len in [0, 2^30] and a multiple of block_size (the FAQ of "The Only Guide You
  *     Need for Sparse Attention Kernels in Long-Context LLMs" answers the
  *     variable-length question by padding to the block size).
  *   block_size: layout block = kernel tile height and width.
@@ -87,6 +87,7 @@ typedef int32_t bsa_status_t;
  *     BSA_F32 : (64 | 128, 64 | 128)          -- exact fp32 kernel
  *   scale: 0 means 1/sqrt(head_dim); otherwise finite and > 0.
  *   schedule: one of BSA_SCHEDULE_*.
+ *   batch * num_heads * (seq_len / block_size) must stay below 2^30.
  */
 typedef struct {
   int32_t batch;

@@ -160,9 +160,7 @@ def test_count_probe_full_size(name):
     p = gpu_plan(w, lay)
     _, lse = run(p, q, k, v)
     got = np.rint(np.exp(lse.double().cpu().numpy()))
-    exp = expected_counts(w, lay)
-    exp = np.broadcast_to(exp[None] if exp.shape[0] == w.heads else exp[None, :1], (w.batch,) + got.shape[1:2] + exp.shape[1:]) \
-        if exp.shape[0] == w.heads else np.broadcast_to(exp[None], got.shape)
+    exp = np.broadcast_to(expected_counts(w, lay)[None], got.shape)   # [1, 1 or H, N]
     bad = np.argwhere(got != exp)
     assert bad.size == 0, f"{len(bad)} rows with a wrong key count, first {bad[:5].tolist()}"
 
@@ -302,14 +300,25 @@ def test_custom_scale():
 
 
 def test_large_magnitude_scores_stay_finite():
-    """Scores up to ~1e3: the online softmax must not overflow or produce NaN."""
+    """Scores of magnitude ~100: no overflow, no NaN, and O within the bf16 bound.
+
+    Here the weights are nearly one-hot, so |O| reaches max|V| (~4) instead of
+    the ~0.1 of the workloads.  Rounding P and O to bf16 (relative 2^-8 each)
+    then bounds the error per element by 2^-8 * (|O| + max|V|), which exceeds
+    the flat 2e-2 of the workloads; that bound is checked here."""
     q, k, v = small_case(N=2048, H=2, Hk=2, seed=10)
     q = (q.float() * 30).to(torch.bfloat16)
     lay = spec(True, "tokens", 900, 0, gk=2)
     out, lse = run(plan_for(q, k, lay), q.cuda(), k.cuda(), v.cuda())
     O_ref, L_ref = oracle.forward(q, k, v, lay, 128)
-    assert torch.isfinite(out.float()).all()
-    check(out.float().cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref, torch.bfloat16, "large scores")
+    O = out.double().cpu().numpy()
+    assert np.isfinite(O).all() and np.isfinite(lse.cpu().numpy()).all()
+    vmax = float(v.abs().max())
+    bound = 2.0 ** -8 * (np.abs(O_ref) + vmax) + 1e-4
+    err = np.abs(O - O_ref)
+    say(f"  large scores: max|dO| = {err.max():.3e}, max err/bound = {(err / bound).max():.3f}")
+    assert np.all(err <= bound)
+    assert np.abs(lse.cpu().numpy() - L_ref).max() <= 1e-3
 
 
 def test_forward_rejects_wrong_device_pointers():
