@@ -98,19 +98,6 @@ __device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
   return __builtin_bit_cast(bf16x4, v);
 }
 
-// Scheduling hint for an M-phase block (32 MFMAs, 48 LDS operand reads, no
-// other vector work): keep about twelve LDS reads in flight ahead of the
-// MFMAs, since in that phase the SIMD has no other MFMA wave to hide latency.
-__device__ __forceinline__ void interleave_mphase() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);    // DS read
-#pragma unroll
-  for (int k = 0; k < 18; ++k) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-  }
-  __builtin_amdgcn_sched_group_barrier(0x008, 14, 0);
-}
-
 // Max of x over lanes l and l ^ 32 (v_permlane32_swap: one result holds the
 // lane's own value, the other its partner's).
 __device__ __forceinline__ float max_with_partner(float x) {
@@ -129,38 +116,15 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-// Ping-pong workgroup: 8 waves in two groups of 4.  Both groups cover the same
-// 128 query rows (32 per wave) and split the row's CSR entries: group 0 takes
-// entries 0, 2, 4, ..., group 1 entries 1, 3, 5, ....  Work runs in phases
-// separated by one workgroup barrier; in every phase one group does MFMA work
-// (P.V of the previous 64-key half, S^T of the next) while the other does the
-// softmax of its current half on the VALU, so each SIMD always holds one wave
-// of each kind (waves w and w + 4 share a SIMD).
-//
-// K and V reach LDS by direct HBM->LDS loads (global_load_lds_dwordx4), one
-// 64-key half at a time, issued in a group's softmax phase into the half-slot
-// its previous MFMA phase released, two of the group's phases before use.  No
-// staging registers and no LDS store instructions.  Each 256-byte LDS row
-// holds its 16 chunks of 16 bytes XOR-swizzled (K: chunk ^ (row & 15), V:
-// chunk ^ 4*(row & 3)) so the MFMA operand reads are free of bank conflicts.
-// At the end the two partial results are merged through LDS:
-// O = (a0 O0 + a1 O1) / (a0 l0 + a1 l1), a_g = 2^(m_g - max(m0, m1)).
-constexpr int kTileBytes = kBN * kD * 2;                  // 32 KB
-typedef __attribute__((address_space(3))) unsigned char lds_u8;
-constexpr int kPPThreads = 512;
-
-// vmcnt(n) with the other counters left alone (gfx9 encoding).
-#define BSA_WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x70 | 0xF00)
-// Workgroup barrier that waits only for this wave's LDS reads (not for the
-// in-flight HBM->LDS loads, which are waited for explicitly).
-__device__ __forceinline__ void phase_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-}
-
-__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void fwd_bf16_d128(FwdParams p, const int32_t* __restrict__ ents) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[4 * kTileBytes];
+// One workgroup of 4 waves per (b, h, q-block); wave w owns query rows
+// 32w .. 32w+31.  Two workgroups share a CU (75 KB of LDS each), so each SIMD
+// holds two independent waves whose MFMA and softmax phases overlap.  Per
+// CSR entry: the K/V tile prefetched into registers during the previous tile
+// is written to LDS between two barriers, the next tile's loads are issued,
+// and the tile is processed in two 64-key halves (S^T, mask, softmax, P.V).
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const int32_t* __restrict__ ents) {
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * kKS];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[kBN * kVS];
 
   const int item = p.work[blockIdx.x];
   if (item < 0) return;
@@ -170,291 +134,169 @@ void fwd_bf16_d128(FwdParams p, const int32_t* __restrict__ ents) {
   const RowDesc row = p.rows[(p.per_head_layout ? h : 0) * p.nb + i];
 
   const int tid = threadIdx.x;
-  // grp stays a vector value on purpose: as a scalar the compiler unswitches
-  // the phase loop on it and runs out of registers.
-  const int grp = tid >> 8;                               // 0 or 1
-  const int wave4 = __builtin_amdgcn_readfirstlane((tid >> 6) & 3);
-  const int lane = tid & 63, r32 = lane & 31, hf = lane >> 5;
-  const int qrow = wave4 * 32 + r32;                      // row within the q-block
+  const int wave = tid >> 6, lane = tid & 63, r32 = lane & 31, hf = lane >> 5;
+  const int qrow = wave * 32 + r32;                       // row within the q-block
   const int64_t qg = int64_t(i) * kBM + qrow;             // global query index
-  unsigned char* Kl = lds + grp * (2 * kTileBytes);       // this group's K tile
-  unsigned char* Vl = Kl + kTileBytes;                    // this group's V tile
 
   const uint16_t* __restrict__ Qp =
       static_cast<const uint16_t*>(p.q) + ((int64_t(b) * p.H + h) * p.N + qg) * kD;
-  const unsigned char* Kg =
-      reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.k) + (int64_t(b) * p.Hkv + hk) * p.N * kD);
-  const unsigned char* Vg =
-      reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.v) + (int64_t(b) * p.Hkv + hk) * p.N * kD);
+  const uint16_t* __restrict__ Kb =
+      static_cast<const uint16_t*>(p.k) + (int64_t(b) * p.Hkv + hk) * p.N * kD;
+  const uint16_t* __restrict__ Vb =
+      static_cast<const uint16_t*>(p.v) + (int64_t(b) * p.Hkv + hk) * p.N * kD;
 
   // Q^T operand: lane (row r32, half hf) holds d = 16c + 8hf .. +7 for c = 0..7.
   bf16x8 qf[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(Qp + c * 16 + hf * 8);
-  // Make the Q loads complete here, before any HBM->LDS load is in flight.
+  // Complete the Q loads here so no wait on them lands inside the loop.
   __asm__ volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]),
                    "v"(qf[6]), "v"(qf[7]));
 
-  // HBM->LDS load of one 64-key half (16 KB) of K or V tile j into rows
-  // 64*hh .. 64*hh+63 of the group's buffer: 4 instructions per wave, each
-  // filling 4 rows (1 KB, lane L -> row +L/16, slot L%16, which holds logical
-  // chunk slot ^ swz(row)).  Within a half, row & 15 = 4u + L/16, so the
-  // swizzled per-lane source offsets do not depend on the half or the tile:
-  // they are computed once (dk[u] for K, dv + 1024u for V).
-  uint32_t dk[4];
+  // K/V staging registers: thread loads rows rr + 16u, 16 bytes at column col8,
+  // of both K and V (coalesced 256-byte rows, 16 threads per row).
+  u32x4 kr[8], vr[8];
+  const int rr = tid >> 4, col8 = (tid & 15) * 8;
+  auto load_kv = [&](int j) {
+    const uint16_t* kp = Kb + int64_t(j) * kBN * kD + rr * kD + col8;
+    const uint16_t* vp = Vb + int64_t(j) * kBN * kD + rr * kD + col8;
 #pragma unroll
-  for (int u = 0; u < 4; ++u)
-    dk[u] = (wave4 * 16 + u * 4 + (lane >> 4)) * 256 + 16 * ((lane & 15) ^ (u * 4 + (lane >> 4)));
-  const uint32_t dv = (wave4 * 16 + (lane >> 4)) * 256 + 16 * ((lane & 15) ^ (4 * (lane >> 4)));
-  auto dma_half = [&](const unsigned char* src, unsigned char* dst, int j, int hh, bool is_v) {
-    const unsigned char* base = src + (int64_t(j) * kBN + hh * 64) * (kD * 2);   // uniform
+    for (int u = 0; u < 8; ++u) kr[u] = *reinterpret_cast<const u32x4*>(kp + u * 16 * kD);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint32_t off = is_v ? dv + u * 1024 : dk[u];
-      __builtin_amdgcn_global_load_lds(
-          base + off, (__attribute__((address_space(3))) void*)(dst + (hh * 64 + wave4 * 16 + u * 4) * 256), 16, 0, 0);
-    }
+    for (int u = 0; u < 8; ++u) vr[u] = *reinterpret_cast<const u32x4*>(vp + u * 16 * kD);
+  };
+  auto store_kv = [&]() {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) *reinterpret_cast<u32x4*>(Ks + (rr + 16 * u) * kKS + col8) = kr[u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) *reinterpret_cast<u32x4*>(Vs + (rr + 16 * u) * kVS + col8) = vr[u];
   };
 
-  // Per-lane LDS addresses of the MFMA operands (the swizzle XOR is folded in),
-  // kept as 32-bit LDS (address space 3) pointers.
-  // K (S^T A operand): row 64*hh + 32*t + r32, logical chunk 2*cc + hf.
-  lds_u8* const Kl3 = (lds_u8*)Kl;    // generic -> LDS address-space cast
-  lds_u8* const Vl3 = (lds_u8*)Vl;
-  const int kx = r32 & 15;
-  lds_u8* kaddr[8];
-#pragma unroll
-  for (int cc = 0; cc < 8; ++cc) kaddr[cc] = Kl3 + r32 * 256 + 16 * ((2 * cc + hf) ^ kx);
-  // V (transposed reads): in 16-lane group g, lane 4*r4 + c4 reads row
-  // 16*c16 + 8*s + 4*hf + r4, columns 32*dt + 16*(g&1) + 4*c4 .. +3, i.e.
-  // logical chunk 4*dt + 2*(g&1) + c4/2 at byte 8*(c4&1); row & 3 == r4.
-  const int r4 = (lane & 15) >> 2, c4 = lane & 3, gp = (lane >> 4) & 1;
-  lds_u8* vaddr[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-    vaddr[dt] = Vl3 + (4 * hf + r4) * 256 + 16 * ((4 * dt + 2 * gp + (c4 >> 1)) ^ (4 * r4)) + 8 * (c4 & 1);
+  // V^T operand of P.V by transposed reads: in 16-lane group g, lane 4*r4 + c4
+  // addresses key row 4*hf + r4 (+ 16*c16, + 8 for the upper 8 keys) and
+  // columns 32*dt + 16*(g & 1) + 4*c4 .. +3; lane l then receives the 4 keys
+  // of column d = 32*dt + (l & 31).
+  const uint16_t* vtr = Vs + (4 * hf + ((lane & 15) >> 2)) * kVS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  auto lds_b128 = [](lds_u8* a) { return *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(a); };
-  auto lds_tr = [](lds_u8* a) {
-    return __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                          reinterpret_cast<__attribute__((address_space(3))) s16x4*>(a)));
-  };
-  // S^T for the 64 keys of half hh: two 32x32 tiles; lane holds row r32, keys
-  // 64*hh + 32*t + 8*(r/4) + 4*hf + r%4 in register r of tile t.
-  auto qk_half = [&](int hh, f32x16 (&sq)[2]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      sq[t] = f32x16{};
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
-        const bf16x8 a = lds_b128(kaddr[cc] + (hh * 64 + t * 32) * 256);
-        sq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], sq[t], 0, 0, 0);
-      }
-    }
-  };
   f32x16 o[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) o[dt] = f32x16{};
-  // O^T += V^T P^T for the 64 keys of half hh.  Accumulator registers
-  // 8q .. 8q+7 of S^T tile t are exactly the 8 keys this lane supplies for the
-  // 16-key chunk 2t + q of the half.
-  auto pv_half = [&](int hh, const bf16x8 (&pq)[4]) {
-#pragma unroll
-    for (int cq = 0; cq < 4; ++cq) {
-      const int c16 = hh * 4 + cq;
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const bf16x4 lo = lds_tr(vaddr[dt] + (c16 * 16) * 256);
-        const bf16x4 hi = lds_tr(vaddr[dt] + (c16 * 16 + 8) * 256);
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pq[cq], o[dt], 0, 0, 0);
-      }
-    }
-  };
-
   float m_ref = -INFINITY;   // reference max (log2 domain, scaled)
   float l_part = 0.f;        // this lane's share of the row sum
   const float c = p.sl2;
   const bool q_global = qg < p.gq32;
 
-  // Softmax of one 64-key half, in place on the VALU: mask (PARTIAL tiles
-  // only), row max, lazy move of the reference max (only when some row's max
-  // grows by more than 2^8, a wave-uniform decision), P = exp2(c*S - m) in
-  // bf16, and the matching rescale of O and l.  The empty volatile asm keeps
-  // the two conditional blocks real branches.
-  auto softmax_half = [&](f32x16 (&sq)[2], int hh, int j, bool partial, bf16x8 (&pq)[4]) {
-    if (partial) {
-      __asm__ volatile("");
-      const int k0 = j * kBN;
-      const int dq = int(qg) - k0;
+  const int e0 = row.start, ne = row.count;
+  if (ne > 0) load_kv(ents[e0] >> 1);
+  for (int e = 0; e < ne; ++e) {
+    const int ent = ents[e0 + e];
+    const int j = ent >> 1;
+    const bool partial = ent & 1;
+    __syncthreads();           // every wave is done with the previous tile
+    store_kv();
+    __syncthreads();
+    if (e + 1 < ne) load_kv(ents[e0 + e + 1] >> 1);
+
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      // S^T for 64 keys: two 32x32 tiles; lane holds row r32, keys
+      // 64*half + 32*t + 8*(r/4) + 4*hf + r%4 in accumulator register r.
+      f32x16 s[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        s[t] = f32x16{};
+        const int kt = half * 2 + t;
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (kt * 32 + r32) * kKS + cc * 16 + hf * 8);
+          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], s[t], 0, 0, 0);
+        }
+      }
+      // Token mask, PARTIAL tiles only.  The empty volatile asm keeps this a
+      // real branch (not a select over every score of every tile).
+      if (partial) {
+        __asm__ volatile("");
+        const int k0 = j * kBN;
+        const int dq = int(qg) - k0;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int koff = half * 64 + t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const int diff = dq - koff;                              // q - k
+            const bool in_w = (p.wl32 < 0 || diff <= p.wl32) & (p.wr32 < 0 || -diff <= p.wr32);
+            const bool rule = !p.token_rule | in_w | (k0 + koff < p.gk32) | q_global;
+            const bool ok = rule & (!p.causal | (diff >= 0));
+            s[t][r] = ok ? s[t][r] : -INFINITY;
+          }
+      }
+      // Row max (in-lane, then with lane l ^ 32), lazy move of the reference
+      // max (only when some row's max grows by more than 2^8: a wave-uniform
+      // decision), P = exp2(c*S - m) in bf16, and the matching rescale.
+      float mx = s[0][0];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int koff = hh * 64 + t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const int diff = dq - koff;                              // q - k
-          const bool in_w = (p.wl32 < 0 || diff <= p.wl32) & (p.wr32 < 0 || -diff <= p.wr32);
-          const bool rule = !p.token_rule | in_w | (k0 + koff < p.gk32) | q_global;
-          const bool ok = rule & (!p.causal | (diff >= 0));
-          sq[t][r] = ok ? sq[t][r] : -INFINITY;
-        }
-    }
-    float mx = sq[0][0];
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
+      mx = max_with_partner(mx);
+      const float m_new = mx * c;
+      const bool moved = __any(m_new > m_ref + 8.f);
+      const float m_use = moved ? fmaxf(m_ref, m_new) : m_ref;
+      const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_use);
+      const float msub = (m_use == -INFINITY) ? 0.f : m_use;
+      // Accumulator registers 8q .. 8q+7 of tile t are exactly the 8 keys this
+      // lane supplies for 16-key chunk 2t + q of the P.V product.
+      bf16x8 pb[4];
+      float lsum = 0.f;
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sq[t][r]);
-    mx = max_with_partner(mx);
-    const float m_new = mx * c;
-    const bool moved = __any(m_new > m_ref + 8.f);
-    const float m_use = moved ? fmaxf(m_ref, m_new) : m_ref;
-    const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_use);
-    const float msub = (m_use == -INFINITY) ? 0.f : m_use;
-    float lsum = 0.f;
+        for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-        for (int ii = 0; ii < 8; ++ii) {
-          const float pv_ = __builtin_amdgcn_exp2f(fmaf(sq[t][q2 * 8 + ii], c, -msub));
-          lsum += pv_;
-          pq[t * 2 + q2][ii] = static_cast<__bf16>(pv_);
-        }
-    l_part = fmaf(l_part, alpha, lsum);
-    if (moved) {
-      __asm__ volatile("");
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    }
-    m_ref = m_use;
-  };
-
-  // Task lists.  Group g owns tiles t = 0 .. n-1 (CSR entries 2t + g).  Its
-  // tasks alternate M (even tau) and V (odd tau): M-task m does P.V of half
-  // m - 1 and S^T of half m, then refills the slots M-task m - 1 released;
-  // V-task v does the softmax of half v.  Tile 0 is loaded before the loop.
-  // Group 1 runs one phase behind group 0.
-  const int e0 = row.start, ne = row.count;
-  const int n = (ne + 1 - grp) >> 1;
-  const int ntask = n > 0 ? 4 * n + 1 : 0;
-  const int n0 = (ne + 1) >> 1, n1 = ne >> 1;
-  const int nphase = max(n0 > 0 ? 4 * n0 + 1 : 0, n1 > 0 ? 4 * n1 + 2 : 0);
-  // The group's CSR entries are cached 64 at a time in one VGPR (lane l holds
-  // tile 64*c + l) and read with v_readlane; a refill happens once every 64
-  // tiles.  ents (= p.entries) is a separate restrict-qualified argument: no
-  // store of this kernel aliases it.
-  int ent_cache = 0, ent_chunk = -1;
-  auto entry_of = [&](int t) {
-    const int chunk = t >> 6;
-    if (chunk != ent_chunk) {
-      const int idx = 2 * ((chunk << 6) + lane) + grp;
-      ent_cache = idx < ne ? ents[e0 + idx] : 0;
-      ent_chunk = chunk;
-      // Complete the refill here; a pending load at the join would make every
-      // later readlane wait for all outstanding loads.
-      __asm__ volatile("" ::"v"(ent_cache));
-    }
-    return __builtin_amdgcn_readlane(ent_cache, t & 63);
-  };
-
-  if (n > 0) {
-    const int j0 = entry_of(0) >> 1;
-    dma_half(Kg, Kl, j0, 0, false);
-    dma_half(Kg, Kl, j0, 1, false);
-    dma_half(Vg, Vl, j0, 0, true);
-    dma_half(Vg, Vl, j0, 1, true);
-    BSA_WAIT_VMCNT(0);
-  }
-  phase_barrier();
-
-  f32x16 s_cur[2];
-  s_cur[0] = f32x16{};
-  s_cur[1] = f32x16{};
-  bf16x8 p_cur[4];
-#pragma unroll
-  for (int cq = 0; cq < 4; ++cq) p_cur[cq] = bf16x8{};
-  for (int ph = 0; ph < nphase; ++ph) {
-    const int tau = ph - grp;
-    if (tau >= 0 && tau < ntask) {
-      if ((tau & 1) == 0) {
-        // Branch-free so the 32 MFMAs and their LDS reads form one block: the
-        // first task multiplies a zero P, the last recomputes an S^T of the
-        // current K tile that is never used.
-        const int m = tau >> 1;
-        pv_half((m + 1) & 1, p_cur);
-        qk_half(m & 1, s_cur);
-        interleave_mphase();
-        // Refill the half-slots M-task m - 1 released (its K half and the V
-        // half it multiplied); both are next read by M-task m + 1.  Issued
-        // after the MFMAs, which keep the matrix pipe busy while the loads are
-        // accepted.
-        if (m >= 1) {
-          const int tk = ((m - 1) >> 1) + 1;              // K(tk) half (m - 1) & 1
-          if (tk < n) {
-            dma_half(Kg, Kl, entry_of(tk) >> 1, (m - 1) & 1, false);
+          for (int ii = 0; ii < 8; ++ii) {
+            const float pv = __builtin_amdgcn_exp2f(fmaf(s[t][q2 * 8 + ii], c, -msub));
+            lsum += pv;
+            pb[t * 2 + q2][ii] = static_cast<__bf16>(pv);
           }
+      l_part = fmaf(l_part, alpha, lsum);
+      if (moved) {
+        __asm__ volatile("");
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      m_ref = m_use;
+      // O^T += V^T P^T over the half's four 16-key chunks.
+#pragma unroll
+      for (int cq = 0; cq < 4; ++cq) {
+        const int c16 = half * 4 + cq;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16x4 lo = lds_read_tr(vtr + (c16 * 16) * kVS + dt * 32);
+          const bf16x4 hi = lds_read_tr(vtr + (c16 * 16 + 8) * kVS + dt * 32);
+          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cq], o[dt], 0, 0, 0);
         }
-        if (m >= 2) {
-          const int tv = ((m - 2) >> 1) + 1;              // V(tv) half m & 1
-          if (tv < n) {
-            dma_half(Vg, Vl, entry_of(tv) >> 1, m & 1, true);
-          }
-        }
-      } else {
-        const int v = tau >> 1;
-        const int t = v >> 1, hh = v & 1;
-        const int ent = entry_of(t);
-        softmax_half(s_cur, hh, ent >> 1, ent & 1, p_cur);
-        // The next M-task reads what the latest M-task loaded (its refills
-        // have this whole phase to land).
-        BSA_WAIT_VMCNT(0);
       }
     }
-    phase_barrier();
   }
 
-  // Merge the two groups' partial results (group 1 hands over through LDS).
-  const float l_g = sum_with_partner(l_part);
-  float* xo = reinterpret_cast<float*>(lds);              // [4 waves][64 regs][64 lanes]
-  float* xm = xo + 4 * 64 * 64;                           // [4 waves][64 lanes]
-  float* xl = xm + 4 * 64;
-  if (grp == 1) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xo[(wave4 * 64 + dt * 16 + r) * 64 + lane] = o[dt][r];
-    xm[wave4 * 64 + lane] = m_ref;
-    xl[wave4 * 64 + lane] = l_g;
-  }
-  __syncthreads();
-  if (grp == 1) return;
-  const float m1 = xm[wave4 * 64 + lane];
-  const float l1 = xl[wave4 * 64 + lane];
-  const float mm = fmaxf(m_ref, m1);
-  const float a0 = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - mm);
-  const float a1 = (m1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m1 - mm);
-  const float l = l_g * a0 + l1 * a1;
+  // Epilogue: O = acc / l (0 for an empty row), LSE = ln2 * (m_ref + log2 l).
+  const float l = sum_with_partner(l_part);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  const float w0 = a0 * inv, w1 = a1 * inv;
   uint16_t* Op = static_cast<uint16_t*>(p.o) + ((int64_t(b) * p.H + h) * p.N + qg) * kD;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-    for (int g4 = 0; g4 < 4; ++g4) {
-      float v4[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        v4[e] = o[dt][4 * g4 + e] * w0 + xo[(wave4 * 64 + dt * 16 + 4 * g4 + e) * 64 + lane] * w1;
+    for (int g = 0; g < 4; ++g) {
       u32x2 pk;
-      pk[0] = uint32_t(bf16_bits(v4[0])) | (uint32_t(bf16_bits(v4[1])) << 16);
-      pk[1] = uint32_t(bf16_bits(v4[2])) | (uint32_t(bf16_bits(v4[3])) << 16);
-      *reinterpret_cast<u32x2*>(Op + dt * 32 + 8 * g4 + 4 * hf) = pk;
+      pk[0] = uint32_t(bf16_bits(o[dt][4 * g + 0] * inv)) | (uint32_t(bf16_bits(o[dt][4 * g + 1] * inv)) << 16);
+      pk[1] = uint32_t(bf16_bits(o[dt][4 * g + 2] * inv)) | (uint32_t(bf16_bits(o[dt][4 * g + 3] * inv)) << 16);
+      *reinterpret_cast<u32x2*>(Op + dt * 32 + 8 * g + 4 * hf) = pk;
     }
   if (hf == 0)
-    p.lse[(int64_t(b) * p.H + h) * p.N + qg] = l > 0.f ? (mm + log2f(l)) * kLn2 : -INFINITY;
+    p.lse[(int64_t(b) * p.H + h) * p.N + qg] = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
 }
 
 // ---------------------------------------------------------------------------
@@ -612,7 +454,7 @@ extern "C" bsa_status_t bsa_forward(const void* q, const void* k, const void* v,
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = hipSuccess;
   if (pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128) {
-    hipLaunchKernelGGL(fwd_bf16_d128, dim3(unsigned(slots)), dim3(kPPThreads), 0, s, prm, prm.entries);
+    hipLaunchKernelGGL(fwd_bf16_d128, dim3(unsigned(slots)), dim3(kThreads), 0, s, prm, prm.entries);
     err = hipGetLastError();
   } else if (pr.dtype == BSA_F32 && pr.head_dim == 64 && pr.block_size == 64) {
     err = launch_f32<64, 64>(prm, slots, s);
