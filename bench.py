@@ -131,6 +131,30 @@ def cpu_baseline(w, lay, q, k, v, flops, seconds=15.0):
             "extrapolated_full_s": round(full_s, 1)}
 
 
+def recorded_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE, each scaled by its plain-copy calibration).
+    None when there is no summary for this kernel and workload, or when the
+    kernel source changed since the counters were taken."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", f"{kernel}_{workload}_hbm.txt")
+    src = os.path.join(here, "block_sparse_flash_bsa_amd", "csrc", "forward.hip")
+    if not os.path.exists(path) or not os.path.exists(src):
+        return None
+    rec = {}
+    with open(path) as f:
+        for line in f:
+            if not line.startswith("#") and ":" in line:
+                key, val = line.split(":", 1)
+                rec[key.strip()] = val.strip()
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("forward_hip_sha256") != sha or "traffic_bytes_per_launch" not in rec:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
 def calibrate_copy(mib):
     """A plain device copy of known size, for scaling HBM byte counters."""
     x = torch.ones(mib * 2 ** 18, dtype=torch.float32, device="cuda")
@@ -188,6 +212,7 @@ def main():
     achieved = flops / (kern_ms * 1e-3) / 1e12
     log(f"[bench] {args.steps} steps: {wall_ms:.3f} ms/forward wall, kernel {kern_ms:.3f} ms "
         f"(min {min(ev_ms):.3f}, max {max(ev_ms):.3f}) -> {achieved:.1f} TFLOP/s")
+    kernel = "fwd_bf16_d128" if w.dtype == torch.bfloat16 else "fwd_f32"
     elem = 2 if w.dtype == torch.bfloat16 else 4
     min_bytes = (q.numel() + k.numel() + v.numel() + out.numel()) * elem + lse.numel() * 4
     result = {
@@ -210,8 +235,9 @@ def main():
         "pct_of_mfma_peak": round(100 * value / peak, 2),
         "plan_ms": round(plan_ms, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
-                     "kernel": "fwd_bf16_d128" if w.dtype == torch.bfloat16 else "fwd_f32",
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": recorded_traffic(kernel, w.name), "traffic_unit": "HBM bytes per launch",
+                     "kernel": kernel,
                      "kernel_ms": round(kern_ms, 4),
                      "algorithmic_flops": flops, "min_hbm_bytes": min_bytes},
     }
