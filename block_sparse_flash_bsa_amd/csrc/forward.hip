@@ -41,6 +41,7 @@ struct FwdParams {
   const RowDesc* rows;
   const int32_t* entries;
   const int32_t* work;
+  const int32_t* pair_work;
   int64_t N;
   int32_t H, Hkv, group, nb, per_head_layout;
   float sl2;  // scale * log2(e)
@@ -116,15 +117,33 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
-// One workgroup of 4 waves per (b, h, q-block); wave w owns query rows
-// 32w .. 32w+31.  Two workgroups share a CU (75 KB of LDS each), so each SIMD
-// holds two independent waves whose MFMA and softmax phases overlap.  Per
-// CSR entry: the K/V tile prefetched into registers during the previous tile
-// is written to LDS between two barriers, the next tile's loads are issued,
-// and the tile is processed in two 64-key halves (S^T, mask, softmax, P.V).
+// One workgroup of 4 waves per (b, h, q-block) work item; wave w owns query
+// rows 32w .. 32w+31.  Two workgroups share a CU (64 KB of LDS each), so each
+// SIMD interleaves two independent waves whose matrix and softmax phases
+// overlap.  K and V each have one 32 KB LDS tile, filled by direct HBM->LDS
+// loads (global_load_lds_dwordx4; no staging registers, no LDS stores).  A
+// tile is processed in two 64-key halves; per CSR entry e the workgroup
+// passes three barriers:
+//   1. K(e) has landed and every wave is done with V(e-1): load V(e), then
+//      S^T and softmax of half 0;
+//   2. V(e) has landed: P.V of half 0, S^T of half 1;
+//   3. every wave is done with K(e): load K(e+1), softmax and P.V of half 1.
+// Each load has at least a softmax plus a matrix phase to land.  LDS rows
+// are 256 bytes with their 16-byte chunks XOR-swizzled (K chunk c of row r at
+// c ^ (r & 15), V chunk c at c ^ 4*(r & 3)), which keeps the 16-byte K reads
+// and the transposed V reads free of bank conflicts.
+constexpr int kTileBytes = kBN * kD * 2;   // 32 KB
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// Wait until at most N of this wave's vector-memory operations are pending,
+// then a workgroup barrier.  The "memory" clobber keeps LDS accesses on their
+// side of the barrier; vector-memory loads issued later are not waited for.
+#define BSA_WAIT_BARRIER(N) \
+  __asm__ volatile("s_waitcnt vmcnt(" #N ")\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+#define BSA_BARRIER() __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const int32_t* __restrict__ ents) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * kKS];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[kBN * kVS];
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kTileBytes];
 
   const int item = p.work[blockIdx.x];
   if (item < 0) return;
@@ -134,49 +153,67 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   const RowDesc row = p.rows[(p.per_head_layout ? h : 0) * p.nb + i];
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, r32 = lane & 31, hf = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r32 = lane & 31, hf = lane >> 5;
   const int qrow = wave * 32 + r32;                       // row within the q-block
   const int64_t qg = int64_t(i) * kBM + qrow;             // global query index
 
   const uint16_t* __restrict__ Qp =
       static_cast<const uint16_t*>(p.q) + ((int64_t(b) * p.H + h) * p.N + qg) * kD;
-  const uint16_t* __restrict__ Kb =
-      static_cast<const uint16_t*>(p.k) + (int64_t(b) * p.Hkv + hk) * p.N * kD;
-  const uint16_t* __restrict__ Vb =
-      static_cast<const uint16_t*>(p.v) + (int64_t(b) * p.Hkv + hk) * p.N * kD;
+  const unsigned char* Kg =
+      reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.k) + (int64_t(b) * p.Hkv + hk) * p.N * kD);
+  const unsigned char* Vg =
+      reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.v) + (int64_t(b) * p.Hkv + hk) * p.N * kD);
 
   // Q^T operand: lane (row r32, half hf) holds d = 16c + 8hf .. +7 for c = 0..7.
   bf16x8 qf[8];
 #pragma unroll
   for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(Qp + c * 16 + hf * 8);
-  // Complete the Q loads here so no wait on them lands inside the loop.
-  __asm__ volatile("" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]), "v"(qf[5]),
-                   "v"(qf[6]), "v"(qf[7]));
+  // Complete the Q loads before the first HBM->LDS load, so the counts of
+  // pending loads below only see those.
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::"v"(qf[0]), "v"(qf[7]) : "memory");
 
-  // K/V staging registers: thread loads rows rr + 16u, 16 bytes at column col8,
-  // of both K and V (coalesced 256-byte rows, 16 threads per row).
-  u32x4 kr[8], vr[8];
-  const int rr = tid >> 4, col8 = (tid & 15) * 8;
-  auto load_kv = [&](int j) {
-    const uint16_t* kp = Kb + int64_t(j) * kBN * kD + rr * kD + col8;
-    const uint16_t* vp = Vb + int64_t(j) * kBN * kD + rr * kD + col8;
+  unsigned char* const Kl = lds;
+  unsigned char* const Vl = lds + kTileBytes;
+  // HBM->LDS load of K or V tile j: wave w fills rows 32w .. 32w+31, 4 rows
+  // (1 KB) per instruction; lane L writes chunk L % 16 of row 4u + L / 16 and
+  // reads the logical chunk the swizzle places there.
+  const int lr = lane >> 4, lc = lane & 15;
+  // Rows 4u + L/16 and 4(u+4) + L/16 share their swizzle, so four 32-bit
+  // per-lane offsets serve all eight K instructions (the upper four add
+  // 4096 bytes to the uniform base); V needs one offset plus 1 KB steps.
+  uint32_t dko[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) kr[u] = *reinterpret_cast<const u32x4*>(kp + u * 16 * kD);
+  for (int u = 0; u < 4; ++u) dko[u] = (4 * u + lr) * 256 + 16 * (lc ^ ((4 * u + lr) & 15));
+  const uint32_t dvo = lr * 256 + 16 * (lc ^ (4 * lr));
+  auto dma_tile = [&](const unsigned char* g, unsigned char* buf, int j, bool is_v) {
+    const unsigned char* src = g + (int64_t(j) * kBN + wave * 32) * (kD * 2);
+    unsigned char* dst = buf + wave * 32 * 256;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) vr[u] = *reinterpret_cast<const u32x4*>(vp + u * 16 * kD);
-  };
-  auto store_kv = [&]() {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) *reinterpret_cast<u32x4*>(Ks + (rr + 16 * u) * kKS + col8) = kr[u];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) *reinterpret_cast<u32x4*>(Vs + (rr + 16 * u) * kVS + col8) = vr[u];
+    for (int u = 0; u < 8; ++u) {
+      const unsigned char* base = src + (u >= 4 ? 4096 : 0);
+      const uint32_t off = is_v ? dvo + (u & 3) * 1024 : dko[u & 3];
+      __builtin_amdgcn_global_load_lds(base + off,
+                                       (__attribute__((address_space(3))) void*)(dst + 4 * u * 256), 16, 0, 0);
+    }
   };
 
-  // V^T operand of P.V by transposed reads: in 16-lane group g, lane 4*r4 + c4
-  // addresses key row 4*hf + r4 (+ 16*c16, + 8 for the upper 8 keys) and
-  // columns 32*dt + 16*(g & 1) + 4*c4 .. +3; lane l then receives the 4 keys
-  // of column d = 32*dt + (l & 31).
-  const uint16_t* vtr = Vs + (4 * hf + ((lane & 15) >> 2)) * kVS + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  // Per-lane LDS operand offsets (swizzle folded in).
+  // K (A operand of S^T): row 32kt + r32, logical chunk 2cc + hf.
+  uint32_t koff[8];
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) koff[cc] = r32 * 256 + 16 * ((2 * cc + hf) ^ (r32 & 15));
+  // V^T operand by transposed reads: in 16-lane group g, lane 4*r4 + c4
+  // addresses key row 16*c16 + 8*s + 4*hf + r4 and columns
+  // 32*dt + 16*(g & 1) + 4*c4 .. +3; lane l then receives the 4 keys of
+  // column d = 32*dt + (l & 31).
+  const int r4 = (lane & 15) >> 2, c4 = lane & 3, gp = (lane >> 4) & 1;
+  uint32_t voff[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+    voff[dt] = (4 * hf + r4) * 256 + 16 * ((4 * dt + 2 * gp + (c4 >> 1)) ^ (4 * r4)) + 8 * (c4 & 1);
+  lds_u8* const Kl3 = (lds_u8*)Kl;    // generic -> LDS address-space casts
+  lds_u8* const Vl3 = (lds_u8*)Vl;
 
   f32x16 o[4];
 #pragma unroll
@@ -186,100 +223,114 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   const float c = p.sl2;
   const bool q_global = qg < p.gq32;
 
+  // S^T for the 64 keys of half hh: two 32x32 tiles; lane holds row r32,
+  // keys 64*hh + 32*t + 8*(r/4) + 4*hf + r%4 in accumulator register r of
+  // tile t.
+  auto qk_half = [&](int hh, f32x16 (&sq)[2]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      sq[t] = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const bf16x8 a = *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(
+            Kl3 + koff[cc] + (hh * 64 + t * 32) * 256);
+        sq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], sq[t], 0, 0, 0);
+      }
+    }
+  };
+  // Softmax of half hh of tile j in place: token mask (PARTIAL tiles only),
+  // row max (in-lane, then with lane l ^ 32), lazy move of the reference max
+  // (only when some row's max grows by more than 2^8: a wave-uniform
+  // decision), P = exp2(c*S - m) in bf16, and the matching rescale of O and
+  // l.  Accumulator registers 8q .. 8q+7 of S^T tile t are exactly the 8 keys
+  // this lane supplies for 16-key chunk 2t + q of the P.V product.  The empty
+  // volatile asm keeps the two conditional blocks real branches.
+  auto softmax_half = [&](f32x16 (&sq)[2], int hh, int j, bool partial, bf16x8 (&pq)[4]) {
+    if (partial) {
+      __asm__ volatile("");
+      const int k0 = j * kBN;
+      const int dq = int(qg) - k0;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int koff_ = hh * 64 + t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const int diff = dq - koff_;                             // q - k
+          const bool in_w = (p.wl32 < 0 || diff <= p.wl32) & (p.wr32 < 0 || -diff <= p.wr32);
+          const bool rule = !p.token_rule | in_w | (k0 + koff_ < p.gk32) | q_global;
+          const bool ok = rule & (!p.causal | (diff >= 0));
+          sq[t][r] = ok ? sq[t][r] : -INFINITY;
+        }
+    }
+    float mx = sq[0][0];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sq[t][r]);
+    mx = max_with_partner(mx);
+    const float m_new = mx * c;
+    const bool moved = __any(m_new > m_ref + 8.f);
+    const float m_use = moved ? fmaxf(m_ref, m_new) : m_ref;
+    const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_use);
+    const float msub = (m_use == -INFINITY) ? 0.f : m_use;
+    float lsum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int ii = 0; ii < 8; ++ii) {
+          const float pv = __builtin_amdgcn_exp2f(fmaf(sq[t][q2 * 8 + ii], c, -msub));
+          lsum += pv;
+          pq[t * 2 + q2][ii] = static_cast<__bf16>(pv);
+        }
+    l_part = fmaf(l_part, alpha, lsum);
+    if (moved) {
+      __asm__ volatile("");
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+    m_ref = m_use;
+  };
+  // O^T += V^T P^T over the four 16-key chunks of half hh.
+  auto pv_half = [&](int hh, const bf16x8 (&pq)[4]) {
+#pragma unroll
+    for (int cq = 0; cq < 4; ++cq) {
+      const int c16 = hh * 4 + cq;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) s16x4*>(Vl3 + voff[dt] + (16 * c16) * 256)));
+        const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            reinterpret_cast<__attribute__((address_space(3))) s16x4*>(Vl3 + voff[dt] + (16 * c16 + 8) * 256)));
+        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pq[cq], o[dt], 0, 0, 0);
+      }
+    }
+  };
+
   const int e0 = row.start, ne = row.count;
-  if (ne > 0) load_kv(ents[e0] >> 1);
+  if (ne > 0) dma_tile(Kg, Kl, ents[e0] >> 1, false);
   for (int e = 0; e < ne; ++e) {
     const int ent = ents[e0 + e];
     const int j = ent >> 1;
     const bool partial = ent & 1;
-    __syncthreads();           // every wave is done with the previous tile
-    store_kv();
-    __syncthreads();
-    if (e + 1 < ne) load_kv(ents[e0 + e + 1] >> 1);
+    f32x16 sq[2];
+    bf16x8 pq[4];
 
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      // S^T for 64 keys: two 32x32 tiles; lane holds row r32, keys
-      // 64*half + 32*t + 8*(r/4) + 4*hf + r%4 in accumulator register r.
-      f32x16 s[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        s[t] = f32x16{};
-        const int kt = half * 2 + t;
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (kt * 32 + r32) * kKS + cc * 16 + hf * 8);
-          s[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], s[t], 0, 0, 0);
-        }
-      }
-      // Token mask, PARTIAL tiles only.  The empty volatile asm keeps this a
-      // real branch (not a select over every score of every tile).
-      if (partial) {
-        __asm__ volatile("");
-        const int k0 = j * kBN;
-        const int dq = int(qg) - k0;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int koff = half * 64 + t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const int diff = dq - koff;                              // q - k
-            const bool in_w = (p.wl32 < 0 || diff <= p.wl32) & (p.wr32 < 0 || -diff <= p.wr32);
-            const bool rule = !p.token_rule | in_w | (k0 + koff < p.gk32) | q_global;
-            const bool ok = rule & (!p.causal | (diff >= 0));
-            s[t][r] = ok ? s[t][r] : -INFINITY;
-          }
-      }
-      // Row max (in-lane, then with lane l ^ 32), lazy move of the reference
-      // max (only when some row's max grows by more than 2^8: a wave-uniform
-      // decision), P = exp2(c*S - m) in bf16, and the matching rescale.
-      float mx = s[0][0];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[t][r]);
-      mx = max_with_partner(mx);
-      const float m_new = mx * c;
-      const bool moved = __any(m_new > m_ref + 8.f);
-      const float m_use = moved ? fmaxf(m_ref, m_new) : m_ref;
-      const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_use);
-      const float msub = (m_use == -INFINITY) ? 0.f : m_use;
-      // Accumulator registers 8q .. 8q+7 of tile t are exactly the 8 keys this
-      // lane supplies for 16-key chunk 2t + q of the P.V product.
-      bf16x8 pb[4];
-      float lsum = 0.f;
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2)
-#pragma unroll
-          for (int ii = 0; ii < 8; ++ii) {
-            const float pv = __builtin_amdgcn_exp2f(fmaf(s[t][q2 * 8 + ii], c, -msub));
-            lsum += pv;
-            pb[t * 2 + q2][ii] = static_cast<__bf16>(pv);
-          }
-      l_part = fmaf(l_part, alpha, lsum);
-      if (moved) {
-        __asm__ volatile("");
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-      }
-      m_ref = m_use;
-      // O^T += V^T P^T over the half's four 16-key chunks.
-#pragma unroll
-      for (int cq = 0; cq < 4; ++cq) {
-        const int c16 = half * 4 + cq;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const bf16x4 lo = lds_read_tr(vtr + (c16 * 16) * kVS + dt * 32);
-          const bf16x4 hi = lds_read_tr(vtr + (c16 * 16 + 8) * kVS + dt * 32);
-          const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[cq], o[dt], 0, 0, 0);
-        }
-      }
-    }
+    BSA_WAIT_BARRIER(0);                 // 1: K(e) landed; V(e-1) released
+    dma_tile(Vg, Vl, j, true);
+    qk_half(0, sq);
+    softmax_half(sq, 0, j, partial, pq);
+    BSA_WAIT_BARRIER(0);                 // 2: V(e) landed (the only load in flight)
+    pv_half(0, pq);
+    qk_half(1, sq);
+    BSA_BARRIER();                       // 3: K(e) released
+    if (e + 1 < ne) dma_tile(Kg, Kl, ents[e0 + e + 1] >> 1, false);
+    softmax_half(sq, 1, j, partial, pq);
+    pv_half(1, pq);
   }
 
   // Epilogue: O = acc / l (0 for an empty row), LSE = ln2 * (m_ref + log2 l).
