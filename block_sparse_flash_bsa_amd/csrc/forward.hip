@@ -16,12 +16,15 @@
 // each lane holds one query row: the row max and row sum are in-lane plus a
 // single exchange between lanes l and l + 32.  O^T = V^T P^T keeps that
 // layout, so the per-row rescale is a per-lane scalar.  K and V are staged in
-// LDS row-major; the V^T operand of P.V is read with ds_read_b64_tr_b16, which
-// transposes 4x4 blocks of 16-bit elements across each group of 16 lanes, so
-// no transpose is done in registers.  The key order inside each 16-key chunk
-// of P follows the S^T accumulator layout, and the V reads use the same order.
-// The softmax runs in the exp2 domain with a lazily updated reference max
-// (the accumulator is rescaled only when a row max grows by more than 2^8).
+// LDS row-major (with an XOR swizzle); the V^T operand of P.V is read with
+// ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit elements across
+// each group of 16 lanes, so no transpose is done in registers.  The key order
+// inside each 16-key chunk of P follows the S^T accumulator layout, and the V
+// reads use the same order.  The softmax runs in the exp2 domain with a lazily
+// updated reference max (the accumulator is rescaled only when a row max grows
+// by more than 2^8), in passes over independent registers: on gfx950 the
+// VALU work per tile is about as large as the matrix work, and dependent
+// instruction chains would leave it latency-bound.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -41,7 +44,6 @@ struct FwdParams {
   const RowDesc* rows;
   const int32_t* entries;
   const int32_t* work;
-  const int32_t* pair_work;
   int64_t N;
   int32_t H, Hkv, group, nb, per_head_layout;
   float sl2;  // scale * log2(e)
@@ -84,20 +86,9 @@ constexpr int kBM = 128;        // query rows per workgroup (= layout block)
 constexpr int kBN = 128;        // keys per CSR entry (= layout block)
 constexpr int kD = 128;         // head dim
 constexpr int kThreads = 256;   // 4 waves of 64
-constexpr int kKS = kD + 8;     // K row stride in LDS (elements): 272 B, conflict-free 16 B reads
-constexpr int kVS = kD + 32;    // V row stride in LDS (elements): 320 B, conflict-free transposed reads
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-// Four 16-bit elements per lane, transposed across each 16-lane group: lane
-// 4c + e of the group receives element e of the 8 bytes addressed by lanes
-// c, 4 + c, 8 + c, 12 + c (in that order).
-__device__ __forceinline__ bf16x4 lds_read_tr(const uint16_t* p) {
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (s16x4 __attribute__((address_space(3)))*)(p));
-  return __builtin_bit_cast(bf16x4, v);
-}
 
 // Max of x over lanes l and l ^ 32 (v_permlane32_swap: one result holds the
 // lane's own value, the other its partner's).
@@ -111,6 +102,14 @@ __device__ __forceinline__ float sum_with_partner(float x) {
   const uint32_t b = __float_as_uint(x);
   const auto sw = __builtin_amdgcn_permlane32_swap(b, b, false, false);
   return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
+// Max of the 16 values of an MFMA accumulator tile as a tree of v_max3.
+__device__ __forceinline__ float max3_tree(const f32x16& v) {
+  const float a = fmaxf(fmaxf(v[0], v[1]), v[2]), b = fmaxf(fmaxf(v[3], v[4]), v[5]);
+  const float c = fmaxf(fmaxf(v[6], v[7]), v[8]), d = fmaxf(fmaxf(v[9], v[10]), v[11]);
+  const float e = fmaxf(fmaxf(v[12], v[13]), v[14]);
+  return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), v[15]));
 }
 
 __device__ __forceinline__ uint16_t bf16_bits(float x) {
@@ -143,7 +142,8 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 #define BSA_BARRIER() __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const int32_t* __restrict__ ents) {
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[2 * kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char Kl[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vl[kTileBytes];
 
   const int item = p.work[blockIdx.x];
   if (item < 0) return;
@@ -171,10 +171,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(Qp + c * 16 + hf * 8);
   // Complete the Q loads before the first HBM->LDS load, so the counts of
   // pending loads below only see those.
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::"v"(qf[0]), "v"(qf[7]) : "memory");
+  __asm__ volatile("s_waitcnt vmcnt(0)" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]),
+                   "v"(qf[5]), "v"(qf[6]), "v"(qf[7]) : "memory");
 
-  unsigned char* const Kl = lds;
-  unsigned char* const Vl = lds + kTileBytes;
   // HBM->LDS load of K or V tile j: wave w fills rows 32w .. 32w+31, 4 rows
   // (1 KB) per instruction; lane L writes chunk L % 16 of row 4u + L / 16 and
   // reads the logical chunk the swizzle places there.
@@ -262,29 +261,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
           sq[t][r] = ok ? sq[t][r] : -INFINITY;
         }
     }
-    float mx = sq[0][0];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sq[t][r]);
+    float mx = fmaxf(max3_tree(sq[0]), max3_tree(sq[1]));
     mx = max_with_partner(mx);
     const float m_new = mx * c;
     const bool moved = __any(m_new > m_ref + 8.f);
     const float m_use = moved ? fmaxf(m_ref, m_new) : m_ref;
     const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_use);
     const float msub = (m_use == -INFINITY) ? 0.f : m_use;
-    float lsum = 0.f;
+    // Independent passes over the 32 scores (exponent argument, exp2, bf16
+    // pack, four partial row sums) keep dependent instructions apart.
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sq[t][r] = fmaf(sq[t][r], c, -msub);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sq[t][r] = __builtin_amdgcn_exp2f(sq[t][r]);
+    float ls[4] = {sq[0][0], sq[0][1], sq[0][2], sq[0][3]};
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
         for (int ii = 0; ii < 8; ++ii) {
-          const float pv = __builtin_amdgcn_exp2f(fmaf(sq[t][q2 * 8 + ii], c, -msub));
-          lsum += pv;
-          pq[t * 2 + q2][ii] = static_cast<__bf16>(pv);
+          if (t > 0 || q2 > 0 || ii >= 4) ls[ii & 3] += sq[t][q2 * 8 + ii];
+          pq[t * 2 + q2][ii] = static_cast<__bf16>(sq[t][q2 * 8 + ii]);
         }
-    l_part = fmaf(l_part, alpha, lsum);
+    l_part = fmaf(l_part, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
     if (moved) {
       __asm__ volatile("");
 #pragma unroll

@@ -15,20 +15,6 @@ struct RowDesc {
   int32_t count;
 };
 
-// Two work items that read the same K/V head, run by one workgroup of the
-// paired kernel over the union of their key-block lists.  item[1] is -1 when
-// the item has no partner.
-struct PairDesc {
-  int32_t item[2];
-  int32_t start;   // first union entry
-  int32_t count;   // union entries
-};
-
-// Union entry encoding: (key block << 4) | state(item 0) | state(item 1) << 2,
-// state 0 = FULL, 1 = PARTIAL (token mask), 2 = not in that item's list.
-constexpr int kPairFull = 0, kPairPartial = 1, kPairAbsent = 2;
-inline int32_t encode_pair_entry(int32_t j, int s0, int s1) { return (j << 4) | s0 | (s1 << 2); }
-
 // Entry encoding in device memory: (key block << 1) | partial.
 inline int32_t encode_entry(int32_t j, bool partial) { return (j << 1) | (partial ? 1 : 0); }
 
@@ -55,11 +41,6 @@ struct bsa_plan {
   std::vector<std::vector<int32_t>> col_idx;   // [layout_heads][nnz_h]
   std::vector<std::vector<uint8_t>> flags;     // [layout_heads][nnz_h]
   std::vector<int32_t> work;                   // [launch slots], -1 = idle
-  // Paired launch (bf16 kernel): pairs, their union entries and launch order.
-  bool paired = false;
-  std::vector<bsa::PairDesc> pairs;
-  std::vector<int32_t> pair_entries;
-  std::vector<int32_t> pair_work;              // [pair launch slots], -1 = idle
   bsa_plan_info_t info{};
   // Device copy (bsa_plan only).
   int device = -1;
@@ -67,9 +48,6 @@ struct bsa_plan {
   const bsa::RowDesc* d_rows = nullptr;        // [layout_heads * nb]
   const int32_t* d_entries = nullptr;          // [nnz]
   const int32_t* d_work = nullptr;             // [launch slots]
-  const bsa::PairDesc* d_pairs = nullptr;
-  const int32_t* d_pair_entries = nullptr;
-  const int32_t* d_pair_work = nullptr;
 };
 
 namespace bsa {
