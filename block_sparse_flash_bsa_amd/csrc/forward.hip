@@ -119,19 +119,32 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 // One workgroup of 4 waves per (b, h, q-block) work item; wave w owns query
 // rows 32w .. 32w+31.  Two workgroups share a CU (64 KB of LDS each), so each
 // SIMD interleaves two independent waves whose matrix and softmax phases
-// overlap.  K and V each have one 32 KB LDS tile, filled by direct HBM->LDS
-// loads (global_load_lds_dwordx4; no staging registers, no LDS stores).  A
-// tile is processed in two 64-key halves; per CSR entry e the workgroup
-// passes three barriers:
-//   1. K(e) has landed and every wave is done with V(e-1): load V(e), then
-//      S^T and softmax of half 0;
-//   2. V(e) has landed: P.V of half 0, S^T of half 1;
-//   3. every wave is done with K(e): load K(e+1), softmax and P.V of half 1.
-// Each load has at least a softmax plus a matrix phase to land.  LDS rows
-// are 256 bytes with their 16-byte chunks XOR-swizzled (K chunk c of row r at
-// c ^ (r & 15), V chunk c at c ^ 4*(r & 3)), which keeps the 16-byte K reads
-// and the transposed V reads free of bank conflicts.
+// overlap.  K has one 32 KB LDS tile and V two 16 KB halves, all filled by
+// direct HBM->LDS loads (global_load_lds_dwordx4; no staging registers, no
+// LDS stores).  A tile is processed in two 64-key halves; per CSR entry e the
+// workgroup passes two barriers:
+//   1. K(e) and the first half of V(e) have landed, and every wave is done
+//      with the second half of V(e-1): load that half of V(e); S^T, softmax
+//      and P.V of half 0; S^T of half 1;
+//   2. the second half of V(e) has landed, and every wave is done with K(e)
+//      and with the first half of V(e): load K(e+1) and the first half of
+//      V(e+1); softmax and P.V of half 1.
+// Every load thus has at least a softmax and a matrix phase to land.  LDS
+// rows are 256 bytes with their 16-byte chunks XOR-swizzled (K chunk c of row
+// r at c ^ (r & 15), V chunk c at c ^ 4*(r & 3)), which keeps the 16-byte K
+// reads and the transposed V reads free of bank conflicts.
 constexpr int kTileBytes = kBN * kD * 2;   // 32 KB
+
+// HBM->LDS load of 16 bytes per lane (1 KB per wave) from sbase + voff into
+// LDS at lds_addr + 16 * lane.  Inline assembly, so the compiler adds no
+// waits of its own for it (its alias tracking of such loads is coarse and
+// would make unrelated LDS reads wait for every load in flight); each use is
+// followed by an explicit s_waitcnt vmcnt and a barrier before the data is
+// read.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 // Wait until at most N of this wave's vector-memory operations are pending,
@@ -139,11 +152,12 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 // side of the barrier; vector-memory loads issued later are not waited for.
 #define BSA_WAIT_BARRIER(N) \
   __asm__ volatile("s_waitcnt vmcnt(" #N ")\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
-#define BSA_BARRIER() __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const int32_t* __restrict__ ents) {
   __shared__ __attribute__((aligned(1024))) unsigned char Kl[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char Vl[kTileBytes];
+  // V as two 64-key halves, refilled at different times.
+  __shared__ __attribute__((aligned(1024))) unsigned char Vl0[kTileBytes / 2];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vl1[kTileBytes / 2];
 
   const int item = p.work[blockIdx.x];
   if (item < 0) return;
@@ -185,16 +199,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
 #pragma unroll
   for (int u = 0; u < 4; ++u) dko[u] = (4 * u + lr) * 256 + 16 * (lc ^ ((4 * u + lr) & 15));
   const uint32_t dvo = lr * 256 + 16 * (lc ^ (4 * lr));
-  auto dma_tile = [&](const unsigned char* g, unsigned char* buf, int j, bool is_v) {
-    const unsigned char* src = g + (int64_t(j) * kBN + wave * 32) * (kD * 2);
-    unsigned char* dst = buf + wave * 32 * 256;
+  // HBM->LDS load of one 64-key half of V tile j (rows 64*hh .. 64*hh+63):
+  // wave w fills rows 64*hh + 16w .. +15 with four instructions.
+  const uint32_t Kl_a = uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)Kl));
+  const uint32_t Vl0_a = uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)Vl0));
+  const uint32_t Vl1_a = uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)Vl1));
+  auto dma_vhalf = [&](int j, int hh) {
+    const unsigned char* src = Vg + (int64_t(j) * kBN + hh * 64 + wave * 16) * (kD * 2);
+    const uint32_t dst = (hh ? Vl1_a : Vl0_a) + wave * 16 * 256;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const unsigned char* base = src + (u >= 4 ? 4096 : 0);
-      const uint32_t off = is_v ? dvo + (u & 3) * 1024 : dko[u & 3];
-      __builtin_amdgcn_global_load_lds(base + off,
-                                       (__attribute__((address_space(3))) void*)(dst + 4 * u * 256), 16, 0, 0);
-    }
+    for (int u = 0; u < 4; ++u) dma16(src, dvo + u * 1024, dst + u * 1024);
+  };
+  auto dma_ktile = [&](int j) {
+    const unsigned char* src = Kg + (int64_t(j) * kBN + wave * 32) * (kD * 2);
+    const uint32_t dst = Kl_a + wave * 32 * 256;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dma16(src + (u >= 4 ? 4096 : 0), dko[u & 3], dst + u * 1024);
   };
 
   // Per-lane LDS operand offsets (swizzle folded in).
@@ -212,7 +232,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   for (int dt = 0; dt < 4; ++dt)
     voff[dt] = (4 * hf + r4) * 256 + 16 * ((4 * dt + 2 * gp + (c4 >> 1)) ^ (4 * r4)) + 8 * (c4 & 1);
   lds_u8* const Kl3 = (lds_u8*)Kl;    // generic -> LDS address-space casts
-  lds_u8* const Vl3 = (lds_u8*)Vl;
+  lds_u8* const V0l3 = (lds_u8*)Vl0;
+  lds_u8* const V1l3 = (lds_u8*)Vl1;
 
   f32x16 o[4];
 #pragma unroll
@@ -235,6 +256,36 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
             Kl3 + koff[cc] + (hh * 64 + t * 32) * 256);
         sq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], sq[t], 0, 0, 0);
       }
+    }
+  };
+  // S^T for the 64 keys of half hh: two 32x32 tiles; lane holds row r32,
+  // keys 64*hh + 32*t + 8*(r/4) + 4*hf + r%4 in accumulator register r of
+  // tile t.  Operands are software-pipelined in batches of four MFMAs: the
+  // next batch's K reads are issued before the current batch's MFMAs, and
+  // scheduling barriers keep that order.
+  auto qk_pipe = [&](int hh, f32x16 (&sq)[2], auto&& after_first_reads) {
+    bf16x8 kb[2][4];
+    auto load = [&](int bt, bf16x8 (&dst)[4]) {
+      const int t = bt >> 1, c0 = (bt & 1) * 4;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        dst[u] = *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(
+            Kl3 + koff[c0 + u] + (hh * 64 + t * 32) * 256);
+    };
+    sq[0] = f32x16{};
+    sq[1] = f32x16{};
+    load(0, kb[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    after_first_reads();
+#pragma unroll
+    for (int bt = 0; bt < 4; ++bt) {
+      if (bt < 3) load(bt + 1, kb[(bt + 1) & 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      const int t = bt >> 1, c0 = (bt & 1) * 4;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        sq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[bt & 1][u], qf[c0 + u], sq[t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // Softmax of half hh of tile j in place: token mask (PARTIAL tiles only),
@@ -302,13 +353,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   auto pv_half = [&](int hh, const bf16x8 (&pq)[4]) {
 #pragma unroll
     for (int cq = 0; cq < 4; ++cq) {
-      const int c16 = hh * 4 + cq;
+      lds_u8* const vb = hh ? V1l3 : V0l3;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) s16x4*>(Vl3 + voff[dt] + (16 * c16) * 256)));
+            reinterpret_cast<__attribute__((address_space(3))) s16x4*>(vb + voff[dt] + (16 * cq) * 256)));
         const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) s16x4*>(Vl3 + voff[dt] + (16 * c16 + 8) * 256)));
+            reinterpret_cast<__attribute__((address_space(3))) s16x4*>(vb + voff[dt] + (16 * cq + 8) * 256)));
         const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pq[cq], o[dt], 0, 0, 0);
       }
@@ -316,7 +367,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   };
 
   const int e0 = row.start, ne = row.count;
-  if (ne > 0) dma_tile(Kg, Kl, ents[e0] >> 1, false);
+  if (ne > 0) {
+    dma_ktile(ents[e0] >> 1);
+    dma_vhalf(ents[e0] >> 1, 0);
+  }
   for (int e = 0; e < ne; ++e) {
     const int ent = ents[e0 + e];
     const int j = ent >> 1;
@@ -324,15 +378,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
     f32x16 sq[2];
     bf16x8 pq[4];
 
-    BSA_WAIT_BARRIER(0);                 // 1: K(e) landed; V(e-1) released
-    dma_tile(Vg, Vl, j, true);
+    BSA_WAIT_BARRIER(0);                 // 1: K(e), V(e) half 0 landed; V(e-1) released
+    dma_vhalf(j, 1);
     qk_half(0, sq);
     softmax_half(sq, 0, j, partial, pq);
-    BSA_WAIT_BARRIER(0);                 // 2: V(e) landed (the only load in flight)
     pv_half(0, pq);
-    qk_half(1, sq);
-    BSA_BARRIER();                       // 3: K(e) released
-    if (e + 1 < ne) dma_tile(Kg, Kl, ents[e0 + e + 1] >> 1, false);
+    qk_pipe(1, sq, [] {});
+    BSA_WAIT_BARRIER(0);                 // 2: V(e) half 1 landed; K(e), V(e) half 0 released
+    if (e + 1 < ne) {
+      const int jn = ents[e0 + e + 1] >> 1;
+      dma_ktile(jn);
+      dma_vhalf(jn, 0);
+    }
     softmax_half(sq, 1, j, partial, pq);
     pv_half(1, pq);
   }
