@@ -242,8 +242,12 @@ def main():
                      "algorithmic_flops": flops, "min_hbm_bytes": min_bytes},
     }
     if not args.no_context:
+        # The other workloads, timed the same way (kernel HIP events), and the
+        # dense causal comparator of the 256K shape on the same kernel.
         ctx = {}
-        for name in ("gqa256k", "dense256k"):
+        for name in ("tiny_f32", "window16k", "random32k", "gqa256k", "dense256k"):
+            if name == w.name:
+                continue
             cw = wl.WORKLOADS[name]
             clay = wl.layout_of(cw)
             cp = plan_for(cw, clay)
@@ -252,10 +256,12 @@ def main():
             q, k, v = wl.make_qkv(cw, "cuda")
             out = torch.empty_like(q)
             lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
-            steps = 5 if name == "gqa256k" else 2
-            cw_ms, cev = time_forward(cp, q, k, v, out, lse, steps, 1)
-            ctx[name] = {"ms_per_forward": round(float(np.mean(cev)), 3),
-                         "tflops": round(cp.flops() / (np.mean(cev) * 1e-3) / 1e12, 1),
+            steps = {"dense256k": 2, "gqa256k": 5}.get(name, 20)
+            cw_ms, cev = time_forward(cp, q, k, v, out, lse, steps, 2)
+            cpeak = PEAK_BF16_TFLOPS if cw.dtype == torch.bfloat16 else PEAK_F32_TFLOPS
+            tf = cp.flops() / (np.mean(cev) * 1e-3) / 1e12
+            ctx[name] = {"ms_per_forward": round(float(np.mean(cev)), 4),
+                         "tflops": round(float(tf), 1), "pct_of_peak": round(100 * tf / cpeak, 2),
                          "active_tiles": cp.info["active_blocks"]}
             log(f"[bench] context {name}: {ctx[name]}")
         ctx["dense_over_sparse_time"] = round(ctx["dense256k"]["ms_per_forward"] /

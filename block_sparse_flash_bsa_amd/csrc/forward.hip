@@ -29,6 +29,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -119,32 +120,24 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 // One workgroup of 4 waves per (b, h, q-block) work item; wave w owns query
 // rows 32w .. 32w+31.  Two workgroups share a CU (64 KB of LDS each), so each
 // SIMD interleaves two independent waves whose matrix and softmax phases
-// overlap.  K has one 32 KB LDS tile and V two 16 KB halves, all filled by
-// direct HBM->LDS loads (global_load_lds_dwordx4; no staging registers, no
-// LDS stores).  A tile is processed in two 64-key halves; per CSR entry e the
-// workgroup passes two barriers:
-//   1. K(e) and the first half of V(e) have landed, and every wave is done
-//      with the second half of V(e-1): load that half of V(e); S^T, softmax
-//      and P.V of half 0; S^T of half 1;
-//   2. the second half of V(e) has landed, and every wave is done with K(e)
-//      and with the first half of V(e): load K(e+1) and the first half of
-//      V(e+1); softmax and P.V of half 1.
-// Every load thus has at least a softmax and a matrix phase to land.  LDS
-// rows are 256 bytes with their 16-byte chunks XOR-swizzled (K chunk c of row
-// r at c ^ (r & 15), V chunk c at c ^ 4*(r & 3)), which keeps the 16-byte K
-// reads and the transposed V reads free of bank conflicts.
-constexpr int kTileBytes = kBN * kD * 2;   // 32 KB
-
-// HBM->LDS load of 16 bytes per lane (1 KB per wave) from sbase + voff into
-// LDS at lds_addr + 16 * lane.  Inline assembly, so the compiler adds no
-// waits of its own for it (its alias tracking of such loads is coarse and
-// would make unrelated LDS reads wait for every load in flight); each use is
-// followed by an explicit s_waitcnt vmcnt and a barrier before the data is
-// read.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
-  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
-                   :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
-}
+// overlap.  K and V are each held as two 16 KB halves (keys 0-63 and 64-127
+// of the current tile), all filled by direct HBM->LDS loads
+// (global_load_lds_dwordx4; no staging registers, no LDS stores).  A tile is
+// processed in two 64-key halves, each after one workgroup barrier:
+//   barrier 1: K and V half 0 of tile e have landed, and every wave is done
+//     with half 1 of tile e-1: load K and V half 1 of tile e, then S^T,
+//     softmax and P.V of keys 0-63;
+//   barrier 2: half 1 of tile e has landed, and every wave is done with half
+//     0: load K and V half 0 of tile e+1, then S^T, softmax and P.V of keys
+//     64-127.
+// Every load has a whole half-tile of work to land, and each barrier issues
+// the same 8 loads per wave, interleaved with the S^T MFMAs that follow it
+// (issued in one burst they stall the wave until the CU's load path has
+// accepted them).  LDS rows are 256 bytes with their 16-byte chunks
+// XOR-swizzled (K chunk c of row r at c ^ (r & 15), V chunk c at
+// c ^ 4*(r & 3)), which keeps the 16-byte K reads and the transposed V reads
+// free of bank conflicts.
+constexpr int kHalfBytes = 64 * kD * 2;   // one 64-key half of K or V: 16 KB
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
 // Wait until at most N of this wave's vector-memory operations are pending,
@@ -153,11 +146,29 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 #define BSA_WAIT_BARRIER(N) \
   __asm__ volatile("s_waitcnt vmcnt(" #N ")\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
 
+// HBM->LDS load of 16 bytes per lane (1 KB per wave) from sbase + voff into
+// LDS at lds_addr + 16 * lane.  Inline assembly, so the compiler adds no
+// waits of its own for it (its alias tracking of such loads is coarse and
+// would make unrelated LDS reads wait for every load in flight); each use is
+// followed by an explicit s_waitcnt vmcnt and a barrier before the data is
+// read.
+// M0 is reserved for the compiler, which therefore does not honour it as a
+// clobber (hence the silenced warning); the compiled kernel has no other use
+// of M0, which a CPU test checks in its assembly.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const int32_t* __restrict__ ents) {
-  __shared__ __attribute__((aligned(1024))) unsigned char Kl[kTileBytes];
-  // V as two 64-key halves, refilled at different times.
-  __shared__ __attribute__((aligned(1024))) unsigned char Vl0[kTileBytes / 2];
-  __shared__ __attribute__((aligned(1024))) unsigned char Vl1[kTileBytes / 2];
+  // Separate arrays per half, so the compiler can tell the halves apart.
+  __shared__ __attribute__((aligned(1024))) unsigned char K0[kHalfBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char K1[kHalfBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char V0[kHalfBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char V1[kHalfBytes];
 
   const int item = p.work[blockIdx.x];
   if (item < 0) return;
@@ -188,42 +199,36 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   __asm__ volatile("s_waitcnt vmcnt(0)" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]),
                    "v"(qf[5]), "v"(qf[6]), "v"(qf[7]) : "memory");
 
-  // HBM->LDS load of K or V tile j: wave w fills rows 32w .. 32w+31, 4 rows
-  // (1 KB) per instruction; lane L writes chunk L % 16 of row 4u + L / 16 and
-  // reads the logical chunk the swizzle places there.
+  // HBM->LDS loads of one 64-key half of K or V tile j: wave w fills rows
+  // 16w .. 16w+15 of the half, 4 rows (1 KB) per instruction; lane L writes
+  // chunk L % 16 of row 4u + L / 16 and reads the logical chunk the swizzle
+  // places there (K: chunk ^ (row & 15), V: chunk ^ 4*(row & 3)).
   const int lr = lane >> 4, lc = lane & 15;
-  // Rows 4u + L/16 and 4(u+4) + L/16 share their swizzle, so four 32-bit
-  // per-lane offsets serve all eight K instructions (the upper four add
-  // 4096 bytes to the uniform base); V needs one offset plus 1 KB steps.
   uint32_t dko[4];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) dko[u] = (4 * u + lr) * 256 + 16 * (lc ^ ((4 * u + lr) & 15));
+  for (int u = 0; u < 4; ++u) dko[u] = (4 * u + lr) * 256 + 16 * (lc ^ (4 * u + lr));
   const uint32_t dvo = lr * 256 + 16 * (lc ^ (4 * lr));
-  // HBM->LDS load of one 64-key half of V tile j (rows 64*hh .. 64*hh+63):
-  // wave w fills rows 64*hh + 16w .. +15 with four instructions.
-  const uint32_t Kl_a = uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)Kl));
-  const uint32_t Vl0_a = uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)Vl0));
-  const uint32_t Vl1_a = uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)Vl1));
-  auto dma_vhalf = [&](int j, int hh) {
-    const unsigned char* src = Vg + (int64_t(j) * kBN + hh * 64 + wave * 16) * (kD * 2);
-    const uint32_t dst = (hh ? Vl1_a : Vl0_a) + wave * 16 * 256;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) dma16(src, dvo + u * 1024, dst + u * 1024);
-  };
-  auto dma_ktile = [&](int j) {
-    const unsigned char* src = Kg + (int64_t(j) * kBN + wave * 32) * (kD * 2);
-    const uint32_t dst = Kl_a + wave * 32 * 256;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) dma16(src + (u >= 4 ? 4096 : 0), dko[u & 3], dst + u * 1024);
+  const uint32_t Ka[2] = {uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)K0)),
+                          uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)K1))};
+  const uint32_t Va[2] = {uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)V0)),
+                          uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)V1))};
+  // Instruction u (0..7) of the 8 loads for half hh of tile j: u < 4 K rows,
+  // u >= 4 V rows.
+  auto dma_half_part = [&](int j, int hh, int u) {
+    const int64_t row0 = int64_t(j) * kBN + hh * 64 + wave * 16;
+    if (u < 4)
+      dma16(Kg + row0 * (kD * 2), dko[u], Ka[hh] + wave * 16 * 256 + u * 1024);
+    else
+      dma16(Vg + row0 * (kD * 2), dvo + (u - 4) * 1024, Va[hh] + wave * 16 * 256 + (u - 4) * 1024);
   };
 
   // Per-lane LDS operand offsets (swizzle folded in).
-  // K (A operand of S^T): row 32kt + r32, logical chunk 2cc + hf.
+  // K (A operand of S^T): row 32t + r32 of a half, logical chunk 2cc + hf.
   uint32_t koff[8];
 #pragma unroll
   for (int cc = 0; cc < 8; ++cc) koff[cc] = r32 * 256 + 16 * ((2 * cc + hf) ^ (r32 & 15));
   // V^T operand by transposed reads: in 16-lane group g, lane 4*r4 + c4
-  // addresses key row 16*c16 + 8*s + 4*hf + r4 and columns
+  // addresses key row 16*cq + 8*s + 4*hf + r4 of a half and columns
   // 32*dt + 16*(g & 1) + 4*c4 .. +3; lane l then receives the 4 keys of
   // column d = 32*dt + (l & 31).
   const int r4 = (lane & 15) >> 2, c4 = lane & 3, gp = (lane >> 4) & 1;
@@ -231,9 +236,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
     voff[dt] = (4 * hf + r4) * 256 + 16 * ((4 * dt + 2 * gp + (c4 >> 1)) ^ (4 * r4)) + 8 * (c4 & 1);
-  lds_u8* const Kl3 = (lds_u8*)Kl;    // generic -> LDS address-space casts
-  lds_u8* const V0l3 = (lds_u8*)Vl0;
-  lds_u8* const V1l3 = (lds_u8*)Vl1;
+  lds_u8* const K3[2] = {(lds_u8*)K0, (lds_u8*)K1};
+  lds_u8* const V3[2] = {(lds_u8*)V0, (lds_u8*)V1};
 
   f32x16 o[4];
 #pragma unroll
@@ -245,41 +249,28 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
 
   // S^T for the 64 keys of half hh: two 32x32 tiles; lane holds row r32,
   // keys 64*hh + 32*t + 8*(r/4) + 4*hf + r%4 in accumulator register r of
-  // tile t.
-  auto qk_half = [&](int hh, f32x16 (&sq)[2]) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      sq[t] = f32x16{};
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
-        const bf16x8 a = *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(
-            Kl3 + koff[cc] + (hh * 64 + t * 32) * 256);
-        sq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[cc], sq[t], 0, 0, 0);
-      }
-    }
-  };
-  // S^T for the 64 keys of half hh: two 32x32 tiles; lane holds row r32,
-  // keys 64*hh + 32*t + 8*(r/4) + 4*hf + r%4 in accumulator register r of
-  // tile t.  Operands are software-pipelined in batches of four MFMAs: the
-  // next batch's K reads are issued before the current batch's MFMAs, and
-  // scheduling barriers keep that order.
-  auto qk_pipe = [&](int hh, f32x16 (&sq)[2], auto&& after_first_reads) {
+  // tile t.  K reads are software-pipelined in batches of four MFMAs (the
+  // next batch's reads are issued before the current batch's MFMAs; the
+  // scheduling barriers keep that order), and dma(k) issues two of the
+  // barrier's loads per batch.
+  auto qk_half = [&](int hh, f32x16 (&sq)[2], auto&& dma) {
+    lds_u8* const kh = hh ? K3[1] : K3[0];
     bf16x8 kb[2][4];
     auto load = [&](int bt, bf16x8 (&dst)[4]) {
       const int t = bt >> 1, c0 = (bt & 1) * 4;
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        dst[u] = *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(
-            Kl3 + koff[c0 + u] + (hh * 64 + t * 32) * 256);
+        dst[u] = *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(kh + koff[c0 + u] + t * 32 * 256);
     };
     sq[0] = f32x16{};
     sq[1] = f32x16{};
     load(0, kb[0]);
     __builtin_amdgcn_sched_barrier(0);
-    after_first_reads();
 #pragma unroll
     for (int bt = 0; bt < 4; ++bt) {
       if (bt < 3) load(bt + 1, kb[(bt + 1) & 1]);
+      dma(2 * bt);
+      dma(2 * bt + 1);
       __builtin_amdgcn_sched_barrier(0);
       const int t = bt >> 1, c0 = (bt & 1) * 4;
 #pragma unroll
@@ -292,9 +283,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   // row max (in-lane, then with lane l ^ 32), lazy move of the reference max
   // (only when some row's max grows by more than 2^8: a wave-uniform
   // decision), P = exp2(c*S - m) in bf16, and the matching rescale of O and
-  // l.  Accumulator registers 8q .. 8q+7 of S^T tile t are exactly the 8 keys
-  // this lane supplies for 16-key chunk 2t + q of the P.V product.  The empty
-  // volatile asm keeps the two conditional blocks real branches.
+  // l, in independent passes over the 32 scores.  Accumulator registers
+  // 8q .. 8q+7 of S^T tile t are exactly the 8 keys this lane supplies for
+  // 16-key chunk 2t + q of the P.V product.  The empty volatile asm keeps the
+  // two conditional blocks real branches.
   auto softmax_half = [&](f32x16 (&sq)[2], int hh, int j, bool partial, bf16x8 (&pq)[4]) {
     if (partial) {
       __asm__ volatile("");
@@ -319,8 +311,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
     const float m_use = moved ? fmaxf(m_ref, m_new) : m_ref;
     const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_use);
     const float msub = (m_use == -INFINITY) ? 0.f : m_use;
-    // Independent passes over the 32 scores (exponent argument, exp2, bf16
-    // pack, four partial row sums) keep dependent instructions apart.
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -351,15 +341,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   };
   // O^T += V^T P^T over the four 16-key chunks of half hh.
   auto pv_half = [&](int hh, const bf16x8 (&pq)[4]) {
+    lds_u8* const vh = hh ? V3[1] : V3[0];
 #pragma unroll
     for (int cq = 0; cq < 4; ++cq) {
-      lds_u8* const vb = hh ? V1l3 : V0l3;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) s16x4*>(vb + voff[dt] + (16 * cq) * 256)));
+            reinterpret_cast<__attribute__((address_space(3))) s16x4*>(vh + voff[dt] + (16 * cq) * 256)));
         const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) s16x4*>(vb + voff[dt] + (16 * cq + 8) * 256)));
+            reinterpret_cast<__attribute__((address_space(3))) s16x4*>(vh + voff[dt] + (16 * cq + 8) * 256)));
         const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pq[cq], o[dt], 0, 0, 0);
       }
@@ -367,32 +357,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   };
 
   const int e0 = row.start, ne = row.count;
-  if (ne > 0) {
-    dma_ktile(ents[e0] >> 1);
-    dma_vhalf(ents[e0] >> 1, 0);
-  }
-  for (int e = 0; e < ne; ++e) {
+  // One CSR entry; the last one (no next tile to load) is peeled off so the
+  // loop body issues its loads unconditionally.
+  auto tile = [&](int e, auto next_c) {
+    constexpr bool has_next = decltype(next_c)::value;
     const int ent = ents[e0 + e];
     const int j = ent >> 1;
     const bool partial = ent & 1;
+    const int jn = has_next ? ents[e0 + e + 1] >> 1 : 0;
     f32x16 sq[2];
     bf16x8 pq[4];
-
-    BSA_WAIT_BARRIER(0);                 // 1: K(e), V(e) half 0 landed; V(e-1) released
-    dma_vhalf(j, 1);
-    qk_half(0, sq);
+    BSA_WAIT_BARRIER(0);                 // 1: half 0 of tile e landed; half 1 of e-1 released
+    qk_half(0, sq, [&](int u) { dma_half_part(j, 1, u); });
     softmax_half(sq, 0, j, partial, pq);
     pv_half(0, pq);
-    qk_pipe(1, sq, [] {});
-    BSA_WAIT_BARRIER(0);                 // 2: V(e) half 1 landed; K(e), V(e) half 0 released
-    if (e + 1 < ne) {
-      const int jn = ents[e0 + e + 1] >> 1;
-      dma_ktile(jn);
-      dma_vhalf(jn, 0);
-    }
+    BSA_WAIT_BARRIER(0);                 // 2: half 1 of tile e landed; half 0 released
+    qk_half(1, sq, [&](int u) {
+      if constexpr (has_next) dma_half_part(jn, 0, u);
+    });
     softmax_half(sq, 1, j, partial, pq);
     pv_half(1, pq);
+  };
+  if (ne > 0) {
+    const int j0 = ents[e0] >> 1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) dma_half_part(j0, 0, u);
   }
+  for (int e = 0; e + 1 < ne; ++e) tile(e, std::true_type{});
+  if (ne > 0) tile(ne - 1, std::false_type{});
 
   // Epilogue: O = acc / l (0 for an empty row), LSE = ln2 * (m_ref + log2 l).
   const float l = sum_with_partner(l_part);

@@ -231,3 +231,28 @@ def test_empty_rows_have_no_entries():
     p = bsattn.plan(1, 1, 1, 512, 128, 128, torch.bfloat16, spec(True, "blocks", bitmap=bm),
                     host_only=True)
     assert p.info["nnz"] == 0
+
+
+def test_bf16_kernel_m0_only_set_for_lds_loads(tmp_path):
+    """The bf16 kernel writes M0 in inline assembly right before each
+    HBM->LDS load; the compiler treats M0 as reserved and does not honour it
+    as a clobber, so its own code must never rely on M0 across those loads.
+    Compile the kernel to gfx950 assembly (works without a GPU) and check that
+    every M0 access in it is one of those load sequences."""
+    import subprocess
+    from block_sparse_flash_bsa_amd import build as bld
+    src = os.path.join(ROOT, "block_sparse_flash_bsa_amd", "csrc", "forward.hip")
+    out = tmp_path / "forward.s"
+    cmd = [bld.hipcc(), "-x", "hip", *bld.HIP_FLAGS, "-O3", "-std=c++17", "--cuda-device-only", "-S",
+           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "block_sparse_flash_bsa_amd", "csrc"),
+           src, "-o", str(out)]
+    subprocess.run(cmd, check=True, capture_output=True)
+    asm = out.read_text()
+    start = asm.index("_ZN3bsa12_GLOBAL__N_113fwd_bf16_d128ENS0_9FwdParamsEPKi:")
+    body = [l.strip() for l in asm[start:asm.index(".Lfunc_end", start)].splitlines()]
+    body = [l for l in body if l and not l.startswith(";")]
+    uses = [k for k, l in enumerate(body) if re.search(r"\bm0\b", l)]
+    assert uses, "expected the HBM->LDS load sequences"
+    for k in uses:
+        assert body[k].startswith("s_mov_b32 m0, s"), body[k]
+        assert body[k + 1].startswith("s_nop") and body[k + 2].startswith("global_load_lds_dwordx4"), body[k:k + 3]
