@@ -53,6 +53,10 @@ struct FwdParams {
   // The same window/global bounds clamped to [-1, N] so tile-local masks use
   // 32-bit arithmetic (N < 2^30 is enforced by the planner).
   int32_t wl32, wr32, gk32, gq32;
+  // Window and causal parts of the token predicate as one range of q - k:
+  // allowed iff (uint32)(q - k - mlo) <= mspan (mlo <= 0, mspan >= 0).
+  int32_t mlo;
+  uint32_t mspan;
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -290,19 +294,32 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   auto softmax_half = [&](f32x16 (&sq)[2], int hh, int j, bool partial, bf16x8 (&pq)[4]) {
     if (partial) {
       __asm__ volatile("");
-      const int k0 = j * kBN;
-      const int dq = int(qg) - k0;
+      // Window and causal bounds: one unsigned range test of q - k per score
+      // (key offsets within the half are compile-time constants).  Global
+      // keys and global query rows, when this half or this wave has any, are
+      // or-ed in per score, still under the causal bound.
+      const int k0 = j * kBN + hh * 64;                            // first key of the half
+      const int dq = int(qg) - k0;                                 // q - k at offset 0
+      const uint32_t dql = uint32_t(dq) - uint32_t(p.mlo);
+      if (p.token_rule && (k0 < p.gk32 || __any(q_global))) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int koff_ = hh * 64 + t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          const int diff = dq - koff_;                             // q - k
-          const bool in_w = (p.wl32 < 0 || diff <= p.wl32) & (p.wr32 < 0 || -diff <= p.wr32);
-          const bool rule = !p.token_rule | in_w | (k0 + koff_ < p.gk32) | q_global;
-          const bool ok = rule & (!p.causal | (diff >= 0));
-          sq[t][r] = ok ? sq[t][r] : -INFINITY;
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int ko = t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            const bool ok = (dql - uint32_t(ko) <= p.mspan) |
+                            (((k0 + ko < p.gk32) | q_global) & (!p.causal | (dq - ko >= 0)));
+            sq[t][r] = ok ? sq[t][r] : -INFINITY;
+          }
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ko = t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+            sq[t][r] = dql - uint32_t(ko) <= p.mspan ? sq[t][r] : -INFINITY;
+          }
+      }
     }
     float mx = fmaxf(max3_tree(sq[0]), max3_tree(sq[1]));
     mx = max_with_partner(mx);
@@ -555,6 +572,20 @@ extern "C" bsa_status_t bsa_forward(const void* q, const void* k, const void* v,
   prm.wr32 = clamp32(plan->wr);
   prm.gk32 = clamp32(plan->gk);
   prm.gq32 = clamp32(plan->gq);
+  {
+    // Range of q - k allowed by the window and the causal cut (|q - k| < N).
+    const int64_t big = pr.seq_len + 1;
+    int64_t lo = -big, hi = big;
+    if (plan->token_rule) {
+      if (plan->wr >= 0) lo = -plan->wr;
+      if (plan->wl >= 0) hi = plan->wl;
+    }
+    if (plan->causal) lo = lo > 0 ? lo : 0;
+    if (lo < -big) lo = -big;
+    if (hi > big) hi = big;
+    prm.mlo = int32_t(lo);
+    prm.mspan = uint32_t(hi - lo);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = hipSuccess;
   if (pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128) {
