@@ -20,11 +20,20 @@
 // ds_read_b64_tr_b16, which transposes 4x4 blocks of 16-bit elements across
 // each group of 16 lanes, so no transpose is done in registers.  The key order
 // inside each 16-key chunk of P follows the S^T accumulator layout, and the V
-// reads use the same order.  The softmax runs in the exp2 domain with a lazily
-// updated reference max (the accumulator is rescaled only when a row max grows
-// by more than 2^8), in passes over independent registers: on gfx950 the
-// VALU work per tile is about as large as the matrix work, and dependent
+// reads use the same order.  The softmax runs in the exp2 domain against a
+// reference max that moves only when some P would reach 2^8 (so the
+// accumulator is rarely rescaled and, in the common case, no row max is
+// computed at all), in passes over independent registers: on gfx950 the VALU
+// work per tile is about as large as the matrix work, and dependent
 // instruction chains would leave it latency-bound.
+//
+// Each 128-key tile is processed as two 64-key halves, one barrier per half.
+// A half's phase runs the P.V product of the previous half first (its V half
+// landed at this barrier), then the scores of this half, then its softmax; the
+// P of this half is kept in registers until the next phase.  So each phase is
+// one block of 32 MFMAs followed by one block of VALU work, and the HBM->LDS
+// loads issued in a phase (the next K half and this half's V) land by the next
+// barrier.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -283,51 +292,38 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Softmax of half hh of tile j in place: token mask (PARTIAL tiles only),
-  // row max (in-lane, then with lane l ^ 32), lazy move of the reference max
-  // (only when some row's max grows by more than 2^8: a wave-uniform
-  // decision), P = exp2(c*S - m) in bf16, and the matching rescale of O and
-  // l, in independent passes over the 32 scores.  Accumulator registers
-  // 8q .. 8q+7 of S^T tile t are exactly the 8 keys this lane supplies for
-  // 16-key chunk 2t + q of the P.V product.  The empty volatile asm keeps the
-  // two conditional blocks real branches.
-  auto softmax_half = [&](f32x16 (&sq)[2], int hh, int j, bool partial, bf16x8 (&pq)[4]) {
-    if (partial) {
-      __asm__ volatile("");
-      // Window and causal bounds: one unsigned range test of q - k per score
-      // (key offsets within the half are compile-time constants).  Global
-      // keys and global query rows, when this half or this wave has any, are
-      // or-ed in per score, still under the causal bound.
-      const int k0 = j * kBN + hh * 64;                            // first key of the half
-      const int dq = int(qg) - k0;                                 // q - k at offset 0
-      const uint32_t dql = uint32_t(dq) - uint32_t(p.mlo);
-      if (p.token_rule && (k0 < p.gk32 || __any(q_global))) {
+  // Token mask of half hh of tile j (PARTIAL tiles only), in place.
+  auto apply_mask = [&](f32x16 (&sq)[2], int hh, int j) {
+    __asm__ volatile("");
+    // Window and causal bounds: one unsigned range test of q - k per score
+    // (key offsets within the half are compile-time constants).  Global
+    // keys and global query rows, when this half or this wave has any, are
+    // or-ed in per score, still under the causal bound.
+    const int k0 = j * kBN + hh * 64;                            // first key of the half
+    const int dq = int(qg) - k0;                                 // q - k at offset 0
+    const uint32_t dql = uint32_t(dq) - uint32_t(p.mlo);
+    if (p.token_rule && (k0 < p.gk32 || __any(q_global))) {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ko = t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            const bool ok = (dql - uint32_t(ko) <= p.mspan) |
-                            (((k0 + ko < p.gk32) | q_global) & (!p.causal | (dq - ko >= 0)));
-            sq[t][r] = ok ? sq[t][r] : -INFINITY;
-          }
-      } else {
+        for (int r = 0; r < 16; ++r) {
+          const int ko = t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          const bool ok = (dql - uint32_t(ko) <= p.mspan) |
+                          (((k0 + ko < p.gk32) | q_global) & (!p.causal | (dq - ko >= 0)));
+          sq[t][r] = ok ? sq[t][r] : -INFINITY;
+        }
+    } else {
 #pragma unroll
-        for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int ko = t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-            sq[t][r] = dql - uint32_t(ko) <= p.mspan ? sq[t][r] : -INFINITY;
-          }
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int ko = t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          sq[t][r] = dql - uint32_t(ko) <= p.mspan ? sq[t][r] : -INFINITY;
+        }
     }
-    float mx = fmaxf(max3_tree(sq[0]), max3_tree(sq[1]));
-    mx = max_with_partner(mx);
-    const float m_new = mx * c;
-    const bool moved = __any(m_new > m_ref + 8.f);
-    const float m_use = moved ? fmaxf(m_ref, m_new) : m_ref;
-    const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_use);
-    const float msub = (m_use == -INFINITY) ? 0.f : m_use;
+  };
+  // P = exp2(c*S - msub) in place, its bf16 copy, and four partial row sums.
+  auto exp_pass = [&](f32x16 (&sq)[2], float msub, bf16x8 (&pq)[4], float (&ls)[4]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -336,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sq[t][r] = __builtin_amdgcn_exp2f(sq[t][r]);
-    float ls[4] = {sq[0][0], sq[0][1], sq[0][2], sq[0][3]};
+    ls[0] = sq[0][0]; ls[1] = sq[0][1]; ls[2] = sq[0][2]; ls[3] = sq[0][3];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -346,6 +342,44 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
           if (t > 0 || q2 > 0 || ii >= 4) ls[ii & 3] += sq[t][q2 * 8 + ii];
           pq[t * 2 + q2][ii] = static_cast<__bf16>(sq[t][q2 * 8 + ii]);
         }
+  };
+  // Softmax of half hh of tile j in place: token mask (PARTIAL tiles only),
+  // P = exp2(c*S - m_ref) in bf16, and the row sums.  The reference max m_ref
+  // stays put while every P is below 2^8, which each lane checks through the
+  // sum of its 32 values; otherwise (and until every row of the wave has a
+  // finite reference) the scores are recomputed, the row max is formed
+  // (in-lane, then with lane l ^ 32), the reference moves to it when some row
+  // max exceeds it by more than 2^8 (a wave-uniform decision), and O and l
+  // are rescaled to match.  Accumulator registers 8q .. 8q+7 of S^T tile t
+  // are exactly the 8 keys this lane supplies for 16-key chunk 2t + q of the
+  // P.V product.  The empty volatile asm keeps the conditional blocks real
+  // branches.
+  auto softmax_half = [&](f32x16 (&sq)[2], int hh, int j, bool partial, bf16x8 (&pq)[4]) {
+    if (partial) {
+      __asm__ volatile("");
+      apply_mask(sq, hh, j);
+    }
+    float ls[4];
+    if (!__any(m_ref == -INFINITY)) {
+      // Common case: keep the reference max (no inf/NaN and every P < 2^8).
+      exp_pass(sq, m_ref, pq, ls);
+      const float ts = (ls[0] + ls[1]) + (ls[2] + ls[3]);
+      if (!__any(!(ts < 256.f))) {
+        l_part += ts;
+        return;
+      }
+      __asm__ volatile("");
+      qk_half(hh, sq, [](int) {});
+      if (partial) apply_mask(sq, hh, j);
+    }
+    float mx = fmaxf(max3_tree(sq[0]), max3_tree(sq[1]));
+    mx = max_with_partner(mx);
+    const float m_new = mx * c;
+    const bool moved = __any(m_new > m_ref + 8.f);
+    const float m_use = moved ? fmaxf(m_ref, m_new) : m_ref;
+    const float alpha = (m_ref == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_use);
+    const float msub = (m_use == -INFINITY) ? 0.f : m_use;
+    exp_pass(sq, msub, pq, ls);
     l_part = fmaf(l_part, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
     if (moved) {
       __asm__ volatile("");
@@ -356,26 +390,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
     }
     m_ref = m_use;
   };
-  // O^T += V^T P^T over the four 16-key chunks of half hh.
+  // O^T += V^T P^T over the four 16-key chunks of V half hh.
   auto pv_half = [&](int hh, const bf16x8 (&pq)[4]) {
     lds_u8* const vh = hh ? V3[1] : V3[0];
+    // Operand k = 4*cq + dt; its two reads are issued two MFMAs ahead (a
+    // deeper window is faster on short runs but draws enough power on long
+    // dense ones to lower the sustained clock).
+    auto ld = [&](int k) {
+      const int cq = k >> 2, dt = k & 3;
+      const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<__attribute__((address_space(3))) s16x4*>(vh + voff[dt] + (16 * cq) * 256)));
+      const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          reinterpret_cast<__attribute__((address_space(3))) s16x4*>(vh + voff[dt] + (16 * cq + 8) * 256)));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 vb[4];
+    vb[0] = ld(0);
+    vb[1] = ld(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int cq = 0; cq < 4; ++cq) {
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) s16x4*>(vh + voff[dt] + (16 * cq) * 256)));
-        const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            reinterpret_cast<__attribute__((address_space(3))) s16x4*>(vh + voff[dt] + (16 * cq + 8) * 256)));
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pq[cq], o[dt], 0, 0, 0);
-      }
+    for (int k = 0; k < 16; ++k) {
+      if (k + 2 < 16) vb[(k + 2) & 3] = ld(k + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      o[k & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vb[k & 3], pq[k >> 2], o[k & 3], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
 
   const int e0 = row.start, ne = row.count;
-  // One CSR entry; the last one (no next tile to load) is peeled off so the
-  // loop body issues its loads unconditionally.
+  // One CSR entry (two phases); the last one (no next tile to load) is peeled
+  // off so the loop body issues its loads unconditionally.
+  bf16x8 pq[4];
   auto tile = [&](int e, auto next_c) {
     constexpr bool has_next = decltype(next_c)::value;
     const int ent = ents[e0 + e];
@@ -383,25 +428,35 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
     const bool partial = ent & 1;
     const int jn = has_next ? ents[e0 + e + 1] >> 1 : 0;
     f32x16 sq[2];
-    bf16x8 pq[4];
-    BSA_WAIT_BARRIER(0);                 // 1: half 0 of tile e landed; half 1 of e-1 released
-    qk_half(0, sq, [&](int u) { dma_half_part(j, 1, u); });
+    BSA_WAIT_BARRIER(0);                 // K half 0 of e and V half 1 of e-1 landed
+    if (e > 0) pv_half(1, pq);
+    qk_half(0, sq, [&](int u) {
+      if (u < 4) dma_half_part(j, 1, u);       // K half 1 of e
+      else dma_half_part(j, 0, u);             // V half 0 of e
+    });
     softmax_half(sq, 0, j, partial, pq);
+    BSA_WAIT_BARRIER(0);                 // K half 1 and V half 0 of e landed
     pv_half(0, pq);
-    BSA_WAIT_BARRIER(0);                 // 2: half 1 of tile e landed; half 0 released
     qk_half(1, sq, [&](int u) {
-      if constexpr (has_next) dma_half_part(jn, 0, u);
+      if (u < 4) {
+        if constexpr (has_next) dma_half_part(jn, 0, u);   // K half 0 of e+1
+      } else {
+        dma_half_part(j, 1, u);                            // V half 1 of e
+      }
     });
     softmax_half(sq, 1, j, partial, pq);
-    pv_half(1, pq);
   };
   if (ne > 0) {
     const int j0 = ents[e0] >> 1;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) dma_half_part(j0, 0, u);
+    for (int u = 0; u < 4; ++u) dma_half_part(j0, 0, u);
   }
   for (int e = 0; e + 1 < ne; ++e) tile(e, std::true_type{});
-  if (ne > 0) tile(ne - 1, std::false_type{});
+  if (ne > 0) {
+    tile(ne - 1, std::false_type{});
+    BSA_WAIT_BARRIER(0);
+    pv_half(1, pq);
+  }
 
   // Epilogue: O = acc / l (0 for an empty row), LSE = ln2 * (m_ref + log2 l).
   const float l = sum_with_partner(l_part);
