@@ -477,15 +477,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
 
 // ---------------------------------------------------------------------------
 // float32 kernel (head_dim 64/128, block 64/128): exact fp32 FMA on the VALU.
-// One thread per query row; K/V tiles staged through LDS in 64-key stages.
+// kF32Lanes consecutive lanes share one query row, each holding a slice of
+// the head dimension of Q and of the accumulator; a score is the sum of their
+// partial dot products, formed by butterfly exchanges.  K/V tiles are staged through LDS in
+// 64-key stages.
 // ---------------------------------------------------------------------------
+constexpr int kF32Lanes = 4;   // lanes per query row
+
 template <int D, int BS>
-__global__ __launch_bounds__(BS) void fwd_f32(FwdParams p) {
+__global__ __launch_bounds__(BS * kF32Lanes) void fwd_f32(FwdParams p) {
   constexpr int KT = BS < 64 ? BS : 64;  // keys per LDS stage
-  constexpr int QS = D + 1;              // padded Q row stride (conflict-free per-thread rows)
+  constexpr int DL = D / kF32Lanes;      // head-dimension slice per lane
+  constexpr int NT = BS * kF32Lanes;     // threads
   extern __shared__ float smem[];
-  float* Qs = smem;                      // [BS][QS]
-  float* Ks = Qs + BS * QS;              // [KT][D]
+  float* Ks = smem;                      // [KT][D]
   float* Vs = Ks + KT * D;               // [KT][D]
 
   const int item = p.work[blockIdx.x];
@@ -495,20 +500,21 @@ __global__ __launch_bounds__(BS) void fwd_f32(FwdParams p) {
   const int hk = h / p.group;
   const RowDesc row = p.rows[(p.per_head_layout ? h : 0) * p.nb + i];
   const int t = threadIdx.x;
+  const int r = t / kF32Lanes, sl = t % kF32Lanes;
   const int64_t q0 = int64_t(i) * BS;
-  const int64_t qg = q0 + t;
+  const int64_t qg = q0 + r;
 
-  const float* Qp = static_cast<const float*>(p.q) + ((int64_t(b) * p.H + h) * p.N + q0) * D;
+  const float* Qp = static_cast<const float*>(p.q) + ((int64_t(b) * p.H + h) * p.N + qg) * D + sl * DL;
   const float* Kb = static_cast<const float*>(p.k) + (int64_t(b) * p.Hkv + hk) * p.N * D;
   const float* Vb = static_cast<const float*>(p.v) + (int64_t(b) * p.Hkv + hk) * p.N * D;
-  for (int x = t; x < BS * D; x += BS) Qs[(x / D) * QS + (x % D)] = Qp[x];
-
-  float acc[D];
+  float qv[DL], acc[DL];
 #pragma unroll
-  for (int d = 0; d < D; ++d) acc[d] = 0.f;
+  for (int d = 0; d < DL; ++d) {
+    qv[d] = Qp[d];
+    acc[d] = 0.f;
+  }
   float m = -INFINITY, l = 0.f;
   const float c = p.sl2;
-  const float* qr = Qs + t * QS;
 
   for (int e = 0; e < row.count; ++e) {
     const int ent = p.entries[row.start + e];
@@ -517,19 +523,21 @@ __global__ __launch_bounds__(BS) void fwd_f32(FwdParams p) {
     for (int st = 0; st < BS / KT; ++st) {
       const int64_t k0 = int64_t(j) * BS + st * KT;
       __syncthreads();
-      for (int x = t; x < KT * D; x += BS) {
-        Ks[x] = Kb[k0 * D + x];
-        Vs[x] = Vb[k0 * D + x];
+      for (int x = t; x < KT * D / 4; x += NT) {
+        reinterpret_cast<float4*>(Ks)[x] = reinterpret_cast<const float4*>(Kb + k0 * D)[x];
+        reinterpret_cast<float4*>(Vs)[x] = reinterpret_cast<const float4*>(Vb + k0 * D)[x];
       }
       __syncthreads();
       for (int kc = 0; kc < KT; kc += 16) {
         float s[16];
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
-          const float* kr = Ks + (kc + kk) * D;
+          const float* kr = Ks + (kc + kk) * D + sl * DL;
           float a = 0.f;
-#pragma unroll 16
-          for (int d = 0; d < D; ++d) a = fmaf(qr[d], kr[d], a);
+#pragma unroll
+          for (int d = 0; d < DL; ++d) a = fmaf(qv[d], kr[d], a);
+#pragma unroll
+          for (int w = 1; w < kF32Lanes; w *= 2) a += __shfl_xor(a, w);
           s[kk] = (partial && !allowed(p, qg, k0 + kc + kk)) ? -INFINITY : a * c;
         }
         float mx = m;
@@ -539,7 +547,7 @@ __global__ __launch_bounds__(BS) void fwd_f32(FwdParams p) {
           const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - mx);
           l *= alpha;
 #pragma unroll
-          for (int d = 0; d < D; ++d) acc[d] *= alpha;
+          for (int d = 0; d < DL; ++d) acc[d] *= alpha;
           m = mx;
         }
         const float msub = (m == -INFINITY) ? 0.f : m;
@@ -547,23 +555,23 @@ __global__ __launch_bounds__(BS) void fwd_f32(FwdParams p) {
         for (int kk = 0; kk < 16; ++kk) {
           const float pv = __builtin_amdgcn_exp2f(s[kk] - msub);
           l += pv;
-          const float* vr = Vs + (kc + kk) * D;
+          const float* vr = Vs + (kc + kk) * D + sl * DL;
 #pragma unroll
-          for (int d = 0; d < D; ++d) acc[d] = fmaf(pv, vr[d], acc[d]);
+          for (int d = 0; d < DL; ++d) acc[d] = fmaf(pv, vr[d], acc[d]);
         }
       }
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  float* Op = static_cast<float*>(p.o) + ((int64_t(b) * p.H + h) * p.N + qg) * D;
+  float* Op = static_cast<float*>(p.o) + ((int64_t(b) * p.H + h) * p.N + qg) * D + sl * DL;
 #pragma unroll
-  for (int d = 0; d < D; ++d) Op[d] = acc[d] * inv;
-  p.lse[(int64_t(b) * p.H + h) * p.N + qg] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  for (int d = 0; d < DL; ++d) Op[d] = acc[d] * inv;
+  if (sl == 0) p.lse[(int64_t(b) * p.H + h) * p.N + qg] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
 }
 
 template <int D, int BS>
 constexpr size_t f32_smem_bytes() {
-  return size_t(BS * (D + 1) + 2 * (BS < 64 ? BS : 64) * D) * sizeof(float);
+  return size_t(2 * (BS < 64 ? BS : 64) * D) * sizeof(float);
 }
 
 template <int D, int BS>
@@ -576,7 +584,7 @@ hipError_t launch_f32(const FwdParams& prm, int64_t slots, hipStream_t stream) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL((fwd_f32<D, BS>), dim3(unsigned(slots)), dim3(BS), smem, stream, prm);
+  hipLaunchKernelGGL((fwd_f32<D, BS>), dim3(unsigned(slots)), dim3(BS * kF32Lanes), smem, stream, prm);
   return hipGetLastError();
 }
 
