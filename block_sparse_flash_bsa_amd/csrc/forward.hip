@@ -262,33 +262,27 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
 
   // S^T for the 64 keys of half hh: two 32x32 tiles; lane holds row r32,
   // keys 64*hh + 32*t + 8*(r/4) + 4*hf + r%4 in accumulator register r of
-  // tile t.  K reads are software-pipelined in batches of four MFMAs (the
-  // next batch's reads are issued before the current batch's MFMAs; the
-  // scheduling barriers keep that order), and dma(k) issues two of the
-  // barrier's loads per batch.
+  // tile t.  The 16 MFMAs alternate between the two tiles' accumulators
+  // (operand k: tile k % 2, d chunk k / 2); each K operand is read from LDS
+  // two MFMAs ahead of its use (the scheduling barriers keep that order), and
+  // dma(u) issues the barrier's loads, one every other MFMA.
   auto qk_half = [&](int hh, f32x16 (&sq)[2], auto&& dma) {
     lds_u8* const kh = hh ? K3[1] : K3[0];
-    bf16x8 kb[2][4];
-    auto load = [&](int bt, bf16x8 (&dst)[4]) {
-      const int t = bt >> 1, c0 = (bt & 1) * 4;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        dst[u] = *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(kh + koff[c0 + u] + t * 32 * 256);
+    auto ld = [&](int k) {
+      return *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(kh + koff[k >> 1] + (k & 1) * 32 * 256);
     };
     sq[0] = f32x16{};
     sq[1] = f32x16{};
-    load(0, kb[0]);
+    bf16x8 kb[4];
+    kb[0] = ld(0);
+    kb[1] = ld(1);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int bt = 0; bt < 4; ++bt) {
-      if (bt < 3) load(bt + 1, kb[(bt + 1) & 1]);
-      dma(2 * bt);
-      dma(2 * bt + 1);
+    for (int k = 0; k < 16; ++k) {
+      if (k + 2 < 16) kb[(k + 2) & 3] = ld(k + 2);
+      if ((k & 1) == 0) dma(k >> 1);
       __builtin_amdgcn_sched_barrier(0);
-      const int t = bt >> 1, c0 = (bt & 1) * 4;
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        sq[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[bt & 1][u], qf[c0 + u], sq[t], 0, 0, 0);
+      sq[k & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[k & 3], qf[k >> 1], sq[k & 1], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
