@@ -166,6 +166,48 @@ def calibrate_copy(mib):
                       "launches": 3}), flush=True)
 
 
+def dynamic_plan_context():
+    """Device-side CSR from a device bitmap (bsa_plan_set_bitmap) against the host planner
+    on the same bitmap: the 32K random layout's per-head Bernoulli(0.10) bitmap, and a
+    256K causal per-head bitmap of the density of the 256K windowed layout (2%)."""
+    res = {}
+    w = wl.WORKLOADS["random32k"]
+    cases = {"random32k": (w, wl.layout_of(w)["bitmap"], False)}
+    g = torch.Generator(device="cuda").manual_seed(5)
+    nb = 262144 // 128
+    bm = (torch.rand((32, nb, nb), generator=g, device="cuda") < 0.02).to(torch.uint8)
+    bm[:, torch.arange(nb), torch.arange(nb)] = 1
+    rw = wl.Workload("router256k", 1, 32, 8, 262144, 128, 128, torch.bfloat16, 5, {})
+    cases["router256k"] = (rw, bm.cpu().numpy(), True)
+    del bm
+    for name, (cw, bitmap, causal) in cases.items():
+        lay = dict(causal=causal, unit="blocks", window_left=-1, window_right=-1, global_keys=0,
+                   global_queries=0, bitmap=bitmap)
+        t = time.perf_counter()
+        hp = plan_for(cw, lay)
+        host_ms = (time.perf_counter() - t) * 1e3
+        dp = bsattn.plan_dynamic(cw.batch, cw.heads, cw.kv_heads, cw.seq_len, cw.head_dim, cw.block,
+                                 cw.dtype, causal, bitmap.shape[0])
+        dbm = torch.from_numpy(np.ascontiguousarray(bitmap, dtype=np.uint8)).cuda()
+        nnz = torch.zeros(1, dtype=torch.int64, device="cuda")
+        for _ in range(3):
+            dp.set_bitmap(dbm, nnz)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            dp.set_bitmap(dbm, nnz)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = {"bitmap": list(bitmap.shape), "causal": causal, "nnz": int(nnz.item()),
+                     "host_plan_ms": round(host_ms, 2),
+                     "device_plan_us": round(e0.elapsed_time(e1) * 1e3 / 20, 1),
+                     "nnz_matches_host": int(nnz.item()) == hp.info["nnz"]}
+        log(f"[bench] dynamic plan {name}: {res[name]}")
+        del dbm, dp, hp
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,9 +308,12 @@ def main():
             log(f"[bench] context {name}: {ctx[name]}")
         ctx["dense_over_sparse_time"] = round(ctx["dense256k"]["ms_per_forward"] /
                                               ctx["gqa256k"]["ms_per_forward"], 2)
+        del q, k, v, out, lse
+        torch.cuda.empty_cache()
+        ctx["dynamic_plan"] = dynamic_plan_context()
         result["context"] = ctx
     if not args.no_cpu_baseline:
-        if q.shape[2] != w.seq_len or q.shape[1] != w.heads:
+        if not args.no_context:      # the context runs replaced the inputs
             q, k, v = wl.make_qkv(w, "cuda")
         log("[bench] timing the CPU oracle on a sample ...")
         result["cpu_baseline"] = cpu_baseline(w, lay, q, k, v, flops, args.cpu_seconds)

@@ -30,8 +30,9 @@ SCHEDULE_DEFAULT, SCHEDULE_XCD, SCHEDULE_LPT, SCHEDULE_ROWMAJOR = 0, 1, 2, 3
 
 # Every entry point include/bsattn.h declares.
 EXPORTS = ("bsa_plan", "bsa_plan_host", "bsa_plan_destroy", "bsa_plan_csr", "bsa_plan_get_info",
-           "bsa_plan_work", "bsa_plan_active_blocks", "bsa_forward", "bsa_status_string",
-           "bsa_last_error", "bsa_abi_version")
+           "bsa_plan_work", "bsa_plan_active_blocks", "bsa_plan_dynamic", "bsa_plan_set_bitmap",
+           "bsa_plan_read_csr", "bsa_forward", "bsa_status_string", "bsa_last_error",
+           "bsa_abi_version")
 
 
 class Problem(ctypes.Structure):
@@ -83,6 +84,10 @@ def lib():
     L.bsa_plan_work.argtypes = [P, POINTER(POINTER(c_int32)), POINTER(c_int64)]
     L.bsa_plan_active_blocks.argtypes = [P]
     L.bsa_plan_active_blocks.restype = c_int64
+    L.bsa_plan_dynamic.argtypes = [POINTER(Problem), POINTER(Layout), POINTER(P)]
+    L.bsa_plan_set_bitmap.argtypes = [P, c_void_p, c_void_p, c_void_p]
+    L.bsa_plan_read_csr.argtypes = [P, c_int32, POINTER(c_int32), POINTER(c_int32), POINTER(c_uint8),
+                                    c_int64, POINTER(c_int64)]
     L.bsa_forward.argtypes = [c_void_p, c_void_p, c_void_p, P, c_void_p, c_void_p, c_void_p]
     L.bsa_status_string.argtypes = [c_int32]
     L.bsa_status_string.restype = c_char_p
@@ -90,7 +95,7 @@ def lib():
     L.bsa_last_error.restype = c_char_p
     L.bsa_abi_version.restype = c_int32
     for name in ("bsa_plan", "bsa_plan_host", "bsa_plan_csr", "bsa_plan_get_info", "bsa_plan_work",
-                 "bsa_forward"):
+                 "bsa_plan_dynamic", "bsa_plan_set_bitmap", "bsa_plan_read_csr", "bsa_forward"):
         getattr(L, name).restype = c_int32
     _lib = L
     return L
@@ -170,6 +175,36 @@ class Plan:
                 "col_idx": np.ctypeslib.as_array(ci, (n,)).copy() if n else np.zeros(0, np.int32),
                 "flags": np.ctypeslib.as_array(fl, (n,)).copy() if n else np.zeros(0, np.uint8)}
 
+    def set_bitmap(self, bitmap, nnz=None):
+        """bsa_plan_set_bitmap on torch.cuda.current_stream(): bitmap is a contiguous uint8
+        CUDA tensor [layout_heads, nb, nb]; nnz, if given, a one-element int64 CUDA tensor
+        that receives the entry count."""
+        import torch
+        nb, lh = self.info["num_blocks"], self.info["layout_heads"]
+        if (not bitmap.is_cuda or bitmap.dtype != torch.uint8 or not bitmap.is_contiguous()
+                or tuple(bitmap.shape) != (lh, nb, nb)):
+            raise ValueError(f"bitmap must be a contiguous uint8 CUDA tensor of shape {(lh, nb, nb)}")
+        if nnz is not None and (not nnz.is_cuda or nnz.dtype != torch.int64 or nnz.numel() != 1):
+            raise ValueError("nnz must be a one-element int64 CUDA tensor")
+        with torch.cuda.device(bitmap.device):
+            stream = torch.cuda.current_stream().cuda_stream
+            _check(lib().bsa_plan_set_bitmap(self.handle, bitmap.data_ptr(),
+                                             nnz.data_ptr() if nnz is not None else None,
+                                             c_void_p(stream)))
+
+    def read_csr(self, layout_head: int = 0):
+        """bsa_plan_read_csr: the device CSR of a dynamic plan, in the format of csr()."""
+        nb = self.info["num_blocks"]
+        rp = np.zeros(nb + 1, np.int32)
+        n = c_int64()
+        cap = nb * nb
+        ci = np.zeros(max(cap, 1), np.int32)
+        fl = np.zeros(max(cap, 1), np.uint8)
+        _check(lib().bsa_plan_read_csr(self.handle, layout_head,
+                                       rp.ctypes.data_as(POINTER(c_int32)), ci.ctypes.data_as(POINTER(c_int32)),
+                                       fl.ctypes.data_as(POINTER(c_uint8)), cap, ctypes.byref(n)))
+        return {"row_ptr": rp, "col_idx": ci[:n.value].copy(), "flags": fl[:n.value].copy()}
+
     def work(self):
         w = POINTER(c_int32)()
         n = c_int64()
@@ -217,6 +252,21 @@ def plan(batch: int, num_heads: int, num_kv_heads: int, seq_len: int, head_dim: 
     _check(fn(ctypes.byref(pr), ctypes.byref(lay), ctypes.byref(h)))
     del keep
     return Plan(h.value, pr, host_only)
+
+
+def plan_dynamic(batch: int, num_heads: int, num_kv_heads: int, seq_len: int, head_dim: int,
+                 block_size: int, dtype, causal: bool, bitmap_heads: int, scale: float = 0.0,
+                 schedule: int = SCHEDULE_DEFAULT) -> Plan:
+    """bsa_plan_dynamic on the current HIP device; feed it bitmaps with Plan.set_bitmap."""
+    pr = make_problem(batch, num_heads, num_kv_heads, seq_len, head_dim, block_size, dtype,
+                      scale, schedule)
+    lay = Layout()
+    lay.causal, lay.unit = int(bool(causal)), UNIT_BLOCKS
+    lay.window_left, lay.window_right, lay.global_keys, lay.global_queries = -1, -1, 0, 0
+    lay.bitmap, lay.bitmap_heads = None, int(bitmap_heads)
+    h = c_void_p()
+    _check(lib().bsa_plan_dynamic(ctypes.byref(pr), ctypes.byref(lay), ctypes.byref(h)))
+    return Plan(h.value, pr, False)
 
 
 def forward(q, k, v, p: Plan, out=None, lse=None):

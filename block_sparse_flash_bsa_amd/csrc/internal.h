@@ -42,12 +42,17 @@ struct bsa_plan {
   std::vector<std::vector<uint8_t>> flags;     // [layout_heads][nnz_h]
   std::vector<int32_t> work;                   // [launch slots], -1 = idle
   bsa_plan_info_t info{};
-  // Device copy (bsa_plan only).
+  // Device copy (bsa_plan and bsa_plan_dynamic).
   int device = -1;
   void* dev_mem = nullptr;
   const bsa::RowDesc* d_rows = nullptr;        // [layout_heads * nb]
-  const int32_t* d_entries = nullptr;          // [nnz]
+  const int32_t* d_entries = nullptr;          // [nnz], or [entry_capacity] for a dynamic plan
   const int32_t* d_work = nullptr;             // [launch slots]
+  // Dynamic plans: the CSR is written on the device by bsa_plan_set_bitmap;
+  // d_counts is its per-row scratch [layout_heads * nb].
+  int32_t dynamic = 0;
+  int64_t entry_capacity = 0;
+  int32_t* d_counts = nullptr;
 };
 
 namespace bsa {

@@ -215,6 +215,7 @@ void build_work(Plan& P) {
   const int64_t group = P.prob.num_heads / P.prob.num_kv_heads;
   const int64_t items = B * H * nb;
   auto cost = [&](int64_t item) -> int64_t {
+    if (P.dynamic) return 1;   // row lengths are only known on the device
     const int64_t i = item % nb, h = (item / nb) % H;
     const auto& rp = P.row_ptr[P.layout_heads == 1 ? 0 : h];
     return int64_t(rp[i + 1] - rp[i]) + 1;
@@ -342,10 +343,95 @@ bsa_status_t make_plan(const bsa_problem_t* problem, const bsa_layout_t* layout,
   return BSA_OK;
 }
 
+// A plan whose CSR the device derives from a device-resident bitmap: the
+// launch order (unit costs) and device arrays sized for the largest CSR.
+bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layout, bsa_plan_t* out) {
+  bsa::clear_error();
+  if (!out) return fail(BSA_ERR_INVALID_ARGUMENT, "out_plan must not be NULL");
+  bsa_status_t st = validate(problem, layout);
+  if (st != BSA_OK) return st;
+  if (layout->bitmap)
+    return fail(BSA_ERR_INVALID_ARGUMENT,
+                "dynamic plan: layout->bitmap must be NULL (the bitmap is passed to bsa_plan_set_bitmap)");
+  if (layout->bitmap_heads != 1 && layout->bitmap_heads != problem->num_heads)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "dynamic plan: bitmap_heads must be 1 or num_heads (%d), got %d",
+                problem->num_heads, layout->bitmap_heads);
+  if (layout->window_left != -1 || layout->window_right != -1 || layout->global_keys != 0 ||
+      layout->global_queries != 0)
+    return fail(BSA_ERR_INVALID_ARGUMENT,
+                "dynamic plan: window_left/right must be -1 and global_keys/queries 0 (the bitmap is the layout)");
+  const int64_t nb = problem->seq_len / problem->block_size;
+  const int64_t per_head = layout->causal ? nb * (nb + 1) / 2 : nb * nb;
+  const int64_t cap = int64_t(layout->bitmap_heads) * per_head;
+  if (cap > INT32_MAX)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "dynamic plan: %lld possible entries exceed 2^31 - 1",
+                (long long)cap);
+  Plan* P = new (std::nothrow) Plan();
+  if (!P) return fail(BSA_ERR_OUT_OF_MEMORY, "host allocation of the plan failed");
+  try {
+    P->prob = *problem;
+    if (P->prob.scale == 0.f) P->prob.scale = 1.0f / std::sqrt(float(problem->head_dim));
+    P->nb = int32_t(nb);
+    P->layout_heads = layout->bitmap_heads;
+    P->causal = layout->causal;
+    P->token_rule = 0;
+    P->dynamic = 1;
+    P->entry_capacity = cap;
+    build_work(*P);
+  } catch (const std::bad_alloc&) {
+    delete P;
+    return fail(BSA_ERR_OUT_OF_MEMORY, "host allocation while building the plan failed");
+  }
+  P->info.layout_heads = P->layout_heads;
+  P->info.num_blocks = int32_t(nb);
+  P->info.nnz = P->info.nnz_partial = P->info.active_blocks = P->info.allowed_pairs = -1;
+  P->info.max_row_entries = -1;
+  if (hipGetDevice(&P->device) != hipSuccess) {
+    delete P;
+    return fail(BSA_ERR_DEVICE, "hipGetDevice failed: no usable HIP device");
+  }
+  // [rows | counts | entries | work], each part 256-byte aligned.
+  const size_t rows = size_t(P->layout_heads) * P->nb;
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  const size_t off_counts = up(rows * sizeof(bsa::RowDesc));
+  const size_t off_entries = off_counts + up(rows * sizeof(int32_t));
+  const size_t off_work = off_entries + up(size_t(cap) * sizeof(int32_t));
+  const size_t bytes = off_work + P->work.size() * sizeof(int32_t) + 16;
+  hipError_t err = hipMalloc(&P->dev_mem, bytes);
+  if (err != hipSuccess) {
+    P->dev_mem = nullptr;
+    delete P;
+    return fail(err == hipErrorOutOfMemory ? BSA_ERR_OUT_OF_MEMORY : BSA_ERR_DEVICE,
+                "hipMalloc(%zu) for the dynamic plan failed: %s", bytes, hipGetErrorString(err));
+  }
+  auto* base = static_cast<unsigned char*>(P->dev_mem);
+  // Empty rows until the first bitmap arrives; the launch order never changes.
+  err = hipMemset(base, 0, off_counts);
+  if (err == hipSuccess && !P->work.empty())
+    err = hipMemcpy(base + off_work, P->work.data(), P->work.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (err != hipSuccess) {
+    (void)hipFree(P->dev_mem);
+    delete P;
+    return fail(BSA_ERR_DEVICE, "dynamic plan upload failed: %s", hipGetErrorString(err));
+  }
+  P->d_rows = reinterpret_cast<const bsa::RowDesc*>(base);
+  P->d_counts = reinterpret_cast<int32_t*>(base + off_counts);
+  P->d_entries = reinterpret_cast<const int32_t*>(base + off_entries);
+  P->d_work = reinterpret_cast<const int32_t*>(base + off_work);
+  P->info.on_device = 1;
+  *out = P;
+  return BSA_OK;
+}
+
 }  // namespace
 }  // namespace bsa
 
 extern "C" {
+
+bsa_status_t bsa_plan_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layout,
+                              bsa_plan_t* out_plan) {
+  return bsa::make_dynamic(problem, layout, out_plan);
+}
 
 bsa_status_t bsa_plan(const bsa_problem_t* problem, const bsa_layout_t* layout, bsa_plan_t* out_plan) {
   return bsa::make_plan(problem, layout, true, out_plan);
@@ -373,6 +459,8 @@ bsa_status_t bsa_plan_csr(bsa_plan_t plan, int32_t layout_head, const int32_t** 
   bsa::clear_error();
   if (!plan || !row_ptr || !col_idx || !flags || !nnz)
     return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "NULL argument to bsa_plan_csr");
+  if (plan->dynamic)
+    return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "dynamic plan: its CSR lives on the device (bsa_plan_read_csr)");
   if (layout_head < 0 || layout_head >= plan->layout_heads)
     return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "layout_head %d out of range [0, %d)", layout_head,
                      plan->layout_heads);

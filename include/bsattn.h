@@ -38,8 +38,9 @@
  * Only Guide You Need for Sparse Attention Kernels in Long-Context LLMs".
  *
  * Threading: calls on different plans may run concurrently; a plan may be
- * used by several streams at once (bsa_forward only reads it).  The last
- * error string is thread-local.
+ * used by several streams at once (bsa_forward only reads it), except that
+ * bsa_plan_set_bitmap rewrites a dynamic plan and must not overlap a forward
+ * that uses it on another stream.  The last error string is thread-local.
  */
 #ifndef BSATTN_H
 #define BSATTN_H
@@ -50,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 1
+#define BSA_ABI_VERSION 2
 
 /* Status codes.  Every entry point that can fail returns one; no exception
  * crosses the ABI.  Out-parameters are written only on BSA_OK. */
@@ -183,6 +184,63 @@ bsa_status_t bsa_plan_work(bsa_plan_t plan, const int32_t** work, int64_t* slots
  * numerator of the active-block FLOP count 4 * block^2 * head_dim per tile).
  * Returns -1 for a NULL plan. */
 int64_t bsa_plan_active_blocks(bsa_plan_t plan);
+
+/* ---------------------------------------------------------------------------
+ * Dynamic plans: the block bitmap lives in device memory and may change from
+ * one forward to the next (for instance the per-head block mask a router or a
+ * top-k block selector produces on the GPU), so the CSR is derived on the
+ * device instead of on the host.  Motivation: rebuilding masks on the host
+ * costs milliseconds per change (FAQ on dynamic sparsity of "How Do Sparse
+ * Attention Kernels Work in GPU Clusters?"); the learned per-head block masks
+ * are those of "Flash-MSA" on "The Only Guide You Need for Sparse Attention
+ * Kernels in Long-Context LLMs".  The predicate is the bitmap branch of the
+ * one above: tile (i, j) of layout head hl is active iff bitmap[hl][i][j] != 0
+ * and (!causal || j <= i); it is PARTIAL iff causal and j == i.
+ * ------------------------------------------------------------------------- */
+
+/* Create a dynamic plan on the current HIP device.  layout->bitmap must be
+ * NULL; layout->bitmap_heads (1 or num_heads) is the head count of the
+ * bitmaps that bsa_plan_set_bitmap will take; layout->causal applies; the
+ * window and global fields must be -1 and 0 (unit is ignored).  Device memory
+ * for the largest possible CSR is allocated here (bitmap_heads * nb * nb
+ * four-byte entries, nb * (nb + 1) / 2 per head when causal) together with a
+ * fixed launch order of every (b, h, q-block) item, locality runs per XCD as
+ * in BSA_SCHEDULE_XCD but with equal item counts (row lengths are not known
+ * on the host).  The CSR starts empty: until the first bsa_plan_set_bitmap a
+ * forward writes O = 0 and LSE = -inf.  Count fields of bsa_plan_info_t that
+ * depend on the bitmap (nnz, nnz_partial, active_blocks, allowed_pairs,
+ * max_row_entries) are -1 and bsa_plan_active_blocks returns -1;
+ * bsa_plan_work returns the fixed launch order, bsa_plan_csr fails with
+ * INVALID_ARGUMENT (bsa_plan_read_csr copies the device CSR back).
+ * Errors: INVALID_ARGUMENT, UNSUPPORTED, OUT_OF_MEMORY, DEVICE, as bsa_plan. */
+bsa_status_t bsa_plan_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layout,
+                              bsa_plan_t* out_plan);
+
+/* Rebuild a dynamic plan's device CSR from d_bitmap, device memory holding
+ * [bitmap_heads][nb][nb] bytes (nonzero = active), asynchronously on `stream`
+ * (a hipStream_t; NULL = default stream): three kernels count each row, scan
+ * the counts and write the ascending entries.  A later bsa_forward on the
+ * same stream (or after synchronisation) uses the new CSR.  If d_nnz is not
+ * NULL it is a device pointer to one int64_t that receives the total number
+ * of entries over all layout heads (multiply by batch, and by num_heads when
+ * bitmap_heads == 1, for the tiles one forward computes).  The bitmap is read
+ * only during the call's kernels; the caller keeps ownership.  Nothing is
+ * allocated.
+ * Errors (before anything is launched): INVALID_ARGUMENT for a NULL plan or
+ * bitmap, a plan that is not dynamic, a bitmap or plan on another device, or
+ * a bitmap pointer that is not device memory; DEVICE if a launch fails. */
+bsa_status_t bsa_plan_set_bitmap(bsa_plan_t plan, const uint8_t* d_bitmap, int64_t* d_nnz,
+                                 void* stream);
+
+/* Copy layout head `layout_head` of a dynamic plan's device CSR to the host
+ * (synchronous: waits for the device): row_ptr [nb + 1] head-local offsets,
+ * col_idx and flags (0 = FULL, 1 = PARTIAL) of up to `capacity` entries, and
+ * the head's entry count in *nnz.  Same format as bsa_plan_csr.
+ * Errors: INVALID_ARGUMENT for NULL pointers, a plan that is not dynamic, a
+ * layout_head out of range or capacity < the head's entry count; DEVICE if a
+ * copy fails. */
+bsa_status_t bsa_plan_read_csr(bsa_plan_t plan, int32_t layout_head, int32_t* row_ptr,
+                               int32_t* col_idx, uint8_t* flags, int64_t capacity, int64_t* nnz);
 
 /* Run the forward pass asynchronously on `stream` (a hipStream_t; NULL = the
  * default stream) of the plan's device.

@@ -256,3 +256,39 @@ def test_bf16_kernel_m0_only_set_for_lds_loads(tmp_path):
     for k in uses:
         assert body[k].startswith("s_mov_b32 m0, s"), body[k]
         assert body[k + 1].startswith("s_nop") and body[k + 2].startswith("global_load_lds_dwordx4"), body[k:k + 3]
+
+
+# ------------------------------------------------------------ dynamic plans
+def test_dynamic_plan_argument_errors():
+    L = bsattn.lib()
+    pr = bsattn.make_problem(1, 2, 2, 1024, 64, 64, torch.float32)
+    h = ctypes.c_void_p()
+
+    def lay(**kw):
+        x = bsattn.Layout()
+        x.causal, x.unit = kw.get("causal", 0), bsattn.UNIT_BLOCKS
+        x.window_left, x.window_right = kw.get("wl", -1), -1
+        x.global_keys, x.global_queries = kw.get("gk", 0), 0
+        x.bitmap_heads = kw.get("heads", 1)
+        bm = kw.get("bitmap")
+        x.bitmap = bm.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8)) if bm is not None else None
+        return x
+
+    bm = np.ones((1, 16, 16), np.uint8)
+    for bad in (lay(bitmap=bm), lay(wl=3), lay(gk=1), lay(heads=3), lay(causal=2)):
+        assert L.bsa_plan_dynamic(ctypes.byref(pr), ctypes.byref(bad), ctypes.byref(h)) == \
+            bsattn.ERR_INVALID_ARGUMENT
+        assert bsattn.lib().bsa_last_error()
+    assert L.bsa_plan_dynamic(ctypes.byref(pr), ctypes.byref(lay()), None) == bsattn.ERR_INVALID_ARGUMENT
+    # Up to 2^31 - 1 possible entries (one int32 offset space).
+    big = bsattn.make_problem(1, 32, 32, 16384 * 64, 64, 64, torch.float32)
+    assert L.bsa_plan_dynamic(ctypes.byref(big), ctypes.byref(lay(heads=32)), ctypes.byref(h)) == \
+        bsattn.ERR_INVALID_ARGUMENT
+    # A static (host) plan is neither updatable nor readable as a dynamic one.
+    hp = bsattn.plan(1, 2, 2, 1024, 64, 64, torch.float32, spec(False, "blocks", 1, 1), host_only=True)
+    assert L.bsa_plan_set_bitmap(hp.handle, bm.ctypes.data, None, None) == bsattn.ERR_INVALID_ARGUMENT
+    rp = np.zeros(17, np.int32)
+    n = ctypes.c_int64()
+    assert L.bsa_plan_read_csr(hp.handle, 0, rp.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, None,
+                               0, ctypes.byref(n)) == bsattn.ERR_INVALID_ARGUMENT
+    assert L.bsa_plan_set_bitmap(None, bm.ctypes.data, None, None) == bsattn.ERR_INVALID_ARGUMENT

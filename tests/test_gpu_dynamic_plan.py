@@ -1,0 +1,147 @@
+"""GPU tests of dynamic plans: the CSR that bsa_plan_set_bitmap derives on the
+device from a device bitmap must equal, bit for bit, the host planner's CSR
+for the same bitmap and the oracle's plan (entries exist iff the tile has an
+allowed pair; PARTIAL iff fewer than block^2), and a forward through a
+dynamic plan must equal a forward through the host-built plan bit for bit
+(same entries, same kernel; only the launch order differs) and match the
+oracle within the library tolerances."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_flash_bsa_amd import bsattn
+from block_sparse_flash_bsa_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bsattn.lib()
+    torch.cuda.set_device(0)
+
+
+def bitmap_layout(bm, causal):
+    return dict(causal=causal, unit="blocks", window_left=-1, window_right=-1, global_keys=0,
+                global_queries=0, bitmap=bm)
+
+
+def random_bitmap(lh, nb, density, seed):
+    rng = np.random.default_rng(seed)
+    bm = (rng.random((lh, nb, nb)) < density).astype(np.uint8)
+    bm[:, np.arange(nb), np.arange(nb)] = 1
+    return bm
+
+
+def assert_same_csr(a, b, what):
+    for key in ("row_ptr", "col_idx", "flags"):
+        assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), f"{what}: {key} differs"
+
+
+@pytest.mark.parametrize("lh,H,nb,bs,density,causal", [
+    (1, 2, 37, 64, 0.3, False),
+    (1, 2, 37, 64, 0.3, True),
+    (4, 4, 64, 64, 0.15, True),
+    (16, 16, 256, 128, 0.10, False),
+])
+def test_device_csr_matches_host_plan_and_oracle(lh, H, nb, bs, density, causal):
+    bm = random_bitmap(lh, nb, density, seed=nb + lh)
+    bm[0, 3, :] = 0                                  # an empty row (the diagonal too)
+    bm[-1, nb - 2, :] = 1                            # a full row
+    N = nb * bs
+    lay = bitmap_layout(bm, causal)
+    dtype = torch.float32 if bs == 64 else torch.bfloat16
+    D = 64 if bs == 64 else 128
+    hp = bsattn.plan(1, H, H, N, D, bs, dtype, lay, host_only=True)
+    ref = oracle.plan(lay, N, bs)
+    dp = bsattn.plan_dynamic(1, H, H, N, D, bs, dtype, causal, lh)
+    nnz = torch.zeros(1, dtype=torch.int64, device="cuda")
+    dp.set_bitmap(torch.from_numpy(bm).cuda(), nnz)
+    torch.cuda.synchronize()
+    total = 0
+    for h in range(lh):
+        got = dp.read_csr(h)
+        assert_same_csr(got, hp.csr(h), f"head {h} vs host plan")
+        assert_same_csr(got, ref[h], f"head {h} vs oracle")
+        total += len(got["col_idx"])
+    assert int(nnz.item()) == total == hp.info["nnz"]
+    say(f"  lh={lh} nb={nb} causal={causal}: {total} entries identical")
+
+
+def test_forward_through_dynamic_plan_is_bitwise_the_static_one():
+    w = wl.small_variant(wl.WORKLOADS["random32k"], 4096, heads=4, kv_heads=2, batch=2)
+    bm = random_bitmap(4, 32, 0.2, seed=3)
+    for causal in (False, True):
+        lay = bitmap_layout(bm, causal)
+        q, k, v = wl.make_qkv(w, "cpu")
+        sp = bsattn.plan(w.batch, w.heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.dtype, lay)
+        dp = bsattn.plan_dynamic(w.batch, w.heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.dtype,
+                                 causal, 4)
+        dp.set_bitmap(torch.from_numpy(bm).cuda())
+        o1, l1 = bsattn.forward(q.cuda(), k.cuda(), v.cuda(), sp)
+        o2, l2 = bsattn.forward(q.cuda(), k.cuda(), v.cuda(), dp)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2), f"causal={causal}"
+        rows = [(b, h, qq) for b in range(2) for h in range(4) for qq in (0, 1, 127, 128, 2049, 4095)]
+        O_ref, L_ref = oracle.forward(q, k, v, lay, w.block, rows=rows)
+        idx = tuple(torch.tensor(x) for x in zip(*rows))
+        eo = float(np.abs(o2[idx].float().cpu().numpy() - O_ref).max())
+        fin = np.isfinite(L_ref)
+        el = float(np.abs(l2[idx].cpu().numpy()[fin] - L_ref[fin]).max()) if fin.any() else 0.0
+        say(f"  causal={causal}: max|dO| {eo:.2e} max|dLSE| {el:.2e}")
+        assert eo <= 2e-2 and el <= 1e-3
+        assert np.array_equal(np.isfinite(l2[idx].cpu().numpy()), fin)
+
+
+def test_new_bitmap_replaces_the_old_one():
+    nb, bs, H = 48, 64, 2
+    dp = bsattn.plan_dynamic(1, H, H, nb * bs, 64, bs, torch.float32, False, 1)
+    first = np.ones((1, nb, nb), np.uint8)
+    second = random_bitmap(1, nb, 0.05, seed=11)
+    q = torch.randn(1, H, nb * bs, 64, generator=torch.Generator().manual_seed(1))
+    k = torch.randn(1, H, nb * bs, 64, generator=torch.Generator().manual_seed(2))
+    v = torch.randn(1, H, nb * bs, 64, generator=torch.Generator().manual_seed(3))
+    for bm in (first, second):
+        dp.set_bitmap(torch.from_numpy(bm).cuda())
+        lay = bitmap_layout(bm, False)
+        assert_same_csr(dp.read_csr(0), oracle.plan(lay, nb * bs, bs)[0], "after update")
+        out, lse = bsattn.forward(q.cuda(), k.cuda(), v.cuda(), dp)
+        torch.cuda.synchronize()
+        rows = [(0, h, qq) for h in range(H) for qq in (0, 700, 3071)]
+        O_ref, L_ref = oracle.forward(q, k, v, lay, bs, rows=rows)
+        idx = tuple(torch.tensor(x) for x in zip(*rows))
+        assert float(np.abs(out[idx].cpu().numpy() - O_ref).max()) <= 1e-5
+        assert float(np.abs(lse[idx].cpu().numpy() - L_ref).max()) <= 1e-5
+
+
+def test_fresh_and_empty_dynamic_plans_give_empty_rows():
+    nb, bs, H = 16, 128, 2
+    dp = bsattn.plan_dynamic(1, H, H, nb * bs, 128, bs, torch.bfloat16, True, H)
+    q = torch.randn(1, H, nb * bs, 128, device="cuda").to(torch.bfloat16)
+    for step in ("fresh", "zeros"):
+        if step == "zeros":
+            dp.set_bitmap(torch.zeros((H, nb, nb), dtype=torch.uint8, device="cuda"))
+        out, lse = bsattn.forward(q, q, q, dp)
+        torch.cuda.synchronize()
+        assert torch.all(out == 0) and torch.all(torch.isneginf(lse)), step
+
+
+def test_set_bitmap_rejects_host_memory_and_static_plans():
+    nb, bs = 8, 64
+    dp = bsattn.plan_dynamic(1, 1, 1, nb * bs, 64, bs, torch.float32, False, 1)
+    host = np.ones((1, nb, nb), np.uint8)
+    st = bsattn.lib().bsa_plan_set_bitmap(dp.handle, host.ctypes.data, None, None)
+    assert st == bsattn.ERR_INVALID_ARGUMENT
+    sp = bsattn.plan(1, 1, 1, nb * bs, 64, bs, torch.float32, bitmap_layout(host, False))
+    dev = torch.from_numpy(host).cuda()
+    st = bsattn.lib().bsa_plan_set_bitmap(sp.handle, dev.data_ptr(), None, None)
+    assert st == bsattn.ERR_INVALID_ARGUMENT
