@@ -118,6 +118,16 @@ def make_qkv(w: Workload, device="cpu"):
     return q, k, v
 
 
+def make_dout(w: Workload, device="cpu"):
+    """Seeded upstream gradient dO [B,H,N,D] for the backward: iid N(0, 1)
+    drawn in float32 from a generator seeded (workload seed + 1000), rounded
+    to the workload dtype."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev).manual_seed(w.seed + 1000)
+    shape = (w.batch, w.heads, w.seq_len, w.head_dim)
+    return torch.randn(shape, generator=g, device=dev, dtype=torch.float32).to(w.dtype)
+
+
 def small_variant(w: Workload, seq_len: int, heads: Optional[int] = None,
                   kv_heads: Optional[int] = None, batch: Optional[int] = None) -> Workload:
     """Same layout rule at a size the oracle finishes in seconds."""

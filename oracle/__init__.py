@@ -3,8 +3,10 @@
 Only tests, the smoke check and the benchmark's CPU-baseline leg use this
 package.  The product package never imports it.
 """
-from .bsa_oracle import (FULL, PARTIAL, allowed_count, allowed_keys, attend_row,
-                         forward, plan, tile_counts)
+from .bsa_oracle import (FULL, PARTIAL, allowed_count, allowed_keys, allowed_queries,
+                         attend_row, backward, backward_dkv_keys, backward_dq_rows,
+                         forward, grad_row, plan, tile_counts)
 
-__all__ = ["FULL", "PARTIAL", "allowed_count", "allowed_keys", "attend_row",
-           "forward", "plan", "tile_counts"]
+__all__ = ["FULL", "PARTIAL", "allowed_count", "allowed_keys", "allowed_queries",
+           "attend_row", "backward", "backward_dkv_keys", "backward_dq_rows",
+           "forward", "grad_row", "plan", "tile_counts"]

@@ -1,4 +1,4 @@
-"""Reference oracle for block-sparse flash attention (forward).
+"""Reference oracle for block-sparse flash attention (forward and backward).
 
 TEST INFRASTRUCTURE ONLY.  This module is a plain, slow, obviously-correct CPU
 implementation used to check the HIP path.  Only the test suite, the smoke
@@ -31,6 +31,13 @@ What it computes (all arithmetic in float64 with numpy):
   materialising the scores), so the oracle is the definition, not the tiled
   algorithm.  An empty A(q) gives O = 0 and LSE = -inf (log of an empty sum).
   GQA: query head h reads KV head h // (H / Hkv).
+
+* `backward(Q, K, V, dO, layout, block_size)` -- the gradients dQ, dK, dV of
+  sum(dO * O) by the chain rule through the forward above, per query over its
+  allowed keys (softmax Jacobian ds = p * (dp - sum p dp)); `backward_dq_rows`
+  and `backward_dkv_keys` evaluate sampled rows and keys of full-size
+  problems, the latter through `allowed_queries`, the predicate evaluated
+  for every query at a fixed key.
 
 * `plan(layout, N, bs)` -- the per-query-block list of key blocks (step three
   of "How Does Flash-MSA Sparse Attention Work?": a query block fetches only
@@ -296,3 +303,136 @@ def plan(layout, N: int, bs: int, brute: Optional[bool] = None):
             "flags": np.asarray(flags, dtype=np.uint8),
         })
     return out
+
+
+# --------------------------------------------------------------------------
+# Backward: gradients of masked softmax attention
+# --------------------------------------------------------------------------
+# For a scalar loss with upstream gradient dO = dLoss/dO, the chain rule
+# through O_q = sum_k p_qk V_k with p_q = softmax(s_q) over A(q) and
+# s_qk = scale * <Q_q, K_k> gives, per query q and allowed key k:
+#     dV_k  += p_qk * dO_q
+#     dp_qk  = <dO_q, V_k>
+#     ds_qk  = p_qk * (dp_qk - sum_k' p_qk' dp_qk')      (softmax Jacobian)
+#     dQ_q  += scale * ds_qk * K_k
+#     dK_k  += scale * ds_qk * Q_q
+# Keys shared by the query heads of a GQA group accumulate over the group.
+# The pages treat the backward only through its cost ("Training Throughput"
+# of "Sparse Attention Kernels vs Full Attention Performance"; forward and
+# backward timings in the FAQ of "How Do Sparse Attention Kernels Work in GPU
+# Clusters?"); the gradient itself is the derivative of the forward defined
+# above, written out here.  sum_k' p_qk' dp_qk' equals <dO_q, O_q>.
+
+def allowed_queries(layout, N: int, bs: int, h: int, k: int) -> np.ndarray:
+    """Sorted int64 array of the queries q of head h with k in A(q).
+
+    The layout predicate evaluated for every q at fixed k (the transpose of
+    allowed_keys): causal_ok && (bitmap ? bitmap[hl][q/bs][k/bs]
+    : in_window || key_global || query_global), in the spec's units.
+    """
+    q = np.arange(N, dtype=np.int64)
+    bm = layout.get("bitmap")
+    if bm is not None:
+        ok = np.asarray(bm)[_layout_head(layout, h), q // bs, k // bs].astype(bool)
+    else:
+        if layout["unit"] == "tokens":
+            qu, ku = q, k
+        else:
+            qu, ku = q // bs, k // bs
+        wl, wr = layout["window_left"], layout["window_right"]
+        in_w = np.ones(N, dtype=bool)
+        if wl >= 0:
+            in_w &= (qu - ku) <= wl
+        if wr >= 0:
+            in_w &= (ku - qu) <= wr
+        ok = in_w | (ku < layout["global_keys"]) | (qu < layout["global_queries"])
+    if layout["causal"]:
+        ok &= k <= q
+    return q[ok]
+
+
+def grad_row(q_vec: np.ndarray, do_vec: np.ndarray, K_rows: np.ndarray,
+             V_rows: np.ndarray, scale: float):
+    """Softmax weights p and score gradients ds of one query over its keys.
+
+    Returns (p, ds) over the gathered keys (float64); empty inputs give empty
+    arrays.
+    """
+    if K_rows.shape[0] == 0:
+        return np.zeros(0), np.zeros(0)
+    s = scale * (K_rows @ q_vec)
+    w = np.exp(s - s.max())
+    p = w / w.sum()
+    dp = V_rows @ do_vec
+    ds = p * (dp - p @ dp)
+    return p, ds
+
+
+def backward(Q, K, V, dO, layout, block_size: int, scale: Optional[float] = None):
+    """Oracle backward over every row: returns (dQ, dK, dV) as float64 arrays
+    shaped like Q, K and V.  Inputs as for `forward`, plus dO shaped like Q."""
+    B, H, N, D = (int(x) for x in Q.shape)
+    Hkv = int(K.shape[1])
+    group = H // Hkv
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    Qd, Kd, Vd, dOd = _f64(Q), _f64(K), _f64(V), _f64(dO)
+    dQ = np.zeros_like(Qd)
+    dK = np.zeros_like(Kd)
+    dV = np.zeros_like(Vd)
+    for b in range(B):
+        for h in range(H):
+            hk = h // group
+            for q in range(N):
+                keys = allowed_keys(layout, N, block_size, h, q)
+                p, ds = grad_row(Qd[b, h, q], dOd[b, h, q], Kd[b, hk, keys], Vd[b, hk, keys], scale)
+                if keys.size == 0:
+                    continue
+                dQ[b, h, q] = scale * (ds @ Kd[b, hk, keys])
+                dK[b, hk, keys] += scale * np.outer(ds, Qd[b, h, q])
+                dV[b, hk, keys] += np.outer(p, dOd[b, h, q])
+    return dQ, dK, dV
+
+
+def backward_dq_rows(Q, K, V, dO, layout, block_size: int, rows, scale: Optional[float] = None):
+    """dQ of the sampled rows (b, h, q) only: float64 [R, D]."""
+    D = int(Q.shape[3])
+    N = int(Q.shape[2])
+    group = int(Q.shape[1]) // int(K.shape[1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    rows = list(rows)
+    out = np.zeros((len(rows), D))
+    for r, (b, h, q) in enumerate(rows):
+        keys = allowed_keys(layout, N, block_size, h, q)
+        Kr = _f64(K[b, h // group][keys])
+        _, ds = grad_row(_f64(Q[b, h, q]), _f64(dO[b, h, q]), Kr, _f64(V[b, h // group][keys]), scale)
+        if keys.size:
+            out[r] = scale * (ds @ Kr)
+    return out
+
+
+def backward_dkv_keys(Q, K, V, dO, layout, block_size: int, keys, scale: Optional[float] = None):
+    """dK and dV of the sampled keys (b, hk, k) only: two float64 [R, D].
+
+    Each key sums over every query of its GQA group's heads that may attend
+    to it; each such query's softmax is formed over its own allowed keys.
+    """
+    H, N, D = (int(x) for x in Q.shape[1:])
+    group = H // int(K.shape[1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    keys = list(keys)
+    dK = np.zeros((len(keys), D))
+    dV = np.zeros((len(keys), D))
+    for r, (b, hk, k) in enumerate(keys):
+        Kb, Vb = K[b, hk], V[b, hk]
+        for h in range(hk * group, (hk + 1) * group):
+            for q in allowed_queries(layout, N, block_size, h, k):
+                ks = allowed_keys(layout, N, block_size, h, int(q))
+                pos = int(np.searchsorted(ks, k))
+                qv, dov = _f64(Q[b, h, q]), _f64(dO[b, h, q])
+                p, ds = grad_row(qv, dov, _f64(Kb[ks]), _f64(Vb[ks]), scale)
+                dK[r] += scale * ds[pos] * qv
+                dV[r] += p[pos] * dov
+    return dK, dV
