@@ -208,6 +208,51 @@ def dynamic_plan_context():
     return res
 
 
+def time_backward(p, q, k, v, out, lse, do, steps, warmup):
+    """Warm up, then time `steps` backwards (three launches each) with a HIP
+    event pair around each on the launch stream; returns the per-step ms."""
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    delta = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    for _ in range(warmup):
+        bsattn.backward(q, k, v, out, lse, do, p, dq, dk, dv, delta)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        bsattn.backward(q, k, v, out, lse, do, p, dq, dk, dv, delta)
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def backward_context(names, steps=5):
+    """bsa_backward on the bf16 workloads: ms per backward (Delta, dQ and dK/dV
+    kernels), TFLOP/s counting the five GEMMs of an attention backward per
+    active tile (S recomputed, dP, dV, dK, dQ: 10 * block^2 * head_dim, the
+    usual 2.5x of the forward) and the seven the kernels execute (S and dP
+    are formed in both the dQ and the dK/dV kernel)."""
+    res = {}
+    for name in names:
+        w = wl.WORKLOADS[name]
+        p = plan_for(w, wl.layout_of(w))
+        q, k, v = wl.make_qkv(w, "cuda")
+        do = wl.make_dout(w, "cuda")
+        out, lse = bsattn.forward(q, k, v, p)
+        ms = float(np.mean(time_backward(p, q, k, v, out, lse, do, steps, 1)))
+        tiles = p.info["active_blocks"]
+        unit = w.block * w.block * w.head_dim
+        alg = 10.0 * unit * tiles / (ms * 1e-3) / 1e12
+        res[name] = {"ms_per_backward": round(ms, 3), "tflops_algorithmic": round(alg, 1),
+                     "pct_of_peak": round(100 * alg / PEAK_BF16_TFLOPS, 2),
+                     "tflops_mfma_executed": round(1.4 * alg, 1), "active_tiles": tiles}
+        log(f"[bench] backward {name}: {res[name]}")
+        del q, k, v, do, out, lse, p
+        torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -218,6 +263,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only time bsa_backward on --workload (for profiling) and print its JSON")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MiB",
                     help="only run a plain device copy of this size (counter calibration)")
     args = ap.parse_args()
@@ -235,6 +282,9 @@ def main():
         calibrate_copy(args.calibrate_copy)
         return
     bsattn.lib()
+    if args.backward_only:
+        print(json.dumps({"backward": backward_context([args.workload], args.steps)}), flush=True)
+        return
 
     w = wl.WORKLOADS[args.workload]
     lay = wl.layout_of(w)
@@ -311,6 +361,7 @@ def main():
         del q, k, v, out, lse
         torch.cuda.empty_cache()
         ctx["dynamic_plan"] = dynamic_plan_context()
+        ctx["backward"] = backward_context(["window16k", "random32k", "winglobal128k", "gqa256k"])
         result["context"] = ctx
     if not args.no_cpu_baseline:
         if not args.no_context:      # the context runs replaced the inputs

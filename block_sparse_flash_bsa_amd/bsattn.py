@@ -31,8 +31,8 @@ SCHEDULE_DEFAULT, SCHEDULE_XCD, SCHEDULE_LPT, SCHEDULE_ROWMAJOR = 0, 1, 2, 3
 # Every entry point include/bsattn.h declares.
 EXPORTS = ("bsa_plan", "bsa_plan_host", "bsa_plan_destroy", "bsa_plan_csr", "bsa_plan_get_info",
            "bsa_plan_work", "bsa_plan_active_blocks", "bsa_plan_dynamic", "bsa_plan_set_bitmap",
-           "bsa_plan_read_csr", "bsa_forward", "bsa_status_string", "bsa_last_error",
-           "bsa_abi_version")
+           "bsa_plan_read_csr", "bsa_forward", "bsa_plan_csr_transposed", "bsa_plan_work_kv",
+           "bsa_backward", "bsa_status_string", "bsa_last_error", "bsa_abi_version")
 
 
 class Problem(ctypes.Structure):
@@ -89,13 +89,18 @@ def lib():
     L.bsa_plan_read_csr.argtypes = [P, c_int32, POINTER(c_int32), POINTER(c_int32), POINTER(c_uint8),
                                     c_int64, POINTER(c_int64)]
     L.bsa_forward.argtypes = [c_void_p, c_void_p, c_void_p, P, c_void_p, c_void_p, c_void_p]
+    L.bsa_plan_csr_transposed.argtypes = [P, c_int32, POINTER(POINTER(c_int32)), POINTER(POINTER(c_int32)),
+                                          POINTER(POINTER(c_uint8)), POINTER(c_int64)]
+    L.bsa_plan_work_kv.argtypes = [P, POINTER(POINTER(c_int32)), POINTER(c_int64)]
+    L.bsa_backward.argtypes = [c_void_p] * 6 + [P] + [c_void_p] * 5
     L.bsa_status_string.argtypes = [c_int32]
     L.bsa_status_string.restype = c_char_p
     L.bsa_last_error.argtypes = []
     L.bsa_last_error.restype = c_char_p
     L.bsa_abi_version.restype = c_int32
     for name in ("bsa_plan", "bsa_plan_host", "bsa_plan_csr", "bsa_plan_get_info", "bsa_plan_work",
-                 "bsa_plan_dynamic", "bsa_plan_set_bitmap", "bsa_plan_read_csr", "bsa_forward"):
+                 "bsa_plan_dynamic", "bsa_plan_set_bitmap", "bsa_plan_read_csr", "bsa_forward",
+                 "bsa_plan_csr_transposed", "bsa_plan_work_kv", "bsa_backward"):
         getattr(L, name).restype = c_int32
     _lib = L
     return L
@@ -211,6 +216,25 @@ class Plan:
         _check(lib().bsa_plan_work(self.handle, ctypes.byref(w), ctypes.byref(n)))
         return np.ctypeslib.as_array(w, (n.value,)).copy() if n.value else np.zeros(0, np.int32)
 
+    def csr_transposed(self, layout_head: int = 0):
+        """bsa_plan_csr_transposed: per k-block, the q-blocks whose lists hold it."""
+        cp, ri, fl = POINTER(c_int32)(), POINTER(c_int32)(), POINTER(c_uint8)()
+        nnz = c_int64()
+        _check(lib().bsa_plan_csr_transposed(self.handle, layout_head, ctypes.byref(cp), ctypes.byref(ri),
+                                             ctypes.byref(fl), ctypes.byref(nnz)))
+        nb = self.info["num_blocks"]
+        n = nnz.value
+        return {"col_ptr": np.ctypeslib.as_array(cp, (nb + 1,)).copy(),
+                "row_idx": np.ctypeslib.as_array(ri, (n,)).copy() if n else np.zeros(0, np.int32),
+                "flags": np.ctypeslib.as_array(fl, (n,)).copy() if n else np.zeros(0, np.uint8)}
+
+    def work_kv(self):
+        """bsa_plan_work_kv: launch order of the dK/dV kernel."""
+        w = POINTER(c_int32)()
+        n = c_int64()
+        _check(lib().bsa_plan_work_kv(self.handle, ctypes.byref(w), ctypes.byref(n)))
+        return np.ctypeslib.as_array(w, (n.value,)).copy() if n.value else np.zeros(0, np.int32)
+
     def active_blocks(self) -> int:
         return int(lib().bsa_plan_active_blocks(self.handle))
 
@@ -292,3 +316,38 @@ def forward(q, k, v, p: Plan, out=None, lse=None):
         _check(lib().bsa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), p.handle,
                                  out.data_ptr(), lse.data_ptr(), c_void_p(stream)))
     return out, lse
+
+
+def backward(q, k, v, out, lse, dout, p: Plan, dq=None, dk=None, dv=None, delta=None):
+    """bsa_backward on torch.cuda.current_stream(); returns (dq, dk, dv).
+
+    out and lse are the forward's outputs for these inputs and this plan;
+    delta (float32 [B, H, N]) is the library's workspace for <dO, O>.
+    """
+    import torch
+    pr = p.problem
+    B, H, Hk, N, D = pr.batch, pr.num_heads, pr.num_kv_heads, pr.seq_len, pr.head_dim
+    dt = torch.bfloat16 if pr.dtype == BF16 else torch.float32
+    qs, ks = (B, H, N, D), (B, Hk, N, D)
+    dev = q.device
+    if dq is None:
+        dq = torch.empty(qs, dtype=dt, device=dev)
+    if dk is None:
+        dk = torch.empty(ks, dtype=dt, device=dev)
+    if dv is None:
+        dv = torch.empty(ks, dtype=dt, device=dev)
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    for name, t, shape, tdt in (("q", q, qs, dt), ("k", k, ks, dt), ("v", v, ks, dt), ("out", out, qs, dt),
+                                ("lse", lse, (B, H, N), torch.float32), ("dout", dout, qs, dt),
+                                ("dq", dq, qs, dt), ("dk", dk, ks, dt), ("dv", dv, ks, dt),
+                                ("delta", delta, (B, H, N), torch.float32)):
+        if not t.is_cuda or t.dtype != tdt or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {tdt} CUDA tensor of shape {shape}, got "
+                             f"{tuple(t.shape)} {t.dtype} on {t.device}")
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream().cuda_stream
+        _check(lib().bsa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                  dout.data_ptr(), p.handle, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                  delta.data_ptr(), c_void_p(stream)))
+    return dq, dk, dv

@@ -1,0 +1,459 @@
+// Block-sparse flash attention backward kernels for gfx950 (CDNA4) and the
+// bsa_backward launcher.
+//
+// The gradients of the forward (masked softmax attention over each query's
+// allowed keys) given dO = dLoss/dO, the forward's O and its log-sum-exp:
+//   p_qk  = exp(scale * <Q_q, K_k> - LSE_q)          (the forward's weights)
+//   Delta_q = <dO_q, O_q>
+//   ds_qk = p_qk * (<dO_q, V_k> - Delta_q)           (softmax Jacobian)
+//   dQ_q  = scale * sum_k ds_qk K_k
+//   dK_k  = scale * sum_q ds_qk Q_q,   dV_k = sum_q p_qk dO_q
+// The pages discuss the backward only through its cost (training throughput
+// of block-sparse vs dense attention in "Sparse Attention Kernels vs Full
+// Attention Performance"); like the forward it visits only the active tiles
+// and never stores a score matrix: every tile's scores are recomputed from Q
+// and K and turned into weights with the saved LSE.
+//
+// Three kernels:
+//   bwd_delta_bf16     Delta_q per row (HBM-bound, 16 lanes per row).
+//   bwd_dq_bf16_d128   one workgroup per (b, h, q-block), walking the
+//                      forward's CSR row: S^T and dP^T = V dO^T on MFMA,
+//                      dS^T in registers, dQ^T += K^T dS^T.
+//   bwd_dkdv_bf16_d128 one workgroup per (b, KV head, k-block), walking the
+//                      transposed CSR over every query head of the GQA group:
+//                      S and dP = dO V^T on MFMA, P and dS in registers,
+//                      dV^T += dO^T P and dK^T += Q^T dS.
+// Splitting dQ from dK/dV recomputes S and dP once more but needs no atomics,
+// so results are deterministic.  Both tile kernels use the forward's MFMA
+// layouts: a 32x32 accumulator tile gives each lane one column (a query in
+// the dQ kernel, a key in the dK/dV kernel) and 16 rows, and accumulator
+// registers 8c .. 8c+7 of tile t are exactly the 8 contraction elements that
+// lane supplies for 16-element chunk 2t + c of the next product's B operand;
+// the matching A operand comes from LDS through ds_read_b64_tr_b16.
+// Tiles are staged through LDS by plain 16-byte loads and stores, one tile
+// pair per step between two barriers.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "internal.h"
+
+namespace bsa {
+namespace {
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const float* lse;
+  const uint16_t* dout;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* delta;
+  const RowDesc* rows;        // forward CSR rows [layout heads * nb]
+  const int32_t* entries;     // (j << 1) | partial
+  const int32_t* work;        // dQ launch order: (b * H + h) * nb + i
+  const RowDesc* cols;        // transposed rows [layout heads * nb]
+  const int32_t* entries_t;   // (i << 1) | partial
+  const int32_t* work_kv;     // dK/dV launch order: (b * Hkv + hk) * nb + j
+  int64_t N;
+  int32_t H, Hkv, group, nb, per_head_layout;
+  float scale, sl2;           // sl2 = scale * log2(e)
+  int32_t causal, token_rule, gk32, gq32;
+  // Window and causal parts of the token predicate as one range of q - k:
+  // allowed iff (uint32)(q - k - mlo) <= mspan.
+  int32_t mlo;
+  uint32_t mspan;
+};
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kD = 128;
+constexpr int kB = 128;           // layout block = tile height and width
+constexpr int kThreads = 256;     // 4 waves of 64
+constexpr int kTileBytes = kB * kD * 2;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+
+// Token predicate inside a PARTIAL tile: the window/causal range of q - k, or
+// a global key / global query row (still under the causal cut).  With
+// token_rule == 0 the range is the causal cut alone.
+__device__ __forceinline__ bool pair_ok(const BwdParams& p, int q, int k) {
+  const bool in_range = uint32_t(q - k) - uint32_t(p.mlo) <= p.mspan;
+  const bool glob = p.token_rule && (k < p.gk32 || q < p.gq32) && (!p.causal || k <= q);
+  return in_range || glob;
+}
+
+// LDS tile layout: row r (256 bytes) with 16-byte chunk c at chunk
+// c ^ 4 * (r & 3).  Row reads of 16 bytes and the transposing 8-byte reads
+// both stay inside one chunk, so either kind sees the logical layout.
+__device__ __forceinline__ uint32_t tile_off(int r, int c) { return r * 256 + 16 * (c ^ (4 * (r & 3))); }
+
+// Copy one contiguous 128 x 128 bf16 tile (256-byte rows) from global memory
+// into LDS: 8 coalesced 16-byte loads per thread, then the swizzled stores.
+__device__ __forceinline__ void stage_tile(lds_u8* dst, const unsigned char* __restrict__ src, int tid) {
+  u32x4 r[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int ci = tid + kThreads * u;
+    r[u] = *reinterpret_cast<const u32x4*>(src + (ci >> 4) * 256 + (ci & 15) * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int ci = tid + kThreads * u;
+    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(dst + tile_off(ci >> 4, ci & 15)) = r[u];
+  }
+}
+
+// A operand (32 rows x 16 contraction elements) by a row read: row
+// row0 + (lane & 31), elements 16 cc + 8 (lane >> 5) .. +7.
+__device__ __forceinline__ bf16x8 read_rows(const lds_u8* base, uint32_t off) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(base + off);
+}
+
+// A operand by two transposing reads: lane l receives, for column
+// d = 32 dt + (l & 31), the 8 rows 16 kc + 4 (l >> 5) + {0..3, 8..11} (the
+// row order of a 16-element chunk of the accumulator layout).
+__device__ __forceinline__ bf16x8 read_cols(const lds_u8* base, uint32_t voff, int kc) {
+  const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4*>(const_cast<lds_u8*>(base) + voff + (16 * kc) * 256)));
+  const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4*>(const_cast<lds_u8*>(base) + voff + (16 * kc + 8) * 256)));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+}
+
+// Store a 32-column x 128-row transposed accumulator (acc[dt] row
+// 32 dt + 8 (r / 4) + 4 hf + r % 4 of this lane's column) as one bf16 row of
+// 128 values at `dst`, times `mul`.
+__device__ __forceinline__ void store_row(uint16_t* dst, const f32x16 (&acc)[4], float mul, int hf) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 pk;
+      pk[0] = uint32_t(bf16_bits(acc[dt][4 * g + 0] * mul)) | (uint32_t(bf16_bits(acc[dt][4 * g + 1] * mul)) << 16);
+      pk[1] = uint32_t(bf16_bits(acc[dt][4 * g + 2] * mul)) | (uint32_t(bf16_bits(acc[dt][4 * g + 3] * mul)) << 16);
+      *reinterpret_cast<u32x2*>(dst + dt * 32 + 8 * g + 4 * hf) = pk;
+    }
+}
+
+// Per-lane offset of the transposing reads (see read_cols): in 16-lane group
+// g, lane 4 r4 + c4 addresses row 4 hf + r4 (plus 16 kc and 8) and columns
+// 32 dt + 16 (g & 1) + 4 c4 .. +3.
+__device__ __forceinline__ uint32_t col_read_off(int lane, int dt) {
+  const int hf = lane >> 5, r4 = (lane & 15) >> 2, c4 = lane & 3, gp = (lane >> 4) & 1;
+  return (4 * hf + r4) * 256 + 16 * ((4 * dt + 2 * gp + (c4 >> 1)) ^ (4 * r4)) + 8 * (c4 & 1);
+}
+
+// ---------------------------------------------------------------------------
+// Delta_q = <dO_q, O_q> in float32: 16 lanes per 128-element row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void bwd_delta_bf16(const uint16_t* __restrict__ o,
+                                                         const uint16_t* __restrict__ dout,
+                                                         float* __restrict__ delta, int64_t rows) {
+  const int64_t row = int64_t(blockIdx.x) * (kThreads / 16) + (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;
+  float s = 0.f;
+  if (row < rows) {
+    const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * kD + c * 8);
+    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + row * kD + c * 8);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s = fmaf(__uint_as_float(a[u] << 16), __uint_as_float(b[u] << 16), s);
+      s = fmaf(__uint_as_float(a[u] & 0xffff0000u), __uint_as_float(b[u] & 0xffff0000u), s);
+    }
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  if (c == 0 && row < rows) delta[row] = s;
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (b, h, q-block); wave w owns query rows 32w .. +31.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char Ksh[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char Vsh[kTileBytes];
+  lds_u8* const Ks = (lds_u8*)Ksh;
+  lds_u8* const Vs = (lds_u8*)Vsh;
+
+  const int item = p.work[blockIdx.x];
+  if (item < 0) return;
+  const int i = item % p.nb;
+  const int bh = item / p.nb;
+  const int h = bh % p.H, b = bh / p.H;
+  const int hk = h / p.group;
+  const RowDesc row = p.rows[(p.per_head_layout ? h : 0) * p.nb + i];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r32 = lane & 31, hf = lane >> 5;
+  const int qg = i * kB + wave * 32 + r32;
+  const int64_t qrow = (int64_t(b) * p.H + h) * p.N + qg;
+
+  // Q^T and dO^T as B operands: lane (row r32, half hf) holds d = 16c + 8hf .. +7.
+  bf16x8 qf[8], df[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    qf[c] = *reinterpret_cast<const bf16x8*>(p.q + qrow * kD + c * 16 + hf * 8);
+    df[c] = *reinterpret_cast<const bf16x8*>(p.dout + qrow * kD + c * 16 + hf * 8);
+  }
+  const float lse = p.lse[qrow];
+  // An empty row (LSE = -inf) has every score masked in every tile it meets.
+  const float lse2 = lse == -INFINITY ? 0.f : lse * kLog2e;
+  const float dlt = p.delta[qrow];
+  const unsigned char* Kg = reinterpret_cast<const unsigned char*>(p.k + (int64_t(b) * p.Hkv + hk) * p.N * kD);
+  const unsigned char* Vg = reinterpret_cast<const unsigned char*>(p.v + (int64_t(b) * p.Hkv + hk) * p.N * kD);
+
+  uint32_t aoff[8], coff[4];
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) aoff[cc] = tile_off(r32, 2 * cc + hf);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) coff[dt] = col_read_off(lane, dt);
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+
+  for (int e = 0; e < row.count; ++e) {
+    const int ent = p.entries[row.start + e];
+    const int j = ent >> 1;
+    const bool partial = ent & 1;
+    __syncthreads();                                   // every wave is done with the last tile
+    stage_tile(Ks, Kg + int64_t(j) * kTileBytes, tid);
+    stage_tile(Vs, Vg + int64_t(j) * kTileBytes, tid);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {                      // keys 32t .. 32t+31 of the tile
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(Ks, aoff[cc] + t * 32 * 256), qf[cc], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(Vs, aoff[cc] + t * 32 * 256), df[cc], dp, 0, 0, 0);
+      }
+      // Register r holds key 32t + 8 (r / 4) + 4 hf + r % 4 of query qg.
+      bf16x8 ds[2];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float x = s[r];
+        if (partial) {
+          const int kk = j * kB + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
+          if (!pair_ok(p, qg, kk)) x = -INFINITY;
+        }
+        const float pr = __builtin_amdgcn_exp2f(fmaf(x, p.sl2, -lse2));
+        ds[r >> 3][r & 7] = static_cast<__bf16>(pr * (dp[r] - dlt));
+      }
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols(Ks, coff[dt], 2 * t + c2), ds[c2], acc[dt],
+                                                            0, 0, 0);
+    }
+  }
+  store_row(p.dq + qrow * kD, acc, p.scale, hf);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (b, KV head, k-block); wave w owns keys
+// 32w .. +31 and walks, for every query head of the group, the q-blocks of
+// the transposed CSR.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_d128(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char Qsh[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char dOsh[kTileBytes];
+  __shared__ __attribute__((aligned(16))) float lse_s[kB];
+  __shared__ __attribute__((aligned(16))) float dlt_s[kB];
+  lds_u8* const Qs = (lds_u8*)Qsh;
+  lds_u8* const dOs = (lds_u8*)dOsh;
+
+  const int item = p.work_kv[blockIdx.x];
+  if (item < 0) return;
+  const int j = item % p.nb;
+  const int bk = item / p.nb;
+  const int hk = bk % p.Hkv, b = bk / p.Hkv;
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r32 = lane & 31, hf = lane >> 5;
+  const int kg = j * kB + wave * 32 + r32;
+  const int64_t krow = (int64_t(b) * p.Hkv + hk) * p.N + kg;
+
+  // K^T and V^T as B operands: lane (key r32, half hf) holds d = 16c + 8hf .. +7.
+  bf16x8 kf[8], vf[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    kf[c] = *reinterpret_cast<const bf16x8*>(p.k + krow * kD + c * 16 + hf * 8);
+    vf[c] = *reinterpret_cast<const bf16x8*>(p.v + krow * kD + c * 16 + hf * 8);
+  }
+  uint32_t aoff[8], coff[4];
+#pragma unroll
+  for (int cc = 0; cc < 8; ++cc) aoff[cc] = tile_off(r32, 2 * cc + hf);
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) coff[dt] = col_read_off(lane, dt);
+
+  f32x16 dk[4], dv[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+
+  for (int g = 0; g < p.group; ++g) {
+    const int h = hk * p.group + g;
+    const RowDesc col = p.cols[(p.per_head_layout ? h : 0) * p.nb + j];
+    const int64_t hbase = (int64_t(b) * p.H + h) * p.N;
+    const unsigned char* Qg = reinterpret_cast<const unsigned char*>(p.q + hbase * kD);
+    const unsigned char* dOg = reinterpret_cast<const unsigned char*>(p.dout + hbase * kD);
+    for (int e = 0; e < col.count; ++e) {
+      const int ent = p.entries_t[col.start + e];
+      const int i = ent >> 1;
+      const bool partial = ent & 1;
+      __syncthreads();                                 // every wave is done with the last tile
+      stage_tile(Qs, Qg + int64_t(i) * kTileBytes, tid);
+      stage_tile(dOs, dOg + int64_t(i) * kTileBytes, tid);
+      if (tid < kB) {
+        const float l = p.lse[hbase + int64_t(i) * kB + tid];
+        lse_s[tid] = l == -INFINITY ? 0.f : l * kLog2e;
+        dlt_s[tid] = p.delta[hbase + int64_t(i) * kB + tid];
+      }
+      __syncthreads();
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {                    // queries 32t .. 32t+31 of the tile
+        f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+        for (int cc = 0; cc < 8; ++cc) {
+          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(Qs, aoff[cc] + t * 32 * 256), kf[cc], s, 0, 0, 0);
+          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(dOs, aoff[cc] + t * 32 * 256), vf[cc], dp, 0, 0, 0);
+        }
+        // Register r holds query 32t + 8 (r / 4) + 4 hf + r % 4 for key kg.
+        bf16x8 pb[2], db[2];
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int q0 = 32 * t + 8 * g4 + 4 * hf;
+          const f32x4 L = *reinterpret_cast<const f32x4*>(lse_s + q0);
+          const f32x4 Dl = *reinterpret_cast<const f32x4*>(dlt_s + q0);
+#pragma unroll
+          for (int r3 = 0; r3 < 4; ++r3) {
+            const int r = 4 * g4 + r3;
+            float x = s[r];
+            if (partial && !pair_ok(p, i * kB + q0 + r3, kg)) x = -INFINITY;
+            const float pr = __builtin_amdgcn_exp2f(fmaf(x, p.sl2, -L[r3]));
+            pb[r >> 3][r & 7] = static_cast<__bf16>(pr);
+            db[r >> 3][r & 7] = static_cast<__bf16>(pr * (dp[r] - Dl[r3]));
+          }
+        }
+#pragma unroll
+        for (int c2 = 0; c2 < 2; ++c2)
+#pragma unroll
+          for (int dt = 0; dt < 4; ++dt) {
+            dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols(dOs, coff[dt], 2 * t + c2), pb[c2], dv[dt],
+                                                             0, 0, 0);
+            dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols(Qs, coff[dt], 2 * t + c2), db[c2], dk[dt],
+                                                             0, 0, 0);
+          }
+      }
+    }
+  }
+  store_row(p.dk + krow * kD, dk, p.scale, hf);
+  store_row(p.dv + krow * kD, dv, 1.f, hf);
+}
+
+}  // namespace
+}  // namespace bsa
+
+extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v, const void* out,
+                                     const float* lse, const void* dout, bsa_plan_t plan, void* dq,
+                                     void* dk, void* dv, float* delta, void* stream) {
+  using namespace bsa;
+  clear_error();
+  if (!plan) return fail(BSA_ERR_INVALID_ARGUMENT, "plan must not be NULL");
+  if (!plan->info.on_device)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "plan was built by bsa_plan_host and has no device copy");
+  if (plan->dynamic)
+    return fail(BSA_ERR_UNSUPPORTED, "the backward needs a static plan (bsa_plan): dynamic plans have no transposed CSR");
+  const bsa_problem_t& pr = plan->prob;
+  if (!(pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128))
+    return fail(BSA_ERR_UNSUPPORTED, "backward kernels exist for bf16, head_dim 128, block 128 only");
+  if (plan->info.work_items == 0) return BSA_OK;
+  if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !delta)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v, out, lse, dout, dq, dk, dv and delta must all be non-NULL");
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(BSA_ERR_DEVICE, "hipGetDevice failed");
+  if (dev != plan->device)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "plan was built on device %d but device %d is current",
+                plan->device, dev);
+  BwdParams prm;
+  prm.q = static_cast<const uint16_t*>(q);
+  prm.k = static_cast<const uint16_t*>(k);
+  prm.v = static_cast<const uint16_t*>(v);
+  prm.o = static_cast<const uint16_t*>(out);
+  prm.lse = lse;
+  prm.dout = static_cast<const uint16_t*>(dout);
+  prm.dq = static_cast<uint16_t*>(dq);
+  prm.dk = static_cast<uint16_t*>(dk);
+  prm.dv = static_cast<uint16_t*>(dv);
+  prm.delta = delta;
+  prm.rows = plan->d_rows;
+  prm.entries = plan->d_entries;
+  prm.work = plan->d_work;
+  prm.cols = plan->d_cols;
+  prm.entries_t = plan->d_entries_t;
+  prm.work_kv = plan->d_work_kv;
+  prm.N = pr.seq_len;
+  prm.H = pr.num_heads;
+  prm.Hkv = pr.num_kv_heads;
+  prm.group = pr.num_heads / pr.num_kv_heads;
+  prm.nb = plan->nb;
+  prm.per_head_layout = plan->layout_heads > 1 ? 1 : 0;
+  prm.scale = pr.scale;
+  prm.sl2 = pr.scale * kLog2e;
+  prm.causal = plan->causal;
+  prm.token_rule = plan->token_rule;
+  auto clamp32 = [&](int64_t x) { return int32_t(x < 0 ? -1 : (x > pr.seq_len ? pr.seq_len : x)); };
+  prm.gk32 = clamp32(plan->gk);
+  prm.gq32 = clamp32(plan->gq);
+  {
+    // Range of q - k allowed by the window and the causal cut (|q - k| < N).
+    const int64_t big = pr.seq_len + 1;
+    int64_t lo = -big, hi = big;
+    if (plan->token_rule) {
+      if (plan->wr >= 0) lo = -plan->wr;
+      if (plan->wl >= 0) hi = plan->wl;
+    }
+    if (plan->causal) lo = lo > 0 ? lo : 0;
+    if (lo < -big) lo = -big;
+    if (hi > big) hi = big;
+    prm.mlo = int32_t(lo);
+    prm.mspan = uint32_t(hi - lo);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t rows = int64_t(pr.batch) * pr.num_heads * pr.seq_len;
+  const int64_t rows_per_block = kThreads / 16;
+  hipLaunchKernelGGL(bwd_delta_bf16, dim3(unsigned((rows + rows_per_block - 1) / rows_per_block)), dim3(kThreads),
+                     0, s, prm.o, prm.dout, prm.delta, rows);
+  hipError_t err = hipGetLastError();
+  if (err == hipSuccess) {
+    hipLaunchKernelGGL(bwd_dq_bf16_d128, dim3(unsigned(plan->info.launch_slots)), dim3(kThreads), 0, s, prm);
+    err = hipGetLastError();
+  }
+  if (err == hipSuccess && !plan->work_kv.empty()) {
+    hipLaunchKernelGGL(bwd_dkdv_bf16_d128, dim3(unsigned(plan->work_kv.size())), dim3(kThreads), 0, s, prm);
+    err = hipGetLastError();
+  }
+  if (err != hipSuccess) return fail(BSA_ERR_DEVICE, "backward kernel launch failed: %s", hipGetErrorString(err));
+  return BSA_OK;
+}

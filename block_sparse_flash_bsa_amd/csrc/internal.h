@@ -42,12 +42,22 @@ struct bsa_plan {
   std::vector<std::vector<uint8_t>> flags;     // [layout_heads][nnz_h]
   std::vector<int32_t> work;                   // [launch slots], -1 = idle
   bsa_plan_info_t info{};
+  // Backward: the CSR transposed (per k-block, the ascending q-blocks whose
+  // lists hold it, same flags) and the launch order of the dK/dV kernel,
+  // items (b * Hkv + hk) * nb + j.  Static plans only.
+  std::vector<std::vector<int32_t>> colT_ptr;  // [layout_heads][nb + 1]
+  std::vector<std::vector<int32_t>> rowT_idx;  // [layout_heads][nnz_h]
+  std::vector<std::vector<uint8_t>> flagsT;    // [layout_heads][nnz_h]
+  std::vector<int32_t> work_kv;                // [launch slots], -1 = idle
   // Device copy (bsa_plan and bsa_plan_dynamic).
   int device = -1;
   void* dev_mem = nullptr;
   const bsa::RowDesc* d_rows = nullptr;        // [layout_heads * nb]
   const int32_t* d_entries = nullptr;          // [nnz], or [entry_capacity] for a dynamic plan
   const int32_t* d_work = nullptr;             // [launch slots]
+  const bsa::RowDesc* d_cols = nullptr;        // [layout_heads * nb] transposed rows
+  const int32_t* d_entries_t = nullptr;        // [nnz] (q block << 1) | partial
+  const int32_t* d_work_kv = nullptr;          // [dK/dV launch slots]
   // Dynamic plans: the CSR is written on the device by bsa_plan_set_bitmap;
   // d_counts is its per-row scratch [layout_heads * nb].
   int32_t dynamic = 0;

@@ -209,6 +209,74 @@ void build_csr(Plan& P, const bsa_layout_t& L) {
   P.info.max_row_entries = int32_t(row_max);
 }
 
+// Cut a locality-ordered item list into one contiguous run per XCD with equal
+// total cost; slot s = kNumXcd * r + x runs the r-th item of XCD x's run
+// (idle slots hold -1).
+template <class Cost>
+std::vector<int32_t> xcd_slots(const std::vector<int32_t>& loc, Cost cost) {
+  int64_t total = 0;
+  for (int32_t it : loc) total += cost(it);
+  std::vector<std::vector<int32_t>> seg(kNumXcd);
+  int64_t acc = 0;
+  for (int32_t it : loc) {
+    const int64_t x = std::min<int64_t>(kNumXcd - 1, (acc * kNumXcd) / std::max<int64_t>(total, 1));
+    seg[x].push_back(it);
+    acc += cost(it);
+  }
+  size_t longest = 0;
+  for (auto& sg : seg) longest = std::max(longest, sg.size());
+  std::vector<int32_t> slots(longest * kNumXcd, -1);
+  for (int x = 0; x < kNumXcd; ++x)
+    for (size_t r = 0; r < seg[x].size(); ++r) slots[r * kNumXcd + x] = seg[x][r];
+  return slots;
+}
+
+// The CSR transposed: for each layout head and k-block j, the ascending
+// q-blocks i whose lists hold j, with the entry's flag.  The dK/dV part of
+// the backward walks these lists.
+void build_transpose(Plan& P) {
+  const int64_t nb = P.nb;
+  P.colT_ptr.assign(P.layout_heads, std::vector<int32_t>(nb + 1, 0));
+  P.rowT_idx.assign(P.layout_heads, {});
+  P.flagsT.assign(P.layout_heads, {});
+  for (int lh = 0; lh < P.layout_heads; ++lh) {
+    const auto& rp = P.row_ptr[lh];
+    const auto& ci = P.col_idx[lh];
+    auto& cp = P.colT_ptr[lh];
+    for (int32_t j : ci) ++cp[j + 1];
+    for (int64_t j = 0; j < nb; ++j) cp[j + 1] += cp[j];
+    std::vector<int32_t> fill(cp.begin(), cp.end() - 1);
+    P.rowT_idx[lh].resize(ci.size());
+    P.flagsT[lh].resize(ci.size());
+    for (int64_t i = 0; i < nb; ++i)          // ascending i keeps every column list sorted
+      for (int32_t e = rp[i]; e < rp[i + 1]; ++e) {
+        const int32_t at = fill[ci[e]]++;
+        P.rowT_idx[lh][at] = int32_t(i);
+        P.flagsT[lh][at] = P.flags[lh][e];
+      }
+  }
+}
+
+// Launch order of the dK/dV kernel: items (b * Hkv + hk) * nb + j in
+// locality order (neighbouring k-blocks of one KV head share the q-blocks
+// they read), cut per XCD by cost = the group's column lengths + 1.
+void build_work_kv(Plan& P) {
+  const int64_t B = P.prob.batch, H = P.prob.num_heads, Hkv = P.prob.num_kv_heads, nb = P.nb;
+  const int64_t group = H / Hkv;
+  std::vector<int32_t> loc(size_t(B * Hkv * nb));
+  std::iota(loc.begin(), loc.end(), 0);
+  auto cost = [&](int64_t item) -> int64_t {
+    const int64_t j = item % nb, hk = (item / nb) % Hkv;
+    int64_t c = 1;
+    for (int64_t h = hk * group; h < (hk + 1) * group; ++h) {
+      const auto& cp = P.colT_ptr[P.layout_heads == 1 ? 0 : h];
+      c += cp[j + 1] - cp[j];
+    }
+    return c;
+  };
+  P.work_kv = loc.empty() ? loc : xcd_slots(loc, cost);
+}
+
 // Launch order.  Item id = (b * H + h) * nb + i; cost = row length + 1.
 void build_work(Plan& P) {
   const int64_t B = P.prob.batch, H = P.prob.num_heads, nb = P.nb;
@@ -241,22 +309,7 @@ void build_work(Plan& P) {
       for (int64_t hk = 0; hk < H / group; ++hk)
         for (int64_t i = 0; i < nb; ++i)
           for (int64_t g = 0; g < group; ++g) loc.push_back(int32_t((b * H + hk * group + g) * nb + i));
-    // Cut it into one contiguous run per XCD with equal total cost.
-    int64_t total = 0;
-    for (int32_t it : loc) total += cost(it);
-    std::vector<std::vector<int32_t>> seg(kNumXcd);
-    int64_t acc = 0;
-    for (int32_t it : loc) {
-      const int64_t x = std::min<int64_t>(kNumXcd - 1, (acc * kNumXcd) / std::max<int64_t>(total, 1));
-      seg[x].push_back(it);
-      acc += cost(it);
-    }
-    size_t longest = 0;
-    for (auto& s : seg) longest = std::max(longest, s.size());
-    // Slot s = kNumXcd * r + x runs the r-th item of XCD x's run.
-    P.work.assign(longest * kNumXcd, -1);
-    for (int x = 0; x < kNumXcd; ++x)
-      for (size_t r = 0; r < seg[x].size(); ++r) P.work[r * kNumXcd + x] = seg[x][r];
+    P.work = xcd_slots(loc, cost);
   }
   P.info.work_items = items;
   P.info.launch_slots = int64_t(P.work.size());
@@ -268,9 +321,15 @@ bsa_status_t upload(Plan& P) {
   const size_t rows = size_t(P.layout_heads) * P.nb;
   const size_t nnz = size_t(P.info.nnz);
   const size_t slots = P.work.size();
+  const size_t slots_kv = P.work_kv.size();
+  auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
+  // [rows | entries | work | transposed rows | transposed entries | dK/dV work]
   const size_t off_entries = rows * sizeof(bsa::RowDesc);
-  const size_t off_work = (off_entries + nnz * sizeof(int32_t) + 255) & ~size_t(255);
-  const size_t bytes = off_work + slots * sizeof(int32_t) + 16;
+  const size_t off_work = up(off_entries + nnz * sizeof(int32_t));
+  const size_t off_cols = up(off_work + slots * sizeof(int32_t));
+  const size_t off_entries_t = up(off_cols + rows * sizeof(bsa::RowDesc));
+  const size_t off_work_kv = up(off_entries_t + nnz * sizeof(int32_t));
+  const size_t bytes = off_work_kv + slots_kv * sizeof(int32_t) + 16;
   std::vector<unsigned char> host(bytes, 0);
   auto* rd = reinterpret_cast<bsa::RowDesc*>(host.data());
   auto* en = reinterpret_cast<int32_t*>(host.data() + off_entries);
@@ -285,6 +344,19 @@ bsa_status_t upload(Plan& P) {
     start += int32_t(P.col_idx[lh].size());
   }
   if (slots) std::memcpy(host.data() + off_work, P.work.data(), slots * sizeof(int32_t));
+  auto* cd = reinterpret_cast<bsa::RowDesc*>(host.data() + off_cols);
+  auto* et = reinterpret_cast<int32_t*>(host.data() + off_entries_t);
+  start = 0;
+  for (int lh = 0; lh < P.layout_heads; ++lh) {
+    for (int64_t j = 0; j < P.nb; ++j) {
+      const int32_t a = P.colT_ptr[lh][j], b = P.colT_ptr[lh][j + 1];
+      cd[size_t(lh) * P.nb + j] = {start + a, b - a};
+    }
+    for (size_t e = 0; e < P.rowT_idx[lh].size(); ++e)
+      et[start + e] = bsa::encode_entry(P.rowT_idx[lh][e], P.flagsT[lh][e] != 0);
+    start += int32_t(P.rowT_idx[lh].size());
+  }
+  if (slots_kv) std::memcpy(host.data() + off_work_kv, P.work_kv.data(), slots_kv * sizeof(int32_t));
   hipError_t err = hipMalloc(&P.dev_mem, bytes);
   if (err != hipSuccess) {
     P.dev_mem = nullptr;
@@ -301,6 +373,9 @@ bsa_status_t upload(Plan& P) {
   P.d_rows = reinterpret_cast<const bsa::RowDesc*>(base);
   P.d_entries = reinterpret_cast<const int32_t*>(base + off_entries);
   P.d_work = reinterpret_cast<const int32_t*>(base + off_work);
+  P.d_cols = reinterpret_cast<const bsa::RowDesc*>(base + off_cols);
+  P.d_entries_t = reinterpret_cast<const int32_t*>(base + off_entries_t);
+  P.d_work_kv = reinterpret_cast<const int32_t*>(base + off_work_kv);
   P.info.on_device = 1;
   return BSA_OK;
 }
@@ -328,6 +403,8 @@ bsa_status_t make_plan(const bsa_problem_t* problem, const bsa_layout_t* layout,
     }
     build_csr(*P, *layout);
     build_work(*P);
+    build_transpose(*P);
+    build_work_kv(*P);
   } catch (const std::bad_alloc&) {
     delete P;
     return fail(BSA_ERR_OUT_OF_MEMORY, "host allocation while building the plan failed");
@@ -487,6 +564,33 @@ bsa_status_t bsa_plan_work(bsa_plan_t plan, const int32_t** work, int64_t* slots
 }
 
 int64_t bsa_plan_active_blocks(bsa_plan_t plan) { return plan ? plan->info.active_blocks : -1; }
+
+bsa_status_t bsa_plan_csr_transposed(bsa_plan_t plan, int32_t layout_head, const int32_t** col_ptr,
+                                     const int32_t** row_idx, const uint8_t** flags, int64_t* nnz) {
+  bsa::clear_error();
+  if (!plan || !col_ptr || !row_idx || !flags || !nnz)
+    return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "NULL argument to bsa_plan_csr_transposed");
+  if (plan->dynamic)
+    return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "dynamic plan: it has no transposed CSR");
+  if (layout_head < 0 || layout_head >= plan->layout_heads)
+    return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "layout_head %d out of range [0, %d)", layout_head,
+                     plan->layout_heads);
+  *col_ptr = plan->colT_ptr[layout_head].data();
+  *row_idx = plan->rowT_idx[layout_head].data();
+  *flags = plan->flagsT[layout_head].data();
+  *nnz = int64_t(plan->rowT_idx[layout_head].size());
+  return BSA_OK;
+}
+
+bsa_status_t bsa_plan_work_kv(bsa_plan_t plan, const int32_t** work, int64_t* slots) {
+  bsa::clear_error();
+  if (!plan || !work || !slots)
+    return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "NULL argument to bsa_plan_work_kv");
+  if (plan->dynamic) return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "dynamic plan: it has no dK/dV launch order");
+  *work = plan->work_kv.data();
+  *slots = int64_t(plan->work_kv.size());
+  return BSA_OK;
+}
 
 const char* bsa_status_string(bsa_status_t s) {
   switch (s) {

@@ -2,7 +2,7 @@
  * libbsattn -- block-sparse flash attention forward for AMD Instinct MI355X
  * (gfx950 / CDNA4).  C ABI: plain structs, plain pointers, status codes.
  *
- * The operation (forward only):
+ * The operation (forward; the backward is declared with bsa_backward):
  *   For every batch b, query head h and query q, with hk = h / (H / Hkv):
  *     A(q)  = { k : allowed(h, q, k) }                 (the sparse layout)
  *     s_k   = scale * dot(Q[b,h,q,:], K[b,hk,k,:])      k in A(q)
@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 2
+#define BSA_ABI_VERSION 3
 
 /* Status codes.  Every entry point that can fail returns one; no exception
  * crosses the ABI.  Out-parameters are written only on BSA_OK. */
@@ -258,6 +258,61 @@ bsa_status_t bsa_plan_read_csr(bsa_plan_t plan, int32_t layout_head, int32_t* ro
  * synchronisation.  A problem with no work items returns BSA_OK at once. */
 bsa_status_t bsa_forward(const void* q, const void* k, const void* v, bsa_plan_t plan,
                          void* out, float* lse, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Backward pass: the gradients of a scalar loss through the forward above,
+ * given its upstream gradient dO = dLoss/dO.  With p_qk = exp(s_qk - LSE_q)
+ * over k in A(q) (zero elsewhere) and Delta_q = <dO_q, O_q>:
+ *   dV_k = sum_q p_qk dO_q
+ *   ds_qk = p_qk * (<dO_q, V_k> - Delta_q)          (softmax Jacobian)
+ *   dQ_q = scale * sum_k ds_qk K_k,   dK_k = scale * sum_q ds_qk Q_q
+ * where keys sum over every query head of their GQA group.  The pages treat
+ * the backward through its cost (training throughput of block-sparse vs
+ * dense attention in "Sparse Attention Kernels vs Full Attention
+ * Performance"; forward and backward timings in the FAQ of "How Do Sparse
+ * Attention Kernels Work in GPU Clusters?"); it reuses the forward's LSE, so
+ * no score matrix is stored here either.  The q-block walk for dQ is the
+ * forward's CSR; the k-block walk for dK and dV is the CSR transposed, which
+ * bsa_plan builds with the plan.
+ * ------------------------------------------------------------------------- */
+
+/* The transposed CSR of one layout head: col_ptr [nb + 1] (head-local
+ * offsets), row_idx [nnz] = the ascending q-blocks whose lists hold k-block
+ * j, flags [nnz] as in bsa_plan_csr.  Plan-owned, valid until
+ * bsa_plan_destroy.  Errors: INVALID_ARGUMENT for NULL pointers, a dynamic
+ * plan, or a layout_head out of range. */
+bsa_status_t bsa_plan_csr_transposed(bsa_plan_t plan, int32_t layout_head, const int32_t** col_ptr,
+                                     const int32_t** row_idx, const uint8_t** flags, int64_t* nnz);
+
+/* Launch order of the dK/dV kernel: slot s runs item work[s] =
+ * (b * num_kv_heads + hk) * nb + j, or -1 for an idle slot.  Plan-owned.
+ * Errors: INVALID_ARGUMENT for NULL pointers or a dynamic plan. */
+bsa_status_t bsa_plan_work_kv(bsa_plan_t plan, const int32_t** work, int64_t* slots);
+
+/* Run the backward pass asynchronously on `stream` (a hipStream_t; NULL =
+ * the default stream) of the plan's device.
+ *   q, k, v : the forward's inputs (layouts as in bsa_forward)
+ *   out, lse: the forward's outputs for exactly these inputs and this plan
+ *   dout    : device, [batch][num_heads][seq_len][head_dim], dtype: dLoss/dO
+ *   dq      : device, like q;   dk, dv: device, like k and v (dtype, bf16
+ *             rounded to nearest even from float32 accumulators)
+ *   delta   : device, float32 [batch][num_heads][seq_len]: caller-owned
+ *             workspace; receives Delta_q = <dO_q, O_q> (computed from the
+ *             rounded out), which the dK/dV kernel reads
+ * Three kernels run in order on the stream: Delta, dQ (one workgroup per
+ * q-block, walking its CSR row) and dK/dV (one workgroup per KV head and
+ * k-block, walking its transposed list over the group's query heads).  Every
+ * element of dq, dk, dv and delta is written (zero rows where nothing
+ * attends).  Outputs must not alias inputs or each other.  Nothing is
+ * allocated or freed.
+ * Supported: static plans (bsa_plan) with dtype BSA_BF16, head_dim 128,
+ * block 128; otherwise UNSUPPORTED (dynamic plans, float32).
+ * Errors (before anything is launched): INVALID_ARGUMENT for NULL pointers, a
+ * host-only plan or a plan made on another device; UNSUPPORTED as above;
+ * DEVICE if a launch fails.  A problem with no work items returns BSA_OK. */
+bsa_status_t bsa_backward(const void* q, const void* k, const void* v, const void* out,
+                          const float* lse, const void* dout, bsa_plan_t plan, void* dq, void* dk,
+                          void* dv, float* delta, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* bsa_status_string(bsa_status_t status);

@@ -292,3 +292,57 @@ def test_dynamic_plan_argument_errors():
     assert L.bsa_plan_read_csr(hp.handle, 0, rp.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), None, None,
                                0, ctypes.byref(n)) == bsattn.ERR_INVALID_ARGUMENT
     assert L.bsa_plan_set_bitmap(None, bm.ctypes.data, None, None) == bsattn.ERR_INVALID_ARGUMENT
+
+
+# ------------------------------------------------ transposed CSR (backward)
+def transpose_of(ref, nb):
+    """Per k-block lists of (q-block, flag) from the oracle's per-q-block lists."""
+    cols = [[] for _ in range(nb)]
+    for i in range(nb):
+        for e in range(ref["row_ptr"][i], ref["row_ptr"][i + 1]):
+            cols[ref["col_idx"][e]].append((i, ref["flags"][e]))
+    col_ptr = np.cumsum([0] + [len(c) for c in cols]).astype(np.int32)
+    row_idx = np.array([i for c in cols for i, _ in c], np.int32)
+    flags = np.array([f for c in cols for _, f in c], np.uint8)
+    return col_ptr, row_idx, flags
+
+
+@pytest.mark.parametrize("name", ["tiny_f32", "window16k", "winglobal128k", "random32k", "gqa256k"])
+def test_transposed_csr_matches_oracle_plan(name):
+    w = wl.WORKLOADS[name]
+    lay = wl.layout_of(w)
+    p = host_plan(w, lay)
+    ref = oracle.plan(lay, w.seq_len, w.block)
+    for lh, r in enumerate(ref):
+        got = p.csr_transposed(lh)
+        cp, ri, fl = transpose_of(r, w.num_blocks)
+        np.testing.assert_array_equal(got["col_ptr"], cp)
+        np.testing.assert_array_equal(got["row_idx"], ri)
+        np.testing.assert_array_equal(got["flags"], fl)
+
+
+@pytest.mark.parametrize("name", ["winglobal128k", "random32k", "gqa256k"])
+def test_kv_work_order_is_a_permutation(name):
+    w = wl.WORKLOADS[name]
+    p = host_plan(w)
+    work = p.work_kv()
+    items = work[work >= 0]
+    np.testing.assert_array_equal(np.sort(items), np.arange(w.batch * w.kv_heads * w.num_blocks))
+    # slot s runs on XCD s % 8: each XCD's items form one contiguous run of the item order
+    for x in range(8):
+        run = work[x::8]
+        run = run[run >= 0]
+        assert np.all(np.diff(run) == 1)
+
+
+def test_transposed_csr_errors():
+    p = bsattn.plan(1, 2, 2, 256, 128, 128, torch.bfloat16, spec(False, "tokens"), host_only=True)
+    with pytest.raises(bsattn.BsaError):
+        p.csr_transposed(2)
+
+
+def test_backward_rejects_host_only_plan():
+    p = bsattn.plan(1, 1, 1, 128, 128, 128, torch.bfloat16, spec(False, "tokens"), host_only=True)
+    st = bsattn.lib().bsa_backward(1, 1, 1, 1, 1, 1, p.handle, 1, 1, 1, 1, None)
+    assert st == bsattn.ERR_INVALID_ARGUMENT
+    assert b"bsa_plan_host" in bsattn.lib().bsa_last_error()

@@ -1,0 +1,230 @@
+"""GPU parity of bsa_backward against the CPU oracle, through the C ABI.
+
+* every element of dQ, dK and dV for each workload's rule at a size the
+  oracle finishes in seconds (several tiles, partial tiles, GQA groups,
+  per-head bitmaps, rows with no allowed key);
+* full-size workloads in the benchmark's launch configuration: sampled dQ
+  rows and sampled dK/dV keys against the oracle's per-row / per-key forms;
+* determinism, and UNSUPPORTED for plans without a backward kernel.
+
+Tolerance, for each of dQ, dK, dV: max abs error <= 1e-2 * max |reference|.
+Derivation: the kernels round P and dS to bf16 before their products
+(relative 2^-9 per term, independent between terms, so a sum's error stays
+below 2^-9 of the sum of |terms|, which for these workloads is within a
+small factor of the largest gradient), Delta uses the bf16 output O
+(relative 2^-9), and the result is rounded to bf16 once more (2^-9 of the
+value); 1e-2 is about five times their sum.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_flash_bsa_amd import bsattn
+from block_sparse_flash_bsa_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+RTOL_OF_MAX = 1e-2
+
+SMALL = {
+    "window16k": wl.small_variant(wl.WORKLOADS["window16k"], 2048, heads=2, kv_heads=2),
+    "winglobal128k": wl.small_variant(wl.WORKLOADS["winglobal128k"], 2048, heads=2, kv_heads=2),
+    "random32k": wl.small_variant(wl.WORKLOADS["random32k"], 2048, heads=2, kv_heads=2, batch=2),
+    "gqa256k": wl.small_variant(wl.WORKLOADS["gqa256k"], 5120, heads=4, kv_heads=1),
+    "dense256k": wl.small_variant(wl.WORKLOADS["dense256k"], 1024, heads=4, kv_heads=2),
+}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    bsattn.lib()      # raises if the library is missing: no fallback
+    torch.cuda.set_device(0)
+
+
+def gpu_plan(w, layout, **kw):
+    return bsattn.plan(w.batch, w.heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.dtype,
+                       layout, **kw)
+
+
+def fwd_bwd(p, q, k, v, do):
+    out, lse = bsattn.forward(q, k, v, p)
+    dq, dk, dv = bsattn.backward(q, k, v, out, lse, do, p)
+    torch.cuda.synchronize()
+    return dq, dk, dv
+
+
+def check(name, got, ref):
+    got = np.asarray(got, dtype=np.float64)
+    assert not np.isnan(got).any(), f"{name}: NaN"
+    scale = float(np.abs(ref).max()) if ref.size else 0.0
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    say(f"  {name}: max|err| = {err:.3e}, max|ref| = {scale:.3e}, ratio {err / max(scale, 1e-30):.2e}")
+    assert err <= RTOL_OF_MAX * scale, f"{name}: error {err} > {RTOL_OF_MAX} * {scale}"
+
+
+# ----------------------------------------------------- every element, small sizes
+@pytest.mark.parametrize("name", list(SMALL))
+def test_backward_all_elements_small(name):
+    w = SMALL[name]
+    say(f"[bwd-small] {w.name} B={w.batch} H={w.heads}/{w.kv_heads} N={w.seq_len}")
+    lay = wl.layout_of(w)
+    q, k, v = wl.make_qkv(w, "cpu")
+    do = wl.make_dout(w, "cpu")
+    p = gpu_plan(w, lay)
+    dq, dk, dv = fwd_bwd(p, q.cuda(), k.cuda(), v.cuda(), do.cuda())
+    rq, rk, rv = oracle.backward(q, k, v, do, lay, w.block)
+    check("dQ", dq.float().cpu().numpy(), rq)
+    check("dK", dk.float().cpu().numpy(), rk)
+    check("dV", dv.float().cpu().numpy(), rv)
+
+
+def test_backward_per_head_bitmap_with_empty_rows():
+    """Per-head causal bitmaps; q-block 3 of head 0 has no active block at all,
+    and under causality the first rows of blocks whose only block is above
+    the diagonal have no allowed key either."""
+    w = wl.WORKLOADS["random32k"].with_shape(name="bitmap-empty", batch=1, heads=2, kv_heads=1,
+                                             seq_len=1024)
+    nb = w.num_blocks
+    rng = np.random.default_rng(5)
+    bm = rng.random((2, nb, nb)) < 0.3
+    bm[0, 3, :] = False
+    bm[1, 5, :] = False
+    bm[1, 5, 6] = True                     # above the diagonal: cut away entirely by causality
+    lay = dict(causal=True, unit="blocks", window_left=-1, window_right=-1, global_keys=0,
+               global_queries=0, bitmap=torch.from_numpy(bm))
+    q, k, v = wl.make_qkv(w, "cpu")
+    do = wl.make_dout(w, "cpu")
+    p = gpu_plan(w, lay)
+    dq, dk, dv = fwd_bwd(p, q.cuda(), k.cuda(), v.cuda(), do.cuda())
+    rq, rk, rv = oracle.backward(q, k, v, do, lay, w.block)
+    assert torch.all(dq[0, 0, 3 * 128:4 * 128] == 0)
+    check("dQ", dq.float().cpu().numpy(), rq)
+    check("dK", dk.float().cpu().numpy(), rk)
+    check("dV", dv.float().cpu().numpy(), rv)
+
+
+def test_backward_token_rule_both_sides_gqa():
+    """Token window on both sides plus global keys and global query rows, GQA 4:1."""
+    w = wl.WORKLOADS["gqa256k"].with_shape(name="two-sided", heads=4, kv_heads=1, seq_len=1536)
+    lay = dict(causal=False, unit="tokens", window_left=200, window_right=77, global_keys=5,
+               global_queries=3, bitmap=None)
+    q, k, v = wl.make_qkv(w, "cpu")
+    do = wl.make_dout(w, "cpu")
+    p = gpu_plan(w, lay)
+    dq, dk, dv = fwd_bwd(p, q.cuda(), k.cuda(), v.cuda(), do.cuda())
+    rq, rk, rv = oracle.backward(q, k, v, do, lay, w.block)
+    check("dQ", dq.float().cpu().numpy(), rq)
+    check("dK", dk.float().cpu().numpy(), rk)
+    check("dV", dv.float().cpu().numpy(), rv)
+
+
+# ---------------------------------------------------------- full size, sampled
+FULL_KEYS = {
+    # keys away from global blocks (a global key is read by every query of the
+    # sequence, which the per-key oracle would take minutes to sum)
+    "window16k": [(0, 0, 0), (0, 31, 8191), (0, 17, 16383), (0, 5, 700)],
+    "winglobal128k": [(0, 3, 65541), (0, 31, 131071), (0, 0, 131072 - 900)],
+    "random32k": [(1, 15, 32767), (0, 2, 20000), (1, 7, 128)],
+    "gqa256k": [(0, 7, 262143), (0, 0, 100000), (0, 3, 262144 - 1500)],
+}
+
+
+def sample_rows(w, n_random=32, seed=0):
+    rng = np.random.default_rng(seed)
+    N, H, B = w.seq_len, w.heads, w.batch
+    qs = [0, 1, 127, 128, 511, 512, 4095, 4096, 4104, N // 2, N - 129, N - 1]
+    rows = [(int(rng.integers(0, B)), int(rng.integers(0, H)), qq) for qq in qs if qq < N]
+    rows += [(int(rng.integers(0, B)), int(rng.integers(0, H)), int(rng.integers(0, N)))
+             for _ in range(n_random)]
+    return rows
+
+
+@pytest.mark.parametrize("name", list(FULL_KEYS))
+def test_backward_full_size_sampled(name):
+    w = wl.WORKLOADS[name]
+    say(f"[bwd-full] {w.name} B={w.batch} H={w.heads}/{w.kv_heads} N={w.seq_len}")
+    lay = wl.layout_of(w)
+    q, k, v = wl.make_qkv(w, "cuda")
+    do = wl.make_dout(w, "cuda")
+    p = gpu_plan(w, lay)
+    dq, dk, dv = fwd_bwd(p, q, k, v, do)
+    group = w.heads // w.kv_heads
+    rows = sample_rows(w)
+    keys = FULL_KEYS[name]
+    heads = sorted({(b, h) for b, h, _ in rows} | {(b, hk * group + g) for b, hk, _ in keys for g in range(group)})
+    kvh = sorted({(b, h // group) for b, h in heads})
+    # Host copies of only the heads the samples touch, indexed like the full
+    # tensors: Q and dO stay bf16 (read one row at a time), K and V are
+    # upcast once to float64 (gathered thousands of rows at a time).
+    parts = {"q": {bh: q[bh].cpu() for bh in heads}, "do": {bh: do[bh].cpu() for bh in heads},
+             "k": {bk: k[bk].double().cpu().numpy() for bk in kvh},
+             "v": {bk: v[bk].double().cpu().numpy() for bk in kvh}}
+
+    class View:
+        """Minimal [b, h] / [b, h, q] indexing over the host copies for the oracle."""
+        def __init__(self, part, shape):
+            self.part, self.shape = part, shape
+
+        def __getitem__(self, idx):
+            if len(idx) == 2:
+                return self.part[idx]
+            return self.part[idx[:2]][idx[2]]
+
+    qs_, ks_ = (w.batch, w.heads, w.seq_len, w.head_dim), (w.batch, w.kv_heads, w.seq_len, w.head_dim)
+    Qv, dOv = View(parts["q"], qs_), View(parts["do"], qs_)
+    Kv, Vv = View(parts["k"], ks_), View(parts["v"], ks_)
+    say(f"  host copies ready: {len(heads)} query heads, {len(kvh)} KV heads")
+    rq = oracle.backward_dq_rows(Qv, Kv, Vv, dOv, lay, w.block, rows)
+    idx = tuple(torch.tensor(x) for x in zip(*rows))
+    check("dQ rows", dq[idx].float().cpu().numpy(), rq)
+    say("  dQ rows checked; summing the sampled keys' columns")
+    rk, rv = oracle.backward_dkv_keys(Qv, Kv, Vv, dOv, lay, w.block, keys)
+    kidx = tuple(torch.tensor(x) for x in zip(*keys))
+    check("dK keys", dk[kidx].float().cpu().numpy(), rk)
+    check("dV keys", dv[kidx].float().cpu().numpy(), rv)
+
+
+# ------------------------------------------------------------------ behaviour
+def test_backward_deterministic_and_overwrites():
+    w = SMALL["gqa256k"]
+    lay = wl.layout_of(w)
+    q, k, v = (x.cuda() for x in wl.make_qkv(w, "cpu"))
+    do = wl.make_dout(w, "cuda")
+    p = gpu_plan(w, lay)
+    out, lse = bsattn.forward(q, k, v, p)
+    a = bsattn.backward(q, k, v, out, lse, do, p)
+    poisoned = [torch.full_like(x, float("nan")) for x in a]
+    delta = torch.full((w.batch, w.heads, w.seq_len), float("nan"), device="cuda")
+    b = bsattn.backward(q, k, v, out, lse, do, p, *poisoned, delta=delta)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    assert not torch.isnan(delta).any()
+
+
+def test_backward_unsupported_plans():
+    w = wl.WORKLOADS["tiny_f32"]
+    lay = wl.layout_of(w)
+    p = gpu_plan(w, lay)
+    q, k, v = (x.cuda() for x in wl.make_qkv(w, "cpu"))
+    out, lse = bsattn.forward(q, k, v, p)
+    with pytest.raises(bsattn.BsaError) as ei:
+        bsattn.backward(q, k, v, out, lse, torch.zeros_like(q), p)
+    assert ei.value.status == bsattn.ERR_UNSUPPORTED
+    wd = SMALL["random32k"]
+    pd = bsattn.plan_dynamic(wd.batch, wd.heads, wd.kv_heads, wd.seq_len, wd.head_dim, wd.block, wd.dtype,
+                             causal=False, bitmap_heads=wd.heads)
+    q, k, v = (x.cuda() for x in wl.make_qkv(wd, "cpu"))
+    out, lse = bsattn.forward(q, k, v, pd)
+    with pytest.raises(bsattn.BsaError) as ei:
+        bsattn.backward(q, k, v, out, lse, torch.zeros_like(q), pd)
+    assert ei.value.status == bsattn.ERR_UNSUPPORTED
