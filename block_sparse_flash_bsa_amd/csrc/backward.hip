@@ -30,8 +30,10 @@
 // registers 8c .. 8c+7 of tile t are exactly the 8 contraction elements that
 // lane supplies for 16-element chunk 2t + c of the next product's B operand;
 // the matching A operand comes from LDS through ds_read_b64_tr_b16.
-// Tiles are staged through LDS by plain 16-byte loads and stores, one tile
-// pair per step between two barriers.
+// Tiles are staged through LDS by plain 16-byte loads and stores between two
+// barriers: K and V of one key block per step in the dQ kernel; in the dK/dV
+// kernel the block's V rows once, then Q and dO in 64-query steps, so that
+// it fits two workgroups per CU.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -98,19 +100,36 @@ __device__ __forceinline__ bool pair_ok(const BwdParams& p, int q, int k) {
 // both stay inside one chunk, so either kind sees the logical layout.
 __device__ __forceinline__ uint32_t tile_off(int r, int c) { return r * 256 + 16 * (c ^ (4 * (r & 3))); }
 
-// Copy one contiguous 128 x 128 bf16 tile (256-byte rows) from global memory
-// into LDS: 8 coalesced 16-byte loads per thread, then the swizzled stores.
-__device__ __forceinline__ void stage_tile(lds_u8* dst, const unsigned char* __restrict__ src, int tid) {
-  u32x4 r[8];
+// LDS layout of K/V rows that are only read row-wise (B operands): chunk c of
+// row r at c ^ (r & 15), which keeps 16-byte reads of 32 rows x 2 chunks free
+// of bank conflicts.
+__device__ __forceinline__ uint32_t rows_off(int r, int c) { return r * 256 + 16 * (c ^ (r & 15)); }
+
+// Copy kRows contiguous rows of 128 bf16 (256 bytes) from global memory into
+// LDS with either layout: coalesced 16-byte loads, kRows / 16 per thread,
+// issued in groups of at most four before their stores.  Thread t moves
+// chunk t % 16 of rows t / 16 + 16 u, so its global and LDS offsets are one
+// base plus u * 4096 (the swizzles depend on the row only through r & 15).
+// The thread index passes through an empty asm so its address arithmetic
+// is redone per call instead of being hoisted out of the caller's loops and
+// held in registers.
+template <int kRows, bool kRowsOnly>
+__device__ __forceinline__ void stage(lds_u8* dst, const unsigned char* __restrict__ src, int tid) {
+  constexpr int kPer = kRows / 16;
+  constexpr int kGroup = kPer < 4 ? kPer : 4;
+  int t = tid;
+  __asm__ volatile("" : "+v"(t));
+  const int r = t >> 4, c = t & 15;
+  const u32x4* g = reinterpret_cast<const u32x4*>(src + t * 16);
+  lds_u8* const l = dst + (kRowsOnly ? rows_off(r, c) : tile_off(r, c));
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int ci = tid + kThreads * u;
-    r[u] = *reinterpret_cast<const u32x4*>(src + (ci >> 4) * 256 + (ci & 15) * 16);
-  }
+  for (int part = 0; part < kPer / kGroup; ++part) {
+    u32x4 v[kGroup];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int ci = tid + kThreads * u;
-    *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(dst + tile_off(ci >> 4, ci & 15)) = r[u];
+    for (int u = 0; u < kGroup; ++u) v[u] = g[(part * kGroup + u) * 256];
+#pragma unroll
+    for (int u = 0; u < kGroup; ++u)
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(l + (part * kGroup + u) * 4096) = v[u];
   }
 }
 
@@ -233,8 +252,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
     const int j = ent >> 1;
     const bool partial = ent & 1;
     __syncthreads();                                   // every wave is done with the last tile
-    stage_tile(Ks, Kg + int64_t(j) * kTileBytes, tid);
-    stage_tile(Vs, Vg + int64_t(j) * kTileBytes, tid);
+    stage<kB, false>(Ks, Kg + int64_t(j) * kTileBytes, tid);
+    stage<kB, true>(Vs, Vg + int64_t(j) * kTileBytes, tid);
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < 4; ++t) {                      // keys 32t .. 32t+31 of the tile
@@ -242,7 +261,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
 #pragma unroll
       for (int cc = 0; cc < 8; ++cc) {
         s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(Ks, aoff[cc] + t * 32 * 256), qf[cc], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(Vs, aoff[cc] + t * 32 * 256), df[cc], dp, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(Vs, rows_off(32 * t + r32, 2 * cc + hf)), df[cc], dp,
+                                                     0, 0, 0);
       }
       // Register r holds key 32t + 8 (r / 4) + 4 hf + r % 4 of query qg.
       bf16x8 ds[2];
@@ -270,15 +290,52 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dK, dV: one workgroup per (b, KV head, k-block); wave w owns keys
 // 32w .. +31 and walks, for every query head of the group, the q-blocks of
-// the transposed CSR.
+// the transposed CSR in steps of 32 queries.  K^T stays in registers as a B
+// operand; the block's V rows sit in LDS for the whole walk and give the B
+// operand of dP by row reads.  Q and dO rows of a step (8 KB each) are
+// double-buffered and filled by direct HBM->LDS loads issued a step ahead,
+// interleaved with the S/dP MFMAs; one barrier per step.  The step's LSE and
+// Delta are loaded a step ahead too (lane l < 32: LSE of query l, else Delta
+// of query l - 32) and parked in a wave-private LDS row.  64 KB + 1 KB of LDS
+// and at most 256 registers: two workgroups share a CU.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_d128(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char Qsh[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char dOsh[kTileBytes];
-  __shared__ __attribute__((aligned(16))) float lse_s[kB];
-  __shared__ __attribute__((aligned(16))) float dlt_s[kB];
-  lds_u8* const Qs = (lds_u8*)Qsh;
-  lds_u8* const dOs = (lds_u8*)dOsh;
+constexpr int kStepRows = 32;
+constexpr int kStepBytes = kStepRows * kD * 2;   // 8 KB
+
+// Wait until at most N of this wave's vector-memory operations are pending,
+// then a workgroup barrier.  The "memory" clobber keeps LDS accesses on their
+// side of the barrier.
+#define BSA_WAIT_BARRIER(N) \
+  __asm__ volatile("s_waitcnt vmcnt(" #N ")\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory")
+
+// HBM->LDS load of 16 bytes per lane (1 KB per wave) from sbase + voff into
+// LDS at lds_addr + 16 * lane, in inline assembly so that the compiler adds
+// no waits of its own for it; each use is followed by BSA_WAIT_BARRIER before
+// the data is read.  M0 is reserved for the compiler, which therefore does
+// not honour it as a clobber; the compiled kernel has no other use of M0
+// (checked on its assembly by a CPU test).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  __asm__ volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                   :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char Vsh[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char Q0[kStepBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char Q1[kStepBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char dO0[kStepBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char dO1[kStepBytes];
+  __shared__ __attribute__((aligned(16))) float priv[4 * 64];
+  lds_u8* const Vs = (lds_u8*)Vsh;
+  lds_u8* const Qb[2] = {(lds_u8*)Q0, (lds_u8*)Q1};
+  lds_u8* const dOb[2] = {(lds_u8*)dO0, (lds_u8*)dO1};
+  const uint32_t Qa[2] = {uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)Q0)),
+                          uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)Q1))};
+  const uint32_t dOa[2] = {uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)dO0)),
+                           uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)dO1))};
 
   const int item = p.work_kv[blockIdx.x];
   if (item < 0) return;
@@ -290,20 +347,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_d128(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r32 = lane & 31, hf = lane >> 5;
   const int kg = j * kB + wave * 32 + r32;
-  const int64_t krow = (int64_t(b) * p.Hkv + hk) * p.N + kg;
-
-  // K^T and V^T as B operands: lane (key r32, half hf) holds d = 16c + 8hf .. +7.
-  bf16x8 kf[8], vf[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    kf[c] = *reinterpret_cast<const bf16x8*>(p.k + krow * kD + c * 16 + hf * 8);
-    vf[c] = *reinterpret_cast<const bf16x8*>(p.v + krow * kD + c * 16 + hf * 8);
-  }
-  uint32_t aoff[8], coff[4];
-#pragma unroll
-  for (int cc = 0; cc < 8; ++cc) aoff[cc] = tile_off(r32, 2 * cc + hf);
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) coff[dt] = col_read_off(lane, dt);
+  const int64_t kvbase = (int64_t(b) * p.Hkv + hk) * p.N;
+  const int64_t krow = kvbase + kg;
 
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -312,60 +357,158 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dkdv_bf16_d128(BwdParams p) {
     dv[dt] = f32x16{};
   }
 
-  for (int g = 0; g < p.group; ++g) {
-    const int h = hk * p.group + g;
-    const RowDesc col = p.cols[(p.per_head_layout ? h : 0) * p.nb + j];
-    const int64_t hbase = (int64_t(b) * p.H + h) * p.N;
-    const unsigned char* Qg = reinterpret_cast<const unsigned char*>(p.q + hbase * kD);
-    const unsigned char* dOg = reinterpret_cast<const unsigned char*>(p.dout + hbase * kD);
-    for (int e = 0; e < col.count; ++e) {
-      const int ent = p.entries_t[col.start + e];
-      const int i = ent >> 1;
-      const bool partial = ent & 1;
-      __syncthreads();                                 // every wave is done with the last tile
-      stage_tile(Qs, Qg + int64_t(i) * kTileBytes, tid);
-      stage_tile(dOs, dOg + int64_t(i) * kTileBytes, tid);
-      if (tid < kB) {
-        const float l = p.lse[hbase + int64_t(i) * kB + tid];
-        lse_s[tid] = l == -INFINITY ? 0.f : l * kLog2e;
-        dlt_s[tid] = p.delta[hbase + int64_t(i) * kB + tid];
-      }
-      __syncthreads();
+  // Cursor over the walk's entries: (query head of the group, entry of its
+  // transposed list); every value is wave-uniform.
+  struct Entry {
+    int h, i, partial;
+  };
+  int cg = 0, ce = 0;
+  RowDesc ccol = p.cols[(p.per_head_layout ? hk * p.group : 0) * p.nb + j];
+  auto next_entry = [&](Entry& out) -> bool {
+    while (ce >= ccol.count) {
+      if (++cg >= p.group) return false;
+      ccol = p.cols[(p.per_head_layout ? hk * p.group + cg : 0) * p.nb + j];
+      ce = 0;
+    }
+    const int ent = p.entries_t[ccol.start + ce];
+    ++ce;
+    out.h = hk * p.group + cg;
+    out.i = ent >> 1;
+    out.partial = ent & 1;
+    return true;
+  };
+
+  Entry cur;
+  bool have = next_entry(cur);
+  if (have) {
+    // K^T as a B operand: lane (key r32, half hf) holds d = 16c + 8hf .. +7.
+    bf16x8 kf[8];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {                    // queries 32t .. 32t+31 of the tile
+    for (int c = 0; c < 8; ++c) kf[c] = *reinterpret_cast<const bf16x8*>(p.k + krow * kD + c * 16 + hf * 8);
+    // V rows of this k-block; the first step's barrier publishes them.
+    stage<kB, true>(Vs, reinterpret_cast<const unsigned char*>(p.v + (kvbase + int64_t(j) * kB) * kD), tid);
+    // Complete these loads before the first HBM->LDS load, so the pending
+    // counts the barriers wait on only see those.
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::"v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]),
+                     "v"(kf[5]), "v"(kf[6]), "v"(kf[7]) : "memory");
+
+    // HBM->LDS loads of one step: wave w fills rows 8w .. 8w+7 of the Q and
+    // dO buffers, 4 rows (1 KB) per instruction; lane L writes chunk L % 16
+    // of row 8w + 4u + L / 16 and reads the logical chunk the tile layout
+    // places there (chunk ^ 4 * (row & 3), and row & 3 = (L / 16) & 3).
+    const uint32_t dvo = (wave * 8 + (lane >> 4)) * 256 + 16 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)));
+    auto dma_step = [&](const Entry& en, int st, int bf, int u) {
+      const int64_t row0 = (int64_t(b) * p.H + en.h) * p.N + int64_t(en.i) * kB + st * kStepRows;
+      const uint32_t lds_off = (wave * 8 + 4 * (u & 1)) * 256;
+      if (u < 2)
+        dma16(p.q + row0 * kD, dvo + 4 * (u & 1) * 256, Qa[bf] + lds_off);
+      else
+        dma16(p.dout + row0 * kD, dvo + 4 * (u & 1) * 256, dOa[bf] + lds_off);
+    };
+    auto load_x = [&](const Entry& en, int st) {
+      const int64_t r0 = (int64_t(b) * p.H + en.h) * p.N + int64_t(en.i) * kB + st * kStepRows;
+      return lane < 32 ? p.lse[r0 + lane] : p.delta[r0 + lane - 32];
+    };
+    // Per-lane LDS operand offsets as one base each, XOR-ed with a constant
+    // per operand (the layouts' swizzles are XORs on the chunk bits):
+    //   Q/dO row reads   tile_off(r32, 2cc + hf)         = bq ^ 32 cc
+    //   V row reads      rows_off(32w + r32, 2cc + hf)   = bv ^ 32 cc
+    //   transposed reads col_read_off(lane, dt)          = bc ^ 64 dt
+    // They pass through an empty asm at every step, so the compiler re-derives
+    // the operand addresses inside the step instead of holding all of them.
+    const int r4 = (lane & 15) >> 2, c4 = lane & 3, gp = (lane >> 4) & 1;
+    const uint32_t bq0 = r32 * 256 + 16 * hf + 64 * (r32 & 3);
+    const uint32_t bv0 = (32 * wave + r32) * 256 + 16 * (hf ^ (r32 & 1)) + 16 * (r32 & 14);
+    const uint32_t bc0 = (4 * hf + r4) * 256 + 16 * (2 * gp + (c4 >> 1)) + 8 * (c4 & 1) + 64 * r4;
+    float* const my = priv + wave * 64;
+
+    float x = load_x(cur, 0);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dma_step(cur, 0, 0, u);
+
+    while (have) {
+      Entry nxt;
+      const bool have_next = next_entry(nxt);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {                 // queries 32st .. 32st+31 of q-block cur.i
+        const int bf = st & 1;
+        lds_u8* const Qs = Qb[bf];
+        lds_u8* const dOs = dOb[bf];
+        BSA_WAIT_BARRIER(0);                           // this step's rows landed; the other buffer is free
+        my[lane] = x;                                  // this step's LSE (lanes < 32) and Delta
+        uint32_t bq = bq0, bv = bv0, bc = bc0;
+        __asm__ volatile("" : "+v"(bq), "+v"(bv), "+v"(bc));
+        const bool pf = st < 3 || have_next;
+        const Entry& te = st < 3 ? cur : nxt;
+        if (pf) x = load_x(te, (st + 1) & 3);
+        // S and dP: 16 MFMAs alternating between the two accumulators; the
+        // operands of MFMA m (a Q or dO row read, and for dP a V row read)
+        // are issued two MFMAs ahead, the next step's loads one every other
+        // MFMA.
         f32x16 s = f32x16{}, dp = f32x16{};
+        auto lda = [&](int m) { return read_rows((m & 1) ? dOs : Qs, bq ^ (32 * (m >> 1))); };
+        auto ldb = [&](int m) { return read_rows(Vs, bv ^ (32 * (m >> 1))); };
+        bf16x8 ab[4], bb[4];
+        ab[0] = lda(0);
+        ab[1] = lda(1);
+        bb[1] = ldb(1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-          s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(Qs, aoff[cc] + t * 32 * 256), kf[cc], s, 0, 0, 0);
-          dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(dOs, aoff[cc] + t * 32 * 256), vf[cc], dp, 0, 0, 0);
+        for (int m = 0; m < 16; ++m) {
+          if (m + 2 < 16) {
+            ab[(m + 2) & 3] = lda(m + 2);
+            if ((m + 2) & 1) bb[(m + 2) & 3] = ldb(m + 2);
+          }
+          if (pf && (m & 1) == 0 && m < 8) dma_step(te, (st + 1) & 3, bf ^ 1, m >> 1);
+          __builtin_amdgcn_sched_barrier(0);
+          if (m & 1)
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[m & 3], bb[m & 3], dp, 0, 0, 0);
+          else
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[m & 3], kf[m >> 1], s, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        // Register r holds query 32t + 8 (r / 4) + 4 hf + r % 4 for key kg.
+        // Register r holds query 32st + 8 (r / 4) + 4 hf + r % 4 of q-block cur.i, for key kg.
+        const int qbase = cur.i * kB + st * kStepRows;
         bf16x8 pb[2], db[2];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
-          const int q0 = 32 * t + 8 * g4 + 4 * hf;
-          const f32x4 L = *reinterpret_cast<const f32x4*>(lse_s + q0);
-          const f32x4 Dl = *reinterpret_cast<const f32x4*>(dlt_s + q0);
+          const int q0 = 8 * g4 + 4 * hf;
+          const f32x4 L = *reinterpret_cast<const f32x4*>(my + q0);
+          const f32x4 Dl = *reinterpret_cast<const f32x4*>(my + 32 + q0);
 #pragma unroll
           for (int r3 = 0; r3 < 4; ++r3) {
             const int r = 4 * g4 + r3;
-            float x = s[r];
-            if (partial && !pair_ok(p, i * kB + q0 + r3, kg)) x = -INFINITY;
-            const float pr = __builtin_amdgcn_exp2f(fmaf(x, p.sl2, -L[r3]));
+            float xs = s[r];
+            if (cur.partial && !pair_ok(p, qbase + q0 + r3, kg)) xs = -INFINITY;
+            // An empty row (LSE = -inf) has every score masked in this tile.
+            const float l2 = L[r3] == -INFINITY ? 0.f : L[r3] * kLog2e;
+            const float pr = __builtin_amdgcn_exp2f(fmaf(xs, p.sl2, -l2));
             pb[r >> 3][r & 7] = static_cast<__bf16>(pr);
             db[r >> 3][r & 7] = static_cast<__bf16>(pr * (dp[r] - Dl[r3]));
           }
         }
+        // dV^T += dO^T P and dK^T += Q^T dS: 16 MFMAs; operand m is query
+        // chunk m >> 3 of the step, d-tile (m >> 1) & 3, dV for even m, dK
+        // for odd m.
+        auto ldc = [&](int m) { return read_cols((m & 1) ? Qs : dOs, bc ^ (64 * ((m >> 1) & 3)), m >> 3); };
+        bf16x8 cb[4];
+        cb[0] = ldc(0);
+        cb[1] = ldc(1);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-          for (int dt = 0; dt < 4; ++dt) {
-            dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols(dOs, coff[dt], 2 * t + c2), pb[c2], dv[dt],
-                                                             0, 0, 0);
-            dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols(Qs, coff[dt], 2 * t + c2), db[c2], dk[dt],
-                                                             0, 0, 0);
-          }
+        for (int m = 0; m < 16; ++m) {
+          if (m + 2 < 16) cb[(m + 2) & 3] = ldc(m + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          const int dt = (m >> 1) & 3;
+          if (m & 1)
+            dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[m & 3], db[m >> 3], dk[dt], 0, 0, 0);
+          else
+            dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[m & 3], pb[m >> 3], dv[dt], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+      cur = nxt;
+      have = have_next;
     }
   }
   store_row(p.dk + krow * kD, dk, p.scale, hf);

@@ -233,22 +233,25 @@ def test_empty_rows_have_no_entries():
     assert p.info["nnz"] == 0
 
 
-def test_bf16_kernel_m0_only_set_for_lds_loads(tmp_path):
-    """The bf16 kernel writes M0 in inline assembly right before each
-    HBM->LDS load; the compiler treats M0 as reserved and does not honour it
-    as a clobber, so its own code must never rely on M0 across those loads.
-    Compile the kernel to gfx950 assembly (works without a GPU) and check that
-    every M0 access in it is one of those load sequences."""
+@pytest.mark.parametrize("source,symbol", [
+    ("forward.hip", "_ZN3bsa12_GLOBAL__N_113fwd_bf16_d128ENS0_9FwdParamsEPKi"),
+    ("backward.hip", "_ZN3bsa12_GLOBAL__N_118bwd_dkdv_bf16_d128ENS0_9BwdParamsE")])
+def test_bf16_kernel_m0_only_set_for_lds_loads(tmp_path, source, symbol):
+    """The bf16 forward and dK/dV kernels write M0 in inline assembly right
+    before each HBM->LDS load; the compiler treats M0 as reserved and does not
+    honour it as a clobber, so its own code must never rely on M0 across those
+    loads.  Compile the kernel to gfx950 assembly (works without a GPU) and
+    check that every M0 access in it is one of those load sequences."""
     import subprocess
     from block_sparse_flash_bsa_amd import build as bld
-    src = os.path.join(ROOT, "block_sparse_flash_bsa_amd", "csrc", "forward.hip")
-    out = tmp_path / "forward.s"
+    src = os.path.join(ROOT, "block_sparse_flash_bsa_amd", "csrc", source)
+    out = tmp_path / (source + ".s")
     cmd = [bld.hipcc(), "-x", "hip", *bld.HIP_FLAGS, "-O3", "-std=c++17", "--cuda-device-only", "-S",
            "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "block_sparse_flash_bsa_amd", "csrc"),
            src, "-o", str(out)]
     subprocess.run(cmd, check=True, capture_output=True)
     asm = out.read_text()
-    start = asm.index("_ZN3bsa12_GLOBAL__N_113fwd_bf16_d128ENS0_9FwdParamsEPKi:")
+    start = asm.index(symbol + ":")
     body = [l.strip() for l in asm[start:asm.index(".Lfunc_end", start)].splitlines()]
     body = [l for l in body if l and not l.startswith(";")]
     uses = [k for k, l in enumerate(body) if re.search(r"\bm0\b", l)]
