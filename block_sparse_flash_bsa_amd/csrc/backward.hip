@@ -95,10 +95,15 @@ __device__ __forceinline__ bool pair_ok(const BwdParams& p, int q, int k) {
   return in_range || glob;
 }
 
-// LDS tile layout: row r (256 bytes) with 16-byte chunk c at chunk
-// c ^ 4 * (r & 3).  Row reads of 16 bytes and the transposing 8-byte reads
-// both stay inside one chunk, so either kind sees the logical layout.
-__device__ __forceinline__ uint32_t tile_off(int r, int c) { return r * 256 + 16 * (c ^ (4 * (r & 3))); }
+// LDS tile layout for rows read both row-wise and transposed: row r (256
+// bytes) with 16-byte chunk c at chunk c ^ tile_swz(r), tile_swz(r) =
+// 4 (r & 3) + ((r >> 2) & 3).  Row reads of 16 bytes and the transposing
+// 8-byte reads both stay inside one chunk, so either kind sees the logical
+// layout; 16 consecutive rows read at one chunk land in 16 different chunks,
+// and the 4 rows x 2 adjacent chunks of a transposing read in 8, so neither
+// read has bank conflicts.
+__device__ __forceinline__ int tile_swz(int r) { return 4 * (r & 3) + ((r >> 2) & 3); }
+__device__ __forceinline__ uint32_t tile_off(int r, int c) { return r * 256 + 16 * (c ^ tile_swz(r)); }
 
 // LDS layout of K/V rows that are only read row-wise (B operands): chunk c of
 // row r at c ^ (r & 15), which keeps 16-byte reads of 32 rows x 2 chunks free
@@ -141,12 +146,14 @@ __device__ __forceinline__ bf16x8 read_rows(const lds_u8* base, uint32_t off) {
 
 // A operand by two transposing reads: lane l receives, for column
 // d = 32 dt + (l & 31), the 8 rows 16 kc + 4 (l >> 5) + {0..3, 8..11} (the
-// row order of a 16-element chunk of the accumulator layout).
-__device__ __forceinline__ bf16x8 read_cols(const lds_u8* base, uint32_t voff, int kc) {
+// row order of a 16-element chunk of the accumulator layout).  off_lo and
+// off_hi address rows 4 (l >> 5) + r4 and that + 8 (see cols_base); 16 kc
+// rows add 16 kc * 256 bytes to both.
+__device__ __forceinline__ bf16x8 read_cols(const lds_u8* base, uint32_t off_lo, uint32_t off_hi, int kc) {
   const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<__attribute__((address_space(3))) s16x4*>(const_cast<lds_u8*>(base) + voff + (16 * kc) * 256)));
+      reinterpret_cast<__attribute__((address_space(3))) s16x4*>(const_cast<lds_u8*>(base) + off_lo + (16 * kc) * 256)));
   const bf16x4 hi = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<__attribute__((address_space(3))) s16x4*>(const_cast<lds_u8*>(base) + voff + (16 * kc + 8) * 256)));
+      reinterpret_cast<__attribute__((address_space(3))) s16x4*>(const_cast<lds_u8*>(base) + off_hi + (16 * kc) * 256)));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
@@ -167,14 +174,6 @@ __device__ __forceinline__ void store_row(uint16_t* dst, const f32x16 (&acc)[4],
       pk[1] = uint32_t(bf16_bits(acc[dt][4 * g + 2] * mul)) | (uint32_t(bf16_bits(acc[dt][4 * g + 3] * mul)) << 16);
       *reinterpret_cast<u32x2*>(dst + dt * 32 + 8 * g + 4 * hf) = pk;
     }
-}
-
-// Per-lane offset of the transposing reads (see read_cols): in 16-lane group
-// g, lane 4 r4 + c4 addresses row 4 hf + r4 (plus 16 kc and 8) and columns
-// 32 dt + 16 (g & 1) + 4 c4 .. +3.
-__device__ __forceinline__ uint32_t col_read_off(int lane, int dt) {
-  const int hf = lane >> 5, r4 = (lane & 15) >> 2, c4 = lane & 3, gp = (lane >> 4) & 1;
-  return (4 * hf + r4) * 256 + 16 * ((4 * dt + 2 * gp + (c4 >> 1)) ^ (4 * r4)) + 8 * (c4 & 1);
 }
 
 // ---------------------------------------------------------------------------
@@ -200,108 +199,6 @@ __global__ __launch_bounds__(kThreads) void bwd_delta_bf16(const uint16_t* __res
   if (c == 0 && row < rows) delta[row] = s;
 }
 
-// ---------------------------------------------------------------------------
-// dQ: one workgroup per (b, h, q-block); wave w owns query rows 32w .. +31.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
-  __shared__ __attribute__((aligned(1024))) unsigned char Ksh[kTileBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char Vsh[kTileBytes];
-  lds_u8* const Ks = (lds_u8*)Ksh;
-  lds_u8* const Vs = (lds_u8*)Vsh;
-
-  const int item = p.work[blockIdx.x];
-  if (item < 0) return;
-  const int i = item % p.nb;
-  const int bh = item / p.nb;
-  const int h = bh % p.H, b = bh / p.H;
-  const int hk = h / p.group;
-  const RowDesc row = p.rows[(p.per_head_layout ? h : 0) * p.nb + i];
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63, r32 = lane & 31, hf = lane >> 5;
-  const int qg = i * kB + wave * 32 + r32;
-  const int64_t qrow = (int64_t(b) * p.H + h) * p.N + qg;
-
-  // Q^T and dO^T as B operands: lane (row r32, half hf) holds d = 16c + 8hf .. +7.
-  bf16x8 qf[8], df[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    qf[c] = *reinterpret_cast<const bf16x8*>(p.q + qrow * kD + c * 16 + hf * 8);
-    df[c] = *reinterpret_cast<const bf16x8*>(p.dout + qrow * kD + c * 16 + hf * 8);
-  }
-  const float lse = p.lse[qrow];
-  // An empty row (LSE = -inf) has every score masked in every tile it meets.
-  const float lse2 = lse == -INFINITY ? 0.f : lse * kLog2e;
-  const float dlt = p.delta[qrow];
-  const unsigned char* Kg = reinterpret_cast<const unsigned char*>(p.k + (int64_t(b) * p.Hkv + hk) * p.N * kD);
-  const unsigned char* Vg = reinterpret_cast<const unsigned char*>(p.v + (int64_t(b) * p.Hkv + hk) * p.N * kD);
-
-  uint32_t aoff[8], coff[4];
-#pragma unroll
-  for (int cc = 0; cc < 8; ++cc) aoff[cc] = tile_off(r32, 2 * cc + hf);
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) coff[dt] = col_read_off(lane, dt);
-
-  f32x16 acc[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
-
-  for (int e = 0; e < row.count; ++e) {
-    const int ent = p.entries[row.start + e];
-    const int j = ent >> 1;
-    const bool partial = ent & 1;
-    __syncthreads();                                   // every wave is done with the last tile
-    stage<kB, false>(Ks, Kg + int64_t(j) * kTileBytes, tid);
-    stage<kB, true>(Vs, Vg + int64_t(j) * kTileBytes, tid);
-    __syncthreads();
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {                      // keys 32t .. 32t+31 of the tile
-      f32x16 s = f32x16{}, dp = f32x16{};
-#pragma unroll
-      for (int cc = 0; cc < 8; ++cc) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(Ks, aoff[cc] + t * 32 * 256), qf[cc], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_rows(Vs, rows_off(32 * t + r32, 2 * cc + hf)), df[cc], dp,
-                                                     0, 0, 0);
-      }
-      // Register r holds key 32t + 8 (r / 4) + 4 hf + r % 4 of query qg.
-      bf16x8 ds[2];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float x = s[r];
-        if (partial) {
-          const int kk = j * kB + 32 * t + 8 * (r >> 2) + 4 * hf + (r & 3);
-          if (!pair_ok(p, qg, kk)) x = -INFINITY;
-        }
-        const float pr = __builtin_amdgcn_exp2f(fmaf(x, p.sl2, -lse2));
-        ds[r >> 3][r & 7] = static_cast<__bf16>(pr * (dp[r] - dlt));
-      }
-#pragma unroll
-      for (int c2 = 0; c2 < 2; ++c2)
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(read_cols(Ks, coff[dt], 2 * t + c2), ds[c2], acc[dt],
-                                                            0, 0, 0);
-    }
-  }
-  store_row(p.dq + qrow * kD, acc, p.scale, hf);
-}
-
-// ---------------------------------------------------------------------------
-// dK, dV: one workgroup per (b, KV head, k-block); wave w owns keys
-// 32w .. +31 and walks, for every query head of the group, the q-blocks of
-// the transposed CSR in steps of 32 queries.  K^T stays in registers as a B
-// operand; the block's V rows sit in LDS for the whole walk and give the B
-// operand of dP by row reads.  Q and dO rows of a step (8 KB each) are
-// double-buffered and filled by direct HBM->LDS loads issued a step ahead,
-// interleaved with the S/dP MFMAs; one barrier per step.  The step's LSE and
-// Delta are loaded a step ahead too (lane l < 32: LSE of query l, else Delta
-// of query l - 32) and parked in a wave-private LDS row.  64 KB + 1 KB of LDS
-// and at most 256 registers: two workgroups share a CU.
-// ---------------------------------------------------------------------------
-constexpr int kStepRows = 32;
-constexpr int kStepBytes = kStepRows * kD * 2;   // 8 KB
-
 // Wait until at most N of this wave's vector-memory operations are pending,
 // then a workgroup barrier.  The "memory" clobber keeps LDS accesses on their
 // side of the barrier.
@@ -322,6 +219,195 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 }
 #pragma clang diagnostic pop
 
+constexpr int kStepRows = 32;
+constexpr int kStepBytes = kStepRows * kD * 2;   // 8 KB
+
+// Per-lane LDS operand offsets of a 32-row step buffer as one base XOR-ed
+// with a constant per operand (the layouts' swizzles are XORs on the chunk
+// bits; a CPU test checks these identities for every lane):
+//   row reads, tile layout  tile_off(r32, 2cc + hf)           = tile_rows_base ^ 32 cc
+//   row reads, row layout   rows_off(32w + r32, 2cc + hf)     = rows_rows_base(w) ^ 32 cc
+//   transposed reads: in 16-lane group g, lane 4 r4 + c4 addresses row
+//   4 hf + r4 + 8 s (s = 0 for the low half, 1 for the high half) and columns
+//   32 dt + 16 (g & 1) + 4 c4 .. +3 in the tile layout    = cols_base(s) ^ 64 dt
+__device__ __forceinline__ uint32_t tile_rows_base(int lane) {
+  const int r32 = lane & 31, hf = lane >> 5, f = tile_swz(r32);
+  return r32 * 256 + 16 * (hf ^ (f & 1)) + 16 * (f & 14);
+}
+__device__ __forceinline__ uint32_t rows_rows_base(int lane, int w) {
+  const int r32 = lane & 31, hf = lane >> 5;
+  return (32 * w + r32) * 256 + 16 * (hf ^ (r32 & 1)) + 16 * (r32 & 14);
+}
+__device__ __forceinline__ uint32_t cols_base(int lane, int s) {
+  const int hf = lane >> 5, r4 = (lane & 15) >> 2, c4 = lane & 3, gp = (lane >> 4) & 1;
+  return (4 * hf + r4 + 8 * s) * 256 + 16 * ((2 * gp + (c4 >> 1)) ^ (hf + 2 * s)) + 8 * (c4 & 1) + 64 * r4;
+}
+
+// ---------------------------------------------------------------------------
+// dQ: one workgroup per (b, h, q-block); wave w owns query rows 32w .. +31
+// and walks the forward's CSR row in steps of 32 keys.  Q^T and dO^T stay in
+// registers as B operands, the row's LSE and Delta in one register each.  K
+// rows (read row-wise for S^T and transposed for dQ^T) and V rows (row-wise
+// for dP^T) of a step are double-buffered and filled by direct HBM->LDS
+// loads issued a step ahead, interleaved with the S^T/dP^T MFMAs; one
+// barrier per step, 32 KB of LDS.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
+  __shared__ __attribute__((aligned(1024))) unsigned char K0[kStepBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char K1[kStepBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char V0[kStepBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char V1[kStepBytes];
+  lds_u8* const Kb[2] = {(lds_u8*)K0, (lds_u8*)K1};
+  lds_u8* const Vb[2] = {(lds_u8*)V0, (lds_u8*)V1};
+  const uint32_t Ka[2] = {uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)K0)),
+                          uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)K1))};
+  const uint32_t Va[2] = {uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)V0)),
+                          uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)V1))};
+
+  const int item = p.work[blockIdx.x];
+  if (item < 0) return;
+  const int i = item % p.nb;
+  const int bh = item / p.nb;
+  const int h = bh % p.H, b = bh / p.H;
+  const int hk = h / p.group;
+  const RowDesc row = p.rows[(p.per_head_layout ? h : 0) * p.nb + i];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63, r32 = lane & 31, hf = lane >> 5;
+  const int qg = i * kB + wave * 32 + r32;
+  const int64_t qrow = (int64_t(b) * p.H + h) * p.N + qg;
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
+
+  if (row.count > 0) {
+    // Q^T and dO^T as B operands: lane (row r32, half hf) holds d = 16c + 8hf .. +7.
+    bf16x8 qf[8], df[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      qf[c] = *reinterpret_cast<const bf16x8*>(p.q + qrow * kD + c * 16 + hf * 8);
+      df[c] = *reinterpret_cast<const bf16x8*>(p.dout + qrow * kD + c * 16 + hf * 8);
+    }
+    const float lse = p.lse[qrow];
+    // An empty row (LSE = -inf) has every score masked in every tile it meets.
+    const float lse2 = lse == -INFINITY ? 0.f : lse * kLog2e;
+    const float dlt = p.delta[qrow];
+    // Complete these loads before the first HBM->LDS load, so the pending
+    // counts the barriers wait on only see those.
+    __asm__ volatile("s_waitcnt vmcnt(0)" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]),
+                     "v"(qf[5]), "v"(qf[6]), "v"(qf[7]), "v"(df[0]), "v"(df[1]), "v"(df[2]), "v"(df[3]),
+                     "v"(df[4]), "v"(df[5]), "v"(df[6]), "v"(df[7]), "v"(lse2), "v"(dlt) : "memory");
+
+    const unsigned char* Kg = reinterpret_cast<const unsigned char*>(p.k + (int64_t(b) * p.Hkv + hk) * p.N * kD);
+    const unsigned char* Vg = reinterpret_cast<const unsigned char*>(p.v + (int64_t(b) * p.Hkv + hk) * p.N * kD);
+    // HBM->LDS loads of one step: wave w fills rows 8w .. 8w+7 of the K and V
+    // buffers, 4 rows (1 KB) per instruction; lane L writes chunk L % 16 of
+    // row R = 8w + 4u + L / 16 and reads the logical chunk the layout places
+    // there (K: chunk ^ tile_swz(R); V: chunk ^ (R & 15)).
+    const int l4 = lane >> 4, lc = lane & 15;
+    auto dma_step = [&](int j, int st, int bf, int u) {
+      const int64_t row0 = int64_t(j) * kB + st * kStepRows;
+      const int R = wave * 8 + 4 * (u & 1) + l4;
+      const uint32_t lds_off = (wave * 8 + 4 * (u & 1)) * 256;
+      if (u < 2)
+        dma16(Kg + row0 * 256, R * 256 + 16 * (lc ^ tile_swz(R)), Ka[bf] + lds_off);
+      else
+        dma16(Vg + row0 * 256, R * 256 + 16 * (lc ^ (R & 15)), Va[bf] + lds_off);
+    };
+    const uint32_t bq0 = tile_rows_base(lane), bv0 = rows_rows_base(lane, 0);
+    const uint32_t bcl0 = cols_base(lane, 0), bch0 = cols_base(lane, 1);
+
+    int e = 0;
+    // Entries are wave-uniform; readfirstlane keeps the load addresses built
+    // from them in scalar registers, as the HBM->LDS loads require.
+    int ent = __builtin_amdgcn_readfirstlane(p.entries[row.start]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dma_step(ent >> 1, 0, 0, u);
+    while (true) {
+      const int j = ent >> 1;
+      const bool partial = ent & 1;
+      const bool have_next = e + 1 < row.count;
+      const int ent_n = have_next ? __builtin_amdgcn_readfirstlane(p.entries[row.start + e + 1]) : 0;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {                 // keys 32st .. 32st+31 of key block j
+        const int bf = st & 1;
+        lds_u8* const Ks = Kb[bf];
+        lds_u8* const Vs = Vb[bf];
+        BSA_WAIT_BARRIER(0);                           // this step's rows landed; the other buffer is free
+        uint32_t bq = bq0, bv = bv0, bcl = bcl0, bch = bch0;
+        __asm__ volatile("" : "+v"(bq), "+v"(bv), "+v"(bcl), "+v"(bch));
+        const bool pf = st < 3 || have_next;
+        const int tj = st < 3 ? j : (ent_n >> 1);
+        // S^T and dP^T: 16 MFMAs alternating between the two accumulators,
+        // each A operand (a K or V row read) issued two MFMAs ahead, the next
+        // step's loads one every other MFMA.
+        f32x16 sc = f32x16{}, dp = f32x16{};
+        auto lda = [&](int m) {
+          return (m & 1) ? read_rows(Vs, bv ^ (32 * (m >> 1))) : read_rows(Ks, bq ^ (32 * (m >> 1)));
+        };
+        bf16x8 ab[4];
+        ab[0] = lda(0);
+        ab[1] = lda(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < 16; ++m) {
+          if (m + 2 < 16) ab[(m + 2) & 3] = lda(m + 2);
+          if (pf && (m & 1) == 0 && m < 8) dma_step(tj, (st + 1) & 3, bf ^ 1, m >> 1);
+          __builtin_amdgcn_sched_barrier(0);
+          if (m & 1)
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[m & 3], df[m >> 1], dp, 0, 0, 0);
+          else
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[m & 3], qf[m >> 1], sc, 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // Register r holds key 32st + 8 (r / 4) + 4 hf + r % 4 of block j, for query qg.
+        bf16x8 ds[2];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = sc[r];
+          if (partial) {
+            const int kk = j * kB + st * kStepRows + 8 * (r >> 2) + 4 * hf + (r & 3);
+            if (!pair_ok(p, qg, kk)) x = -INFINITY;
+          }
+          const float pr = __builtin_amdgcn_exp2f(fmaf(x, p.sl2, -lse2));
+          ds[r >> 3][r & 7] = static_cast<__bf16>(pr * (dp[r] - dlt));
+        }
+        // dQ^T += K^T dS^T: key chunk m >> 2 of the step, d-tile m & 3.
+        auto ldc = [&](int m) { return read_cols(Ks, bcl ^ (64 * (m & 3)), bch ^ (64 * (m & 3)), m >> 2); };
+        bf16x8 cb[4];
+        cb[0] = ldc(0);
+        cb[1] = ldc(1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          if (m + 2 < 8) cb[(m + 2) & 3] = ldc(m + 2);
+          __builtin_amdgcn_sched_barrier(0);
+          acc[m & 3] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[m & 3], ds[m >> 2], acc[m & 3], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      if (!have_next) break;
+      ++e;
+      ent = ent_n;
+    }
+  }
+  store_row(p.dq + qrow * kD, acc, p.scale, hf);
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV: one workgroup per (b, KV head, k-block); wave w owns keys
+// 32w .. +31 and walks, for every query head of the group, the q-blocks of
+// the transposed CSR in steps of 32 queries.  K^T stays in registers as a B
+// operand; the block's V rows sit in LDS for the whole walk and give the B
+// operand of dP by row reads.  Q and dO rows of a step (8 KB each) are
+// double-buffered and filled by direct HBM->LDS loads issued a step ahead,
+// interleaved with the S/dP MFMAs; one barrier per step.  The step's LSE and
+// Delta are loaded a step ahead too (lane l < 32: LSE of query l, else Delta
+// of query l - 32) and parked in a wave-private LDS row.  64 KB + 1 KB of LDS
+// and at most 256 registers: two workgroups share a CU.
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char Vsh[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char Q0[kStepBytes];
@@ -370,7 +456,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
       ccol = p.cols[(p.per_head_layout ? hk * p.group + cg : 0) * p.nb + j];
       ce = 0;
     }
-    const int ent = p.entries_t[ccol.start + ce];
+    const int ent = __builtin_amdgcn_readfirstlane(p.entries_t[ccol.start + ce]);
     ++ce;
     out.h = hk * p.group + cg;
     out.i = ent >> 1;
@@ -394,32 +480,28 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
 
     // HBM->LDS loads of one step: wave w fills rows 8w .. 8w+7 of the Q and
     // dO buffers, 4 rows (1 KB) per instruction; lane L writes chunk L % 16
-    // of row 8w + 4u + L / 16 and reads the logical chunk the tile layout
-    // places there (chunk ^ 4 * (row & 3), and row & 3 = (L / 16) & 3).
-    const uint32_t dvo = (wave * 8 + (lane >> 4)) * 256 + 16 * ((lane & 15) ^ (4 * ((lane >> 4) & 3)));
+    // of row R = 8w + 4u + L / 16 and reads the logical chunk the tile layout
+    // places there (chunk ^ tile_swz(R)).
     auto dma_step = [&](const Entry& en, int st, int bf, int u) {
       const int64_t row0 = (int64_t(b) * p.H + en.h) * p.N + int64_t(en.i) * kB + st * kStepRows;
+      const int R = wave * 8 + 4 * (u & 1) + (lane >> 4);
+      const uint32_t voff = R * 256 + 16 * ((lane & 15) ^ tile_swz(R));
       const uint32_t lds_off = (wave * 8 + 4 * (u & 1)) * 256;
       if (u < 2)
-        dma16(p.q + row0 * kD, dvo + 4 * (u & 1) * 256, Qa[bf] + lds_off);
+        dma16(p.q + row0 * kD, voff, Qa[bf] + lds_off);
       else
-        dma16(p.dout + row0 * kD, dvo + 4 * (u & 1) * 256, dOa[bf] + lds_off);
+        dma16(p.dout + row0 * kD, voff, dOa[bf] + lds_off);
     };
     auto load_x = [&](const Entry& en, int st) {
       const int64_t r0 = (int64_t(b) * p.H + en.h) * p.N + int64_t(en.i) * kB + st * kStepRows;
       return lane < 32 ? p.lse[r0 + lane] : p.delta[r0 + lane - 32];
     };
-    // Per-lane LDS operand offsets as one base each, XOR-ed with a constant
-    // per operand (the layouts' swizzles are XORs on the chunk bits):
-    //   Q/dO row reads   tile_off(r32, 2cc + hf)         = bq ^ 32 cc
-    //   V row reads      rows_off(32w + r32, 2cc + hf)   = bv ^ 32 cc
-    //   transposed reads col_read_off(lane, dt)          = bc ^ 64 dt
-    // They pass through an empty asm at every step, so the compiler re-derives
-    // the operand addresses inside the step instead of holding all of them.
-    const int r4 = (lane & 15) >> 2, c4 = lane & 3, gp = (lane >> 4) & 1;
-    const uint32_t bq0 = r32 * 256 + 16 * hf + 64 * (r32 & 3);
-    const uint32_t bv0 = (32 * wave + r32) * 256 + 16 * (hf ^ (r32 & 1)) + 16 * (r32 & 14);
-    const uint32_t bc0 = (4 * hf + r4) * 256 + 16 * (2 * gp + (c4 >> 1)) + 8 * (c4 & 1) + 64 * r4;
+    // Operand offset bases (Q/dO row reads, V row reads, transposed reads);
+    // they pass through an empty asm at every step, so the compiler
+    // re-derives the operand addresses inside the step instead of holding
+    // all of them in registers.
+    const uint32_t bq0 = tile_rows_base(lane), bv0 = rows_rows_base(lane, wave);
+    const uint32_t bcl0 = cols_base(lane, 0), bch0 = cols_base(lane, 1);
     float* const my = priv + wave * 64;
 
     float x = load_x(cur, 0);
@@ -436,8 +518,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
         lds_u8* const dOs = dOb[bf];
         BSA_WAIT_BARRIER(0);                           // this step's rows landed; the other buffer is free
         my[lane] = x;                                  // this step's LSE (lanes < 32) and Delta
-        uint32_t bq = bq0, bv = bv0, bc = bc0;
-        __asm__ volatile("" : "+v"(bq), "+v"(bv), "+v"(bc));
+        uint32_t bq = bq0, bv = bv0, bcl = bcl0, bch = bch0;
+        __asm__ volatile("" : "+v"(bq), "+v"(bv), "+v"(bcl), "+v"(bch));
         const bool pf = st < 3 || have_next;
         const Entry& te = st < 3 ? cur : nxt;
         if (pf) x = load_x(te, (st + 1) & 3);
@@ -490,7 +572,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
         // dV^T += dO^T P and dK^T += Q^T dS: 16 MFMAs; operand m is query
         // chunk m >> 3 of the step, d-tile (m >> 1) & 3, dV for even m, dK
         // for odd m.
-        auto ldc = [&](int m) { return read_cols((m & 1) ? Qs : dOs, bc ^ (64 * ((m >> 1) & 3)), m >> 3); };
+        auto ldc = [&](int m) {
+          const int dt = (m >> 1) & 3;
+          return read_cols((m & 1) ? Qs : dOs, bcl ^ (64 * dt), bch ^ (64 * dt), m >> 3);
+        };
         bf16x8 cb[4];
         cb[0] = ldc(0);
         cb[1] = ldc(1);

@@ -235,7 +235,8 @@ def test_empty_rows_have_no_entries():
 
 @pytest.mark.parametrize("source,symbol", [
     ("forward.hip", "_ZN3bsa12_GLOBAL__N_113fwd_bf16_d128ENS0_9FwdParamsEPKi"),
-    ("backward.hip", "_ZN3bsa12_GLOBAL__N_118bwd_dkdv_bf16_d128ENS0_9BwdParamsE")])
+    ("backward.hip", "_ZN3bsa12_GLOBAL__N_118bwd_dkdv_bf16_d128ENS0_9BwdParamsE"),
+    ("backward.hip", "_ZN3bsa12_GLOBAL__N_116bwd_dq_bf16_d128ENS0_9BwdParamsE")])
 def test_bf16_kernel_m0_only_set_for_lds_loads(tmp_path, source, symbol):
     """The bf16 forward and dK/dV kernels write M0 in inline assembly right
     before each HBM->LDS load; the compiler treats M0 as reserved and does not
@@ -349,3 +350,43 @@ def test_backward_rejects_host_only_plan():
     st = bsattn.lib().bsa_backward(1, 1, 1, 1, 1, 1, p.handle, 1, 1, 1, 1, None)
     assert st == bsattn.ERR_INVALID_ARGUMENT
     assert b"bsa_plan_host" in bsattn.lib().bsa_last_error()
+
+
+def test_backward_operand_offset_identities():
+    """The backward kernels address LDS operands as one per-lane base XOR-ed
+    with a per-operand constant.  The identities behind that, written out for
+    every lane: the tile layout (chunk c of row r at c ^ (4 (r & 3) +
+    ((r >> 2) & 3))), the row layout (c ^ (r & 15)) and the transposing reads
+    (lane 4 r4 + c4 of 16-lane group g reads row 4 hf + r4 + 8 s, columns
+    32 dt + 16 (g & 1) + 4 c4 .. +3, in the tile layout)."""
+    def tile_swz(r):
+        return 4 * (r & 3) + ((r >> 2) & 3)
+
+    def tile_off(r, c):
+        return r * 256 + 16 * (c ^ tile_swz(r))
+
+    def rows_off(r, c):
+        return r * 256 + 16 * (c ^ (r & 15))
+
+    def col_read(lane, dt, s):
+        hf, r4, c4, gp = lane >> 5, (lane & 15) >> 2, lane & 3, (lane >> 4) & 1
+        row = 4 * hf + r4 + 8 * s
+        return tile_off(row, 4 * dt + 2 * gp + (c4 >> 1)) + 8 * (c4 & 1)
+
+    for w in range(4):
+        for lane in range(64):
+            r32, hf = lane & 31, lane >> 5
+            r4, c4, gp = (lane & 15) >> 2, lane & 3, (lane >> 4) & 1
+            f = tile_swz(r32)
+            tile_rows_base = r32 * 256 + 16 * (hf ^ (f & 1)) + 16 * (f & 14)
+            rows_rows_base = (32 * w + r32) * 256 + 16 * (hf ^ (r32 & 1)) + 16 * (r32 & 14)
+            for cc in range(8):
+                assert tile_rows_base ^ (32 * cc) == tile_off(r32, 2 * cc + hf)
+                assert rows_rows_base ^ (32 * cc) == rows_off(32 * w + r32, 2 * cc + hf)
+            for s in (0, 1):
+                cols_base = ((4 * hf + r4 + 8 * s) * 256 + 16 * ((2 * gp + (c4 >> 1)) ^ (hf + 2 * s))
+                             + 8 * (c4 & 1) + 64 * r4)
+                for dt in range(4):
+                    assert cols_base ^ (64 * dt) == col_read(lane, dt, s)
+                for kc in range(8):         # 16 kc more rows keep the row's swizzle
+                    assert tile_swz(4 * hf + r4 + 8 * s + 16 * kc) == tile_swz(4 * hf + r4 + 8 * s)
