@@ -60,7 +60,10 @@ struct BwdParams {
   const int32_t* work;        // dQ launch order: (b * H + h) * nb + i
   const RowDesc* cols;        // transposed rows [layout heads * nb]
   const int32_t* entries_t;   // (i << 1) | partial
-  const int32_t* work_kv;     // dK/dV launch order: (b * Hkv + hk) * nb + j
+  const int32_t* kv_desc;     // dK/dV launch order: per slot {item (b * Hkv + hk) * nb + j,
+                              // first and end entry of the group's walk, partial slot or -1}
+  const int32_t* kv_reduce;   // per split column {item, first partial slot, count, 0}
+  float* kv_scratch;          // float32 partials [slot][dK, dV][128 keys][128]
   int64_t N;
   int32_t H, Hkv, group, nb, per_head_layout;
   float scale, sl2;           // sl2 = scale * log2(e)
@@ -423,8 +426,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
   const uint32_t dOa[2] = {uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)dO0)),
                            uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)dO1))};
 
-  const int item = p.work_kv[blockIdx.x];
+  const int item = p.kv_desc[4 * blockIdx.x];
   if (item < 0) return;
+  const int walk_begin = p.kv_desc[4 * blockIdx.x + 1];
+  const int walk_end = p.kv_desc[4 * blockIdx.x + 2];
+  const int partial_slot = p.kv_desc[4 * blockIdx.x + 3];
   const int j = item % p.nb;
   const int bk = item / p.nb;
   const int hk = bk % p.Hkv, b = bk / p.Hkv;
@@ -443,21 +449,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
     dv[dt] = f32x16{};
   }
 
-  // Cursor over the walk's entries: (query head of the group, entry of its
-  // transposed list); every value is wave-uniform.
+  // Cursor over this slot's part [walk_begin, walk_end) of the walk: the
+  // group's transposed lists one after another, as (query head of the group,
+  // entry of its list); every value is wave-uniform.
   struct Entry {
     int h, i, partial;
   };
-  int cg = 0, ce = 0;
+  int cg = 0, ce = walk_begin, left = walk_end - walk_begin;
   RowDesc ccol = p.cols[(p.per_head_layout ? hk * p.group : 0) * p.nb + j];
   auto next_entry = [&](Entry& out) -> bool {
+    if (left <= 0) return false;
     while (ce >= ccol.count) {
+      ce -= ccol.count;
       if (++cg >= p.group) return false;
       ccol = p.cols[(p.per_head_layout ? hk * p.group + cg : 0) * p.nb + j];
-      ce = 0;
     }
     const int ent = __builtin_amdgcn_readfirstlane(p.entries_t[ccol.start + ce]);
     ++ce;
+    --left;
     out.h = hk * p.group + cg;
     out.i = ent >> 1;
     out.partial = ent & 1;
@@ -596,8 +605,51 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
       have = have_next;
     }
   }
-  store_row(p.dk + krow * kD, dk, p.scale, hf);
-  store_row(p.dv + krow * kD, dv, 1.f, hf);
+  if (partial_slot < 0) {
+    store_row(p.dk + krow * kD, dk, p.scale, hf);
+    store_row(p.dv + krow * kD, dv, 1.f, hf);
+  } else {
+    // One chunk of a split column: float32 partial sums, unscaled.
+    float* const part = p.kv_scratch + int64_t(partial_slot) * 2 * kB * kD + (wave * 32 + r32) * kD;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d = dt * 32 + 8 * g4 + 4 * hf;
+        *reinterpret_cast<f32x4*>(part + d) =
+            f32x4{dk[dt][4 * g4], dk[dt][4 * g4 + 1], dk[dt][4 * g4 + 2], dk[dt][4 * g4 + 3]};
+        *reinterpret_cast<f32x4*>(part + kB * kD + d) =
+            f32x4{dv[dt][4 * g4], dv[dt][4 * g4 + 1], dv[dt][4 * g4 + 2], dv[dt][4 * g4 + 3]};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split columns: dK = scale * sum of the chunks' partials, dV = their sum, in
+// chunk order (deterministic); one workgroup per split column, 4 values per
+// thread and step.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void bwd_kv_reduce(BwdParams p) {
+  const int item = p.kv_reduce[4 * blockIdx.x];
+  const int first = p.kv_reduce[4 * blockIdx.x + 1];
+  const int count = p.kv_reduce[4 * blockIdx.x + 2];
+  const int j = item % p.nb;
+  const int bk = item / p.nb;
+  const int hk = bk % p.Hkv, b = bk / p.Hkv;
+  const int64_t row0 = (int64_t(b) * p.Hkv + hk) * p.N + int64_t(j) * kB;
+  for (int v = threadIdx.x; v < 2 * kB * kD / 4; v += kThreads) {
+    const int tensor = v / (kB * kD / 4);              // 0: dK, 1: dV
+    const int e = 4 * (v % (kB * kD / 4));             // element (key * 128 + d) of the tile
+    f32x4 acc = f32x4{};
+    for (int c = 0; c < count; ++c)
+      acc += *reinterpret_cast<const f32x4*>(p.kv_scratch + (int64_t(first + c) * 2 + tensor) * kB * kD + e);
+    const float mul = tensor == 0 ? p.scale : 1.f;
+    u32x2 pk;
+    pk[0] = uint32_t(bf16_bits(acc[0] * mul)) | (uint32_t(bf16_bits(acc[1] * mul)) << 16);
+    pk[1] = uint32_t(bf16_bits(acc[2] * mul)) | (uint32_t(bf16_bits(acc[3] * mul)) << 16);
+    uint16_t* const dst = (tensor == 0 ? p.dk : p.dv) + row0 * kD + e;
+    *reinterpret_cast<u32x2*>(dst) = pk;
+  }
 }
 
 }  // namespace
@@ -617,6 +669,8 @@ extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v
   if (!(pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128))
     return fail(BSA_ERR_UNSUPPORTED, "backward kernels exist for bf16, head_dim 128, block 128 only");
   if (plan->info.work_items == 0) return BSA_OK;
+  if (plan->kv_partials > 0 && !plan->d_kv_scratch)
+    return fail(BSA_ERR_DEVICE, "plan has split dK/dV columns but no partial-sum scratch");
   if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !delta)
     return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v, out, lse, dout, dq, dk, dv and delta must all be non-NULL");
   int dev = -1;
@@ -640,7 +694,9 @@ extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v
   prm.work = plan->d_work;
   prm.cols = plan->d_cols;
   prm.entries_t = plan->d_entries_t;
-  prm.work_kv = plan->d_work_kv;
+  prm.kv_desc = plan->d_work_kv;
+  prm.kv_reduce = plan->d_kv_reduce;
+  prm.kv_scratch = plan->d_kv_scratch;
   prm.N = pr.seq_len;
   prm.H = pr.num_heads;
   prm.Hkv = pr.num_kv_heads;
@@ -680,6 +736,10 @@ extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v
   }
   if (err == hipSuccess && !plan->work_kv.empty()) {
     hipLaunchKernelGGL(bwd_dkdv_bf16_d128, dim3(unsigned(plan->work_kv.size())), dim3(kThreads), 0, s, prm);
+    err = hipGetLastError();
+  }
+  if (err == hipSuccess && !plan->kv_reduce.empty()) {
+    hipLaunchKernelGGL(bwd_kv_reduce, dim3(unsigned(plan->kv_reduce.size())), dim3(kThreads), 0, s, prm);
     err = hipGetLastError();
   }
   if (err != hipSuccess) return fail(BSA_ERR_DEVICE, "backward kernel launch failed: %s", hipGetErrorString(err));

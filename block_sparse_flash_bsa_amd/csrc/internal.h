@@ -48,7 +48,19 @@ struct bsa_plan {
   std::vector<std::vector<int32_t>> colT_ptr;  // [layout_heads][nb + 1]
   std::vector<std::vector<int32_t>> rowT_idx;  // [layout_heads][nnz_h]
   std::vector<std::vector<uint8_t>> flagsT;    // [layout_heads][nnz_h]
-  std::vector<int32_t> work_kv;                // [launch slots], -1 = idle
+  std::vector<int32_t> work_kv;                // [launch slots] item, -1 = idle
+  // A long column (the k-block of a global key is read by every q-block) is
+  // cut into chunks of at most kv_chunk entries of the group's walk; slot s
+  // runs entries [kv_desc[s].begin, .end) and writes its float32 partial dK,
+  // dV to scratch slot kv_desc[s].partial (-1: a whole column, written as the
+  // final bf16 rows).  kv_reduce lists the split columns and their partials.
+  struct KvDesc {
+    int32_t item, begin, end, partial;
+  };
+  std::vector<KvDesc> kv_desc;                 // [launch slots]
+  std::vector<KvDesc> kv_reduce;               // {item, first partial, count, 0}
+  int32_t kv_chunk = 0;
+  int64_t kv_partials = 0;
   // Device copy (bsa_plan and bsa_plan_dynamic).
   int device = -1;
   void* dev_mem = nullptr;
@@ -57,7 +69,10 @@ struct bsa_plan {
   const int32_t* d_work = nullptr;             // [launch slots]
   const bsa::RowDesc* d_cols = nullptr;        // [layout_heads * nb] transposed rows
   const int32_t* d_entries_t = nullptr;        // [nnz] (q block << 1) | partial
-  const int32_t* d_work_kv = nullptr;          // [dK/dV launch slots]
+  const int32_t* d_work_kv = nullptr;          // [dK/dV launch slots] as int4 KvDesc
+  const int32_t* d_kv_reduce = nullptr;        // [split columns] as int4 KvDesc
+  float* d_kv_scratch = nullptr;               // [kv_partials][2][128][128] float32
+  void* dev_scratch = nullptr;                 // allocation behind d_kv_scratch
   // Dynamic plans: the CSR is written on the device by bsa_plan_set_bitmap;
   // d_counts is its per-row scratch [layout_heads * nb].
   int32_t dynamic = 0;

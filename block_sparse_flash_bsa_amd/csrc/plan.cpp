@@ -259,22 +259,56 @@ void build_transpose(Plan& P) {
 
 // Launch order of the dK/dV kernel: items (b * Hkv + hk) * nb + j in
 // locality order (neighbouring k-blocks of one KV head share the q-blocks
-// they read), cut per XCD by cost = the group's column lengths + 1.
+// they read), cut per XCD by cost.  An item's walk is the concatenation of
+// its group's transposed lists; walks longer than kv_chunk entries (twice the
+// mean, at least 64) are cut into chunks that run as separate workgroups and
+// write float32 partials, summed in chunk order by a reduction kernel, so a
+// global key's column does not serialise the launch's tail.
 void build_work_kv(Plan& P) {
   const int64_t B = P.prob.batch, H = P.prob.num_heads, Hkv = P.prob.num_kv_heads, nb = P.nb;
   const int64_t group = H / Hkv;
-  std::vector<int32_t> loc(size_t(B * Hkv * nb));
-  std::iota(loc.begin(), loc.end(), 0);
-  auto cost = [&](int64_t item) -> int64_t {
+  const int64_t items = B * Hkv * nb;
+  auto walk = [&](int64_t item) -> int64_t {
     const int64_t j = item % nb, hk = (item / nb) % Hkv;
-    int64_t c = 1;
+    int64_t c = 0;
     for (int64_t h = hk * group; h < (hk + 1) * group; ++h) {
       const auto& cp = P.colT_ptr[P.layout_heads == 1 ? 0 : h];
       c += cp[j + 1] - cp[j];
     }
     return c;
   };
-  P.work_kv = loc.empty() ? loc : xcd_slots(loc, cost);
+  int64_t total = 0;
+  for (int64_t it = 0; it < items; ++it) total += walk(it);
+  const int64_t mean = items ? (total + items - 1) / items : 0;
+  P.kv_chunk = int32_t(std::max<int64_t>(64, 2 * mean));
+  // Pieces in locality order: (item, begin, end, partial slot).
+  std::vector<Plan::KvDesc> pieces;
+  P.kv_reduce.clear();
+  int64_t partials = 0;
+  for (int64_t it = 0; it < items; ++it) {
+    const int64_t n = walk(it);
+    if (n <= P.kv_chunk) {
+      pieces.push_back({int32_t(it), 0, int32_t(n), -1});
+      continue;
+    }
+    const int64_t chunks = (n + P.kv_chunk - 1) / P.kv_chunk;
+    P.kv_reduce.push_back({int32_t(it), int32_t(partials), int32_t(chunks), 0});
+    for (int64_t c = 0; c < chunks; ++c)
+      pieces.push_back({int32_t(it), int32_t(c * n / chunks), int32_t((c + 1) * n / chunks), int32_t(partials + c)});
+    partials += chunks;
+  }
+  P.kv_partials = partials;
+  std::vector<int32_t> loc(pieces.size());
+  std::iota(loc.begin(), loc.end(), 0);
+  const std::vector<int32_t> slots =
+      loc.empty() ? loc : xcd_slots(loc, [&](int64_t k) { return int64_t(pieces[k].end - pieces[k].begin) + 1; });
+  P.work_kv.assign(slots.size(), -1);
+  P.kv_desc.assign(slots.size(), {-1, 0, 0, -1});
+  for (size_t s = 0; s < slots.size(); ++s)
+    if (slots[s] >= 0) {
+      P.kv_desc[s] = pieces[slots[s]];
+      P.work_kv[s] = pieces[slots[s]].item;
+    }
 }
 
 // Launch order.  Item id = (b * H + h) * nb + i; cost = row length + 1.
@@ -329,7 +363,8 @@ bsa_status_t upload(Plan& P) {
   const size_t off_cols = up(off_work + slots * sizeof(int32_t));
   const size_t off_entries_t = up(off_cols + rows * sizeof(bsa::RowDesc));
   const size_t off_work_kv = up(off_entries_t + nnz * sizeof(int32_t));
-  const size_t bytes = off_work_kv + slots_kv * sizeof(int32_t) + 16;
+  const size_t off_kv_reduce = up(off_work_kv + slots_kv * sizeof(Plan::KvDesc));
+  const size_t bytes = off_kv_reduce + P.kv_reduce.size() * sizeof(Plan::KvDesc) + 16;
   std::vector<unsigned char> host(bytes, 0);
   auto* rd = reinterpret_cast<bsa::RowDesc*>(host.data());
   auto* en = reinterpret_cast<int32_t*>(host.data() + off_entries);
@@ -356,7 +391,9 @@ bsa_status_t upload(Plan& P) {
       et[start + e] = bsa::encode_entry(P.rowT_idx[lh][e], P.flagsT[lh][e] != 0);
     start += int32_t(P.rowT_idx[lh].size());
   }
-  if (slots_kv) std::memcpy(host.data() + off_work_kv, P.work_kv.data(), slots_kv * sizeof(int32_t));
+  if (slots_kv) std::memcpy(host.data() + off_work_kv, P.kv_desc.data(), slots_kv * sizeof(Plan::KvDesc));
+  if (!P.kv_reduce.empty())
+    std::memcpy(host.data() + off_kv_reduce, P.kv_reduce.data(), P.kv_reduce.size() * sizeof(Plan::KvDesc));
   hipError_t err = hipMalloc(&P.dev_mem, bytes);
   if (err != hipSuccess) {
     P.dev_mem = nullptr;
@@ -376,6 +413,20 @@ bsa_status_t upload(Plan& P) {
   P.d_cols = reinterpret_cast<const bsa::RowDesc*>(base + off_cols);
   P.d_entries_t = reinterpret_cast<const int32_t*>(base + off_entries_t);
   P.d_work_kv = reinterpret_cast<const int32_t*>(base + off_work_kv);
+  P.d_kv_reduce = reinterpret_cast<const int32_t*>(base + off_kv_reduce);
+  if (P.kv_partials > 0 && P.prob.dtype == BSA_BF16 && P.prob.head_dim == 128 && P.prob.block_size == 128) {
+    // float32 partial dK and dV of every chunk of a split column.
+    const size_t sbytes = size_t(P.kv_partials) * 2 * 128 * 128 * sizeof(float);
+    err = hipMalloc(&P.dev_scratch, sbytes);
+    if (err != hipSuccess) {
+      P.dev_scratch = nullptr;
+      (void)hipFree(P.dev_mem);
+      P.dev_mem = nullptr;
+      return fail(err == hipErrorOutOfMemory ? BSA_ERR_OUT_OF_MEMORY : BSA_ERR_DEVICE,
+                  "hipMalloc(%zu) for the backward's partial sums failed: %s", sbytes, hipGetErrorString(err));
+    }
+    P.d_kv_scratch = static_cast<float*>(P.dev_scratch);
+  }
   P.info.on_device = 1;
   return BSA_OK;
 }
@@ -526,6 +577,7 @@ void bsa_plan_destroy(bsa_plan_t plan) {
     (void)hipGetDevice(&cur);
     if (cur != plan->device) (void)hipSetDevice(plan->device);
     (void)hipFree(plan->dev_mem);
+    if (plan->dev_scratch) (void)hipFree(plan->dev_scratch);
     if (cur != plan->device && cur >= 0) (void)hipSetDevice(cur);
   }
   delete plan;

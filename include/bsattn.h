@@ -40,7 +40,9 @@
  * Threading: calls on different plans may run concurrently; a plan may be
  * used by several streams at once (bsa_forward only reads it), except that
  * bsa_plan_set_bitmap rewrites a dynamic plan and must not overlap a forward
- * that uses it on another stream.  The last error string is thread-local.
+ * that uses it on another stream, and bsa_backward calls with one plan must
+ * not overlap each other (they share the plan's partial-sum scratch).  The
+ * last error string is thread-local.
  */
 #ifndef BSATTN_H
 #define BSATTN_H
@@ -285,8 +287,12 @@ bsa_status_t bsa_plan_csr_transposed(bsa_plan_t plan, int32_t layout_head, const
                                      const int32_t** row_idx, const uint8_t** flags, int64_t* nnz);
 
 /* Launch order of the dK/dV kernel: slot s runs item work[s] =
- * (b * num_kv_heads + hk) * nb + j, or -1 for an idle slot.  Plan-owned.
- * Errors: INVALID_ARGUMENT for NULL pointers or a dynamic plan. */
+ * (b * num_kv_heads + hk) * nb + j, or -1 for an idle slot.  An item whose
+ * walk (the transposed lists of its group's query heads, one after another)
+ * is longer than twice the mean, such as the k-block of a global key, is cut
+ * into chunks that occupy several slots; their float32 partial sums live in
+ * plan-owned device scratch and a reduction kernel adds them in chunk order.
+ * Plan-owned.  Errors: INVALID_ARGUMENT for NULL pointers or a dynamic plan. */
 bsa_status_t bsa_plan_work_kv(bsa_plan_t plan, const int32_t** work, int64_t* slots);
 
 /* Run the backward pass asynchronously on `stream` (a hipStream_t; NULL =
@@ -299,9 +305,11 @@ bsa_status_t bsa_plan_work_kv(bsa_plan_t plan, const int32_t** work, int64_t* sl
  *   delta   : device, float32 [batch][num_heads][seq_len]: caller-owned
  *             workspace; receives Delta_q = <dO_q, O_q> (computed from the
  *             rounded out), which the dK/dV kernel reads
- * Three kernels run in order on the stream: Delta, dQ (one workgroup per
- * q-block, walking its CSR row) and dK/dV (one workgroup per KV head and
- * k-block, walking its transposed list over the group's query heads).  Every
+ * Kernels run in order on the stream: Delta, dQ (one workgroup per
+ * q-block, walking its CSR row), dK/dV (one workgroup per KV head and
+ * k-block, walking its transposed list over the group's query heads, or per
+ * chunk of a long walk) and, if the plan split any walk, the reduction of
+ * the chunks' partial sums.  Every
  * element of dq, dk, dv and delta is written (zero rows where nothing
  * attends).  Outputs must not alias inputs or each other.  Nothing is
  * allocated or freed.

@@ -331,12 +331,14 @@ def test_kv_work_order_is_a_permutation(name):
     p = host_plan(w)
     work = p.work_kv()
     items = work[work >= 0]
-    np.testing.assert_array_equal(np.sort(items), np.arange(w.batch * w.kv_heads * w.num_blocks))
-    # slot s runs on XCD s % 8: each XCD's items form one contiguous run of the item order
+    # every item is covered; only long walks (global-key columns) take several slots
+    np.testing.assert_array_equal(np.unique(items), np.arange(w.batch * w.kv_heads * w.num_blocks))
+    assert len(items) - len(np.unique(items)) < 0.05 * len(items)
+    # slot s runs on XCD s % 8: each XCD's items form one contiguous, ordered run of the item order
     for x in range(8):
         run = work[x::8]
         run = run[run >= 0]
-        assert np.all(np.diff(run) == 1)
+        assert np.all(np.diff(run) >= 0) and np.all(np.diff(run) <= 1)
 
 
 def test_transposed_csr_errors():

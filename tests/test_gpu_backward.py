@@ -127,6 +127,35 @@ def test_backward_token_rule_both_sides_gqa():
     check("dV", dv.float().cpu().numpy(), rv)
 
 
+def test_backward_split_columns():
+    """Walks longer than twice the mean are cut into chunks whose float32
+    partials a reduction kernel adds: the 8 global keys' k-block (read by
+    every q-block of all 4 heads) and, with per-head bitmaps, dense columns."""
+    w = wl.WORKLOADS["gqa256k"].with_shape(name="split-global", heads=4, kv_heads=1, seq_len=4096)
+    lay = dict(causal=True, unit="tokens", window_left=255, window_right=0, global_keys=8,
+               global_queries=0, bitmap=None)
+    nb = w.num_blocks
+    rng = np.random.default_rng(6)
+    bm = rng.random((4, nb, nb)) < 0.05
+    bm[:, :, 3] = True                      # k-block 3 read by every q-block of every head
+    bm[1, :, 17] = True
+    bm[:, np.arange(nb), np.arange(nb)] = True
+    lay_bm = dict(causal=False, unit="blocks", window_left=-1, window_right=-1, global_keys=0,
+                  global_queries=0, bitmap=torch.from_numpy(bm))
+    for name, ly in (("global keys", lay), ("dense bitmap columns", lay_bm)):
+        say(f"[bwd-split] {name}")
+        p = gpu_plan(w, ly)
+        work = p.work_kv()
+        assert len(work[work >= 0]) > len(np.unique(work[work >= 0])), "expected split columns"
+        q, k, v = wl.make_qkv(w, "cpu")
+        do = wl.make_dout(w, "cpu")
+        dq, dk, dv = fwd_bwd(p, q.cuda(), k.cuda(), v.cuda(), do.cuda())
+        rq, rk, rv = oracle.backward(q, k, v, do, ly, w.block)
+        check("dQ", dq.float().cpu().numpy(), rq)
+        check("dK", dk.float().cpu().numpy(), rk)
+        check("dV", dv.float().cpu().numpy(), rv)
+
+
 # ---------------------------------------------------------- full size, sampled
 FULL_KEYS = {
     # keys away from global blocks (a global key is read by every query of the
