@@ -132,12 +132,12 @@ def allowed_keys(layout, N: int, bs: int, h: int, q: int) -> np.ndarray:
             return np.zeros(0, dtype=np.int64)
         return np.unique(np.concatenate(parts)).astype(np.int64)
     lh = _layout_head(layout, h)
-    nb = N // bs
+    nb = -(-N // bs)                     # a last, shorter block when bs does not divide N
     i = q // bs
     blocks = [j for j in range(nb) if _block_active(layout, lh, i, j)]
     if not blocks:
         return np.zeros(0, dtype=np.int64)
-    keys = np.concatenate([np.arange(j * bs, (j + 1) * bs) for j in blocks])
+    keys = np.concatenate([np.arange(j * bs, min((j + 1) * bs, N)) for j in blocks])
     if layout["causal"]:
         keys = keys[keys <= q]
     return keys.astype(np.int64)
@@ -224,9 +224,9 @@ def forward(Q, K, V, layout, block_size: int, scale: Optional[float] = None,
 # --------------------------------------------------------------------------
 def _tile_counts_bruteforce(layout, N: int, bs: int, h: int, i: int) -> np.ndarray:
     """Allowed-pair count of every tile (i, j) by enumerating A(q)."""
-    nb = N // bs
+    nb = -(-N // bs)
     counts = np.zeros(nb, dtype=np.int64)
-    for q in range(i * bs, (i + 1) * bs):
+    for q in range(i * bs, min((i + 1) * bs, N)):
         keys = allowed_keys(layout, N, bs, h, q)
         counts += np.bincount(keys // bs, minlength=nb)
     return counts
@@ -234,10 +234,10 @@ def _tile_counts_bruteforce(layout, N: int, bs: int, h: int, i: int) -> np.ndarr
 
 def _tile_counts_intervals(layout, N: int, bs: int, i: int) -> np.ndarray:
     """Same counts for a token-unit spec, by interval overlap per query."""
-    nb = N // bs
+    nb = -(-N // bs)
     counts = np.zeros(nb, dtype=np.int64)
     full_mid = np.zeros(nb + 1, dtype=np.int64)      # difference array of whole-block runs
-    for q in range(i * bs, (i + 1) * bs):
+    for q in range(i * bs, min((i + 1) * bs, N)):
         for lo, hi, sign in _intervals_tokens(layout, N, q):
             if lo > hi:
                 continue
@@ -255,17 +255,20 @@ def _tile_counts_intervals(layout, N: int, bs: int, i: int) -> np.ndarray:
 
 
 def _tile_counts_blocks(layout, N: int, bs: int, h: int, i: int) -> np.ndarray:
-    """Counts for block-unit specs and bitmaps: whole tiles, causal cuts the diagonal."""
-    nb = N // bs
+    """Counts for block-unit specs and bitmaps: whole tiles, causal cuts the
+    diagonal; a last, shorter block has only its rows below N."""
+    nb = -(-N // bs)
     lh = _layout_head(layout, h)
     counts = np.zeros(nb, dtype=np.int64)
+    rows_i = min(bs, N - i * bs)                     # queries of block i
     for j in range(nb):
         if not _block_active(layout, lh, i, j):
             continue
+        cols_j = min(bs, N - j * bs)                 # keys of block j
         if not layout["causal"] or j < i:
-            counts[j] = bs * bs
+            counts[j] = rows_i * cols_j
         elif j == i:
-            counts[j] = bs * (bs + 1) // 2           # pairs with k <= q inside the tile
+            counts[j] = rows_i * (rows_i + 1) // 2   # pairs with k <= q inside the tile
     return counts
 
 
@@ -282,9 +285,11 @@ def plan(layout, N: int, bs: int, brute: Optional[bool] = None):
 
     Returns a list (one per layout head) of dicts with int32 `row_ptr` [nb+1],
     int32 `col_idx` [nnz] and uint8 `flags` [nnz] (0 = FULL, 1 = PARTIAL).
+    When bs does not divide N the last block is shorter; a tile is FULL only
+    if all bs * bs of its pairs exist and are allowed, so tiles touching that
+    block are PARTIAL.
     """
-    assert N % bs == 0, "sequence length must be a multiple of the block size"
-    nb = N // bs
+    nb = -(-N // bs)
     if brute is None:
         brute = N <= 1024
     out = []

@@ -378,3 +378,63 @@ def test_pins_catch_planted_missing_scale(monkeypatch):
     _, L = bsa_oracle.forward(Q, K, V, spec(False, "tokens"), 32)
     lse = torch.logsumexp(Q @ K.transpose(-1, -2) / math.sqrt(8), -1).numpy()
     assert np.abs(L - lse).max() > 1e-3
+
+
+# ------------------------------------------- ragged lengths (bs does not divide N)
+# The last block holds N mod bs rows; keys and queries at or beyond N do not
+# exist.  The masks below are built for exactly N positions (triu/tril/kron
+# trimmed to N), independently of the oracle's block and interval code.
+@pytest.mark.parametrize("N,W,G,GQ", [(200, 37, 3, 0), (130, 0, 0, 0), (333, 100, 8, 5)])
+def test_ragged_token_rule_bruteforce(N, W, G, GQ):
+    Q, K, V = rand_qkv(1, 2, 1, N, 8, 20)
+    mask = band(N, W, 0)
+    mask[:, :G] = True
+    mask[:GQ, :] = True
+    mask &= np.tril(np.ones((N, N), bool))
+    assert_close(*oracle.forward(Q, K, V, spec(True, "tokens", W, 0, G, GQ), 64),
+                 *dense_masked(Q, K, V, mask))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_block_rule_and_bitmap_bruteforce(causal):
+    N, bs = 300, 64                                  # 5 blocks, the last with 44 rows
+    nb = -(-N // bs)
+    i, j = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
+    grid = (np.abs(i - j) <= 1) | (j < 1)
+    mask = np.kron(grid, np.ones((bs, bs))).astype(bool)[:N, :N]
+    if causal:
+        mask &= np.tril(np.ones((N, N), bool))
+    Q, K, V = rand_qkv(1, 2, 2, N, 8, 21)
+    assert_close(*oracle.forward(Q, K, V, spec(causal, "blocks", 1, 1, 1, 0), bs), *dense_masked(Q, K, V, mask))
+    bm = grid[None].astype(np.uint8)
+    assert_close(*oracle.forward(Q, K, V, spec(causal, "blocks", bitmap=bm), bs), *dense_masked(Q, K, V, mask))
+
+
+def test_ragged_dense_equals_sdpa():
+    N = 190
+    Q, K, V = rand_qkv(1, 2, 2, N, 16, 22)
+    O, L = oracle.forward(Q, K, V, spec(True, "tokens"), 64)
+    ref = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=True)
+    assert_close(O, L, ref.numpy(), torch.logsumexp(
+        (Q @ K.transpose(-1, -2) / 4.0).masked_fill(~torch.ones(N, N, dtype=torch.bool).tril(), -math.inf),
+        -1).numpy())
+
+
+def test_ragged_plan_counts_bruteforce_and_flags():
+    rng = np.random.default_rng(23)
+    for _ in range(60):
+        bs = int(rng.choice([8, 16, 32]))
+        N = bs * int(rng.integers(1, 7)) + int(rng.integers(1, bs))
+        unit = str(rng.choice(["tokens", "blocks"]))
+        lim = N if unit == "tokens" else -(-N // bs)
+        lay = spec(bool(rng.integers(0, 2)), unit, int(rng.integers(-1, lim + 2)), int(rng.integers(-1, lim + 2)),
+                   int(rng.integers(0, lim + 1)), int(rng.integers(0, lim + 1)))
+        fast = oracle.plan(lay, N, bs, brute=False)[0]
+        slow = oracle.plan(lay, N, bs, brute=True)[0]
+        for key in ("row_ptr", "col_idx", "flags"):
+            np.testing.assert_array_equal(fast[key], slow[key], err_msg=f"{lay} N={N} bs={bs}")
+        nb = -(-N // bs)
+        last = slow["col_idx"] == nb - 1     # tiles touching the short block are never FULL
+        assert np.all(slow["flags"][last] == oracle.PARTIAL)
+        rows_last = slice(slow["row_ptr"][nb - 1], slow["row_ptr"][nb])
+        assert np.all(slow["flags"][rows_last] == oracle.PARTIAL)

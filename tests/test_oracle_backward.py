@@ -266,3 +266,16 @@ def test_pins_catch_planted_swapped_key_value_roles(monkeypatch):
     Q, K, V, dO, ref = _dense_case()
     got = bsa_oracle.backward(Q, K, V, dO, spec(False, "tokens"), 32)
     assert np.abs(got[0] - ref[0]).max() > 1e-3
+
+
+@pytest.mark.parametrize("N,causal", [(200, True), (150, False)])
+def test_ragged_length_bruteforce(N, causal):
+    """A last, shorter block (bs = 64 does not divide N): autograd through the
+    masked attention of exactly N positions."""
+    Q, K, V, dO = rand4(1, 2, 1, N, 8, 16)
+    mask = band(N, 30, 0 if causal else 30)
+    mask[:, :2] = True
+    if causal:
+        mask &= np.tril(np.ones((N, N), bool))
+    close3(oracle.backward(Q, K, V, dO, spec(causal, "tokens", 30, 0 if causal else 30, 2), 64),
+           autograd_masked(Q, K, V, dO, mask))
