@@ -67,6 +67,7 @@ struct BwdParams {
   int64_t N;
   int32_t H, Hkv, group, nb, per_head_layout;
   float scale, sl2;           // sl2 = scale * log2(e)
+  int32_t N32;                // N as int32 (N <= 2^30)
   int32_t causal, token_rule, gk32, gq32;
   // Window and causal parts of the token predicate as one range of q - k:
   // allowed iff (uint32)(q - k - mlo) <= mspan.
@@ -92,10 +93,12 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 // Token predicate inside a PARTIAL tile: the window/causal range of q - k, or
 // a global key / global query row (still under the causal cut).  With
 // token_rule == 0 the range is the causal cut alone.
+// Positions at or beyond the end of a ragged sequence do not exist (every
+// tile of its last block is PARTIAL).
 __device__ __forceinline__ bool pair_ok(const BwdParams& p, int q, int k) {
   const bool in_range = uint32_t(q - k) - uint32_t(p.mlo) <= p.mspan;
   const bool glob = p.token_rule && (k < p.gk32 || q < p.gq32) && (!p.causal || k <= q);
-  return in_range || glob;
+  return (in_range || glob) && q < p.N32 && k < p.N32;
 }
 
 // LDS tile layout for rows read both row-wise and transposed: row r (256
@@ -121,20 +124,26 @@ __device__ __forceinline__ uint32_t rows_off(int r, int c) { return r * 256 + 16
 // The thread index passes through an empty asm so its address arithmetic
 // is redone per call instead of being hoisted out of the caller's loops and
 // held in registers.
+// Rows at or beyond valid_rows (the end of a ragged sequence) are loaded from
+// row valid_rows - 1.
 template <int kRows, bool kRowsOnly>
-__device__ __forceinline__ void stage(lds_u8* dst, const unsigned char* __restrict__ src, int tid) {
+__device__ __forceinline__ void stage(lds_u8* dst, const unsigned char* __restrict__ src, int tid,
+                                      int valid_rows = kRows) {
   constexpr int kPer = kRows / 16;
   constexpr int kGroup = kPer < 4 ? kPer : 4;
   int t = tid;
   __asm__ volatile("" : "+v"(t));
   const int r = t >> 4, c = t & 15;
-  const u32x4* g = reinterpret_cast<const u32x4*>(src + t * 16);
+  const u32x4* g = reinterpret_cast<const u32x4*>(src + c * 16);
   lds_u8* const l = dst + (kRowsOnly ? rows_off(r, c) : tile_off(r, c));
 #pragma unroll
   for (int part = 0; part < kPer / kGroup; ++part) {
     u32x4 v[kGroup];
 #pragma unroll
-    for (int u = 0; u < kGroup; ++u) v[u] = g[(part * kGroup + u) * 256];
+    for (int u = 0; u < kGroup; ++u) {
+      const int row = r + 16 * (part * kGroup + u);
+      v[u] = g[(row < valid_rows ? row : valid_rows - 1) * 16];
+    }
 #pragma unroll
     for (int u = 0; u < kGroup; ++u)
       *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(l + (part * kGroup + u) * 4096) = v[u];
@@ -255,6 +264,9 @@ __device__ __forceinline__ uint32_t cols_base(int lane, int s) {
 // loads issued a step ahead, interleaved with the S^T/dP^T MFMAs; one
 // barrier per step, 32 KB of LDS.
 // ---------------------------------------------------------------------------
+// kRagged: the sequence ends inside its last block; rows at or beyond N load
+// row N - 1, are masked, and are not written.
+template <bool kRagged>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char K0[kStepBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char K1[kStepBytes];
@@ -280,6 +292,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
   const int lane = tid & 63, r32 = lane & 31, hf = lane >> 5;
   const int qg = i * kB + wave * 32 + r32;
   const int64_t qrow = (int64_t(b) * p.H + h) * p.N + qg;
+  const int64_t qrow_ld = kRagged && qg >= p.N ? qrow - qg + p.N - 1 : qrow;   // row to load from
 
   f32x16 acc[4];
 #pragma unroll
@@ -290,13 +303,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
     bf16x8 qf[8], df[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      qf[c] = *reinterpret_cast<const bf16x8*>(p.q + qrow * kD + c * 16 + hf * 8);
-      df[c] = *reinterpret_cast<const bf16x8*>(p.dout + qrow * kD + c * 16 + hf * 8);
+      qf[c] = *reinterpret_cast<const bf16x8*>(p.q + qrow_ld * kD + c * 16 + hf * 8);
+      df[c] = *reinterpret_cast<const bf16x8*>(p.dout + qrow_ld * kD + c * 16 + hf * 8);
     }
-    const float lse = p.lse[qrow];
+    const float lse = p.lse[qrow_ld];
     // An empty row (LSE = -inf) has every score masked in every tile it meets.
     const float lse2 = lse == -INFINITY ? 0.f : lse * kLog2e;
-    const float dlt = p.delta[qrow];
+    const float dlt = p.delta[qrow_ld];
     // Complete these loads before the first HBM->LDS load, so the pending
     // counts the barriers wait on only see those.
     __asm__ volatile("s_waitcnt vmcnt(0)" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]),
@@ -311,13 +324,18 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
     // there (K: chunk ^ tile_swz(R); V: chunk ^ (R & 15)).
     const int l4 = lane >> 4, lc = lane & 15;
     auto dma_step = [&](int j, int st, int bf, int u) {
-      const int64_t row0 = int64_t(j) * kB + st * kStepRows;
       const int R = wave * 8 + 4 * (u & 1) + l4;
       const uint32_t lds_off = (wave * 8 + 4 * (u & 1)) * 256;
+      const uint32_t chunk = 16 * (u < 2 ? (lc ^ tile_swz(R)) : (lc ^ (R & 15)));
+      // Source row relative to the key block's first row (below N); in a
+      // ragged last block rows at or beyond N read row N - 1.
+      int rel = st * kStepRows + R;
+      if (kRagged && j == p.nb - 1) rel = rel < p.N32 - j * kB ? rel : p.N32 - j * kB - 1;
+      const int64_t tile0 = int64_t(j) * kB;
       if (u < 2)
-        dma16(Kg + row0 * 256, R * 256 + 16 * (lc ^ tile_swz(R)), Ka[bf] + lds_off);
+        dma16(Kg + tile0 * 256, rel * 256 + chunk, Ka[bf] + lds_off);
       else
-        dma16(Vg + row0 * 256, R * 256 + 16 * (lc ^ (R & 15)), Va[bf] + lds_off);
+        dma16(Vg + tile0 * 256, rel * 256 + chunk, Va[bf] + lds_off);
     };
     const uint32_t bq0 = tile_rows_base(lane), bv0 = rows_rows_base(lane, 0);
     const uint32_t bcl0 = cols_base(lane, 0), bch0 = cols_base(lane, 1);
@@ -396,7 +414,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
       ent = ent_n;
     }
   }
-  store_row(p.dq + qrow * kD, acc, p.scale, hf);
+  if (!kRagged || qg < p.N) store_row(p.dq + qrow * kD, acc, p.scale, hf);
 }
 
 // ---------------------------------------------------------------------------
@@ -411,6 +429,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
 // of query l - 32) and parked in a wave-private LDS row.  64 KB + 1 KB of LDS
 // and at most 256 registers: two workgroups share a CU.
 // ---------------------------------------------------------------------------
+template <bool kRagged>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char Vsh[kTileBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char Q0[kStepBytes];
@@ -479,9 +498,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
     // K^T as a B operand: lane (key r32, half hf) holds d = 16c + 8hf .. +7.
     bf16x8 kf[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) kf[c] = *reinterpret_cast<const bf16x8*>(p.k + krow * kD + c * 16 + hf * 8);
+    for (int c = 0; c < 8; ++c)
+      kf[c] = *reinterpret_cast<const bf16x8*>(p.k + (kRagged && kg >= p.N ? kvbase + p.N - 1 : krow) * kD +
+                                               c * 16 + hf * 8);
     // V rows of this k-block; the first step's barrier publishes them.
-    stage<kB, true>(Vs, reinterpret_cast<const unsigned char*>(p.v + (kvbase + int64_t(j) * kB) * kD), tid);
+    stage<kB, true>(Vs, reinterpret_cast<const unsigned char*>(p.v + (kvbase + int64_t(j) * kB) * kD), tid,
+                    kRagged ? (p.N32 - j * kB < kB ? p.N32 - j * kB : kB) : kB);
     // Complete these loads before the first HBM->LDS load, so the pending
     // counts the barriers wait on only see those.
     __asm__ volatile("s_waitcnt vmcnt(0)" ::"v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]),
@@ -492,18 +514,24 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
     // of row R = 8w + 4u + L / 16 and reads the logical chunk the tile layout
     // places there (chunk ^ tile_swz(R)).
     auto dma_step = [&](const Entry& en, int st, int bf, int u) {
-      const int64_t row0 = (int64_t(b) * p.H + en.h) * p.N + int64_t(en.i) * kB + st * kStepRows;
+      // Source row relative to the q-block's first row (below N); in a
+      // ragged last block rows at or beyond N read row N - 1.
+      const int64_t tile0 = (int64_t(b) * p.H + en.h) * p.N + int64_t(en.i) * kB;
       const int R = wave * 8 + 4 * (u & 1) + (lane >> 4);
-      const uint32_t voff = R * 256 + 16 * ((lane & 15) ^ tile_swz(R));
+      int rel = st * kStepRows + R;
+      if (kRagged && en.i == p.nb - 1) rel = rel < p.N32 - en.i * kB ? rel : p.N32 - en.i * kB - 1;
+      const uint32_t voff = rel * 256 + 16 * ((lane & 15) ^ tile_swz(R));
       const uint32_t lds_off = (wave * 8 + 4 * (u & 1)) * 256;
       if (u < 2)
-        dma16(p.q + row0 * kD, voff, Qa[bf] + lds_off);
+        dma16(p.q + tile0 * kD, voff, Qa[bf] + lds_off);
       else
-        dma16(p.dout + row0 * kD, voff, dOa[bf] + lds_off);
+        dma16(p.dout + tile0 * kD, voff, dOa[bf] + lds_off);
     };
     auto load_x = [&](const Entry& en, int st) {
-      const int64_t r0 = (int64_t(b) * p.H + en.h) * p.N + int64_t(en.i) * kB + st * kStepRows;
-      return lane < 32 ? p.lse[r0 + lane] : p.delta[r0 + lane - 32];
+      int qi = en.i * kB + st * kStepRows + (lane & 31);
+      if (kRagged) qi = qi < p.N32 ? qi : p.N32 - 1;
+      const int64_t r = (int64_t(b) * p.H + en.h) * p.N + qi;
+      return lane < 32 ? p.lse[r] : p.delta[r];
     };
     // Operand offset bases (Q/dO row reads, V row reads, transposed reads);
     // they pass through an empty asm at every step, so the compiler
@@ -606,8 +634,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
     }
   }
   if (partial_slot < 0) {
-    store_row(p.dk + krow * kD, dk, p.scale, hf);
-    store_row(p.dv + krow * kD, dv, 1.f, hf);
+    if (!kRagged || kg < p.N) {
+      store_row(p.dk + krow * kD, dk, p.scale, hf);
+      store_row(p.dv + krow * kD, dv, 1.f, hf);
+    }
   } else {
     // One chunk of a split column: float32 partial sums, unscaled.
     float* const part = p.kv_scratch + int64_t(partial_slot) * 2 * kB * kD + (wave * 32 + r32) * kD;
@@ -640,6 +670,7 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_reduce(BwdParams p) {
   for (int v = threadIdx.x; v < 2 * kB * kD / 4; v += kThreads) {
     const int tensor = v / (kB * kD / 4);              // 0: dK, 1: dV
     const int e = 4 * (v % (kB * kD / 4));             // element (key * 128 + d) of the tile
+    if (int64_t(j) * kB + e / kD >= p.N) continue;     // beyond a ragged sequence's end
     f32x4 acc = f32x4{};
     for (int c = 0; c < count; ++c)
       acc += *reinterpret_cast<const f32x4*>(p.kv_scratch + (int64_t(first + c) * 2 + tensor) * kB * kD + e);
@@ -698,6 +729,7 @@ extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v
   prm.kv_reduce = plan->d_kv_reduce;
   prm.kv_scratch = plan->d_kv_scratch;
   prm.N = pr.seq_len;
+  prm.N32 = int32_t(pr.seq_len);
   prm.H = pr.num_heads;
   prm.Hkv = pr.num_kv_heads;
   prm.group = pr.num_heads / pr.num_kv_heads;
@@ -725,17 +757,24 @@ extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v
     prm.mspan = uint32_t(hi - lo);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool ragged = pr.seq_len % kB != 0;
   const int64_t rows = int64_t(pr.batch) * pr.num_heads * pr.seq_len;
   const int64_t rows_per_block = kThreads / 16;
   hipLaunchKernelGGL(bwd_delta_bf16, dim3(unsigned((rows + rows_per_block - 1) / rows_per_block)), dim3(kThreads),
                      0, s, prm.o, prm.dout, prm.delta, rows);
   hipError_t err = hipGetLastError();
   if (err == hipSuccess) {
-    hipLaunchKernelGGL(bwd_dq_bf16_d128, dim3(unsigned(plan->info.launch_slots)), dim3(kThreads), 0, s, prm);
+    if (ragged)
+      hipLaunchKernelGGL(bwd_dq_bf16_d128<true>, dim3(unsigned(plan->info.launch_slots)), dim3(kThreads), 0, s, prm);
+    else
+      hipLaunchKernelGGL(bwd_dq_bf16_d128<false>, dim3(unsigned(plan->info.launch_slots)), dim3(kThreads), 0, s, prm);
     err = hipGetLastError();
   }
   if (err == hipSuccess && !plan->work_kv.empty()) {
-    hipLaunchKernelGGL(bwd_dkdv_bf16_d128, dim3(unsigned(plan->work_kv.size())), dim3(kThreads), 0, s, prm);
+    if (ragged)
+      hipLaunchKernelGGL(bwd_dkdv_bf16_d128<true>, dim3(unsigned(plan->work_kv.size())), dim3(kThreads), 0, s, prm);
+    else
+      hipLaunchKernelGGL(bwd_dkdv_bf16_d128<false>, dim3(unsigned(plan->work_kv.size())), dim3(kThreads), 0, s, prm);
     err = hipGetLastError();
   }
   if (err == hipSuccess && !plan->kv_reduce.empty()) {

@@ -75,6 +75,7 @@ constexpr float kLn2 = 0.6931471805599453f;
 // window/global part is uniform over the tile and already true for every
 // planned tile, so only causality remains.
 __device__ __forceinline__ bool allowed(const FwdParams& p, int64_t q, int64_t k) {
+  if (k >= p.N) return false;                     // beyond a ragged sequence's end
   if (p.causal && k > q) return false;
   if (!p.token_rule) return true;
   const bool in_w = (p.wl < 0 || q - k <= p.wl) && (p.wr < 0 || k - q <= p.wr);
@@ -176,6 +177,12 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 }
 #pragma clang diagnostic pop
 
+// kRagged: the sequence ends inside its last block (N % 128 != 0).  Rows at or
+// beyond N are loaded from row N - 1 instead (and, for keys, masked: every
+// tile of the last key block is PARTIAL), and no output row at or beyond N is
+// written.  The instance for whole blocks compiles to the same code as
+// without the flag.
+template <bool kRagged>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const int32_t* __restrict__ ents) {
   // Separate arrays per half, so the compiler can tell the halves apart.
   __shared__ __attribute__((aligned(1024))) unsigned char K0[kHalfBytes];
@@ -196,8 +203,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   const int qrow = wave * 32 + r32;                       // row within the q-block
   const int64_t qg = int64_t(i) * kBM + qrow;             // global query index
 
+  const int64_t qld = kRagged && qg >= p.N ? p.N - 1 : qg;   // row to load Q from
   const uint16_t* __restrict__ Qp =
-      static_cast<const uint16_t*>(p.q) + ((int64_t(b) * p.H + h) * p.N + qg) * kD;
+      static_cast<const uint16_t*>(p.q) + ((int64_t(b) * p.H + h) * p.N + qld) * kD;
   const unsigned char* Kg =
       reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.k) + (int64_t(b) * p.Hkv + hk) * p.N * kD);
   const unsigned char* Vg =
@@ -229,6 +237,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   // u >= 4 V rows.
   auto dma_half_part = [&](int j, int hh, int u) {
     const int64_t row0 = int64_t(j) * kBN + hh * 64 + wave * 16;
+    if (kRagged && j == p.nb - 1) {
+      // Last key block of a ragged sequence: lane rows at or beyond N read
+      // row N - 1 (offsets from the block's first row, which is below N).
+      const int64_t tile0 = int64_t(j) * kBN;
+      const int64_t rl = row0 + 4 * (u & 3) + lr;
+      const int64_t rc = rl < p.N ? rl : p.N - 1;
+      const uint32_t chunk = (u < 4 ? dko[u] : dvo) & 255u;
+      const uint32_t voff = uint32_t(rc - tile0) * 256u + chunk;
+      if (u < 4)
+        dma16(Kg + tile0 * (kD * 2), voff, Ka[hh] + wave * 16 * 256 + u * 1024);
+      else
+        dma16(Vg + tile0 * (kD * 2), voff, Va[hh] + wave * 16 * 256 + (u - 4) * 1024);
+      return;
+    }
     if (u < 4)
       dma16(Kg + row0 * (kD * 2), dko[u], Ka[hh] + wave * 16 * 256 + u * 1024);
     else
@@ -313,6 +335,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
         for (int r = 0; r < 16; ++r) {
           const int ko = t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
           sq[t][r] = dql - uint32_t(ko) <= p.mspan ? sq[t][r] : -INFINITY;
+        }
+    }
+    if (kRagged && j == p.nb - 1) {
+      // Keys at or beyond the end of a ragged sequence do not exist.
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int ko = t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
+          sq[t][r] = k0 + ko < p.N ? sq[t][r] : -INFINITY;
         }
     }
   };
@@ -455,6 +487,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   // Epilogue: O = acc / l (0 for an empty row), LSE = ln2 * (m_ref + log2 l).
   const float l = sum_with_partner(l_part);
   const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (kRagged && qg >= p.N) return;              // beyond a ragged sequence's end
   uint16_t* Op = static_cast<uint16_t*>(p.o) + ((int64_t(b) * p.H + h) * p.N + qg) * kD;
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
@@ -498,7 +531,8 @@ __global__ __launch_bounds__(BS * kF32Lanes) void fwd_f32(FwdParams p) {
   const int64_t q0 = int64_t(i) * BS;
   const int64_t qg = q0 + r;
 
-  const float* Qp = static_cast<const float*>(p.q) + ((int64_t(b) * p.H + h) * p.N + qg) * D + sl * DL;
+  const int64_t qld = qg < p.N ? qg : p.N - 1;   // rows beyond a ragged end load row N - 1
+  const float* Qp = static_cast<const float*>(p.q) + ((int64_t(b) * p.H + h) * p.N + qld) * D + sl * DL;
   const float* Kb = static_cast<const float*>(p.k) + (int64_t(b) * p.Hkv + hk) * p.N * D;
   const float* Vb = static_cast<const float*>(p.v) + (int64_t(b) * p.Hkv + hk) * p.N * D;
   float qv[DL], acc[DL];
@@ -518,8 +552,11 @@ __global__ __launch_bounds__(BS * kF32Lanes) void fwd_f32(FwdParams p) {
       const int64_t k0 = int64_t(j) * BS + st * KT;
       __syncthreads();
       for (int x = t; x < KT * D / 4; x += NT) {
-        reinterpret_cast<float4*>(Ks)[x] = reinterpret_cast<const float4*>(Kb + k0 * D)[x];
-        reinterpret_cast<float4*>(Vs)[x] = reinterpret_cast<const float4*>(Vb + k0 * D)[x];
+        // Keys beyond a ragged end load row N - 1; the mask removes them.
+        const int64_t kr = k0 + x / (D / 4) < p.N ? k0 + x / (D / 4) : p.N - 1;
+        const int64_t src = kr * D + (x % (D / 4)) * 4;
+        reinterpret_cast<float4*>(Ks)[x] = *reinterpret_cast<const float4*>(Kb + src);
+        reinterpret_cast<float4*>(Vs)[x] = *reinterpret_cast<const float4*>(Vb + src);
       }
       __syncthreads();
       for (int kc = 0; kc < KT; kc += 16) {
@@ -557,6 +594,7 @@ __global__ __launch_bounds__(BS * kF32Lanes) void fwd_f32(FwdParams p) {
     }
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (qg >= p.N) return;                          // beyond a ragged sequence's end
   float* Op = static_cast<float*>(p.o) + ((int64_t(b) * p.H + h) * p.N + qg) * D + sl * DL;
 #pragma unroll
   for (int d = 0; d < DL; ++d) Op[d] = acc[d] * inv;
@@ -646,7 +684,10 @@ extern "C" bsa_status_t bsa_forward(const void* q, const void* k, const void* v,
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = hipSuccess;
   if (pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128) {
-    hipLaunchKernelGGL(fwd_bf16_d128, dim3(unsigned(slots)), dim3(kThreads), 0, s, prm, prm.entries);
+    if (pr.seq_len % kBN != 0)
+      hipLaunchKernelGGL(fwd_bf16_d128<true>, dim3(unsigned(slots)), dim3(kThreads), 0, s, prm, prm.entries);
+    else
+      hipLaunchKernelGGL(fwd_bf16_d128<false>, dim3(unsigned(slots)), dim3(kThreads), 0, s, prm, prm.entries);
     err = hipGetLastError();
   } else if (pr.dtype == BSA_F32 && pr.head_dim == 64 && pr.block_size == 64) {
     err = launch_f32<64, 64>(prm, slots, s);

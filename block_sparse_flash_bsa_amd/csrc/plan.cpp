@@ -70,11 +70,12 @@ struct TokenRule {
 // Pair count of tile (i, j) for a token-unit spec.  O(1) when the tile is
 // wholly inside the allowed region, else one interval count per query.
 int64_t tile_count_tokens(const TokenRule& r, int64_t bs, int64_t i, int64_t j) {
-  const int64_t q0 = i * bs, q1 = q0 + bs - 1, k0 = j * bs, k1 = k0 + bs - 1;
+  // The last block of a ragged sequence ends at N - 1.
+  const int64_t q0 = i * bs, q1 = std::min(q0 + bs, r.N) - 1, k0 = j * bs, k1 = std::min(k0 + bs, r.N) - 1;
   const bool causal_full = !r.causal || k1 <= q0;
   if (causal_full) {
     const bool win_full = (r.wl < 0 || q1 - k0 <= r.wl) && (r.wr < 0 || k1 - q0 <= r.wr);
-    if (win_full || k1 < r.gk || q1 < r.gq) return bs * bs;
+    if (win_full || k1 < r.gk || q1 < r.gq) return (q1 - q0 + 1) * (k1 - k0 + 1);
   }
   int64_t c = 0;
   for (int64_t q = q0; q <= q1; ++q) c += r.count(q, k0, k1);
@@ -101,10 +102,8 @@ bsa_status_t validate(const bsa_problem_t* p, const bsa_layout_t* L) {
   if (p->head_dim < 1 || p->block_size < 1)
     return fail(BSA_ERR_INVALID_ARGUMENT, "head_dim and block_size must be >= 1 (got %d, %d)",
                 p->head_dim, p->block_size);
-  if (p->seq_len < 0 || p->seq_len % p->block_size != 0)
-    return fail(BSA_ERR_INVALID_ARGUMENT,
-                "seq_len (%lld) must be >= 0 and a multiple of block_size (%d); pad the sequence",
-                (long long)p->seq_len, p->block_size);
+  if (p->seq_len < 0)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "seq_len (%lld) must be >= 0", (long long)p->seq_len);
   if (!(std::isfinite(p->scale) && p->scale >= 0.f))
     return fail(BSA_ERR_INVALID_ARGUMENT, "scale must be 0 (default) or finite and > 0");
   if (p->schedule < BSA_SCHEDULE_DEFAULT || p->schedule > BSA_SCHEDULE_ROWMAJOR)
@@ -120,7 +119,7 @@ bsa_status_t validate(const bsa_problem_t* p, const bsa_layout_t* L) {
   if (L->bitmap && L->bitmap_heads != 1 && L->bitmap_heads != p->num_heads)
     return fail(BSA_ERR_INVALID_ARGUMENT, "bitmap_heads must be 1 or num_heads (%d), got %d",
                 p->num_heads, L->bitmap_heads);
-  const int64_t nb = p->seq_len / p->block_size;
+  const int64_t nb = (p->seq_len + p->block_size - 1) / p->block_size;
   const int64_t items = int64_t(p->batch) * p->num_heads * nb;
   if (p->seq_len > (int64_t(1) << 30))
     return fail(BSA_ERR_INVALID_ARGUMENT, "seq_len %lld exceeds 2^30", (long long)p->seq_len);
@@ -134,11 +133,12 @@ bsa_status_t validate(const bsa_problem_t* p, const bsa_layout_t* L) {
 }
 
 void build_csr(Plan& P, const bsa_layout_t& L) {
-  const int64_t bs = P.prob.block_size, nb = P.nb;
+  const int64_t bs = P.prob.block_size, nb = P.nb, N = P.prob.seq_len;
   const TokenRule rule{L.causal != 0, P.prob.seq_len, L.window_left, L.window_right,
                        L.global_keys, L.global_queries};
   const bool tokens = !L.bitmap && L.unit == BSA_UNIT_TOKENS;
-  const int64_t full = bs * bs, diag = bs * (bs + 1) / 2;
+  const int64_t full = bs * bs;
+  auto len = [&](int64_t blk) { return std::min(bs, N - blk * bs); };   // rows of block blk
   P.row_ptr.assign(P.layout_heads, std::vector<int32_t>(nb + 1, 0));
   P.col_idx.assign(P.layout_heads, {});
   P.flags.assign(P.layout_heads, {});
@@ -180,7 +180,7 @@ void build_csr(Plan& P, const bsa_layout_t& L) {
         for (int64_t j = 0; j < nb; ++j) {
           const bool on = bm ? bm[i * nb + j] != 0 : block_rule(L, i, j);
           if (!on) continue;
-          const int64_t c = (!L.causal || j < i) ? full : (j == i ? diag : 0);
+          const int64_t c = (!L.causal || j < i) ? len(i) * len(j) : (j == i ? len(i) * (len(i) + 1) / 2 : 0);
           if (c == 0) continue;
           cols.push_back(int32_t(j));
           flg.push_back(c == full ? 0 : 1);
@@ -442,7 +442,7 @@ bsa_status_t make_plan(const bsa_problem_t* problem, const bsa_layout_t* layout,
   try {
     P->prob = *problem;
     if (P->prob.scale == 0.f) P->prob.scale = 1.0f / std::sqrt(float(problem->head_dim));
-    P->nb = int32_t(problem->seq_len / problem->block_size);
+    P->nb = int32_t((problem->seq_len + problem->block_size - 1) / problem->block_size);
     P->layout_heads = layout->bitmap ? layout->bitmap_heads : 1;
     P->causal = layout->causal;
     P->token_rule = (!layout->bitmap && layout->unit == BSA_UNIT_TOKENS) ? 1 : 0;
@@ -488,6 +488,10 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
       layout->global_queries != 0)
     return fail(BSA_ERR_INVALID_ARGUMENT,
                 "dynamic plan: window_left/right must be -1 and global_keys/queries 0 (the bitmap is the layout)");
+  if (problem->seq_len % problem->block_size != 0)
+    return fail(BSA_ERR_INVALID_ARGUMENT,
+                "dynamic plan: seq_len (%lld) must be a multiple of block_size (%d)",
+                (long long)problem->seq_len, problem->block_size);
   const int64_t nb = problem->seq_len / problem->block_size;
   const int64_t per_head = layout->causal ? nb * (nb + 1) / 2 : nb * nb;
   const int64_t cap = int64_t(layout->bitmap_heads) * per_head;

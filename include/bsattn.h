@@ -81,9 +81,14 @@ typedef int32_t bsa_status_t;
 /* The attention problem a plan is prepared for.
  *   batch >= 0, num_heads >= 1, num_kv_heads >= 1, num_heads % num_kv_heads == 0
  *     (query head h reads KV head h / (num_heads / num_kv_heads)).
- *   seq_len in [0, 2^30] and a multiple of block_size (the FAQ of "The Only Guide You
- *     Need for Sparse Attention Kernels in Long-Context LLMs" answers the
- *     variable-length question by padding to the block size).
+ *   seq_len in [0, 2^30].  When block_size does not divide it, the last block
+ *     is shorter: positions at or beyond seq_len neither attend nor are
+ *     attended (the kernels pad virtually: they read row seq_len - 1 in place
+ *     of missing rows, mask them, and write no row beyond seq_len - 1), and
+ *     every tile touching that block is PARTIAL.  The FAQ of "The Only Guide
+ *     You Need for Sparse Attention Kernels in Long-Context LLMs" answers the
+ *     variable-length question by padding to the block size; this does that
+ *     padding inside the kernels.  Dynamic plans need a multiple of the block.
  *   block_size: layout block = kernel tile height and width.
  *   Supported (dtype, head_dim, block_size):
  *     BSA_BF16: (128, 128)                    -- MFMA kernel
@@ -109,7 +114,7 @@ typedef struct {
  *   window_left, window_right >= -1 (-1 = unbounded), inclusive distances.
  *   global_keys, global_queries >= 0.
  *   bitmap: NULL, or a HOST array uint8 [bitmap_heads][nb][nb] (nb =
- *     seq_len / block_size), nonzero = block active, row = q-block, column =
+ *     ceil(seq_len / block_size)), nonzero = block active, row = q-block, column =
  *     k-block; it replaces window/global (causal still applies).  The plan
  *     copies what it needs; the caller keeps ownership.  bitmap_heads is 1
  *     (shared by every head) or num_heads (one layout per query head); the
@@ -133,7 +138,7 @@ typedef struct bsa_plan* bsa_plan_t;
 /* Summary of a plan (all counts exact). */
 typedef struct {
   int32_t layout_heads;      /* 1 or num_heads */
-  int32_t num_blocks;        /* nb = seq_len / block_size */
+  int32_t num_blocks;        /* nb = ceil(seq_len / block_size) */
   int64_t nnz;               /* CSR entries over all layout heads */
   int64_t nnz_partial;       /* of which PARTIAL (token mask applied) */
   int64_t active_blocks;     /* sum over (b, h) of the row lengths: tiles computed per forward */

@@ -161,7 +161,6 @@ def expect_error(status, **over):
 
 def test_invalid_arguments():
     E = bsattn.ERR_INVALID_ARGUMENT
-    expect_error(E, seq_len=1000)                        # not a multiple of the block
     expect_error(E, seq_len=-128)
     expect_error(E, num_heads=3, num_kv_heads=2)
     expect_error(E, num_kv_heads=0)
@@ -234,9 +233,12 @@ def test_empty_rows_have_no_entries():
 
 
 @pytest.mark.parametrize("source,symbol", [
-    ("forward.hip", "_ZN3bsa12_GLOBAL__N_113fwd_bf16_d128ENS0_9FwdParamsEPKi"),
-    ("backward.hip", "_ZN3bsa12_GLOBAL__N_118bwd_dkdv_bf16_d128ENS0_9BwdParamsE"),
-    ("backward.hip", "_ZN3bsa12_GLOBAL__N_116bwd_dq_bf16_d128ENS0_9BwdParamsE")])
+    ("forward.hip", "_ZN3bsa12_GLOBAL__N_113fwd_bf16_d128ILb0EEEvNS0_9FwdParamsEPKi"),
+    ("forward.hip", "_ZN3bsa12_GLOBAL__N_113fwd_bf16_d128ILb1EEEvNS0_9FwdParamsEPKi"),
+    ("backward.hip", "_ZN3bsa12_GLOBAL__N_118bwd_dkdv_bf16_d128ILb0EEEvNS0_9BwdParamsE"),
+    ("backward.hip", "_ZN3bsa12_GLOBAL__N_118bwd_dkdv_bf16_d128ILb1EEEvNS0_9BwdParamsE"),
+    ("backward.hip", "_ZN3bsa12_GLOBAL__N_116bwd_dq_bf16_d128ILb0EEEvNS0_9BwdParamsE"),
+    ("backward.hip", "_ZN3bsa12_GLOBAL__N_116bwd_dq_bf16_d128ILb1EEEvNS0_9BwdParamsE")])
 def test_bf16_kernel_m0_only_set_for_lds_loads(tmp_path, source, symbol):
     """The bf16 forward and dK/dV kernels write M0 in inline assembly right
     before each HBM->LDS load; the compiler treats M0 as reserved and does not
@@ -392,3 +394,36 @@ def test_backward_operand_offset_identities():
                     assert cols_base ^ (64 * dt) == col_read(lane, dt, s)
                 for kc in range(8):         # 16 kc more rows keep the row's swizzle
                     assert tile_swz(4 * hf + r4 + 8 * s + 16 * kc) == tile_swz(4 * hf + r4 + 8 * s)
+
+
+# -------------------------------------------------- ragged lengths (host plans)
+RAGGED_LAYOUTS = [
+    dict(causal=True, unit="tokens", window_left=300, window_right=0, global_keys=5, global_queries=0, bitmap=None),
+    dict(causal=False, unit="tokens", window_left=77, window_right=200, global_keys=0, global_queries=3, bitmap=None),
+    dict(causal=True, unit="blocks", window_left=2, window_right=0, global_keys=1, global_queries=1, bitmap=None),
+    dict(causal=False, unit="blocks", window_left=1, window_right=1, global_keys=0, global_queries=0, bitmap=None),
+]
+
+
+@pytest.mark.parametrize("N", [1, 127, 129, 1000, 4097])
+@pytest.mark.parametrize("li", range(len(RAGGED_LAYOUTS)))
+def test_ragged_plan_matches_oracle(N, li):
+    lay = RAGGED_LAYOUTS[li]
+    for dtype, D, bs in ((torch.bfloat16, 128, 128), (torch.float32, 64, 64)):
+        p = bsattn.plan(1, 2, 1, N, D, bs, dtype, lay, host_only=True)
+        assert p.info["num_blocks"] == -(-N // bs)
+        assert_same_plan(p, oracle.plan(lay, N, bs, brute=N <= 1024))
+        if N <= 1000:
+            assert p.info["allowed_pairs"] == 2 * sum(oracle.allowed_count(lay, N, bs, 0, q) for q in range(N))
+
+
+def test_ragged_bitmap_plan_matches_oracle():
+    N, bs = 1000, 128
+    nb = -(-N // bs)
+    bm = (np.random.default_rng(31).random((2, nb, nb)) < 0.4).astype(np.uint8)
+    for causal in (False, True):
+        lay = spec(causal, "blocks", bitmap=bm)
+        p = bsattn.plan(1, 2, 2, N, 128, bs, torch.bfloat16, lay, host_only=True)
+        assert_same_plan(p, oracle.plan(lay, N, bs, brute=True))
+        total = sum(oracle.allowed_count(lay, N, bs, h, q) for h in range(2) for q in range(N))
+        assert p.info["allowed_pairs"] == total

@@ -156,6 +156,36 @@ def test_backward_split_columns():
         check("dV", dv.float().cpu().numpy(), rv)
 
 
+@pytest.mark.parametrize("N,causal", [(1000, True), (700, False)])
+def test_backward_ragged_length(N, causal):
+    """The block does not divide N: rows beyond N exist nowhere, gradients of
+    the last rows are exact, and nothing is written beyond the last row."""
+    w = wl.WORKLOADS["gqa256k"].with_shape(name=f"ragged{N}", heads=4, kv_heads=1, seq_len=N)
+    lay = dict(causal=causal, unit="tokens", window_left=200, window_right=0 if causal else 90,
+               global_keys=5, global_queries=0 if causal else 2, bitmap=None)
+    q, k, v = wl.make_qkv(w, "cpu")
+    do = wl.make_dout(w, "cpu")
+    p = gpu_plan(w, lay)
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    out, lse = bsattn.forward(qc, kc, vc, p)
+
+    def guarded(shape):
+        n = int(np.prod(shape))
+        buf = torch.full((n + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+        return buf[:n].view(shape), buf[n:]
+    dq, gq = guarded(tuple(q.shape))
+    dk, gk = guarded(tuple(k.shape))
+    dv, gv = guarded(tuple(v.shape))
+    bsattn.backward(qc, kc, vc, out, lse, doc, p, dq, dk, dv)
+    torch.cuda.synchronize()
+    for g in (gq, gk, gv):
+        assert torch.isnan(g).all(), "write beyond the last row"
+    rq, rk, rv = oracle.backward(q, k, v, do, lay, w.block)
+    check("dQ", dq.float().cpu().numpy(), rq)
+    check("dK", dk.float().cpu().numpy(), rk)
+    check("dV", dv.float().cpu().numpy(), rv)
+
+
 # ---------------------------------------------------------- full size, sampled
 FULL_KEYS = {
     # keys away from global blocks (a global key is read by every query of the

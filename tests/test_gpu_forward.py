@@ -328,3 +328,58 @@ def test_forward_rejects_wrong_device_pointers():
     assert st == bsattn.ERR_INVALID_ARGUMENT
     with pytest.raises(ValueError):
         bsattn.forward(q, k, v, p)          # host tensors are refused by the binding
+
+
+# ------------------------------------------- ragged lengths (block does not divide N)
+RAGGED = [
+    (1000, dict(causal=True, unit="tokens", window_left=300, window_right=0, global_keys=5,
+                global_queries=0, bitmap=None)),
+    (129, dict(causal=False, unit="tokens", window_left=-1, window_right=-1, global_keys=0,
+               global_queries=0, bitmap=None)),
+    (4097, dict(causal=True, unit="blocks", window_left=2, window_right=0, global_keys=1,
+                global_queries=1, bitmap=None)),
+    (700, dict(causal=False, unit="tokens", window_left=77, window_right=200, global_keys=0,
+               global_queries=3, bitmap=None)),
+]
+
+
+def guarded(shape, dtype):
+    """A contiguous tensor of `shape` at the start of a NaN-filled buffer with a
+    guard region behind it, to catch writes beyond the last row."""
+    n = int(np.prod(shape))
+    buf = torch.full((n + 4096,), float("nan"), dtype=dtype, device="cuda")
+    return buf[:n].view(shape), buf[n:]
+
+
+@pytest.mark.parametrize("case", range(len(RAGGED)))
+def test_ragged_length_parity_bf16(case):
+    N, lay = RAGGED[case]
+    w = wl.WORKLOADS["gqa256k"].with_shape(name=f"ragged{N}", heads=4, kv_heads=2, seq_len=N)
+    say(f"[ragged] bf16 N={N} {lay}")
+    q, k, v = wl.make_qkv(w, "cpu")
+    p = gpu_plan(w, lay)
+    out, og = guarded((1, 4, N, 128), torch.bfloat16)
+    lse, lg = guarded((1, 4, N), torch.float32)
+    run(p, q.cuda(), k.cuda(), v.cuda(), out, lse)
+    assert torch.isnan(og).all() and torch.isnan(lg).all(), "write beyond the last row"
+    O_ref, L_ref = oracle.forward(q, k, v, lay, w.block)
+    check(out.float().cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref, w.dtype, w.name)
+    # Q = 0: every weight is exactly 1, so exp(LSE) is the exact allowed count.
+    out0, lse0 = run(p, torch.zeros_like(q).cuda(), k.cuda(), v.cuda())
+    cnt = np.array([[oracle.allowed_count(lay, N, 128, h, qq) for qq in range(N)] for h in range(4)])
+    np.testing.assert_array_equal(np.rint(np.exp(lse0[0].double().cpu().numpy())), cnt)
+
+
+def test_ragged_length_parity_f32():
+    N = 1000
+    lay = dict(causal=True, unit="tokens", window_left=150, window_right=0, global_keys=3,
+               global_queries=0, bitmap=None)
+    w = wl.WORKLOADS["tiny_f32"].with_shape(name="ragged-f32", seq_len=N)
+    q, k, v = wl.make_qkv(w, "cpu")
+    p = gpu_plan(w, lay)
+    out, og = guarded((1, 2, N, 64), torch.float32)
+    lse, lg = guarded((1, 2, N), torch.float32)
+    run(p, q.cuda(), k.cuda(), v.cuda(), out, lse)
+    assert torch.isnan(og).all() and torch.isnan(lg).all(), "write beyond the last row"
+    O_ref, L_ref = oracle.forward(q, k, v, lay, w.block)
+    check(out.cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref, w.dtype, w.name)
