@@ -694,8 +694,6 @@ extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v
   if (!plan) return fail(BSA_ERR_INVALID_ARGUMENT, "plan must not be NULL");
   if (!plan->info.on_device)
     return fail(BSA_ERR_INVALID_ARGUMENT, "plan was built by bsa_plan_host and has no device copy");
-  if (plan->dynamic)
-    return fail(BSA_ERR_UNSUPPORTED, "the backward needs a static plan (bsa_plan): dynamic plans have no transposed CSR");
   const bsa_problem_t& pr = plan->prob;
   if (!(pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128))
     return fail(BSA_ERR_UNSUPPORTED, "backward kernels exist for bf16, head_dim 128, block 128 only");

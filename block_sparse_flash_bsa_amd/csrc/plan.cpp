@@ -510,6 +510,15 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
     P->dynamic = 1;
     P->entry_capacity = cap;
     build_work(*P);
+    // dK/dV launch order: every (b, KV head, k-block) walks its whole column
+    // (lengths are only known on the device, so nothing is split).
+    const int64_t kv_items = int64_t(problem->batch) * problem->num_kv_heads * nb;
+    std::vector<int32_t> loc(static_cast<size_t>(kv_items));
+    std::iota(loc.begin(), loc.end(), 0);
+    P->work_kv = loc.empty() ? loc : xcd_slots(loc, [](int64_t) { return int64_t(1); });
+    P->kv_desc.assign(P->work_kv.size(), {-1, 0, 0, -1});
+    for (size_t s = 0; s < P->work_kv.size(); ++s)
+      if (P->work_kv[s] >= 0) P->kv_desc[s] = {P->work_kv[s], 0, INT32_MAX, -1};
   } catch (const std::bad_alloc&) {
     delete P;
     return fail(BSA_ERR_OUT_OF_MEMORY, "host allocation while building the plan failed");
@@ -522,13 +531,17 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
     delete P;
     return fail(BSA_ERR_DEVICE, "hipGetDevice failed: no usable HIP device");
   }
-  // [rows | counts | entries | work], each part 256-byte aligned.
+  // [rows | counts | entries | work | transposed rows | transposed entries |
+  // dK/dV work], each part 256-byte aligned.
   const size_t rows = size_t(P->layout_heads) * P->nb;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t off_counts = up(rows * sizeof(bsa::RowDesc));
   const size_t off_entries = off_counts + up(rows * sizeof(int32_t));
   const size_t off_work = off_entries + up(size_t(cap) * sizeof(int32_t));
-  const size_t bytes = off_work + P->work.size() * sizeof(int32_t) + 16;
+  const size_t off_cols = off_work + up(P->work.size() * sizeof(int32_t));
+  const size_t off_entries_t = off_cols + up(rows * sizeof(bsa::RowDesc));
+  const size_t off_work_kv = off_entries_t + up(size_t(cap) * sizeof(int32_t));
+  const size_t bytes = off_work_kv + P->kv_desc.size() * sizeof(Plan::KvDesc) + 16;
   hipError_t err = hipMalloc(&P->dev_mem, bytes);
   if (err != hipSuccess) {
     P->dev_mem = nullptr;
@@ -537,10 +550,15 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
                 "hipMalloc(%zu) for the dynamic plan failed: %s", bytes, hipGetErrorString(err));
   }
   auto* base = static_cast<unsigned char*>(P->dev_mem);
-  // Empty rows until the first bitmap arrives; the launch order never changes.
+  // Empty rows and columns until the first bitmap arrives; the launch orders
+  // never change.
   err = hipMemset(base, 0, off_counts);
+  if (err == hipSuccess) err = hipMemset(base + off_cols, 0, rows * sizeof(bsa::RowDesc));
   if (err == hipSuccess && !P->work.empty())
     err = hipMemcpy(base + off_work, P->work.data(), P->work.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (err == hipSuccess && !P->kv_desc.empty())
+    err = hipMemcpy(base + off_work_kv, P->kv_desc.data(), P->kv_desc.size() * sizeof(Plan::KvDesc),
+                    hipMemcpyHostToDevice);
   if (err != hipSuccess) {
     (void)hipFree(P->dev_mem);
     delete P;
@@ -550,6 +568,10 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
   P->d_counts = reinterpret_cast<int32_t*>(base + off_counts);
   P->d_entries = reinterpret_cast<const int32_t*>(base + off_entries);
   P->d_work = reinterpret_cast<const int32_t*>(base + off_work);
+  P->d_cols = reinterpret_cast<const bsa::RowDesc*>(base + off_cols);
+  P->d_entries_t = reinterpret_cast<const int32_t*>(base + off_entries_t);
+  P->d_work_kv = reinterpret_cast<const int32_t*>(base + off_work_kv);
+  P->d_kv_reduce = nullptr;
   P->info.on_device = 1;
   *out = P;
   return BSA_OK;
@@ -627,7 +649,7 @@ bsa_status_t bsa_plan_csr_transposed(bsa_plan_t plan, int32_t layout_head, const
   if (!plan || !col_ptr || !row_idx || !flags || !nnz)
     return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "NULL argument to bsa_plan_csr_transposed");
   if (plan->dynamic)
-    return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "dynamic plan: it has no transposed CSR");
+    return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "dynamic plan: its transposed CSR lives on the device");
   if (layout_head < 0 || layout_head >= plan->layout_heads)
     return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "layout_head %d out of range [0, %d)", layout_head,
                      plan->layout_heads);
@@ -642,7 +664,6 @@ bsa_status_t bsa_plan_work_kv(bsa_plan_t plan, const int32_t** work, int64_t* sl
   bsa::clear_error();
   if (!plan || !work || !slots)
     return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "NULL argument to bsa_plan_work_kv");
-  if (plan->dynamic) return bsa::fail(BSA_ERR_INVALID_ARGUMENT, "dynamic plan: it has no dK/dV launch order");
   *work = plan->work_kv.data();
   *slots = int64_t(plan->work_kv.size());
   return BSA_OK;

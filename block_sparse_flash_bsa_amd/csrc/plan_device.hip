@@ -108,6 +108,47 @@ __global__ __launch_bounds__(kRowThreads) void fill_rows(const uint8_t* __restri
   }
 }
 
+// The transposed CSR for the backward: counts[col] = entries of column
+// (layout head * nb + j), i.e. the q-blocks i with bitmap[hl][i][j] != 0 (and
+// i >= j for a causal layout).  The column is read with stride nb.
+__global__ __launch_bounds__(kRowThreads) void count_cols(const uint8_t* __restrict__ bm, int nb, int causal,
+                                                          int32_t* __restrict__ counts) {
+  __shared__ int red[kRowThreads / 64];
+  const int col = blockIdx.x;
+  const int j = col % nb;
+  const uint8_t* c0 = bm + size_t(col / nb) * nb * nb + j;
+  int c = 0;
+  for (int i = (causal ? j : 0) + threadIdx.x; i < nb; i += kRowThreads) c += c0[size_t(i) * nb] != 0;
+  const int total = block_sum(c, red);
+  if (threadIdx.x == 0) counts[col] = total;
+}
+
+// The entries of each column, ascending in i: entry = (i << 1) | partial.
+__global__ __launch_bounds__(kRowThreads) void fill_cols(const uint8_t* __restrict__ bm, int nb, int causal,
+                                                         const RowDesc* __restrict__ cols,
+                                                         int32_t* __restrict__ entries) {
+  __shared__ int wsum[kRowThreads / 64];
+  const int col = blockIdx.x;
+  const int j = col % nb;
+  const uint8_t* c0 = bm + size_t(col / nb) * nb * nb + j;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int32_t* out = entries + cols[col].start;
+  int base = 0;
+  for (int i0 = causal ? j : 0; i0 < nb; i0 += kRowThreads) {
+    const int i = i0 + threadIdx.x;
+    const bool on = i < nb && c0[size_t(i) * nb] != 0;
+    const uint64_t m = __ballot(on);
+    const int below = __popcll(m & ((uint64_t(1) << lane) - 1));
+    if (lane == 0) wsum[wave] = __popcll(m);
+    __syncthreads();
+    int off = base;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    if (on) out[off + below] = (i << 1) | ((causal && i == j) ? 1 : 0);
+    base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
+    __syncthreads();
+  }
+}
+
 }  // namespace
 }  // namespace bsa
 
@@ -143,6 +184,14 @@ extern "C" bsa_status_t bsa_plan_set_bitmap(bsa_plan_t plan, const uint8_t* d_bi
   hipLaunchKernelGGL(scan_rows, dim3(1), dim3(kScanThreads), 0, s, plan->d_counts, rows, d_rows, d_nnz);
   hipLaunchKernelGGL(fill_rows, dim3(unsigned(rows)), dim3(kRowThreads), 0, s, d_bitmap, nb, plan->causal,
                      d_rows, d_entries);
+  // The same entries per k-block column, for the backward's dK/dV walk.
+  auto* d_cols = const_cast<RowDesc*>(plan->d_cols);
+  auto* d_entries_t = const_cast<int32_t*>(plan->d_entries_t);
+  hipLaunchKernelGGL(count_cols, dim3(unsigned(rows)), dim3(kRowThreads), 0, s, d_bitmap, nb, plan->causal,
+                     plan->d_counts);
+  hipLaunchKernelGGL(scan_rows, dim3(1), dim3(kScanThreads), 0, s, plan->d_counts, rows, d_cols, nullptr);
+  hipLaunchKernelGGL(fill_cols, dim3(unsigned(rows)), dim3(kRowThreads), 0, s, d_bitmap, nb, plan->causal,
+                     d_cols, d_entries_t);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(BSA_ERR_DEVICE, "planner launch failed: %s", hipGetErrorString(err));
   return BSA_OK;

@@ -213,7 +213,8 @@ int64_t bsa_plan_active_blocks(bsa_plan_t plan);
  * four-byte entries, nb * (nb + 1) / 2 per head when causal) together with a
  * fixed launch order of every (b, h, q-block) item, locality runs per XCD as
  * in BSA_SCHEDULE_XCD but with equal item counts (row lengths are not known
- * on the host).  The CSR starts empty: until the first bsa_plan_set_bitmap a
+ * on the host), and the same for the backward's transposed lists and its
+ * (b, KV head, k-block) items.  The CSR starts empty: until the first bsa_plan_set_bitmap a
  * forward writes O = 0 and LSE = -inf.  Count fields of bsa_plan_info_t that
  * depend on the bitmap (nnz, nnz_partial, active_blocks, allowed_pairs,
  * max_row_entries) are -1 and bsa_plan_active_blocks returns -1;
@@ -226,7 +227,8 @@ bsa_status_t bsa_plan_dynamic(const bsa_problem_t* problem, const bsa_layout_t* 
 /* Rebuild a dynamic plan's device CSR from d_bitmap, device memory holding
  * [bitmap_heads][nb][nb] bytes (nonzero = active), asynchronously on `stream`
  * (a hipStream_t; NULL = default stream): three kernels count each row, scan
- * the counts and write the ascending entries.  A later bsa_forward on the
+ * the counts and write the ascending entries, and three more do the same per
+ * k-block column (the transposed lists bsa_backward walks).  A later bsa_forward on the
  * same stream (or after synchronisation) uses the new CSR.  If d_nnz is not
  * NULL it is a device pointer to one int64_t that receives the total number
  * of entries over all layout heads (multiply by batch, and by num_heads when
@@ -297,7 +299,8 @@ bsa_status_t bsa_plan_csr_transposed(bsa_plan_t plan, int32_t layout_head, const
  * is longer than twice the mean, such as the k-block of a global key, is cut
  * into chunks that occupy several slots; their float32 partial sums live in
  * plan-owned device scratch and a reduction kernel adds them in chunk order.
- * Plan-owned.  Errors: INVALID_ARGUMENT for NULL pointers or a dynamic plan. */
+ * Dynamic plans never split (their column lengths live on the device).
+ * Plan-owned.  Errors: INVALID_ARGUMENT for NULL pointers. */
 bsa_status_t bsa_plan_work_kv(bsa_plan_t plan, const int32_t** work, int64_t* slots);
 
 /* Run the backward pass asynchronously on `stream` (a hipStream_t; NULL =
@@ -318,8 +321,8 @@ bsa_status_t bsa_plan_work_kv(bsa_plan_t plan, const int32_t** work, int64_t* sl
  * element of dq, dk, dv and delta is written (zero rows where nothing
  * attends).  Outputs must not alias inputs or each other.  Nothing is
  * allocated or freed.
- * Supported: static plans (bsa_plan) with dtype BSA_BF16, head_dim 128,
- * block 128; otherwise UNSUPPORTED (dynamic plans, float32).
+ * Supported: plans (static or dynamic) with dtype BSA_BF16, head_dim 128,
+ * block 128; otherwise UNSUPPORTED (float32).
  * Errors (before anything is launched): INVALID_ARGUMENT for NULL pointers, a
  * host-only plan or a plan made on another device; UNSUPPORTED as above;
  * DEVICE if a launch fails.  A problem with no work items returns BSA_OK. */

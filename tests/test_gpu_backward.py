@@ -270,6 +270,31 @@ def test_backward_deterministic_and_overwrites():
     assert not torch.isnan(delta).any()
 
 
+def test_backward_custom_scale_stream_and_empty_problems():
+    """A non-default scale (enters P and the scale of dQ, dK), a non-default
+    stream, and problems with no work items (returns at once)."""
+    w = wl.WORKLOADS["window16k"].with_shape(name="scale", heads=2, kv_heads=2, seq_len=1024)
+    lay = wl.layout_of(w)
+    q, k, v = wl.make_qkv(w, "cpu")
+    do = wl.make_dout(w, "cpu")
+    p = gpu_plan(w, lay, scale=0.05)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+        out, lse = bsattn.forward(qc, kc, vc, p)
+        dq, dk, dv = bsattn.backward(qc, kc, vc, out, lse, doc, p)
+    stream.synchronize()
+    rq, rk, rv = oracle.backward(q, k, v, do, lay, w.block, scale=0.05)
+    check("dQ", dq.float().cpu().numpy(), rq)
+    check("dK", dk.float().cpu().numpy(), rk)
+    check("dV", dv.float().cpu().numpy(), rv)
+    for B, N in ((0, 1024), (1, 0)):
+        pe = bsattn.plan(B, 2, 2, N, 128, 128, torch.bfloat16, lay)
+        z = torch.empty((B, 2, N, 128), dtype=torch.bfloat16, device="cuda")
+        l0 = torch.empty((B, 2, N), dtype=torch.float32, device="cuda")
+        bsattn.backward(z, z, z, z, l0, z, pe)
+
+
 def test_backward_unsupported_plans():
     w = wl.WORKLOADS["tiny_f32"]
     lay = wl.layout_of(w)
@@ -279,11 +304,31 @@ def test_backward_unsupported_plans():
     with pytest.raises(bsattn.BsaError) as ei:
         bsattn.backward(q, k, v, out, lse, torch.zeros_like(q), p)
     assert ei.value.status == bsattn.ERR_UNSUPPORTED
-    wd = SMALL["random32k"]
-    pd = bsattn.plan_dynamic(wd.batch, wd.heads, wd.kv_heads, wd.seq_len, wd.head_dim, wd.block, wd.dtype,
-                             causal=False, bitmap_heads=wd.heads)
-    q, k, v = (x.cuda() for x in wl.make_qkv(wd, "cpu"))
-    out, lse = bsattn.forward(q, k, v, pd)
-    with pytest.raises(bsattn.BsaError) as ei:
-        bsattn.backward(q, k, v, out, lse, torch.zeros_like(q), pd)
-    assert ei.value.status == bsattn.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_through_dynamic_plan(causal):
+    """A dynamic plan builds the transposed lists on the device; its backward
+    equals the static plan's of the same bitmap bit for bit (no walk is split
+    at this density) and the oracle within tolerance."""
+    w = SMALL["random32k"]
+    lay = wl.layout_of(w)
+    lay["causal"] = causal
+    bm = lay["bitmap"].to(torch.uint8)
+    q, k, v = wl.make_qkv(w, "cpu")
+    do = wl.make_dout(w, "cpu")
+    ps = gpu_plan(w, lay)
+    work = ps.work_kv()
+    assert len(work[work >= 0]) == len(np.unique(work[work >= 0]))
+    pd = bsattn.plan_dynamic(w.batch, w.heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.dtype,
+                             causal=causal, bitmap_heads=w.heads)
+    pd.set_bitmap(bm.cuda().contiguous())
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    gs = fwd_bwd(ps, qc, kc, vc, doc)
+    gd = fwd_bwd(pd, qc, kc, vc, doc)
+    for a, b_ in zip(gs, gd):
+        assert torch.equal(a, b_)
+    rq, rk, rv = oracle.backward(q, k, v, do, lay, w.block)
+    check("dQ", gd[0].float().cpu().numpy(), rq)
+    check("dK", gd[1].float().cpu().numpy(), rk)
+    check("dV", gd[2].float().cpu().numpy(), rv)
