@@ -383,16 +383,21 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
             sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[m & 3], qf[m >> 1], sc, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
-        // Register r holds key 32st + 8 (r / 4) + 4 hf + r % 4 of block j, for query qg.
+        // Register r holds key 32st + 8 (r / 4) + 4 hf + r % 4 of block j, for
+        // query qg.  The token mask runs only in PARTIAL tiles (the empty asm
+        // keeps the branch a real, wave-uniform one).
+        if (partial) {
+          __asm__ volatile("");
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int kk = j * kB + st * kStepRows + 8 * (r >> 2) + 4 * hf + (r & 3);
+            sc[r] = pair_ok(p, qg, kk) ? sc[r] : -INFINITY;
+          }
+        }
         bf16x8 ds[2];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float x = sc[r];
-          if (partial) {
-            const int kk = j * kB + st * kStepRows + 8 * (r >> 2) + 4 * hf + (r & 3);
-            if (!pair_ok(p, qg, kk)) x = -INFINITY;
-          }
-          const float pr = __builtin_amdgcn_exp2f(fmaf(x, p.sl2, -lse2));
+          const float pr = __builtin_amdgcn_exp2f(fmaf(sc[r], p.sl2, -lse2));
           ds[r >> 3][r & 7] = static_cast<__bf16>(pr * (dp[r] - dlt));
         }
         // dQ^T += K^T dS^T: key chunk m >> 2 of the step, d-tile m & 3.
@@ -554,7 +559,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
         lds_u8* const Qs = Qb[bf];
         lds_u8* const dOs = dOb[bf];
         BSA_WAIT_BARRIER(0);                           // this step's rows landed; the other buffer is free
-        my[lane] = x;                                  // this step's LSE (lanes < 32) and Delta
+        // This step's LSE (lanes < 32, as LSE * log2 e, 0 for an empty row:
+        // every score of such a row is masked in this tile) and Delta.
+        my[lane] = lane < 32 ? (x == -INFINITY ? 0.f : x * kLog2e) : x;
         uint32_t bq = bq0, bv = bv0, bcl = bcl0, bch = bch0;
         __asm__ volatile("" : "+v"(bq), "+v"(bv), "+v"(bcl), "+v"(bch));
         const bool pf = st < 3 || have_next;
@@ -586,8 +593,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
             s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ab[m & 3], kf[m >> 1], s, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
         }
-        // Register r holds query 32st + 8 (r / 4) + 4 hf + r % 4 of q-block cur.i, for key kg.
+        // Register r holds query 32st + 8 (r / 4) + 4 hf + r % 4 of q-block
+        // cur.i, for key kg.  The token mask runs only in PARTIAL tiles.
         const int qbase = cur.i * kB + st * kStepRows;
+        if (cur.partial) {
+          __asm__ volatile("");
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[r] = pair_ok(p, qbase + 8 * (r >> 2) + 4 * hf + (r & 3), kg) ? s[r] : -INFINITY;
+        }
         bf16x8 pb[2], db[2];
 #pragma unroll
         for (int g4 = 0; g4 < 4; ++g4) {
@@ -597,11 +611,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
 #pragma unroll
           for (int r3 = 0; r3 < 4; ++r3) {
             const int r = 4 * g4 + r3;
-            float xs = s[r];
-            if (cur.partial && !pair_ok(p, qbase + q0 + r3, kg)) xs = -INFINITY;
-            // An empty row (LSE = -inf) has every score masked in this tile.
-            const float l2 = L[r3] == -INFINITY ? 0.f : L[r3] * kLog2e;
-            const float pr = __builtin_amdgcn_exp2f(fmaf(xs, p.sl2, -l2));
+            const float pr = __builtin_amdgcn_exp2f(fmaf(s[r], p.sl2, -L[r3]));
             pb[r >> 3][r & 7] = static_cast<__bf16>(pr);
             db[r >> 3][r & 7] = static_cast<__bf16>(pr * (dp[r] - Dl[r3]));
           }
