@@ -1,13 +1,15 @@
 """ctypes binding over libbsattn (include/bsattn.h).
 
-Argument marshalling only: every step of the forward runs in the library's
-HIP kernels; PyTorch provides device memory and the current stream.
+Argument marshalling only: every step of the forward and backward runs in
+the library's HIP kernels; PyTorch provides device memory and the current
+stream.
 
     p = plan(batch=1, num_heads=32, num_kv_heads=32, seq_len=16384, head_dim=128,
              block_size=128, dtype=torch.bfloat16,
              layout=dict(causal=True, unit="tokens", window_left=511, window_right=0,
                          global_keys=0, global_queries=0, bitmap=None))
     out, lse = forward(q, k, v, p)
+    dq, dk, dv = backward(q, k, v, out, lse, dout, p)
 
 The library is loaded on first use; if it has not been built the call raises
 (there is no fallback path).

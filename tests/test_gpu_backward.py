@@ -156,6 +156,38 @@ def test_backward_split_columns():
         check("dV", dv.float().cpu().numpy(), rv)
 
 
+def test_backward_ragged_split_last_column():
+    """A split walk on the short last block of a ragged sequence: the
+    reduction writes only the rows below N of that block."""
+    N = 4000                                      # 32 blocks, the last with 32 rows
+    w = wl.WORKLOADS["gqa256k"].with_shape(name="ragged-split", heads=4, kv_heads=1, seq_len=N)
+    nb = -(-N // 128)
+    rng = np.random.default_rng(7)
+    bm = rng.random((4, nb, nb)) < 0.05
+    bm[:, :, nb - 1] = True                       # every q-block reads the short last block
+    bm[:, np.arange(nb), np.arange(nb)] = True
+    lay = dict(causal=False, unit="blocks", window_left=-1, window_right=-1, global_keys=0,
+               global_queries=0, bitmap=torch.from_numpy(bm))
+    p = gpu_plan(w, lay)
+    work = p.work_kv()
+    assert np.sum(work == nb - 1) > 1, "expected the last column's walk to be split"
+    q, k, v = wl.make_qkv(w, "cpu")
+    do = wl.make_dout(w, "cpu")
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    out, lse = bsattn.forward(qc, kc, vc, p)
+    n = int(np.prod(k.shape))
+    bufk = torch.full((n + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    bufv = torch.full((n + 4096,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    dk, dv = bufk[:n].view(k.shape), bufv[:n].view(v.shape)
+    dq, _, _ = bsattn.backward(qc, kc, vc, out, lse, doc, p, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert torch.isnan(bufk[n:]).all() and torch.isnan(bufv[n:]).all(), "write beyond the last row"
+    rq, rk, rv = oracle.backward(q, k, v, do, lay, w.block)
+    check("dQ", dq.float().cpu().numpy(), rq)
+    check("dK", dk.float().cpu().numpy(), rk)
+    check("dV", dv.float().cpu().numpy(), rv)
+
+
 @pytest.mark.parametrize("N,causal", [(1000, True), (700, False)])
 def test_backward_ragged_length(N, causal):
     """The block does not divide N: rows beyond N exist nowhere, gradients of
