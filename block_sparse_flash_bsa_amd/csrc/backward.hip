@@ -693,6 +693,238 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_reduce(BwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// float32 backward (head_dim 64 | 128, block 64 | 128): exact fp32 FMAs on the
+// VALU, for fp32 inputs (the exact-precision path; small problems).  As in the
+// fp32 forward, 4 consecutive lanes share one row, each holding a quarter of
+// the head dimension, and a dot product is their partial sums combined by two
+// butterfly exchanges.  dQ: one workgroup per (b, h, q-block) over its CSR
+// row, K and V staged through LDS in stages of up to 64 keys.  dK/dV: one
+// workgroup per (b, KV head, k-block) over its transposed lists (whole walks;
+// the fp32 path does not split them), Q, dO, LSE and Delta staged likewise.
+// ---------------------------------------------------------------------------
+constexpr int kF32Lanes = 4;
+
+__device__ __forceinline__ float quad_sum(float a) {
+#pragma unroll
+  for (int w = 1; w < kF32Lanes; w *= 2) a += __shfl_xor(a, w);
+  return a;
+}
+
+// Delta_q = <dO_q, O_q> for float32 rows of D values, 16 lanes per row.
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_delta_f32(const float* __restrict__ o, const float* __restrict__ dout,
+                                                        float* __restrict__ delta, int64_t rows) {
+  const int64_t row = int64_t(blockIdx.x) * (kThreads / 16) + (threadIdx.x >> 4);
+  const int c = threadIdx.x & 15;
+  float s = 0.f;
+  if (row < rows) {
+#pragma unroll
+    for (int d = c; d < D; d += 16) s = fmaf(o[row * D + d], dout[row * D + d], s);
+  }
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+  if (c == 0 && row < rows) delta[row] = s;
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(BS * kF32Lanes) void bwd_dq_f32(BwdParams p) {
+  constexpr int KT = BS < 64 ? BS : 64;  // keys per LDS stage
+  constexpr int DL = D / kF32Lanes;      // head-dimension slice per lane
+  constexpr int NT = BS * kF32Lanes;     // threads
+  extern __shared__ float smem[];
+  float* Ks = smem;                      // [KT][D]
+  float* Vs = Ks + KT * D;               // [KT][D]
+
+  const int item = p.work[blockIdx.x];
+  if (item < 0) return;
+  const int i = item % p.nb;
+  const int bh = item / p.nb;
+  const int h = bh % p.H, b = bh / p.H;
+  const int hk = h / p.group;
+  const RowDesc row = p.rows[(p.per_head_layout ? h : 0) * p.nb + i];
+  const int t = threadIdx.x;
+  const int r = t / kF32Lanes, sl = t % kF32Lanes;
+  const int qg = i * BS + r;
+  const int64_t hb = (int64_t(b) * p.H + h) * p.N;
+  const int64_t qld = hb + (qg < p.N ? qg : p.N - 1);     // rows beyond a ragged end load row N - 1
+  const float* fq = reinterpret_cast<const float*>(p.q);
+  const float* fdo = reinterpret_cast<const float*>(p.dout);
+  const float* Kb = reinterpret_cast<const float*>(p.k) + (int64_t(b) * p.Hkv + hk) * p.N * D;
+  const float* Vb = reinterpret_cast<const float*>(p.v) + (int64_t(b) * p.Hkv + hk) * p.N * D;
+  float qv[DL], dov[DL], acc[DL];
+#pragma unroll
+  for (int d = 0; d < DL; ++d) {
+    qv[d] = fq[qld * D + sl * DL + d];
+    dov[d] = fdo[qld * D + sl * DL + d];
+    acc[d] = 0.f;
+  }
+  const float lse = p.lse[qld];
+  const float lse2 = lse == -INFINITY ? 0.f : lse * kLog2e;   // empty rows: every score is masked
+  const float dlt = p.delta[qld];
+
+  for (int e = 0; e < row.count; ++e) {
+    const int ent = p.entries[row.start + e];
+    const int j = ent >> 1;
+    const bool partial = ent & 1;
+    for (int st = 0; st < BS / KT; ++st) {
+      const int k0 = j * BS + st * KT;
+      __syncthreads();
+      for (int x = t; x < KT * D / 4; x += NT) {
+        const int64_t kr = k0 + x / (D / 4) < p.N ? k0 + x / (D / 4) : p.N - 1;
+        const int64_t src = kr * D + (x % (D / 4)) * 4;
+        reinterpret_cast<float4*>(Ks)[x] = *reinterpret_cast<const float4*>(Kb + src);
+        reinterpret_cast<float4*>(Vs)[x] = *reinterpret_cast<const float4*>(Vb + src);
+      }
+      __syncthreads();
+      for (int kk = 0; kk < KT; ++kk) {
+        const float* kr = Ks + kk * D + sl * DL;
+        const float* vr = Vs + kk * D + sl * DL;
+        float a = 0.f, c = 0.f;
+#pragma unroll
+        for (int d = 0; d < DL; ++d) {
+          a = fmaf(qv[d], kr[d], a);
+          c = fmaf(dov[d], vr[d], c);
+        }
+        a = quad_sum(a);
+        c = quad_sum(c);
+        const float pr = (partial && !pair_ok(p, qg, k0 + kk)) ? 0.f : __builtin_amdgcn_exp2f(fmaf(a, p.sl2, -lse2));
+        const float ds = pr * (c - dlt);
+#pragma unroll
+        for (int d = 0; d < DL; ++d) acc[d] = fmaf(ds, kr[d], acc[d]);
+      }
+    }
+  }
+  if (qg >= p.N) return;
+  float* dq = reinterpret_cast<float*>(p.dq) + (hb + qg) * D + sl * DL;
+#pragma unroll
+  for (int d = 0; d < DL; ++d) dq[d] = acc[d] * p.scale;
+}
+
+template <int D, int BS>
+__global__ __launch_bounds__(BS * kF32Lanes) void bwd_dkdv_f32(BwdParams p) {
+  constexpr int QT = BS < 64 ? BS : 64;  // queries per LDS stage
+  constexpr int DL = D / kF32Lanes;
+  constexpr int NT = BS * kF32Lanes;
+  extern __shared__ float smem[];
+  float* Qs = smem;                      // [QT][D]
+  float* dOs = Qs + QT * D;              // [QT][D]
+  float* Ls = dOs + QT * D;              // [QT] LSE * log2(e) (0 for empty rows)
+  float* Dls = Ls + QT;                  // [QT] Delta
+
+  const int item = blockIdx.x;           // (b * Hkv + hk) * nb + j, every item once
+  const int j = item % p.nb;
+  const int bk = item / p.nb;
+  const int hk = bk % p.Hkv, b = bk / p.Hkv;
+  const int t = threadIdx.x;
+  const int r = t / kF32Lanes, sl = t % kF32Lanes;
+  const int kg = j * BS + r;
+  const int64_t kvb = (int64_t(b) * p.Hkv + hk) * p.N;
+  const int64_t kld = kvb + (kg < p.N ? kg : p.N - 1);
+  const float* fk = reinterpret_cast<const float*>(p.k);
+  const float* fv = reinterpret_cast<const float*>(p.v);
+  float kv[DL], vv[DL], dk[DL], dv[DL];
+#pragma unroll
+  for (int d = 0; d < DL; ++d) {
+    kv[d] = fk[kld * D + sl * DL + d];
+    vv[d] = fv[kld * D + sl * DL + d];
+    dk[d] = 0.f;
+    dv[d] = 0.f;
+  }
+  for (int g = 0; g < p.group; ++g) {
+    const int h = hk * p.group + g;
+    const RowDesc col = p.cols[(p.per_head_layout ? h : 0) * p.nb + j];
+    const int64_t hb = (int64_t(b) * p.H + h) * p.N;
+    const float* Qb = reinterpret_cast<const float*>(p.q) + hb * D;
+    const float* dOb = reinterpret_cast<const float*>(p.dout) + hb * D;
+    for (int e = 0; e < col.count; ++e) {
+      const int ent = p.entries_t[col.start + e];
+      const int i = ent >> 1;
+      const bool partial = ent & 1;
+      for (int st = 0; st < BS / QT; ++st) {
+        const int q0 = i * BS + st * QT;
+        __syncthreads();
+        for (int x = t; x < QT * D / 4; x += NT) {
+          const int64_t qr = q0 + x / (D / 4) < p.N ? q0 + x / (D / 4) : p.N - 1;
+          const int64_t src = qr * D + (x % (D / 4)) * 4;
+          reinterpret_cast<float4*>(Qs)[x] = *reinterpret_cast<const float4*>(Qb + src);
+          reinterpret_cast<float4*>(dOs)[x] = *reinterpret_cast<const float4*>(dOb + src);
+        }
+        for (int x = t; x < QT; x += NT) {
+          const int64_t qr = hb + (q0 + x < p.N ? q0 + x : p.N - 1);
+          const float l = p.lse[qr];
+          Ls[x] = l == -INFINITY ? 0.f : l * kLog2e;
+          Dls[x] = p.delta[qr];
+        }
+        __syncthreads();
+        for (int qq = 0; qq < QT; ++qq) {
+          const float* qr = Qs + qq * D + sl * DL;
+          const float* dr = dOs + qq * D + sl * DL;
+          float a = 0.f, c = 0.f;
+#pragma unroll
+          for (int d = 0; d < DL; ++d) {
+            a = fmaf(qr[d], kv[d], a);
+            c = fmaf(dr[d], vv[d], c);
+          }
+          a = quad_sum(a);
+          c = quad_sum(c);
+          const float pr =
+              (partial && !pair_ok(p, q0 + qq, kg)) ? 0.f : __builtin_amdgcn_exp2f(fmaf(a, p.sl2, -Ls[qq]));
+          const float ds = pr * (c - Dls[qq]);
+#pragma unroll
+          for (int d = 0; d < DL; ++d) {
+            dv[d] = fmaf(pr, dr[d], dv[d]);
+            dk[d] = fmaf(ds, qr[d], dk[d]);
+          }
+        }
+      }
+    }
+  }
+  if (kg >= p.N) return;
+  float* dkp = reinterpret_cast<float*>(p.dk) + (kvb + kg) * D + sl * DL;
+  float* dvp = reinterpret_cast<float*>(p.dv) + (kvb + kg) * D + sl * DL;
+#pragma unroll
+  for (int d = 0; d < DL; ++d) {
+    dkp[d] = dk[d] * p.scale;
+    dvp[d] = dv[d];
+  }
+}
+
+template <int D, int BS>
+hipError_t launch_f32_backward(const BwdParams& prm, const Plan& plan, hipStream_t s) {
+  constexpr int T = (BS < 64 ? BS : 64);
+  constexpr size_t smem_dq = size_t(2 * T * D) * sizeof(float);
+  constexpr size_t smem_kv = size_t(2 * T * D + 2 * T) * sizeof(float);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_f32<D, BS>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem_dq));
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_f32<D, BS>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, int(smem_kv));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const bsa_problem_t& pr = plan.prob;
+  const int64_t rows = int64_t(pr.batch) * pr.num_heads * pr.seq_len;
+  const int64_t rows_per_block = kThreads / 16;
+  hipLaunchKernelGGL(bwd_delta_f32<D>, dim3(unsigned((rows + rows_per_block - 1) / rows_per_block)), dim3(kThreads),
+                     0, s, static_cast<const float*>(static_cast<const void*>(prm.o)),
+                     static_cast<const float*>(static_cast<const void*>(prm.dout)), prm.delta, rows);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL((bwd_dq_f32<D, BS>), dim3(unsigned(plan.info.launch_slots)), dim3(BS * kF32Lanes), smem_dq, s,
+                     prm);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int64_t kv_items = int64_t(pr.batch) * pr.num_kv_heads * plan.nb;
+  if (kv_items > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_f32<D, BS>), dim3(unsigned(kv_items)), dim3(BS * kF32Lanes), smem_kv, s, prm);
+    err = hipGetLastError();
+  }
+  return err;
+}
+
 }  // namespace
 }  // namespace bsa
 
@@ -705,10 +937,13 @@ extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v
   if (!plan->info.on_device)
     return fail(BSA_ERR_INVALID_ARGUMENT, "plan was built by bsa_plan_host and has no device copy");
   const bsa_problem_t& pr = plan->prob;
-  if (!(pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128))
-    return fail(BSA_ERR_UNSUPPORTED, "backward kernels exist for bf16, head_dim 128, block 128 only");
+  const bool bf16 = pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128;
+  const bool f32 = pr.dtype == BSA_F32 && (pr.head_dim == 64 || pr.head_dim == 128) &&
+                   (pr.block_size == 64 || pr.block_size == 128);
+  if (!bf16 && !f32)
+    return fail(BSA_ERR_UNSUPPORTED, "no backward kernel for this (dtype, head_dim, block_size)");
   if (plan->info.work_items == 0) return BSA_OK;
-  if (plan->kv_partials > 0 && !plan->d_kv_scratch)
+  if (bf16 && plan->kv_partials > 0 && !plan->d_kv_scratch)
     return fail(BSA_ERR_DEVICE, "plan has split dK/dV columns but no partial-sum scratch");
   if (!q || !k || !v || !out || !lse || !dout || !dq || !dk || !dv || !delta)
     return fail(BSA_ERR_INVALID_ARGUMENT, "q, k, v, out, lse, dout, dq, dk, dv and delta must all be non-NULL");
@@ -765,6 +1000,15 @@ extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v
     prm.mspan = uint32_t(hi - lo);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (f32) {
+    hipError_t e = hipSuccess;
+    if (pr.head_dim == 64 && pr.block_size == 64) e = launch_f32_backward<64, 64>(prm, *plan, s);
+    else if (pr.head_dim == 64) e = launch_f32_backward<64, 128>(prm, *plan, s);
+    else if (pr.block_size == 64) e = launch_f32_backward<128, 64>(prm, *plan, s);
+    else e = launch_f32_backward<128, 128>(prm, *plan, s);
+    if (e != hipSuccess) return fail(BSA_ERR_DEVICE, "backward kernel launch failed: %s", hipGetErrorString(e));
+    return BSA_OK;
+  }
   const bool ragged = pr.seq_len % kB != 0;
   const int64_t rows = int64_t(pr.batch) * pr.num_heads * pr.seq_len;
   const int64_t rows_per_block = kThreads / 16;

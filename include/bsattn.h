@@ -308,8 +308,8 @@ bsa_status_t bsa_plan_work_kv(bsa_plan_t plan, const int32_t** work, int64_t* sl
  *   q, k, v : the forward's inputs (layouts as in bsa_forward)
  *   out, lse: the forward's outputs for exactly these inputs and this plan
  *   dout    : device, [batch][num_heads][seq_len][head_dim], dtype: dLoss/dO
- *   dq      : device, like q;   dk, dv: device, like k and v (dtype, bf16
- *             rounded to nearest even from float32 accumulators)
+ *   dq      : device, like q;   dk, dv: device, like k and v (dtype; bf16
+ *             is rounded to nearest even from float32 accumulators)
  *   delta   : device, float32 [batch][num_heads][seq_len]: caller-owned
  *             workspace; receives Delta_q = <dO_q, O_q> (computed from the
  *             rounded out), which the dK/dV kernel reads
@@ -321,8 +321,10 @@ bsa_status_t bsa_plan_work_kv(bsa_plan_t plan, const int32_t** work, int64_t* sl
  * element of dq, dk, dv and delta is written (zero rows where nothing
  * attends).  Outputs must not alias inputs or each other.  Nothing is
  * allocated or freed.
- * Supported: plans (static or dynamic) with dtype BSA_BF16, head_dim 128,
- * block 128; otherwise UNSUPPORTED (float32).
+ * Supported: every (dtype, head_dim, block_size) bsa_plan accepts, static or
+ * dynamic: BSA_BF16 (128, 128) on MFMA; BSA_F32 (64 | 128, 64 | 128) with
+ * exact fp32 FMAs (outputs float32; the fp32 path walks long k-block lists
+ * whole instead of splitting them).
  * Errors (before anything is launched): INVALID_ARGUMENT for NULL pointers, a
  * host-only plan or a plan made on another device; UNSUPPORTED as above;
  * DEVICE if a launch fails.  A problem with no work items returns BSA_OK. */
