@@ -228,11 +228,12 @@ def time_backward(p, q, k, v, out, lse, do, steps, warmup):
 
 
 def backward_context(names, steps=5):
-    """bsa_backward on the bf16 workloads: ms per backward (Delta, dQ and dK/dV
+    """bsa_backward on the workloads: ms per backward (Delta, dQ and dK/dV
     kernels), TFLOP/s counting the five GEMMs of an attention backward per
     active tile (S recomputed, dP, dV, dK, dQ: 10 * block^2 * head_dim, the
-    usual 2.5x of the forward) and the seven the kernels execute (S and dP
-    are formed in both the dQ and the dK/dV kernel)."""
+    usual 2.5x of the forward) against the dtype's peak, and the seven the
+    kernels execute (S and dP are formed in both the dQ and the dK/dV
+    kernel)."""
     res = {}
     for name in names:
         w = wl.WORKLOADS[name]
@@ -244,8 +245,9 @@ def backward_context(names, steps=5):
         tiles = p.info["active_blocks"]
         unit = w.block * w.block * w.head_dim
         alg = 10.0 * unit * tiles / (ms * 1e-3) / 1e12
+        peak = PEAK_BF16_TFLOPS if w.dtype == torch.bfloat16 else PEAK_F32_TFLOPS
         res[name] = {"ms_per_backward": round(ms, 3), "tflops_algorithmic": round(alg, 1),
-                     "pct_of_peak": round(100 * alg / PEAK_BF16_TFLOPS, 2),
+                     "pct_of_peak": round(100 * alg / peak, 2),
                      "tflops_mfma_executed": round(1.4 * alg, 1), "active_tiles": tiles}
         log(f"[bench] backward {name}: {res[name]}")
         del q, k, v, do, out, lse, p
@@ -361,7 +363,7 @@ def main():
         del q, k, v, out, lse
         torch.cuda.empty_cache()
         ctx["dynamic_plan"] = dynamic_plan_context()
-        ctx["backward"] = backward_context(["window16k", "random32k", "winglobal128k", "gqa256k"])
+        ctx["backward"] = backward_context(["tiny_f32", "window16k", "random32k", "winglobal128k", "gqa256k"])
         result["context"] = ctx
     if not args.no_cpu_baseline:
         if not args.no_context:      # the context runs replaced the inputs
