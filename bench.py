@@ -327,6 +327,11 @@ def main():
                    "layout": {k_: v_ for k_, v_ in w.layout.items() if k_ != "bitmap"},
                    "active_tiles": p.info["active_blocks"], "schedule": args.schedule},
         "pct_of_mfma_peak": round(100 * value / peak, 2),
+        # Kernel-event percentiles over the timed launches, and the rate that
+        # counts only allowed (q, k) pairs (4 * head_dim FLOPs each) instead
+        # of whole tiles.
+        "kernel_ms_p10_p50_p90": [round(float(x), 4) for x in np.percentile(ev_ms, [10, 50, 90])],
+        "token_exact_tflops": round(4.0 * w.head_dim * p.info["allowed_pairs"] / (kern_ms * 1e-3) / 1e12, 2),
         "plan_ms": round(plan_ms, 2),
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4),

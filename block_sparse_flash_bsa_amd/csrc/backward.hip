@@ -14,7 +14,7 @@
 // and never stores a score matrix: every tile's scores are recomputed from Q
 // and K and turned into weights with the saved LSE.
 //
-// Three kernels:
+// Kernels:
 //   bwd_delta_bf16     Delta_q per row (HBM-bound, 16 lanes per row).
 //   bwd_dq_bf16_d128   one workgroup per (b, h, q-block), walking the
 //                      forward's CSR row: S^T and dP^T = V dO^T on MFMA,
@@ -23,6 +23,7 @@
 //                      transposed CSR over every query head of the GQA group:
 //                      S and dP = dO V^T on MFMA, P and dS in registers,
 //                      dV^T += dO^T P and dK^T += Q^T dS.
+//   bwd_kv_reduce      sums the float32 partials of walks the plan split.
 // Splitting dQ from dK/dV recomputes S and dP once more but needs no atomics,
 // so results are deterministic.  Both tile kernels use the forward's MFMA
 // layouts: a 32x32 accumulator tile gives each lane one column (a query in
@@ -30,10 +31,11 @@
 // registers 8c .. 8c+7 of tile t are exactly the 8 contraction elements that
 // lane supplies for 16-element chunk 2t + c of the next product's B operand;
 // the matching A operand comes from LDS through ds_read_b64_tr_b16.
-// Tiles are staged through LDS by plain 16-byte loads and stores between two
-// barriers: K and V of one key block per step in the dQ kernel; in the dK/dV
-// kernel the block's V rows once, then Q and dO in 64-query steps, so that
-// it fits two workgroups per CU.
+// Both tile kernels walk their lists in 32-row steps whose rows (K and V in
+// the dQ kernel; Q and dO in the dK/dV kernel, which keeps its block's V rows
+// in LDS for the whole walk) are double-buffered in LDS and filled by direct
+// HBM->LDS loads issued a step ahead, one barrier per step; two workgroups
+// share a CU.  float32 kernels for fp32 inputs follow at the end.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
