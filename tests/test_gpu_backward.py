@@ -380,3 +380,48 @@ def test_backward_through_dynamic_plan(causal):
     check("dQ", gd[0].float().cpu().numpy(), rq)
     check("dK", gd[1].float().cpu().numpy(), rk)
     check("dV", gd[2].float().cpu().numpy(), rv)
+
+
+def test_beyond_2g_elements_forward_backward():
+    """The 256K GQA rule with batch 2: Q, O, dO and dQ hold 2^31 elements
+    each, so the last rows sit beyond every 32-bit element index.  Sampled
+    output rows, dQ rows and dK/dV keys at the ends of the buffers."""
+    w = wl.WORKLOADS["gqa256k"].with_shape(name="gqa256k-b2", batch=2)
+    assert w.batch * w.heads * w.seq_len * w.head_dim >= 2 ** 31
+    say(f"[max-size] {w.name} B={w.batch} H={w.heads}/{w.kv_heads} N={w.seq_len}")
+    lay = wl.layout_of(w)
+    q, k, v = wl.make_qkv(w, "cuda")
+    do = wl.make_dout(w, "cuda")
+    p = gpu_plan(w, lay)
+    out, lse = bsattn.forward(q, k, v, p)
+    dq, dk, dv = bsattn.backward(q, k, v, out, lse, do, p)
+    torch.cuda.synchronize()
+    N = w.seq_len
+    rows = [(1, 31, N - 1), (1, 31, N - 129), (1, 30, N // 2), (0, 0, 0), (1, 0, 4096), (1, 17, 200000)]
+    keys = [(1, 7, N - 1), (1, 7, N - 700)]
+    heads = sorted({(b, h) for b, h, _ in rows} | {(b, hk * 4 + g) for b, hk, _ in keys for g in range(4)})
+    kvh = sorted({(b, h // 4) for b, h in heads})
+    parts = {"q": {bh: q[bh].cpu() for bh in heads}, "do": {bh: do[bh].cpu() for bh in heads},
+             "k": {bk: k[bk].double().cpu().numpy() for bk in kvh},
+             "v": {bk: v[bk].double().cpu().numpy() for bk in kvh}}
+
+    class View:
+        def __init__(self, part, shape):
+            self.part, self.shape = part, shape
+
+        def __getitem__(self, idx):
+            return self.part[idx] if len(idx) == 2 else self.part[idx[:2]][idx[2]]
+
+    qs_, ks_ = tuple(q.shape), tuple(k.shape)
+    Qv, dOv, Kv, Vv = View(parts["q"], qs_), View(parts["do"], qs_), View(parts["k"], ks_), View(parts["v"], ks_)
+    O_ref, L_ref = oracle.forward(Qv, Kv, Vv, lay, w.block, rows=rows)
+    idx = tuple(torch.tensor(x) for x in zip(*rows))
+    eo = float(np.abs(out[idx].float().cpu().numpy() - O_ref).max())
+    el = float(np.abs(lse[idx].cpu().numpy() - L_ref).max())
+    say(f"  O: max|err| {eo:.3e}, LSE: max|err| {el:.3e}")
+    assert eo <= 2e-2 and el <= 1e-3
+    check("dQ rows", dq[idx].float().cpu().numpy(), oracle.backward_dq_rows(Qv, Kv, Vv, dOv, lay, w.block, rows))
+    rk, rv = oracle.backward_dkv_keys(Qv, Kv, Vv, dOv, lay, w.block, keys)
+    kidx = tuple(torch.tensor(x) for x in zip(*keys))
+    check("dK keys", dk[kidx].float().cpu().numpy(), rk)
+    check("dV keys", dv[kidx].float().cpu().numpy(), rv)
