@@ -255,6 +255,37 @@ def backward_context(names, steps=5):
     return res
 
 
+def mfma_probe(workgroups=512, iters=200000):
+    """Sustained bf16 MFMA rate of this GPU (libbsattn_probe: independent
+    v_mfma_f32_32x32x16_bf16 chains on register operands, 2 waves per SIMD on
+    every CU): the measured peak the attention kernel is also reported
+    against, since the chip clocks down under sustained matrix load."""
+    import ctypes
+    from block_sparse_flash_bsa_amd import build as bld
+    L = ctypes.CDLL(bld.PROBE_LIB)
+    L.bsa_probe_mfma.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    L.bsa_probe_mfma.restype = ctypes.c_int32
+    L.bsa_probe_mfma_flops.argtypes = [ctypes.c_int64, ctypes.c_int32]
+    L.bsa_probe_mfma_flops.restype = ctypes.c_double
+    out = torch.empty(workgroups * 256, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+    run = lambda n: L.bsa_probe_mfma(n, workgroups, ctypes.c_void_p(out.data_ptr()),
+                                     ctypes.c_void_p(stream.cuda_stream))
+    if run(iters // 10) != 0:
+        raise RuntimeError("MFMA probe launch failed")
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    run(iters)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b)
+    tf = L.bsa_probe_mfma_flops(iters, workgroups) / (ms * 1e-3) / 1e12
+    log(f"[bench] MFMA probe: {ms:.1f} ms, {tf:.1f} TFLOP/s")
+    return {"tflops": round(tf, 1), "ms": round(ms, 2), "workgroups": workgroups, "iters": iters,
+            "instruction": "v_mfma_f32_32x32x16_bf16"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -340,6 +371,11 @@ def main():
                      "kernel_ms": round(kern_ms, 4),
                      "algorithmic_flops": flops, "min_hbm_bytes": min_bytes},
     }
+    if w.dtype == torch.bfloat16:
+        probe = mfma_probe()
+        result["roofline"]["measured_peak"] = probe["tflops"]
+        result["roofline"]["frac_of_measured_peak"] = round(achieved / probe["tflops"], 4)
+        result["mfma_probe"] = probe
     if not args.no_context:
         # The other workloads, timed the same way (kernel HIP events), and the
         # dense causal comparator of the 256K shape on the same kernel.

@@ -1,4 +1,5 @@
-"""Build libbsattn.so in-tree with hipcc for gfx950.
+"""Build libbsattn.so (and the benchmark's libbsattn_probe.so) in-tree with
+hipcc for gfx950.
 
     python -m block_sparse_flash_bsa_amd.build          # build (always recompiles)
 
@@ -17,6 +18,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libbsattn.so")
+PROBE_LIB = os.path.join(PKG, "libbsattn_probe.so")   # benchmark's MFMA-rate probe
 ARCH = os.environ.get("BSA_OFFLOAD_ARCH", "gfx950")
 ROCM_INCLUDE = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include")
 
@@ -56,6 +58,15 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    # The benchmark's MFMA throughput probe, a library of its own.
+    pobj = os.path.join(objdir, "probe.hip.o")
+    cmd = [cc, *COMMON, *HIP_FLAGS, "-x", "hip", "-c", os.path.join(CSRC, "probe.hip"), "-o", pobj]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    ptmp = PROBE_LIB + ".tmp"
+    subprocess.run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", pobj, "-o", ptmp], check=True)
+    os.replace(ptmp, PROBE_LIB)
     return LIB
 
 

@@ -427,3 +427,20 @@ def test_ragged_bitmap_plan_matches_oracle():
         assert_same_plan(p, oracle.plan(lay, N, bs, brute=True))
         total = sum(oracle.allowed_count(lay, N, bs, h, q) for h in range(2) for q in range(N))
         assert p.info["allowed_pairs"] == total
+
+
+def test_probe_library_exports_its_header():
+    """The benchmark's MFMA-rate probe (include/bsattn_probe.h) is built into a
+    library of its own and exports exactly what its header declares."""
+    from block_sparse_flash_bsa_amd import build as bld
+    text = open(os.path.join(ROOT, "include", "bsattn_probe.h")).read()
+    declared = set(re.findall(r"\b(bsa_\w+)\s*\(", text))
+    assert declared == {"bsa_probe_mfma", "bsa_probe_mfma_flops"}
+    L = ctypes.CDLL(bld.PROBE_LIB)
+    for name in declared:
+        assert hasattr(L, name), name
+    L.bsa_probe_mfma_flops.argtypes = [ctypes.c_int64, ctypes.c_int32]
+    L.bsa_probe_mfma_flops.restype = ctypes.c_double
+    assert L.bsa_probe_mfma_flops(10, 3) == 3 * 4 * 4 * 10 * 32768
+    L.bsa_probe_mfma.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    assert L.bsa_probe_mfma(0, 1, None, None) == 1          # argument errors return before any HIP call
