@@ -398,6 +398,15 @@ def main():
             ctx[name] = {"ms_per_forward": round(float(np.mean(cev)), 4),
                          "tflops": round(float(tf), 1), "pct_of_peak": round(100 * tf / cpeak, 2),
                          "active_tiles": cp.info["active_blocks"]}
+            if name in ("tiny_f32", "window16k"):
+                # Microsecond-scale launches: 100 back to back between one event pair.
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(100):
+                    bsattn.forward(q, k, v, cp, out, lse)
+                b.record()
+                torch.cuda.synchronize()
+                ctx[name]["ms_per_forward_100_back_to_back"] = round(a.elapsed_time(b) / 100, 4)
             log(f"[bench] context {name}: {ctx[name]}")
         ctx["dense_over_sparse_time"] = round(ctx["dense256k"]["ms_per_forward"] /
                                               ctx["gqa256k"]["ms_per_forward"], 2)
