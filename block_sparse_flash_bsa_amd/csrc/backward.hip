@@ -897,16 +897,14 @@ hipError_t launch_f32_backward(const BwdParams& prm, const Plan& plan, hipStream
   constexpr int T = (BS < 64 ? BS : 64);
   constexpr size_t smem_dq = size_t(2 * T * D) * sizeof(float);
   constexpr size_t smem_kv = size_t(2 * T * D + 2 * T) * sizeof(float);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_f32<D, BS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem_dq));
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_f32<D, BS>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, int(smem_kv));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // Set on every launch (a host-side call): the attribute is per device, and
+  // a process may launch on several.
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dq_f32<D, BS>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(smem_dq));
+  if (e == hipSuccess)
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&bwd_dkdv_f32<D, BS>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(smem_kv));
+  if (e != hipSuccess) return e;
   const bsa_problem_t& pr = plan.prob;
   const int64_t rows = int64_t(pr.batch) * pr.num_heads * pr.seq_len;
   const int64_t rows_per_block = kThreads / 16;

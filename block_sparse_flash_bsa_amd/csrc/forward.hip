@@ -609,13 +609,11 @@ constexpr size_t f32_smem_bytes() {
 template <int D, int BS>
 hipError_t launch_f32(const FwdParams& prm, int64_t slots, hipStream_t stream) {
   constexpr size_t smem = f32_smem_bytes<D, BS>();
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_f32<D, BS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  // Set on every launch (a host-side call): the attribute is per device, and
+  // a process may launch on several.
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&fwd_f32<D, BS>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(smem));
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL((fwd_f32<D, BS>), dim3(unsigned(slots)), dim3(BS * kF32Lanes), smem, stream, prm);
   return hipGetLastError();
 }
