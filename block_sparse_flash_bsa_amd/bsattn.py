@@ -34,7 +34,8 @@ SCHEDULE_DEFAULT, SCHEDULE_XCD, SCHEDULE_LPT, SCHEDULE_ROWMAJOR = 0, 1, 2, 3
 EXPORTS = ("bsa_plan", "bsa_plan_host", "bsa_plan_destroy", "bsa_plan_csr", "bsa_plan_get_info",
            "bsa_plan_work", "bsa_plan_active_blocks", "bsa_plan_dynamic", "bsa_plan_set_bitmap",
            "bsa_plan_read_csr", "bsa_forward", "bsa_plan_csr_transposed", "bsa_plan_work_kv",
-           "bsa_backward", "bsa_status_string", "bsa_last_error", "bsa_abi_version")
+           "bsa_backward", "bsa_forward_varlen", "bsa_status_string", "bsa_last_error",
+           "bsa_abi_version")
 
 
 class Problem(ctypes.Structure):
@@ -95,6 +96,7 @@ def lib():
                                           POINTER(POINTER(c_uint8)), POINTER(c_int64)]
     L.bsa_plan_work_kv.argtypes = [P, POINTER(POINTER(c_int32)), POINTER(c_int64)]
     L.bsa_backward.argtypes = [c_void_p] * 6 + [P] + [c_void_p] * 5
+    L.bsa_forward_varlen.argtypes = [c_void_p, c_void_p, c_void_p, P, c_void_p, c_void_p, c_void_p, c_void_p]
     L.bsa_status_string.argtypes = [c_int32]
     L.bsa_status_string.restype = c_char_p
     L.bsa_last_error.argtypes = []
@@ -102,7 +104,7 @@ def lib():
     L.bsa_abi_version.restype = c_int32
     for name in ("bsa_plan", "bsa_plan_host", "bsa_plan_csr", "bsa_plan_get_info", "bsa_plan_work",
                  "bsa_plan_dynamic", "bsa_plan_set_bitmap", "bsa_plan_read_csr", "bsa_forward",
-                 "bsa_plan_csr_transposed", "bsa_plan_work_kv", "bsa_backward"):
+                 "bsa_plan_csr_transposed", "bsa_plan_work_kv", "bsa_backward", "bsa_forward_varlen"):
         getattr(L, name).restype = c_int32
     _lib = L
     return L
@@ -353,3 +355,34 @@ def backward(q, k, v, out, lse, dout, p: Plan, dq=None, dk=None, dv=None, delta=
                                   dout.data_ptr(), p.handle, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                   delta.data_ptr(), c_void_p(stream)))
     return dq, dk, dv
+
+
+def forward_varlen(q, k, v, p: Plan, seq_lens, out=None, lse=None):
+    """bsa_forward_varlen on torch.cuda.current_stream(): batch entry b uses its
+    first seq_lens[b] positions (seq_lens: int32 CUDA tensor [batch]); rows
+    beyond come out as empty rows (O = 0, LSE = -inf).  Returns (out, lse)."""
+    import torch
+    pr = p.problem
+    B, H, N, D = pr.batch, pr.num_heads, pr.seq_len, pr.head_dim
+    if (not seq_lens.is_cuda or seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,)
+            or not seq_lens.is_contiguous()):
+        raise ValueError(f"seq_lens must be a contiguous int32 CUDA tensor of shape ({B},)")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    if out is None:
+        out = torch.empty((B, H, N, D), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    Hk = pr.num_kv_heads
+    for name, t, shape in (("q", q, (B, H, N, D)), ("k", k, (B, Hk, N, D)), ("v", v, (B, Hk, N, D)),
+                           ("out", out, (B, H, N, D))):
+        if tuple(t.shape) != shape or t.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bf16 of shape {shape}")
+    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 CUDA tensor of shape (B, H, N)")
+    with torch.cuda.device(q.device):
+        stream = torch.cuda.current_stream().cuda_stream
+        _check(lib().bsa_forward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), p.handle, seq_lens.data_ptr(),
+                                        out.data_ptr(), lse.data_ptr(), c_void_p(stream)))
+    return out, lse

@@ -66,6 +66,9 @@ struct FwdParams {
   // allowed iff (uint32)(q - k - mlo) <= mspan (mlo <= 0, mspan >= 0).
   int32_t mlo;
   uint32_t mspan;
+  // Variable-length batch (bsa_forward_varlen): device int32 [batch], entry b
+  // uses its first seq_lens[b] positions; nullptr otherwise.
+  const int32_t* seq_lens;
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -177,9 +180,13 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
 }
 #pragma clang diagnostic pop
 
-// kRagged: the sequence ends inside its last block (N % 128 != 0).  Rows at or
-// beyond N are loaded from row N - 1 instead (and, for keys, masked: every
-// tile of the last key block is PARTIAL), and no output row at or beyond N is
+// kRagged: the sequence of this batch entry ends inside a block: N % 128 != 0,
+// or a variable-length batch whose entry b has Nb = seq_lens[b] <= N
+// positions.  The walk stops at the last key block below Nb; tiles of the
+// last block (row or column) are masked token by token (keys and queries at
+// or beyond Nb do not exist; rows beyond Nb come out as empty rows, O = 0 and
+// LSE = -inf); loads of rows at or beyond Nb read row Nb - 1 instead (padding
+// is never read, so it may hold anything), and no row at or beyond N is
 // written.  The instance for whole blocks compiles to the same code as
 // without the flag.
 template <bool kRagged>
@@ -196,6 +203,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   decode(p, item, b, h, i);
   const int hk = h / p.group;
   const RowDesc row = p.rows[(p.per_head_layout ? h : 0) * p.nb + i];
+  // Length of this batch entry's sequence and its block count (kRagged).
+  int Nb = int(p.N);
+  if (kRagged && p.seq_lens) {
+    const int x = p.seq_lens[b];
+    Nb = x < 0 ? 0 : (x > Nb ? Nb : x);
+  }
+  const int nbb = (Nb + kBM - 1) / kBM;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -203,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   const int qrow = wave * 32 + r32;                       // row within the q-block
   const int64_t qg = int64_t(i) * kBM + qrow;             // global query index
 
-  const int64_t qld = kRagged && qg >= p.N ? p.N - 1 : qg;   // row to load Q from
+  const int64_t qld = kRagged && qg >= Nb ? (Nb > 0 ? Nb - 1 : 0) : qg;   // row to load Q from
   const uint16_t* __restrict__ Qp =
       static_cast<const uint16_t*>(p.q) + ((int64_t(b) * p.H + h) * p.N + qld) * kD;
   const unsigned char* Kg =
@@ -237,12 +251,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   // u >= 4 V rows.
   auto dma_half_part = [&](int j, int hh, int u) {
     const int64_t row0 = int64_t(j) * kBN + hh * 64 + wave * 16;
-    if (kRagged && j == p.nb - 1) {
-      // Last key block of a ragged sequence: lane rows at or beyond N read
-      // row N - 1 (offsets from the block's first row, which is below N).
+    if (kRagged && j == nbb - 1) {
+      // Last key block of the sequence: lane rows at or beyond Nb read row
+      // Nb - 1 (offsets from the block's first row, which is below Nb).
       const int64_t tile0 = int64_t(j) * kBN;
       const int64_t rl = row0 + 4 * (u & 3) + lr;
-      const int64_t rc = rl < p.N ? rl : p.N - 1;
+      const int64_t rc = rl < Nb ? rl : Nb - 1;
       const uint32_t chunk = (u < 4 ? dko[u] : dvo) & 255u;
       const uint32_t voff = uint32_t(rc - tile0) * 256u + chunk;
       if (u < 4)
@@ -337,14 +351,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
           sq[t][r] = dql - uint32_t(ko) <= p.mspan ? sq[t][r] : -INFINITY;
         }
     }
-    if (kRagged && j == p.nb - 1) {
-      // Keys at or beyond the end of a ragged sequence do not exist.
+    if (kRagged && (j == nbb - 1 || i == nbb - 1)) {
+      // Keys and queries at or beyond the end of the sequence do not exist.
+      const bool row_ok = qg < Nb;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ko = t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          sq[t][r] = k0 + ko < p.N ? sq[t][r] : -INFINITY;
+          sq[t][r] = ((k0 + ko < Nb) & row_ok) ? sq[t][r] : -INFINITY;
         }
     }
   };
@@ -443,7 +458,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
     }
   };
 
-  const int e0 = row.start, ne = row.count;
+  const int e0 = row.start;
+  // kRagged: the walk ends at the last key block below Nb (entries ascend).
+  auto walk_length = [&]() {
+    int n = i >= nbb ? 0 : row.count;
+    while (n > 0 && (ents[e0 + n - 1] >> 1) >= nbb) --n;
+    return n;
+  };
+  const int ne = kRagged ? walk_length() : row.count;
   // One CSR entry (two phases); the last one (no next tile to load) is peeled
   // off so the loop body issues its loads unconditionally.
   bf16x8 pq[4];
@@ -451,7 +473,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
     constexpr bool has_next = decltype(next_c)::value;
     const int ent = ents[e0 + e];
     const int j = ent >> 1;
-    const bool partial = ent & 1;
+    // Tiles of the sequence's last block are masked token by token even where
+    // the plan (made for N) calls them FULL.
+    const bool partial = (ent & 1) || (kRagged && (Nb % kBN) != 0 && (j == nbb - 1 || i == nbb - 1));
     const int jn = has_next ? ents[e0 + e + 1] >> 1 : 0;
     f32x16 sq[2];
     BSA_WAIT_BARRIER(0);                 // K half 0 of e and V half 1 of e-1 landed
@@ -621,8 +645,11 @@ hipError_t launch_f32(const FwdParams& prm, int64_t slots, hipStream_t stream) {
 }  // namespace
 }  // namespace bsa
 
-extern "C" bsa_status_t bsa_forward(const void* q, const void* k, const void* v, bsa_plan_t plan,
-                                    void* out, float* lse, void* stream) {
+namespace bsa {
+namespace {
+
+bsa_status_t forward_impl(const void* q, const void* k, const void* v, bsa_plan_t plan, const int32_t* seq_lens,
+                          void* out, float* lse, void* stream) {
   using namespace bsa;
   clear_error();
   if (!plan) return fail(BSA_ERR_INVALID_ARGUMENT, "plan must not be NULL");
@@ -644,6 +671,7 @@ extern "C" bsa_status_t bsa_forward(const void* q, const void* k, const void* v,
   prm.v = v;
   prm.o = out;
   prm.lse = lse;
+  prm.seq_lens = seq_lens;
   prm.rows = plan->d_rows;
   prm.entries = plan->d_entries;
   prm.work = plan->d_work;
@@ -682,7 +710,7 @@ extern "C" bsa_status_t bsa_forward(const void* q, const void* k, const void* v,
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = hipSuccess;
   if (pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128) {
-    if (pr.seq_len % kBN != 0)
+    if (pr.seq_len % kBN != 0 || seq_lens)
       hipLaunchKernelGGL(fwd_bf16_d128<true>, dim3(unsigned(slots)), dim3(kThreads), 0, s, prm, prm.entries);
     else
       hipLaunchKernelGGL(fwd_bf16_d128<false>, dim3(unsigned(slots)), dim3(kThreads), 0, s, prm, prm.entries);
@@ -700,4 +728,31 @@ extern "C" bsa_status_t bsa_forward(const void* q, const void* k, const void* v,
   }
   if (err != hipSuccess) return fail(BSA_ERR_DEVICE, "kernel launch failed: %s", hipGetErrorString(err));
   return BSA_OK;
+}
+
+}  // namespace
+}  // namespace bsa
+
+extern "C" bsa_status_t bsa_forward(const void* q, const void* k, const void* v, bsa_plan_t plan,
+                                    void* out, float* lse, void* stream) {
+  return bsa::forward_impl(q, k, v, plan, nullptr, out, lse, stream);
+}
+
+extern "C" bsa_status_t bsa_forward_varlen(const void* q, const void* k, const void* v, bsa_plan_t plan,
+                                           const int32_t* seq_lens, void* out, float* lse, void* stream) {
+  using namespace bsa;
+  clear_error();
+  if (!plan) return fail(BSA_ERR_INVALID_ARGUMENT, "plan must not be NULL");
+  const bsa_problem_t& pr = plan->prob;
+  if (!(pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128))
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_varlen has a kernel for bf16, head_dim 128, block 128 only");
+  if (plan->info.work_items == 0) return BSA_OK;
+  if (!seq_lens) return fail(BSA_ERR_INVALID_ARGUMENT, "seq_lens must not be NULL");
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, seq_lens) != hipSuccess || attr.type != hipMemoryTypeDevice ||
+      attr.device != plan->device) {
+    (void)hipGetLastError();
+    return fail(BSA_ERR_INVALID_ARGUMENT, "seq_lens must be device memory of device %d", plan->device);
+  }
+  return forward_impl(q, k, v, plan, seq_lens, out, lse, stream);
 }

@@ -332,6 +332,26 @@ bsa_status_t bsa_backward(const void* q, const void* k, const void* v, const voi
                           const float* lse, const void* dout, bsa_plan_t plan, void* dq, void* dk,
                           void* dv, float* delta, void* stream);
 
+/* Variable-length batch: the same forward, where batch entry b uses only its
+ * first seq_lens[b] positions of the padded [batch][heads][seq_len][head_dim]
+ * buffers.  Its positions at or beyond seq_lens[b] neither attend nor are
+ * attended, and their rows of out and lse are written as empty rows (O = 0,
+ * LSE = -inf).  Padding is never read, so it may hold anything.  The layout
+ * rule applies to each entry as to a sequence of seq_lens[b] positions; the
+ * plan is the one for seq_len (the maximum), and its tiles beyond an entry's
+ * length are skipped, its last partial block masked token by token.  This is
+ * the variable-length counterpart of padding to the block size (FAQ of "The
+ * Only Guide You Need for Sparse Attention Kernels in Long-Context LLMs";
+ * variable-length sequences in production kernels, "Sparse Attention
+ * Kernels vs Full Attention Performance").
+ *   seq_lens: device int32 [batch]; values are clamped to [0, seq_len].
+ * Other arguments as bsa_forward.  Supported: bf16, head_dim 128, block 128
+ * (static or dynamic plans); otherwise UNSUPPORTED.
+ * Errors: as bsa_forward, plus INVALID_ARGUMENT for a NULL seq_lens or one
+ * that is not device memory of the plan's device. */
+bsa_status_t bsa_forward_varlen(const void* q, const void* k, const void* v, bsa_plan_t plan,
+                                const int32_t* seq_lens, void* out, float* lse, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* bsa_status_string(bsa_status_t status);
 

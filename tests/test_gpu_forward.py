@@ -383,3 +383,82 @@ def test_ragged_length_parity_f32():
     assert torch.isnan(og).all() and torch.isnan(lg).all(), "write beyond the last row"
     O_ref, L_ref = oracle.forward(q, k, v, lay, w.block)
     check(out.cpu().numpy(), lse.cpu().numpy(), O_ref, L_ref, w.dtype, w.name)
+
+
+# ------------------------------------------------------- variable-length batches
+def varlen_inputs(w, lens):
+    """Padded Q, K, V with NaN in every position at or beyond each entry's length."""
+    q, k, v = wl.make_qkv(w, "cpu")
+    for b, L in enumerate(lens):
+        for t in (q, k, v):
+            t[b, :, L:] = float("nan")
+    return q, k, v
+
+
+@pytest.mark.parametrize("kind", ["window", "bitmap", "dense"])
+def test_forward_varlen_parity(kind):
+    """Batch entry b uses its first lens[b] positions of padded buffers: rows
+    below the length match the oracle on the trimmed sequence, rows beyond
+    are empty rows (O = 0, LSE = -inf), and NaN padding is never read."""
+    Nmax, lens = 1500, [1500, 640, 333, 0]
+    w = wl.WORKLOADS["gqa256k"].with_shape(name=f"varlen-{kind}", batch=4, heads=4, kv_heads=2, seq_len=Nmax)
+    nb = -(-Nmax // 128)
+    if kind == "window":
+        lay = dict(causal=True, unit="tokens", window_left=300, window_right=0, global_keys=5,
+                   global_queries=0, bitmap=None)
+    elif kind == "bitmap":
+        bm = np.random.default_rng(9).random((4, nb, nb)) < 0.3
+        bm[:, np.arange(nb), np.arange(nb)] = True
+        lay = dict(causal=False, unit="blocks", window_left=-1, window_right=-1, global_keys=0,
+                   global_queries=0, bitmap=torch.from_numpy(bm))
+    else:
+        lay = dict(causal=False, unit="tokens", window_left=-1, window_right=-1, global_keys=0,
+                   global_queries=0, bitmap=None)
+    say(f"[varlen] {kind} Nmax={Nmax} lens={lens}")
+    q, k, v = varlen_inputs(w, lens)
+    p = gpu_plan(w, lay)
+    out, lse = bsattn.forward_varlen(q.cuda(), k.cuda(), v.cuda(), p,
+                                     torch.tensor(lens, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    out, lse = out.float().cpu().numpy(), lse.cpu().numpy()
+    for b, L in enumerate(lens):
+        assert np.all(out[b, :, L:] == 0) and np.all(lse[b, :, L:] == -np.inf), f"entry {b}: rows beyond {L}"
+        if L == 0:
+            continue
+        ly = dict(lay)
+        if ly["bitmap"] is not None:
+            nbl = -(-L // 128)
+            ly["bitmap"] = ly["bitmap"][:, :nbl, :nbl]
+        O_ref, L_ref = oracle.forward(q[b:b + 1, :, :L], k[b:b + 1, :, :L], v[b:b + 1, :, :L], ly, 128)
+        check(out[b:b + 1, :, :L], lse[b:b + 1, :, :L], O_ref, L_ref, torch.bfloat16, f"{kind} entry {b} (L={L})")
+
+
+@pytest.mark.parametrize("Nmax", [1500, 1024])
+def test_forward_varlen_full_lengths_equal_plain_forward(Nmax):
+    """With every length at the maximum, the variable-length call gives
+    bit for bit what bsa_forward gives."""
+    w = wl.WORKLOADS["gqa256k"].with_shape(name="varlen-full", batch=2, heads=4, kv_heads=2, seq_len=Nmax)
+    lay = wl.layout_of(w)
+    q, k, v = (x.cuda() for x in wl.make_qkv(w, "cpu"))
+    p = gpu_plan(w, lay)
+    o1, l1 = run(p, q, k, v)
+    o2, l2 = bsattn.forward_varlen(q, k, v, p, torch.full((2,), Nmax, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_forward_varlen_rejects_bad_arguments():
+    w = wl.WORKLOADS["tiny_f32"]
+    p = gpu_plan(w, wl.layout_of(w))
+    q = wl.make_qkv(w, "cpu")[0].cuda()
+    lens = torch.full((1,), 1024, dtype=torch.int32, device="cuda")
+    st = bsattn.lib().bsa_forward_varlen(q.data_ptr(), q.data_ptr(), q.data_ptr(), p.handle, lens.data_ptr(),
+                                         q.data_ptr(), q.data_ptr(), None)
+    assert st == bsattn.ERR_UNSUPPORTED                     # fp32: no variable-length kernel
+    wb = wl.small_variant(wl.WORKLOADS["window16k"], 1024, heads=2, kv_heads=2)
+    pb = gpu_plan(wb, wl.layout_of(wb))
+    qb, kb, vb = (x.cuda() for x in wl.make_qkv(wb, "cpu"))
+    host_lens = torch.full((1,), 512, dtype=torch.int32)
+    st = bsattn.lib().bsa_forward_varlen(qb.data_ptr(), kb.data_ptr(), vb.data_ptr(), pb.handle,
+                                         host_lens.data_ptr(), qb.data_ptr(), qb.data_ptr(), None)
+    assert st == bsattn.ERR_INVALID_ARGUMENT                # host memory for seq_lens
