@@ -34,7 +34,7 @@ SCHEDULE_DEFAULT, SCHEDULE_XCD, SCHEDULE_LPT, SCHEDULE_ROWMAJOR = 0, 1, 2, 3
 EXPORTS = ("bsa_plan", "bsa_plan_host", "bsa_plan_destroy", "bsa_plan_csr", "bsa_plan_get_info",
            "bsa_plan_work", "bsa_plan_active_blocks", "bsa_plan_dynamic", "bsa_plan_set_bitmap",
            "bsa_plan_read_csr", "bsa_forward", "bsa_plan_csr_transposed", "bsa_plan_work_kv",
-           "bsa_backward", "bsa_forward_varlen", "bsa_status_string", "bsa_last_error",
+           "bsa_backward", "bsa_forward_varlen", "bsa_backward_varlen", "bsa_status_string", "bsa_last_error",
            "bsa_abi_version")
 
 
@@ -97,6 +97,7 @@ def lib():
     L.bsa_plan_work_kv.argtypes = [P, POINTER(POINTER(c_int32)), POINTER(c_int64)]
     L.bsa_backward.argtypes = [c_void_p] * 6 + [P] + [c_void_p] * 5
     L.bsa_forward_varlen.argtypes = [c_void_p, c_void_p, c_void_p, P, c_void_p, c_void_p, c_void_p, c_void_p]
+    L.bsa_backward_varlen.argtypes = [c_void_p] * 6 + [P] + [c_void_p] * 6
     L.bsa_status_string.argtypes = [c_int32]
     L.bsa_status_string.restype = c_char_p
     L.bsa_last_error.argtypes = []
@@ -104,7 +105,8 @@ def lib():
     L.bsa_abi_version.restype = c_int32
     for name in ("bsa_plan", "bsa_plan_host", "bsa_plan_csr", "bsa_plan_get_info", "bsa_plan_work",
                  "bsa_plan_dynamic", "bsa_plan_set_bitmap", "bsa_plan_read_csr", "bsa_forward",
-                 "bsa_plan_csr_transposed", "bsa_plan_work_kv", "bsa_backward", "bsa_forward_varlen"):
+                 "bsa_plan_csr_transposed", "bsa_plan_work_kv", "bsa_backward", "bsa_forward_varlen",
+                 "bsa_backward_varlen"):
         getattr(L, name).restype = c_int32
     _lib = L
     return L
@@ -328,6 +330,22 @@ def backward(q, k, v, out, lse, dout, p: Plan, dq=None, dk=None, dv=None, delta=
     out and lse are the forward's outputs for these inputs and this plan;
     delta (float32 [B, H, N]) is the library's workspace for <dO, O>.
     """
+    return _backward(q, k, v, out, lse, dout, p, None, dq, dk, dv, delta)
+
+
+def backward_varlen(q, k, v, out, lse, dout, p: Plan, seq_lens, dq=None, dk=None, dv=None, delta=None):
+    """bsa_backward_varlen on torch.cuda.current_stream(): the backward of
+    forward_varlen with the same seq_lens (int32 CUDA tensor [batch]); rows of
+    dq, dk, dv beyond an entry's length come out zero.  Returns (dq, dk, dv)."""
+    import torch
+    B = p.problem.batch
+    if (not seq_lens.is_cuda or seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,)
+            or not seq_lens.is_contiguous()):
+        raise ValueError(f"seq_lens must be a contiguous int32 CUDA tensor of shape ({B},)")
+    return _backward(q, k, v, out, lse, dout, p, seq_lens, dq, dk, dv, delta)
+
+
+def _backward(q, k, v, out, lse, dout, p, seq_lens, dq, dk, dv, delta):
     import torch
     pr = p.problem
     B, H, Hk, N, D = pr.batch, pr.num_heads, pr.num_kv_heads, pr.seq_len, pr.head_dim
@@ -351,9 +369,16 @@ def backward(q, k, v, out, lse, dout, p: Plan, dq=None, dk=None, dv=None, delta=
                              f"{tuple(t.shape)} {t.dtype} on {t.device}")
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream().cuda_stream
-        _check(lib().bsa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                                  dout.data_ptr(), p.handle, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                                  delta.data_ptr(), c_void_p(stream)))
+        if seq_lens is None:
+            st = lib().bsa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                    dout.data_ptr(), p.handle, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                                    delta.data_ptr(), c_void_p(stream))
+        else:
+            st = lib().bsa_backward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                           lse.data_ptr(), dout.data_ptr(), p.handle, seq_lens.data_ptr(),
+                                           dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), delta.data_ptr(),
+                                           c_void_p(stream))
+        _check(st)
     return dq, dk, dv
 
 

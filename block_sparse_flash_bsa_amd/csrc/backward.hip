@@ -75,6 +75,9 @@ struct BwdParams {
   // allowed iff (uint32)(q - k - mlo) <= mspan.
   int32_t mlo;
   uint32_t mspan;
+  // Variable-length batch (bsa_backward_varlen): device int32 [batch], entry b
+  // uses its first seq_lens[b] positions; nullptr otherwise.
+  const int32_t* seq_lens;
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -95,12 +98,23 @@ typedef __attribute__((address_space(3))) unsigned char lds_u8;
 // Token predicate inside a PARTIAL tile: the window/causal range of q - k, or
 // a global key / global query row (still under the causal cut).  With
 // token_rule == 0 the range is the causal cut alone.
-// Positions at or beyond the end of a ragged sequence do not exist (every
-// tile of its last block is PARTIAL).
-__device__ __forceinline__ bool pair_ok(const BwdParams& p, int q, int k) {
+// Positions at or beyond the sequence's length n do not exist (every tile of
+// its last block is treated as PARTIAL).
+__device__ __forceinline__ bool pair_ok(const BwdParams& p, int q, int k, int n) {
   const bool in_range = uint32_t(q - k) - uint32_t(p.mlo) <= p.mspan;
   const bool glob = p.token_rule && (k < p.gk32 || q < p.gq32) && (!p.causal || k <= q);
-  return (in_range || glob) && q < p.N32 && k < p.N32;
+  return (in_range || glob) && q < n && k < n;
+}
+
+// Length of batch entry b's sequence: seq_lens[b] clamped to [0, N] in a
+// variable-length batch, else N.
+__device__ __forceinline__ int entry_length(const BwdParams& p, int b) {
+  int n = p.N32;
+  if (p.seq_lens) {
+    const int x = p.seq_lens[b];
+    n = x < 0 ? 0 : (x > n ? n : x);
+  }
+  return n;
 }
 
 // LDS tile layout for rows read both row-wise and transposed: row r (256
@@ -266,8 +280,11 @@ __device__ __forceinline__ uint32_t cols_base(int lane, int s) {
 // loads issued a step ahead, interleaved with the S^T/dP^T MFMAs; one
 // barrier per step, 32 KB of LDS.
 // ---------------------------------------------------------------------------
-// kRagged: the sequence ends inside its last block; rows at or beyond N load
-// row N - 1, are masked, and are not written.
+// kRagged: the sequence ends inside its last block, or the batch entries
+// have lengths of their own (seq_lens).  With Nb the entry's length, rows at
+// or beyond Nb load row Nb - 1 and are masked; the walk stops at the entry's
+// last block; rows in [Nb, N) get dQ = 0 and rows at or beyond N are not
+// written.
 template <bool kRagged>
 __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) unsigned char K0[kStepBytes];
@@ -288,19 +305,28 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
   const int h = bh % p.H, b = bh / p.H;
   const int hk = h / p.group;
   const RowDesc row = p.rows[(p.per_head_layout ? h : 0) * p.nb + i];
+  const int Nb = kRagged ? entry_length(p, b) : p.N32;
+  const int nbb = (Nb + kB - 1) / kB;
+  // The CSR row lists ascending key blocks: the walk is its prefix below the
+  // entry's last block (none for a q-block beyond it).
+  int ne = row.count;
+  if (kRagged) {
+    ne = i >= nbb ? 0 : row.count;
+    while (ne > 0 && (p.entries[row.start + ne - 1] >> 1) >= nbb) --ne;
+  }
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63, r32 = lane & 31, hf = lane >> 5;
   const int qg = i * kB + wave * 32 + r32;
   const int64_t qrow = (int64_t(b) * p.H + h) * p.N + qg;
-  const int64_t qrow_ld = kRagged && qg >= p.N ? qrow - qg + p.N - 1 : qrow;   // row to load from
+  const int64_t qrow_ld = kRagged && qg >= Nb ? qrow - qg + (Nb > 0 ? Nb - 1 : 0) : qrow;   // row to load from
 
   f32x16 acc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 
-  if (row.count > 0) {
+  if (ne > 0) {
     // Q^T and dO^T as B operands: lane (row r32, half hf) holds d = 16c + 8hf .. +7.
     bf16x8 qf[8], df[8];
 #pragma unroll
@@ -329,10 +355,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
       const int R = wave * 8 + 4 * (u & 1) + l4;
       const uint32_t lds_off = (wave * 8 + 4 * (u & 1)) * 256;
       const uint32_t chunk = 16 * (u < 2 ? (lc ^ tile_swz(R)) : (lc ^ (R & 15)));
-      // Source row relative to the key block's first row (below N); in a
-      // ragged last block rows at or beyond N read row N - 1.
+      // Source row relative to the key block's first row (below Nb); in the
+      // entry's ragged last block rows at or beyond Nb read row Nb - 1.
       int rel = st * kStepRows + R;
-      if (kRagged && j == p.nb - 1) rel = rel < p.N32 - j * kB ? rel : p.N32 - j * kB - 1;
+      if (kRagged && j == nbb - 1) rel = rel < Nb - j * kB ? rel : Nb - j * kB - 1;
       const int64_t tile0 = int64_t(j) * kB;
       if (u < 2)
         dma16(Kg + tile0 * 256, rel * 256 + chunk, Ka[bf] + lds_off);
@@ -350,8 +376,10 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
     for (int u = 0; u < 4; ++u) dma_step(ent >> 1, 0, 0, u);
     while (true) {
       const int j = ent >> 1;
-      const bool partial = ent & 1;
-      const bool have_next = e + 1 < row.count;
+      // Tiles touching a short last block of the entry are masked whatever
+      // the plan's flag.
+      const bool partial = (ent & 1) || (kRagged && (Nb % kB) != 0 && (j == nbb - 1 || i == nbb - 1));
+      const bool have_next = e + 1 < ne;
       const int ent_n = have_next ? __builtin_amdgcn_readfirstlane(p.entries[row.start + e + 1]) : 0;
 #pragma unroll
       for (int st = 0; st < 4; ++st) {                 // keys 32st .. 32st+31 of key block j
@@ -393,7 +421,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int kk = j * kB + st * kStepRows + 8 * (r >> 2) + 4 * hf + (r & 3);
-            sc[r] = pair_ok(p, qg, kk) ? sc[r] : -INFINITY;
+            sc[r] = pair_ok(p, qg, kk, Nb) ? sc[r] : -INFINITY;
           }
         }
         bf16x8 ds[2];
@@ -460,6 +488,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
   const int j = item % p.nb;
   const int bk = item / p.nb;
   const int hk = bk % p.Hkv, b = bk / p.Hkv;
+  const int Nb = kRagged ? entry_length(p, b) : p.N32;
+  const int nbb = (Nb + kB - 1) / kB;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -477,20 +507,29 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
 
   // Cursor over this slot's part [walk_begin, walk_end) of the walk: the
   // group's transposed lists one after another, as (query head of the group,
-  // entry of its list); every value is wave-uniform.
+  // entry of its list); every value is wave-uniform.  The lists are ascending
+  // in q-block, so under kRagged the first q-block beyond the entry's last
+  // skips the rest of its list; a k-block beyond it has no walk.
   struct Entry {
     int h, i, partial;
   };
   int cg = 0, ce = walk_begin, left = walk_end - walk_begin;
+  if (kRagged && j >= nbb) left = 0;
   RowDesc ccol = p.cols[(p.per_head_layout ? hk * p.group : 0) * p.nb + j];
   auto next_entry = [&](Entry& out) -> bool {
-    if (left <= 0) return false;
-    while (ce >= ccol.count) {
-      ce -= ccol.count;
-      if (++cg >= p.group) return false;
-      ccol = p.cols[(p.per_head_layout ? hk * p.group + cg : 0) * p.nb + j];
+    int ent;
+    while (true) {
+      if (left <= 0) return false;
+      while (ce >= ccol.count) {
+        ce -= ccol.count;
+        if (++cg >= p.group) return false;
+        ccol = p.cols[(p.per_head_layout ? hk * p.group + cg : 0) * p.nb + j];
+      }
+      ent = __builtin_amdgcn_readfirstlane(p.entries_t[ccol.start + ce]);
+      if (!kRagged || (ent >> 1) < nbb) break;
+      left -= ccol.count - ce;
+      ce = ccol.count;
     }
-    const int ent = __builtin_amdgcn_readfirstlane(p.entries_t[ccol.start + ce]);
     ++ce;
     --left;
     out.h = hk * p.group + cg;
@@ -506,11 +545,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
     bf16x8 kf[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c)
-      kf[c] = *reinterpret_cast<const bf16x8*>(p.k + (kRagged && kg >= p.N ? kvbase + p.N - 1 : krow) * kD +
+      kf[c] = *reinterpret_cast<const bf16x8*>(p.k + (kRagged && kg >= Nb ? kvbase + Nb - 1 : krow) * kD +
                                                c * 16 + hf * 8);
     // V rows of this k-block; the first step's barrier publishes them.
     stage<kB, true>(Vs, reinterpret_cast<const unsigned char*>(p.v + (kvbase + int64_t(j) * kB) * kD), tid,
-                    kRagged ? (p.N32 - j * kB < kB ? p.N32 - j * kB : kB) : kB);
+                    kRagged ? (Nb - j * kB < kB ? Nb - j * kB : kB) : kB);
     // Complete these loads before the first HBM->LDS load, so the pending
     // counts the barriers wait on only see those.
     __asm__ volatile("s_waitcnt vmcnt(0)" ::"v"(kf[0]), "v"(kf[1]), "v"(kf[2]), "v"(kf[3]), "v"(kf[4]),
@@ -521,12 +560,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
     // of row R = 8w + 4u + L / 16 and reads the logical chunk the tile layout
     // places there (chunk ^ tile_swz(R)).
     auto dma_step = [&](const Entry& en, int st, int bf, int u) {
-      // Source row relative to the q-block's first row (below N); in a
-      // ragged last block rows at or beyond N read row N - 1.
+      // Source row relative to the q-block's first row (below Nb); in the
+      // entry's ragged last block rows at or beyond Nb read row Nb - 1.
       const int64_t tile0 = (int64_t(b) * p.H + en.h) * p.N + int64_t(en.i) * kB;
       const int R = wave * 8 + 4 * (u & 1) + (lane >> 4);
       int rel = st * kStepRows + R;
-      if (kRagged && en.i == p.nb - 1) rel = rel < p.N32 - en.i * kB ? rel : p.N32 - en.i * kB - 1;
+      if (kRagged && en.i == nbb - 1) rel = rel < Nb - en.i * kB ? rel : Nb - en.i * kB - 1;
       const uint32_t voff = rel * 256 + 16 * ((lane & 15) ^ tile_swz(R));
       const uint32_t lds_off = (wave * 8 + 4 * (u & 1)) * 256;
       if (u < 2)
@@ -536,7 +575,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
     };
     auto load_x = [&](const Entry& en, int st) {
       int qi = en.i * kB + st * kStepRows + (lane & 31);
-      if (kRagged) qi = qi < p.N32 ? qi : p.N32 - 1;
+      if (kRagged) qi = qi < Nb ? qi : Nb - 1;
       const int64_t r = (int64_t(b) * p.H + en.h) * p.N + qi;
       return lane < 32 ? p.lse[r] : p.delta[r];
     };
@@ -598,11 +637,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
         // Register r holds query 32st + 8 (r / 4) + 4 hf + r % 4 of q-block
         // cur.i, for key kg.  The token mask runs only in PARTIAL tiles.
         const int qbase = cur.i * kB + st * kStepRows;
-        if (cur.partial) {
+        if (cur.partial || (kRagged && (Nb % kB) != 0 && (cur.i == nbb - 1 || j == nbb - 1))) {
           __asm__ volatile("");
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            s[r] = pair_ok(p, qbase + 8 * (r >> 2) + 4 * hf + (r & 3), kg) ? s[r] : -INFINITY;
+            s[r] = pair_ok(p, qbase + 8 * (r >> 2) + 4 * hf + (r & 3), kg, Nb) ? s[r] : -INFINITY;
         }
         bf16x8 pb[2], db[2];
 #pragma unroll
@@ -790,7 +829,7 @@ __global__ __launch_bounds__(BS * kF32Lanes) void bwd_dq_f32(BwdParams p) {
         }
         a = quad_sum(a);
         c = quad_sum(c);
-        const float pr = (partial && !pair_ok(p, qg, k0 + kk)) ? 0.f : __builtin_amdgcn_exp2f(fmaf(a, p.sl2, -lse2));
+        const float pr = (partial && !pair_ok(p, qg, k0 + kk, p.N32)) ? 0.f : __builtin_amdgcn_exp2f(fmaf(a, p.sl2, -lse2));
         const float ds = pr * (c - dlt);
 #pragma unroll
         for (int d = 0; d < DL; ++d) acc[d] = fmaf(ds, kr[d], acc[d]);
@@ -871,7 +910,7 @@ __global__ __launch_bounds__(BS * kF32Lanes) void bwd_dkdv_f32(BwdParams p) {
           a = quad_sum(a);
           c = quad_sum(c);
           const float pr =
-              (partial && !pair_ok(p, q0 + qq, kg)) ? 0.f : __builtin_amdgcn_exp2f(fmaf(a, p.sl2, -Ls[qq]));
+              (partial && !pair_ok(p, q0 + qq, kg, p.N32)) ? 0.f : __builtin_amdgcn_exp2f(fmaf(a, p.sl2, -Ls[qq]));
           const float ds = pr * (c - Dls[qq]);
 #pragma unroll
           for (int d = 0; d < DL; ++d) {
@@ -925,14 +964,9 @@ hipError_t launch_f32_backward(const BwdParams& prm, const Plan& plan, hipStream
   return err;
 }
 
-}  // namespace
-}  // namespace bsa
-
-extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v, const void* out,
-                                     const float* lse, const void* dout, bsa_plan_t plan, void* dq,
-                                     void* dk, void* dv, float* delta, void* stream) {
-  using namespace bsa;
-  clear_error();
+bsa_status_t backward_impl(const void* q, const void* k, const void* v, const void* out, const float* lse,
+                           const void* dout, bsa_plan_t plan, const int32_t* seq_lens, void* dq, void* dk, void* dv,
+                           float* delta, void* stream) {
   if (!plan) return fail(BSA_ERR_INVALID_ARGUMENT, "plan must not be NULL");
   if (!plan->info.on_device)
     return fail(BSA_ERR_INVALID_ARGUMENT, "plan was built by bsa_plan_host and has no device copy");
@@ -973,6 +1007,7 @@ extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v
   prm.kv_scratch = plan->d_kv_scratch;
   prm.N = pr.seq_len;
   prm.N32 = int32_t(pr.seq_len);
+  prm.seq_lens = seq_lens;
   prm.H = pr.num_heads;
   prm.Hkv = pr.num_kv_heads;
   prm.group = pr.num_heads / pr.num_kv_heads;
@@ -1009,7 +1044,7 @@ extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v
     if (e != hipSuccess) return fail(BSA_ERR_DEVICE, "backward kernel launch failed: %s", hipGetErrorString(e));
     return BSA_OK;
   }
-  const bool ragged = pr.seq_len % kB != 0;
+  const bool ragged = pr.seq_len % kB != 0 || seq_lens;
   const int64_t rows = int64_t(pr.batch) * pr.num_heads * pr.seq_len;
   const int64_t rows_per_block = kThreads / 16;
   hipLaunchKernelGGL(bwd_delta_bf16, dim3(unsigned((rows + rows_per_block - 1) / rows_per_block)), dim3(kThreads),
@@ -1035,4 +1070,35 @@ extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v
   }
   if (err != hipSuccess) return fail(BSA_ERR_DEVICE, "backward kernel launch failed: %s", hipGetErrorString(err));
   return BSA_OK;
+}
+
+}  // namespace
+}  // namespace bsa
+
+extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v, const void* out,
+                                     const float* lse, const void* dout, bsa_plan_t plan, void* dq,
+                                     void* dk, void* dv, float* delta, void* stream) {
+  bsa::clear_error();
+  return bsa::backward_impl(q, k, v, out, lse, dout, plan, nullptr, dq, dk, dv, delta, stream);
+}
+
+extern "C" bsa_status_t bsa_backward_varlen(const void* q, const void* k, const void* v, const void* out,
+                                            const float* lse, const void* dout, bsa_plan_t plan,
+                                            const int32_t* seq_lens, void* dq, void* dk, void* dv, float* delta,
+                                            void* stream) {
+  using namespace bsa;
+  clear_error();
+  if (!plan) return fail(BSA_ERR_INVALID_ARGUMENT, "plan must not be NULL");
+  const bsa_problem_t& pr = plan->prob;
+  if (!(pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128))
+    return fail(BSA_ERR_UNSUPPORTED, "bsa_backward_varlen has kernels for bf16, head_dim 128, block 128 only");
+  if (plan->info.work_items == 0) return BSA_OK;
+  if (!seq_lens) return fail(BSA_ERR_INVALID_ARGUMENT, "seq_lens must not be NULL");
+  hipPointerAttribute_t attr{};
+  if (hipPointerGetAttributes(&attr, seq_lens) != hipSuccess || attr.type != hipMemoryTypeDevice ||
+      attr.device != plan->device) {
+    (void)hipGetLastError();
+    return fail(BSA_ERR_INVALID_ARGUMENT, "seq_lens must be device memory of device %d", plan->device);
+  }
+  return backward_impl(q, k, v, out, lse, dout, plan, seq_lens, dq, dk, dv, delta, stream);
 }

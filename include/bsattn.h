@@ -352,6 +352,24 @@ bsa_status_t bsa_backward(const void* q, const void* k, const void* v, const voi
 bsa_status_t bsa_forward_varlen(const void* q, const void* k, const void* v, bsa_plan_t plan,
                                 const int32_t* seq_lens, void* out, float* lse, void* stream);
 
+/* Variable-length batch: the backward of bsa_forward_varlen.  Batch entry b
+ * uses its first seq_lens[b] positions; the gradients of those positions are
+ * the ones of a sequence of seq_lens[b] positions under the same layout
+ * (the dQ walks stop at the entry's last block, the dK/dV walks skip q-blocks
+ * beyond it, and its last partial block is masked token by token).  Rows of
+ * dq, dk and dv at or beyond seq_lens[b] are written as zeros.  Padding of
+ * q, k, v, out, lse and dout is never read, so it may hold anything; the
+ * padded rows of delta hold <dO, O> of whatever the padding holds.
+ *   seq_lens: device int32 [batch]; values are clamped to [0, seq_len]; the
+ *             same array that produced out and lse.
+ * Other arguments as bsa_backward.  Supported: bf16, head_dim 128, block 128
+ * (static or dynamic plans); otherwise UNSUPPORTED.
+ * Errors: as bsa_backward, plus INVALID_ARGUMENT for a NULL seq_lens or one
+ * that is not device memory of the plan's device. */
+bsa_status_t bsa_backward_varlen(const void* q, const void* k, const void* v, const void* out,
+                                 const float* lse, const void* dout, bsa_plan_t plan, const int32_t* seq_lens,
+                                 void* dq, void* dk, void* dv, float* delta, void* stream);
+
 /* Static description of a status code (never NULL). */
 const char* bsa_status_string(bsa_status_t status);
 

@@ -425,3 +425,108 @@ def test_beyond_2g_elements_forward_backward():
     kidx = tuple(torch.tensor(x) for x in zip(*keys))
     check("dK keys", dk[kidx].float().cpu().numpy(), rk)
     check("dV keys", dv[kidx].float().cpu().numpy(), rv)
+
+
+# ------------------------------------------------------ variable-length batches
+def _varlen_case(kind):
+    """(workload, layout, lengths) of a padded variable-length batch."""
+    if kind == "split":
+        # GQA group of 4 over one KV head; k-blocks 3 and the last are read by
+        # every q-block, so their dK/dV walks are split into chunks, and the
+        # shorter entries end inside those walks.
+        N, lens = 4000, [4000, 2500, 1000]
+        w = wl.WORKLOADS["gqa256k"].with_shape(name="varlen-split", batch=3, heads=4, kv_heads=1, seq_len=N)
+        nb = -(-N // 128)
+        bm = np.random.default_rng(11).random((4, nb, nb)) < 0.05
+        bm[:, :, 3] = True
+        bm[:, :, nb - 1] = True
+        bm[:, np.arange(nb), np.arange(nb)] = True
+        lay = dict(causal=False, unit="blocks", window_left=-1, window_right=-1, global_keys=0,
+                   global_queries=0, bitmap=torch.from_numpy(bm))
+        return w, lay, lens
+    N, lens = 1500, [1500, 640, 333, 0]
+    w = wl.WORKLOADS["gqa256k"].with_shape(name=f"varlen-{kind}", batch=4, heads=4, kv_heads=2, seq_len=N)
+    if kind == "window":
+        lay = dict(causal=True, unit="tokens", window_left=300, window_right=0, global_keys=5,
+                   global_queries=0, bitmap=None)
+    else:
+        nb = -(-N // 128)
+        bm = np.random.default_rng(9).random((4, nb, nb)) < 0.3
+        bm[:, np.arange(nb), np.arange(nb)] = True
+        lay = dict(causal=False, unit="blocks", window_left=-1, window_right=-1, global_keys=0,
+                   global_queries=0, bitmap=torch.from_numpy(bm))
+    return w, lay, lens
+
+
+@pytest.mark.parametrize("kind", ["window", "bitmap", "split"])
+def test_backward_varlen_parity(kind):
+    """Batch entry b uses its first lens[b] positions: its gradients match the
+    oracle's on the trimmed sequence, rows beyond the length are zero, and
+    the NaN padding of Q, K, V and dO is never read."""
+    w, lay, lens = _varlen_case(kind)
+    say(f"[bwd-varlen] {kind} B={w.batch} H={w.heads}/{w.kv_heads} Nmax={w.seq_len} lens={lens}")
+    q, k, v = wl.make_qkv(w, "cpu")
+    do = wl.make_dout(w, "cpu")
+    for b, L in enumerate(lens):
+        for t in (q, k, v, do):
+            t[b, :, L:] = float("nan")
+    p = gpu_plan(w, lay)
+    if kind == "split":
+        work = p.work_kv()
+        assert len(work[work >= 0]) > len(np.unique(work[work >= 0])), "expected split columns"
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    out, lse = bsattn.forward_varlen(qc, kc, vc, p, sl)
+    dq, dk, dv = bsattn.backward_varlen(qc, kc, vc, out, lse, doc, p, sl)
+    torch.cuda.synchronize()
+    dq, dk, dv = (x.float().cpu().numpy() for x in (dq, dk, dv))
+    for b, L in enumerate(lens):
+        for name, g in (("dQ", dq), ("dK", dk), ("dV", dv)):
+            assert np.all(g[b, :, L:] == 0), f"entry {b}: {name} rows beyond {L} not zero"
+        if L == 0:
+            continue
+        ly = dict(lay)
+        if ly["bitmap"] is not None:
+            nbl = -(-L // 128)
+            ly["bitmap"] = ly["bitmap"][:, :nbl, :nbl]
+        sl_b = (slice(b, b + 1), slice(None), slice(0, L))
+        rq, rk, rv = oracle.backward(q[sl_b], k[sl_b], v[sl_b], do[sl_b], ly, w.block)
+        check(f"entry {b} (L={L}) dQ", dq[sl_b], rq)
+        check(f"entry {b} (L={L}) dK", dk[sl_b], rk)
+        check(f"entry {b} (L={L}) dV", dv[sl_b], rv)
+
+
+@pytest.mark.parametrize("N", [1500, 1024])
+def test_backward_varlen_full_lengths_equal_plain_backward(N):
+    """With every length at the maximum, the variable-length backward gives
+    bit for bit what bsa_backward gives."""
+    w = wl.WORKLOADS["gqa256k"].with_shape(name="varlen-full", batch=2, heads=4, kv_heads=2, seq_len=N)
+    lay = wl.layout_of(w)
+    q, k, v = (x.cuda() for x in wl.make_qkv(w, "cpu"))
+    do = wl.make_dout(w, "cuda")
+    p = gpu_plan(w, lay)
+    out, lse = bsattn.forward(q, k, v, p)
+    g1 = bsattn.backward(q, k, v, out, lse, do, p)
+    g2 = bsattn.backward_varlen(q, k, v, out, lse, do, p, torch.full((2,), N, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_backward_varlen_rejects_bad_arguments():
+    w = wl.WORKLOADS["tiny_f32"]
+    p = gpu_plan(w, wl.layout_of(w))
+    x = wl.make_qkv(w, "cpu")[0].cuda()
+    lens = torch.full((1,), 1024, dtype=torch.int32, device="cuda")
+    ptr = x.data_ptr()
+    st = bsattn.lib().bsa_backward_varlen(ptr, ptr, ptr, ptr, ptr, ptr, p.handle, lens.data_ptr(), ptr, ptr, ptr,
+                                          ptr, None)
+    assert st == bsattn.ERR_UNSUPPORTED                     # fp32: no variable-length kernels
+    wb = wl.small_variant(wl.WORKLOADS["window16k"], 1024, heads=2, kv_heads=2)
+    pb = gpu_plan(wb, wl.layout_of(wb))
+    y = wl.make_qkv(wb, "cpu")[0].cuda()
+    host_lens = torch.full((1,), 512, dtype=torch.int32)
+    ptr = y.data_ptr()
+    st = bsattn.lib().bsa_backward_varlen(ptr, ptr, ptr, ptr, ptr, ptr, pb.handle, host_lens.data_ptr(), ptr, ptr,
+                                          ptr, ptr, None)
+    assert st == bsattn.ERR_INVALID_ARGUMENT                # host memory for seq_lens
