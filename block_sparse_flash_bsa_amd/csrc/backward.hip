@@ -707,9 +707,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // Split columns: dK = scale * sum of the chunks' partials, dV = their sum, in
-// chunk order (deterministic); one workgroup per split column, 4 values per
-// thread and step.
+// chunk order (deterministic); kReduceParts workgroups per split column
+// (blockIdx.y), 4 values per thread.
 // ---------------------------------------------------------------------------
+constexpr int kReduceParts = 2 * kB * kD / 4 / kThreads;   // 32
+
 __global__ __launch_bounds__(kThreads) void bwd_kv_reduce(BwdParams p) {
   const int item = p.kv_reduce[4 * blockIdx.x];
   const int first = p.kv_reduce[4 * blockIdx.x + 1];
@@ -718,20 +720,19 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_reduce(BwdParams p) {
   const int bk = item / p.nb;
   const int hk = bk % p.Hkv, b = bk / p.Hkv;
   const int64_t row0 = (int64_t(b) * p.Hkv + hk) * p.N + int64_t(j) * kB;
-  for (int v = threadIdx.x; v < 2 * kB * kD / 4; v += kThreads) {
-    const int tensor = v / (kB * kD / 4);              // 0: dK, 1: dV
-    const int e = 4 * (v % (kB * kD / 4));             // element (key * 128 + d) of the tile
-    if (int64_t(j) * kB + e / kD >= p.N) continue;     // beyond a ragged sequence's end
-    f32x4 acc = f32x4{};
-    for (int c = 0; c < count; ++c)
-      acc += *reinterpret_cast<const f32x4*>(p.kv_scratch + (int64_t(first + c) * 2 + tensor) * kB * kD + e);
-    const float mul = tensor == 0 ? p.scale : 1.f;
-    u32x2 pk;
-    pk[0] = uint32_t(bf16_bits(acc[0] * mul)) | (uint32_t(bf16_bits(acc[1] * mul)) << 16);
-    pk[1] = uint32_t(bf16_bits(acc[2] * mul)) | (uint32_t(bf16_bits(acc[3] * mul)) << 16);
-    uint16_t* const dst = (tensor == 0 ? p.dk : p.dv) + row0 * kD + e;
-    *reinterpret_cast<u32x2*>(dst) = pk;
-  }
+  const int v = blockIdx.y * kThreads + threadIdx.x;
+  const int tensor = v / (kB * kD / 4);              // 0: dK, 1: dV
+  const int e = 4 * (v % (kB * kD / 4));             // element (key * 128 + d) of the tile
+  if (int64_t(j) * kB + e / kD >= p.N) return;       // beyond a ragged sequence's end
+  f32x4 acc = f32x4{};
+  for (int c = 0; c < count; ++c)
+    acc += *reinterpret_cast<const f32x4*>(p.kv_scratch + (int64_t(first + c) * 2 + tensor) * kB * kD + e);
+  const float mul = tensor == 0 ? p.scale : 1.f;
+  u32x2 pk;
+  pk[0] = uint32_t(bf16_bits(acc[0] * mul)) | (uint32_t(bf16_bits(acc[1] * mul)) << 16);
+  pk[1] = uint32_t(bf16_bits(acc[2] * mul)) | (uint32_t(bf16_bits(acc[3] * mul)) << 16);
+  uint16_t* const dst = (tensor == 0 ? p.dk : p.dv) + row0 * kD + e;
+  *reinterpret_cast<u32x2*>(dst) = pk;
 }
 
 // ---------------------------------------------------------------------------
@@ -1065,7 +1066,8 @@ bsa_status_t backward_impl(const void* q, const void* k, const void* v, const vo
     err = hipGetLastError();
   }
   if (err == hipSuccess && !plan->kv_reduce.empty()) {
-    hipLaunchKernelGGL(bwd_kv_reduce, dim3(unsigned(plan->kv_reduce.size())), dim3(kThreads), 0, s, prm);
+    hipLaunchKernelGGL(bwd_kv_reduce, dim3(unsigned(plan->kv_reduce.size()), kReduceParts), dim3(kThreads), 0, s,
+                       prm);
     err = hipGetLastError();
   }
   if (err != hipSuccess) return fail(BSA_ERR_DEVICE, "backward kernel launch failed: %s", hipGetErrorString(err));
