@@ -530,3 +530,23 @@ def test_backward_varlen_rejects_bad_arguments():
     st = bsattn.lib().bsa_backward_varlen(ptr, ptr, ptr, ptr, ptr, ptr, pb.handle, host_lens.data_ptr(), ptr, ptr,
                                           ptr, ptr, None)
     assert st == bsattn.ERR_INVALID_ARGUMENT                # host memory for seq_lens
+
+
+def test_varlen_lengths_are_clamped():
+    """Lengths below 0 or above seq_len act as 0 and seq_len (forward and
+    backward give bit for bit the results of the clamped lengths)."""
+    N = 1000
+    w = wl.WORKLOADS["gqa256k"].with_shape(name="varlen-clamp", batch=3, heads=4, kv_heads=2, seq_len=N)
+    lay = wl.layout_of(w)
+    q, k, v = (x.cuda() for x in wl.make_qkv(w, "cpu"))
+    do = wl.make_dout(w, "cuda")
+    p = gpu_plan(w, lay)
+    res = []
+    for lens in ([-7, N + 333, 2 ** 31 - 1], [0, N, N]):
+        sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        o, l = bsattn.forward_varlen(q, k, v, p, sl)
+        res.append((o, l) + bsattn.backward_varlen(q, k, v, o, l, do, p, sl))
+    torch.cuda.synchronize()
+    for name, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), *res):
+        assert torch.equal(a, b), f"{name} differs"
+    assert torch.all(res[0][0][0] == 0) and torch.all(res[0][1][0] == -float("inf"))
