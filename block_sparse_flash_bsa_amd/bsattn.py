@@ -33,7 +33,8 @@ SCHEDULE_DEFAULT, SCHEDULE_XCD, SCHEDULE_LPT, SCHEDULE_ROWMAJOR = 0, 1, 2, 3
 # Every entry point include/bsattn.h declares.
 EXPORTS = ("bsa_plan", "bsa_plan_host", "bsa_plan_destroy", "bsa_plan_csr", "bsa_plan_get_info",
            "bsa_plan_work", "bsa_plan_active_blocks", "bsa_plan_dynamic", "bsa_plan_set_bitmap",
-           "bsa_plan_read_csr", "bsa_forward", "bsa_plan_csr_transposed", "bsa_plan_work_kv",
+           "bsa_plan_read_csr", "bsa_plan_read_csr_transposed", "bsa_forward",
+           "bsa_plan_csr_transposed", "bsa_plan_work_kv",
            "bsa_backward", "bsa_forward_varlen", "bsa_backward_varlen", "bsa_status_string", "bsa_last_error",
            "bsa_abi_version")
 
@@ -91,6 +92,7 @@ def lib():
     L.bsa_plan_set_bitmap.argtypes = [P, c_void_p, c_void_p, c_void_p]
     L.bsa_plan_read_csr.argtypes = [P, c_int32, POINTER(c_int32), POINTER(c_int32), POINTER(c_uint8),
                                     c_int64, POINTER(c_int64)]
+    L.bsa_plan_read_csr_transposed.argtypes = L.bsa_plan_read_csr.argtypes
     L.bsa_forward.argtypes = [c_void_p, c_void_p, c_void_p, P, c_void_p, c_void_p, c_void_p]
     L.bsa_plan_csr_transposed.argtypes = [P, c_int32, POINTER(POINTER(c_int32)), POINTER(POINTER(c_int32)),
                                           POINTER(POINTER(c_uint8)), POINTER(c_int64)]
@@ -104,8 +106,8 @@ def lib():
     L.bsa_last_error.restype = c_char_p
     L.bsa_abi_version.restype = c_int32
     for name in ("bsa_plan", "bsa_plan_host", "bsa_plan_csr", "bsa_plan_get_info", "bsa_plan_work",
-                 "bsa_plan_dynamic", "bsa_plan_set_bitmap", "bsa_plan_read_csr", "bsa_forward",
-                 "bsa_plan_csr_transposed", "bsa_plan_work_kv", "bsa_backward", "bsa_forward_varlen",
+                 "bsa_plan_dynamic", "bsa_plan_set_bitmap", "bsa_plan_read_csr", "bsa_plan_read_csr_transposed",
+                 "bsa_forward", "bsa_plan_csr_transposed", "bsa_plan_work_kv", "bsa_backward", "bsa_forward_varlen",
                  "bsa_backward_varlen"):
         getattr(L, name).restype = c_int32
     _lib = L
@@ -205,16 +207,25 @@ class Plan:
 
     def read_csr(self, layout_head: int = 0):
         """bsa_plan_read_csr: the device CSR of a dynamic plan, in the format of csr()."""
+        rp, ci, fl = self._read_device(lib().bsa_plan_read_csr, layout_head)
+        return {"row_ptr": rp, "col_idx": ci, "flags": fl}
+
+    def read_csr_transposed(self, layout_head: int = 0):
+        """bsa_plan_read_csr_transposed: the device-built transposed lists of a
+        dynamic plan, in the format of csr_transposed()."""
+        cp, ri, fl = self._read_device(lib().bsa_plan_read_csr_transposed, layout_head)
+        return {"col_ptr": cp, "row_idx": ri, "flags": fl}
+
+    def _read_device(self, fn, layout_head):
         nb = self.info["num_blocks"]
-        rp = np.zeros(nb + 1, np.int32)
+        ptr = np.zeros(nb + 1, np.int32)
         n = c_int64()
         cap = nb * nb
-        ci = np.zeros(max(cap, 1), np.int32)
+        idx = np.zeros(max(cap, 1), np.int32)
         fl = np.zeros(max(cap, 1), np.uint8)
-        _check(lib().bsa_plan_read_csr(self.handle, layout_head,
-                                       rp.ctypes.data_as(POINTER(c_int32)), ci.ctypes.data_as(POINTER(c_int32)),
-                                       fl.ctypes.data_as(POINTER(c_uint8)), cap, ctypes.byref(n)))
-        return {"row_ptr": rp, "col_idx": ci[:n.value].copy(), "flags": fl[:n.value].copy()}
+        _check(fn(self.handle, layout_head, ptr.ctypes.data_as(POINTER(c_int32)), idx.ctypes.data_as(POINTER(c_int32)),
+                  fl.ctypes.data_as(POINTER(c_uint8)), cap, ctypes.byref(n)))
+        return ptr, idx[:n.value].copy(), fl[:n.value].copy()
 
     def work(self):
         w = POINTER(c_int32)()

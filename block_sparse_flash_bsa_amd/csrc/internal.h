@@ -74,10 +74,12 @@ struct bsa_plan {
   float* d_kv_scratch = nullptr;               // [kv_partials][2][128][128] float32
   void* dev_scratch = nullptr;                 // allocation behind d_kv_scratch
   // Dynamic plans: the CSR is written on the device by bsa_plan_set_bitmap;
-  // d_counts is its per-row scratch [layout_heads * nb].
+  // d_counts is its per-row scratch [layout_heads * nb], d_scan the scan's
+  // per-block sums [ceil(layout_heads * nb / 1024) + 1].
   int32_t dynamic = 0;
   int64_t entry_capacity = 0;
   int32_t* d_counts = nullptr;
+  int64_t* d_scan = nullptr;
 };
 
 namespace bsa {

@@ -532,7 +532,7 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
     return fail(BSA_ERR_DEVICE, "hipGetDevice failed: no usable HIP device");
   }
   // [rows | counts | entries | work | transposed rows | transposed entries |
-  // dK/dV work], each part 256-byte aligned.
+  // dK/dV work | scan block sums], each part 256-byte aligned.
   const size_t rows = size_t(P->layout_heads) * P->nb;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t off_counts = up(rows * sizeof(bsa::RowDesc));
@@ -541,7 +541,8 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
   const size_t off_cols = off_work + up(P->work.size() * sizeof(int32_t));
   const size_t off_entries_t = off_cols + up(rows * sizeof(bsa::RowDesc));
   const size_t off_work_kv = off_entries_t + up(size_t(cap) * sizeof(int32_t));
-  const size_t bytes = off_work_kv + P->kv_desc.size() * sizeof(Plan::KvDesc) + 16;
+  const size_t off_scan = off_work_kv + up(P->kv_desc.size() * sizeof(Plan::KvDesc));
+  const size_t bytes = off_scan + ((rows + 1023) / 1024 + 1) * sizeof(int64_t);
   hipError_t err = hipMalloc(&P->dev_mem, bytes);
   if (err != hipSuccess) {
     P->dev_mem = nullptr;
@@ -571,6 +572,7 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
   P->d_cols = reinterpret_cast<const bsa::RowDesc*>(base + off_cols);
   P->d_entries_t = reinterpret_cast<const int32_t*>(base + off_entries_t);
   P->d_work_kv = reinterpret_cast<const int32_t*>(base + off_work_kv);
+  P->d_scan = reinterpret_cast<int64_t*>(base + off_scan);
   P->d_kv_reduce = nullptr;
   P->info.on_device = 1;
   *out = P;

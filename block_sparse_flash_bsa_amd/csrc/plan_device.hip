@@ -6,8 +6,9 @@
 // of layout head hl is an entry iff bitmap[hl][i][j] != 0 and, for a causal
 // layout, j <= i; the diagonal tile of a causal layout is PARTIAL (the
 // token-exact causal cut), every other entry FULL.  Entries are ascending in
-// j.  Three kernels: count the entries of each row, scan the counts into row
-// offsets, write each row's entries.  The per-query-block lists follow step
+// j.  Three steps: count the entries of each row, scan the counts into row
+// offsets (three small kernels), write each row's entries; then the same for
+// the k-block columns the backward walks.  The per-query-block lists follow step
 // three of "How Does Flash-MSA Sparse Attention Work?" and the precomputed
 // block offsets of the FAQ on sparse kernels slower than dense ("How Do
 // Sparse Attention Kernels Work in GPU Clusters?"); building them on the
@@ -25,7 +26,6 @@ namespace bsa {
 namespace {
 
 constexpr int kRowThreads = 256;    // threads per row (4 waves)
-constexpr int kScanThreads = 1024;
 
 // Sum of v over the workgroup (blockDim.x == kRowThreads); all threads get it.
 __device__ __forceinline__ int block_sum(int v, int* red) {
@@ -53,32 +53,91 @@ __global__ __launch_bounds__(kRowThreads) void count_rows(const uint8_t* __restr
   if (threadIdx.x == 0) counts[row] = total;
 }
 
-// rows[row] = {exclusive prefix of counts, counts[row]}; *d_nnz = total.
-// One workgroup; thread t owns a contiguous run of rows.
-__global__ __launch_bounds__(kScanThreads) void scan_rows(const int32_t* __restrict__ counts, int n,
-                                                          RowDesc* __restrict__ rows, int64_t* d_nnz) {
-  __shared__ int64_t part[kScanThreads];
-  const int t = threadIdx.x;
-  const int per = (n + kScanThreads - 1) / kScanThreads;
-  const int a = min(n, t * per), b = min(n, a + per);
-  int64_t s = 0;
-  for (int x = a; x < b; ++x) s += counts[x];
-  part[t] = s;
+// rows[x] = {exclusive prefix of counts, counts[x]} over all n rows, and
+// *d_nnz = the total: per-block sums of kScanBlock counts, one workgroup
+// scanning those sums in place (sums[nblk] = total), and each block's local
+// scan offset by its sum's prefix.
+constexpr int kScanBlock = 1024;
+constexpr int kScanWaves = kScanBlock / 64;
+constexpr int kSmallScanBlocks = 8;     // up to this many blocks of rows: one-workgroup scan
+
+// Inclusive scan of v over the workgroup (blockDim.x == kScanBlock); total
+// receives the workgroup's sum.  wsum: kScanWaves values of LDS.
+__device__ __forceinline__ long long block_scan(long long v, long long* wsum, long long& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const long long y = __shfl_up(v, d);
+    if (lane >= d) v += y;
+  }
+  if (lane == 63) wsum[wave] = v;
   __syncthreads();
-  // Inclusive Hillis-Steele scan of the per-thread sums.
-  for (int off = 1; off < kScanThreads; off <<= 1) {
-    const int64_t add = t >= off ? part[t - off] : 0;
-    __syncthreads();
-    part[t] += add;
-    __syncthreads();
+  if (wave == 0) {
+    long long w = lane < kScanWaves ? wsum[lane] : 0;
+#pragma unroll
+    for (int d = 1; d < kScanWaves; d <<= 1) {
+      const long long y = __shfl_up(w, d);
+      if (lane >= d) w += y;
+    }
+    if (lane < kScanWaves) wsum[lane] = w;
   }
-  int64_t start = part[t] - s;
-  for (int x = a; x < b; ++x) {
-    const int32_t c = counts[x];
-    rows[x] = {int32_t(start), c};
-    start += c;
+  __syncthreads();
+  total = wsum[kScanWaves - 1];
+  return v + (wave ? wsum[wave - 1] : 0);
+}
+
+__global__ __launch_bounds__(kScanBlock) void scan_block_sums(const int32_t* __restrict__ counts, int n,
+                                                              int64_t* __restrict__ sums) {
+  __shared__ long long wsum[kScanWaves];
+  const int x = blockIdx.x * kScanBlock + threadIdx.x;
+  long long total;
+  block_scan(x < n ? counts[x] : 0, wsum, total);
+  if (threadIdx.x == 0) sums[blockIdx.x] = total;
+}
+
+__global__ __launch_bounds__(kScanBlock) void scan_sums(int64_t* __restrict__ sums, int nblk) {
+  __shared__ long long wsum[kScanWaves];
+  long long carry = 0;
+  for (int c0 = 0; c0 < nblk; c0 += kScanBlock) {
+    const int x = c0 + threadIdx.x;
+    const long long v = x < nblk ? sums[x] : 0;
+    long long total;
+    const long long inc = block_scan(v, wsum, total);
+    __syncthreads();                                   // wsum is reused by the next chunk
+    if (x < nblk) sums[x] = carry + inc - v;           // exclusive prefix
+    carry += total;
   }
-  if (t == kScanThreads - 1 && d_nnz) *d_nnz = part[t];
+  if (threadIdx.x == 0) sums[nblk] = carry;
+}
+
+// The whole scan in one workgroup, chunk by chunk (few rows: one launch
+// instead of three).
+__global__ __launch_bounds__(kScanBlock) void scan_small(const int32_t* __restrict__ counts, int n,
+                                                         RowDesc* __restrict__ rows, int64_t* d_nnz) {
+  __shared__ long long wsum[kScanWaves];
+  long long carry = 0;
+  for (int c0 = 0; c0 < n; c0 += kScanBlock) {
+    const int x = c0 + threadIdx.x;
+    const int32_t c = x < n ? counts[x] : 0;
+    long long total;
+    const long long inc = block_scan(c, wsum, total);
+    __syncthreads();                                   // wsum is reused by the next chunk
+    if (x < n) rows[x] = {int32_t(carry + inc - c), c};
+    carry += total;
+  }
+  if (d_nnz && threadIdx.x == 0) *d_nnz = carry;
+}
+
+__global__ __launch_bounds__(kScanBlock) void scan_apply(const int32_t* __restrict__ counts, int n,
+                                                         const int64_t* __restrict__ sums, int nblk,
+                                                         RowDesc* __restrict__ rows, int64_t* d_nnz) {
+  __shared__ long long wsum[kScanWaves];
+  const int x = blockIdx.x * kScanBlock + threadIdx.x;
+  const int32_t c = x < n ? counts[x] : 0;
+  long long total;
+  const long long inc = block_scan(c, wsum, total);
+  if (x < n) rows[x] = {int32_t(sums[blockIdx.x] + inc - c), c};
+  if (d_nnz && blockIdx.x == 0 && threadIdx.x == 0) *d_nnz = sums[nblk];
 }
 
 // The entries of each row, ascending: entry = (j << 1) | partial.
@@ -108,45 +167,76 @@ __global__ __launch_bounds__(kRowThreads) void fill_rows(const uint8_t* __restri
   }
 }
 
-// The transposed CSR for the backward: counts[col] = entries of column
-// (layout head * nb + j), i.e. the q-blocks i with bitmap[hl][i][j] != 0 (and
-// i >= j for a causal layout).  The column is read with stride nb.
-__global__ __launch_bounds__(kRowThreads) void count_cols(const uint8_t* __restrict__ bm, int nb, int causal,
-                                                          int32_t* __restrict__ counts) {
-  __shared__ int red[kRowThreads / 64];
-  const int col = blockIdx.x;
-  const int j = col % nb;
-  const uint8_t* c0 = bm + size_t(col / nb) * nb * nb + j;
-  int c = 0;
-  for (int i = (causal ? j : 0) + threadIdx.x; i < nb; i += kRowThreads) c += c0[size_t(i) * nb] != 0;
-  const int total = block_sum(c, red);
-  if (threadIdx.x == 0) counts[col] = total;
+// The transposed CSR for the backward: the q-blocks i of each k-block column
+// (layout head * nb + j) with bitmap[hl][i][j] != 0 (and i >= j for a causal
+// layout), ascending, entry = (i << 1) | partial.  One workgroup per strip of
+// kStrip columns of one layout head: lane l of every wave owns column
+// j0 + l, so each wave reads kStrip consecutive bytes of a row per load, and
+// wave w owns the contiguous row chunk [w * chunk, (w + 1) * chunk).  The
+// count kernel adds the chunks' counts; the fill kernel recounts its chunk,
+// takes the counts of the chunks above it as its offset in the column's list
+// and writes its entries in row order, so every list comes out ascending.
+constexpr int kStrip = 64;
+constexpr int kChunks = 16;
+constexpr int kStripThreads = kStrip * kChunks;
+
+struct StripCursor {
+  const uint8_t* col;   // bitmap byte (row 0, this lane's column)
+  int j, i0, i1;        // column; rows [i0, i1) of this wave's chunk
+  bool valid;
+};
+
+__device__ __forceinline__ StripCursor strip_cursor(const uint8_t* bm, int nb, int causal) {
+  const int strips = (nb + kStrip - 1) / kStrip;
+  const int hl = blockIdx.x / strips, s = blockIdx.x % strips;
+  const int lane = threadIdx.x % kStrip, w = threadIdx.x / kStrip;
+  const int chunk = (nb + kChunks - 1) / kChunks;
+  StripCursor c;
+  c.j = s * kStrip + lane;
+  c.valid = c.j < nb;
+  c.col = bm + size_t(hl) * nb * nb + (c.valid ? c.j : 0);
+  c.i0 = min(nb, w * chunk);
+  c.i1 = min(nb, c.i0 + chunk);
+  if (causal && c.i0 < c.j) c.i0 = min(c.j, c.i1);
+  return c;
 }
 
-// The entries of each column, ascending in i: entry = (i << 1) | partial.
-__global__ __launch_bounds__(kRowThreads) void fill_cols(const uint8_t* __restrict__ bm, int nb, int causal,
-                                                         const RowDesc* __restrict__ cols,
-                                                         int32_t* __restrict__ entries) {
-  __shared__ int wsum[kRowThreads / 64];
-  const int col = blockIdx.x;
-  const int j = col % nb;
-  const uint8_t* c0 = bm + size_t(col / nb) * nb * nb + j;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int32_t* out = entries + cols[col].start;
-  int base = 0;
-  for (int i0 = causal ? j : 0; i0 < nb; i0 += kRowThreads) {
-    const int i = i0 + threadIdx.x;
-    const bool on = i < nb && c0[size_t(i) * nb] != 0;
-    const uint64_t m = __ballot(on);
-    const int below = __popcll(m & ((uint64_t(1) << lane) - 1));
-    if (lane == 0) wsum[wave] = __popcll(m);
-    __syncthreads();
-    int off = base;
-    for (int w = 0; w < wave; ++w) off += wsum[w];
-    if (on) out[off + below] = (i << 1) | ((causal && i == j) ? 1 : 0);
-    base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
+__device__ __forceinline__ int strip_count(const StripCursor& c, int nb) {
+  int n = 0;
+  if (c.valid)
+    for (int i = c.i0; i < c.i1; ++i) n += c.col[size_t(i) * nb] != 0;
+  return n;
+}
+
+__global__ __launch_bounds__(kStripThreads) void count_cols(const uint8_t* __restrict__ bm, int nb, int causal,
+                                                            int32_t* __restrict__ counts) {
+  __shared__ int part[kChunks][kStrip];
+  const StripCursor c = strip_cursor(bm, nb, causal);
+  const int lane = threadIdx.x % kStrip, w = threadIdx.x / kStrip;
+  part[w][lane] = strip_count(c, nb);
+  __syncthreads();
+  if (w == 0 && c.valid) {
+    int total = 0;
+    for (int x = 0; x < kChunks; ++x) total += part[x][lane];
+    const int strips = (nb + kStrip - 1) / kStrip;
+    counts[(blockIdx.x / strips) * nb + c.j] = total;
   }
+}
+
+__global__ __launch_bounds__(kStripThreads) void fill_cols(const uint8_t* __restrict__ bm, int nb, int causal,
+                                                           const RowDesc* __restrict__ cols,
+                                                           int32_t* __restrict__ entries) {
+  __shared__ int part[kChunks][kStrip];
+  const StripCursor c = strip_cursor(bm, nb, causal);
+  const int lane = threadIdx.x % kStrip, w = threadIdx.x / kStrip;
+  part[w][lane] = strip_count(c, nb);
+  __syncthreads();
+  if (!c.valid) return;
+  const int strips = (nb + kStrip - 1) / kStrip;
+  int off = cols[(blockIdx.x / strips) * nb + c.j].start;
+  for (int x = 0; x < w; ++x) off += part[x][lane];
+  for (int i = c.i0; i < c.i1; ++i)
+    if (c.col[size_t(i) * nb] != 0) entries[off++] = (i << 1) | ((causal && i == c.j) ? 1 : 0);
 }
 
 }  // namespace
@@ -181,28 +271,44 @@ extern "C" bsa_status_t bsa_plan_set_bitmap(bsa_plan_t plan, const uint8_t* d_bi
   auto* d_entries = const_cast<int32_t*>(plan->d_entries);
   hipLaunchKernelGGL(count_rows, dim3(unsigned(rows)), dim3(kRowThreads), 0, s, d_bitmap, nb, plan->causal,
                      plan->d_counts);
-  hipLaunchKernelGGL(scan_rows, dim3(1), dim3(kScanThreads), 0, s, plan->d_counts, rows, d_rows, d_nnz);
+  const int nblk = (rows + kScanBlock - 1) / kScanBlock;
+  auto scan = [&](RowDesc* out, int64_t* nnz_out) {
+    if (nblk <= kSmallScanBlocks) {
+      hipLaunchKernelGGL(scan_small, dim3(1), dim3(kScanBlock), 0, s, plan->d_counts, rows, out, nnz_out);
+      return;
+    }
+    hipLaunchKernelGGL(scan_block_sums, dim3(unsigned(nblk)), dim3(kScanBlock), 0, s, plan->d_counts, rows,
+                       plan->d_scan);
+    hipLaunchKernelGGL(scan_sums, dim3(1), dim3(kScanBlock), 0, s, plan->d_scan, nblk);
+    hipLaunchKernelGGL(scan_apply, dim3(unsigned(nblk)), dim3(kScanBlock), 0, s, plan->d_counts, rows,
+                       plan->d_scan, nblk, out, nnz_out);
+  };
+  scan(d_rows, d_nnz);
   hipLaunchKernelGGL(fill_rows, dim3(unsigned(rows)), dim3(kRowThreads), 0, s, d_bitmap, nb, plan->causal,
                      d_rows, d_entries);
   // The same entries per k-block column, for the backward's dK/dV walk.
   auto* d_cols = const_cast<RowDesc*>(plan->d_cols);
   auto* d_entries_t = const_cast<int32_t*>(plan->d_entries_t);
-  hipLaunchKernelGGL(count_cols, dim3(unsigned(rows)), dim3(kRowThreads), 0, s, d_bitmap, nb, plan->causal,
+  const unsigned strips = unsigned(plan->layout_heads) * unsigned((nb + kStrip - 1) / kStrip);
+  hipLaunchKernelGGL(count_cols, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal,
                      plan->d_counts);
-  hipLaunchKernelGGL(scan_rows, dim3(1), dim3(kScanThreads), 0, s, plan->d_counts, rows, d_cols, nullptr);
-  hipLaunchKernelGGL(fill_cols, dim3(unsigned(rows)), dim3(kRowThreads), 0, s, d_bitmap, nb, plan->causal,
-                     d_cols, d_entries_t);
+  scan(d_cols, nullptr);
+  hipLaunchKernelGGL(fill_cols, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal, d_cols,
+                     d_entries_t);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(BSA_ERR_DEVICE, "planner launch failed: %s", hipGetErrorString(err));
   return BSA_OK;
 }
 
-extern "C" bsa_status_t bsa_plan_read_csr(bsa_plan_t plan, int32_t layout_head, int32_t* row_ptr,
-                                          int32_t* col_idx, uint8_t* flags, int64_t capacity, int64_t* nnz) {
-  using namespace bsa;
-  clear_error();
+namespace bsa {
+namespace {
+
+// Copies layout head layout_head of a device CSR (descriptors d_desc, entries
+// d_ent) to the host in the format of bsa_plan_csr.
+bsa_status_t read_device_csr(bsa_plan_t plan, const RowDesc* d_desc, const int32_t* d_ent, int32_t layout_head,
+                             int32_t* row_ptr, int32_t* col_idx, uint8_t* flags, int64_t capacity, int64_t* nnz) {
   if (!plan || !row_ptr || !nnz || (capacity > 0 && (!col_idx || !flags)))
-    return fail(BSA_ERR_INVALID_ARGUMENT, "NULL argument to bsa_plan_read_csr");
+    return fail(BSA_ERR_INVALID_ARGUMENT, "NULL argument to a device CSR read");
   if (!plan->dynamic) return fail(BSA_ERR_INVALID_ARGUMENT, "plan was not made by bsa_plan_dynamic");
   if (layout_head < 0 || layout_head >= plan->layout_heads)
     return fail(BSA_ERR_INVALID_ARGUMENT, "layout_head %d out of range [0, %d)", layout_head,
@@ -210,7 +316,7 @@ extern "C" bsa_status_t bsa_plan_read_csr(bsa_plan_t plan, int32_t layout_head, 
   const int nb = plan->nb;
   std::vector<RowDesc> rd(nb);
   if (hipDeviceSynchronize() != hipSuccess ||
-      (nb && hipMemcpy(rd.data(), plan->d_rows + size_t(layout_head) * nb, nb * sizeof(RowDesc),
+      (nb && hipMemcpy(rd.data(), d_desc + size_t(layout_head) * nb, nb * sizeof(RowDesc),
                        hipMemcpyDeviceToHost) != hipSuccess))
     return fail(BSA_ERR_DEVICE, "reading the device CSR failed: %s", hipGetErrorString(hipGetLastError()));
   const int64_t first = nb ? rd[0].start : 0;
@@ -219,8 +325,8 @@ extern "C" bsa_status_t bsa_plan_read_csr(bsa_plan_t plan, int32_t layout_head, 
     return fail(BSA_ERR_INVALID_ARGUMENT, "capacity %lld is below the head's %lld entries",
                 (long long)capacity, (long long)count);
   std::vector<int32_t> en(static_cast<size_t>(count));
-  if (count && hipMemcpy(en.data(), plan->d_entries + first, size_t(count) * sizeof(int32_t),
-                         hipMemcpyDeviceToHost) != hipSuccess)
+  if (count && hipMemcpy(en.data(), d_ent + first, size_t(count) * sizeof(int32_t), hipMemcpyDeviceToHost) !=
+                   hipSuccess)
     return fail(BSA_ERR_DEVICE, "reading the device CSR failed: %s", hipGetErrorString(hipGetLastError()));
   row_ptr[0] = 0;
   for (int i = 0; i < nb; ++i) row_ptr[i + 1] = int32_t(rd[i].start - first + rd[i].count);
@@ -230,4 +336,22 @@ extern "C" bsa_status_t bsa_plan_read_csr(bsa_plan_t plan, int32_t layout_head, 
   }
   *nnz = count;
   return BSA_OK;
+}
+
+}  // namespace
+}  // namespace bsa
+
+extern "C" bsa_status_t bsa_plan_read_csr(bsa_plan_t plan, int32_t layout_head, int32_t* row_ptr,
+                                          int32_t* col_idx, uint8_t* flags, int64_t capacity, int64_t* nnz) {
+  bsa::clear_error();
+  return bsa::read_device_csr(plan, plan ? plan->d_rows : nullptr, plan ? plan->d_entries : nullptr, layout_head,
+                              row_ptr, col_idx, flags, capacity, nnz);
+}
+
+extern "C" bsa_status_t bsa_plan_read_csr_transposed(bsa_plan_t plan, int32_t layout_head, int32_t* col_ptr,
+                                                     int32_t* row_idx, uint8_t* flags, int64_t capacity,
+                                                     int64_t* nnz) {
+  bsa::clear_error();
+  return bsa::read_device_csr(plan, plan ? plan->d_cols : nullptr, plan ? plan->d_entries_t : nullptr,
+                              layout_head, col_ptr, row_idx, flags, capacity, nnz);
 }

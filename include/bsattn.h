@@ -251,6 +251,13 @@ bsa_status_t bsa_plan_set_bitmap(bsa_plan_t plan, const uint8_t* d_bitmap, int64
 bsa_status_t bsa_plan_read_csr(bsa_plan_t plan, int32_t layout_head, int32_t* row_ptr,
                                int32_t* col_idx, uint8_t* flags, int64_t capacity, int64_t* nnz);
 
+/* The same for the transposed lists a dynamic plan builds on the device for
+ * the backward (per k-block column, the q-blocks that attend to it,
+ * ascending), in the format of bsa_plan_csr_transposed: col_ptr [nb + 1],
+ * row_idx and flags [capacity].  Synchronous; errors as bsa_plan_read_csr. */
+bsa_status_t bsa_plan_read_csr_transposed(bsa_plan_t plan, int32_t layout_head, int32_t* col_ptr,
+                                          int32_t* row_idx, uint8_t* flags, int64_t capacity, int64_t* nnz);
+
 /* Run the forward pass asynchronously on `stream` (a hipStream_t; NULL = the
  * default stream) of the plan's device.
  *   q   : device, [batch][num_heads][seq_len][head_dim], contiguous, dtype

@@ -52,6 +52,7 @@ def assert_same_csr(a, b, what):
     (1, 2, 37, 64, 0.3, True),
     (4, 4, 64, 64, 0.15, True),
     (16, 16, 256, 128, 0.10, False),
+    (2, 2, 130, 64, 0.2, True),
 ])
 def test_device_csr_matches_host_plan_and_oracle(lh, H, nb, bs, density, causal):
     bm = random_bitmap(lh, nb, density, seed=nb + lh)
@@ -73,8 +74,46 @@ def test_device_csr_matches_host_plan_and_oracle(lh, H, nb, bs, density, causal)
         assert_same_csr(got, hp.csr(h), f"head {h} vs host plan")
         assert_same_csr(got, ref[h], f"head {h} vs oracle")
         total += len(got["col_idx"])
+        # The transposed lists built on the device: per column j, the rows i
+        # whose oracle list holds j, ascending, with the same flags.
+        gt = dp.read_csr_transposed(h)
+        rp, ci, fl = (np.asarray(ref[h][key]) for key in ("row_ptr", "col_idx", "flags"))
+        cols = [[] for _ in range(nb)]
+        for i in range(nb):
+            for e in range(rp[i], rp[i + 1]):
+                cols[ci[e]].append((i, fl[e]))
+        want_ptr = np.concatenate([[0], np.cumsum([len(c) for c in cols])])
+        assert np.array_equal(gt["col_ptr"], want_ptr), f"head {h}: col_ptr"
+        assert np.array_equal(gt["row_idx"], [i for c in cols for i, _ in c]), f"head {h}: row_idx"
+        assert np.array_equal(gt["flags"], [f for c in cols for _, f in c]), f"head {h}: flags"
+        ht = hp.csr_transposed(h)
+        assert all(np.array_equal(gt[key], ht[key]) for key in ("col_ptr", "row_idx", "flags"))
     assert int(nnz.item()) == total == hp.info["nnz"]
-    say(f"  lh={lh} nb={nb} causal={causal}: {total} entries identical")
+    say(f"  lh={lh} nb={nb} causal={causal}: {total} entries identical, transposed lists too")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_device_csr_many_rows_matches_host_plan(causal):
+    """More rows than the one-workgroup scan takes (8 x 1100 rows): the
+    blocked three-kernel scan gives the host planner's CSR and transposed
+    lists bit for bit."""
+    lh, nb, bs = 8, 1100, 64
+    bm = random_bitmap(lh, nb, 0.01, seed=17)
+    bm[2, 700, :] = 1                                # a full row
+    bm[5, :, 9] = 1                                  # a full column
+    lay = bitmap_layout(bm, causal)
+    hp = bsattn.plan(1, lh, lh, nb * bs, 64, bs, torch.float32, lay, host_only=True)
+    dp = bsattn.plan_dynamic(1, lh, lh, nb * bs, 64, bs, torch.float32, causal, lh)
+    nnz = torch.zeros(1, dtype=torch.int64, device="cuda")
+    dp.set_bitmap(torch.from_numpy(bm).cuda(), nnz)
+    torch.cuda.synchronize()
+    assert int(nnz.item()) == hp.info["nnz"]
+    for h in range(lh):
+        assert_same_csr(dp.read_csr(h), hp.csr(h), f"head {h}")
+        gt, ht = dp.read_csr_transposed(h), hp.csr_transposed(h)
+        for key in ("col_ptr", "row_idx", "flags"):
+            assert np.array_equal(gt[key], ht[key]), f"head {h}: transposed {key}"
+    say(f"  causal={causal}: {hp.info['nnz']} entries identical")
 
 
 def test_forward_through_dynamic_plan_is_bitwise_the_static_one():
