@@ -226,9 +226,9 @@ bsa_status_t bsa_plan_dynamic(const bsa_problem_t* problem, const bsa_layout_t* 
 
 /* Rebuild a dynamic plan's device CSR from d_bitmap, device memory holding
  * [bitmap_heads][nb][nb] bytes (nonzero = active), asynchronously on `stream`
- * (a hipStream_t; NULL = default stream): three kernels count each row, scan
- * the counts and write the ascending entries, and three more do the same per
- * k-block column (the transposed lists bsa_backward walks).  A later bsa_forward on the
+ * (a hipStream_t; NULL = default stream): kernels count each row, scan the
+ * counts and write the ascending entries, then do the same per k-block
+ * column (the transposed lists bsa_backward walks).  A later bsa_forward on the
  * same stream (or after synchronisation) uses the new CSR.  If d_nnz is not
  * NULL it is a device pointer to one int64_t that receives the total number
  * of entries over all layout heads (multiply by batch, and by num_heads when
