@@ -449,3 +449,31 @@ def test_probe_library_exports_its_header():
     assert L.bsa_probe_mfma_flops(10, 3) == 3 * 4 * 4 * 10 * 32768
     L.bsa_probe_mfma.argtypes = [ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
     assert L.bsa_probe_mfma(0, 1, None, None) == 1          # argument errors return before any HIP call
+
+
+def test_varlen_and_transposed_read_argument_errors():
+    """Errors the variable-length entry points and the transposed-list read
+    report before touching the device."""
+    L = bsattn.lib()
+    one = ctypes.c_void_p(1)
+    assert L.bsa_forward_varlen(one, one, one, None, one, one, one, None) == bsattn.ERR_INVALID_ARGUMENT
+    assert L.bsa_backward_varlen(one, one, one, one, one, one, None, one, one, one, one, one, None) == \
+        bsattn.ERR_INVALID_ARGUMENT
+    f32 = bsattn.plan(1, 2, 2, 1024, 64, 64, torch.float32, spec(False, "blocks", 1, 1), host_only=True)
+    assert L.bsa_forward_varlen(one, one, one, f32.handle, one, one, one, None) == bsattn.ERR_UNSUPPORTED
+    assert L.bsa_backward_varlen(one, one, one, one, one, one, f32.handle, one, one, one, one, one, None) == \
+        bsattn.ERR_UNSUPPORTED
+    bf = bsattn.plan(2, 2, 2, 1024, 128, 128, torch.bfloat16, spec(True, "tokens", 300), host_only=True)
+    assert L.bsa_forward_varlen(one, one, one, bf.handle, None, one, one, None) == bsattn.ERR_INVALID_ARGUMENT
+    assert b"seq_lens" in L.bsa_last_error()
+    assert L.bsa_backward_varlen(one, one, one, one, one, one, bf.handle, None, one, one, one, one, None) == \
+        bsattn.ERR_INVALID_ARGUMENT
+    assert b"seq_lens" in L.bsa_last_error()
+    # The transposed lists of a static plan are read with bsa_plan_csr_transposed, not from the device.
+    cp = np.zeros(9, np.int32)
+    n = ctypes.c_int64()
+    i32 = ctypes.POINTER(ctypes.c_int32)
+    assert L.bsa_plan_read_csr_transposed(bf.handle, 0, cp.ctypes.data_as(i32), None, None, 0,
+                                          ctypes.byref(n)) == bsattn.ERR_INVALID_ARGUMENT
+    assert L.bsa_plan_read_csr_transposed(None, 0, cp.ctypes.data_as(i32), None, None, 0,
+                                          ctypes.byref(n)) == bsattn.ERR_INVALID_ARGUMENT
