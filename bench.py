@@ -255,6 +255,53 @@ def backward_context(names, steps=5):
     return res
 
 
+def lengths_context(steps=5):
+    """Sequence lengths the block does not divide, and variable-length batches,
+    on the 128K window+global rule at B=4, H=32, N=32K: the whole-block kernel,
+    the ragged-tail kernel at N - 64, and bsa_forward_varlen at full and at
+    mixed lengths; TFLOP/s counts the active tiles of each entry's own length."""
+    base = wl.WORKLOADS["winglobal128k"]
+    lay = wl.layout_of(base)
+    res = {}
+
+    def rate(flops, ms):
+        return round(flops / (ms * 1e-3) / 1e12, 1)
+
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in evs:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    N = 32768
+    for name, n in (("whole_blocks", N), ("ragged_tail", N - 64)):
+        w = base.with_shape(name=name, batch=4, seq_len=n)
+        p = plan_for(w, lay)
+        q, k, v = wl.make_qkv(w, "cuda")
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+        ms = timed(lambda: bsattn.forward(q, k, v, p, out, lse))
+        res[name] = {"seq_len": n, "ms_per_forward": round(ms, 4), "tflops": rate(p.flops(), ms)}
+        if name == "whole_blocks":
+            for lname, lens in (("varlen_full", [N] * 4), ("varlen_mixed", [N, 24000, 16000, 7000])):
+                sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+                ms = timed(lambda: bsattn.forward_varlen(q, k, v, p, sl, out, lse))
+                useful = sum(plan_for(base.with_shape(batch=1, seq_len=L), lay, host_only=True).flops()
+                             for L in lens)
+                res[lname] = {"seq_lens": lens, "ms_per_forward": round(ms, 4), "tflops": rate(useful, ms)}
+        del q, k, v, out, lse, p
+        torch.cuda.empty_cache()
+    log(f"[bench] lengths: {res}")
+    return res
+
+
 def mfma_probe(workgroups=512, iters=200000):
     """Sustained bf16 MFMA rate of this GPU (libbsattn_probe: independent
     v_mfma_f32_32x32x16_bf16 chains on register operands, 2 waves per SIMD on
@@ -413,6 +460,7 @@ def main():
         del q, k, v, out, lse
         torch.cuda.empty_cache()
         ctx["dynamic_plan"] = dynamic_plan_context()
+        ctx["lengths"] = lengths_context()
         ctx["backward"] = backward_context(["tiny_f32", "window16k", "random32k", "winglobal128k", "gqa256k"])
         result["context"] = ctx
     if not args.no_cpu_baseline:

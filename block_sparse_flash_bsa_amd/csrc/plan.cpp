@@ -259,7 +259,8 @@ void build_transpose(Plan& P) {
 
 // Launch order of the dK/dV kernel: items (b * Hkv + hk) * nb + j in
 // locality order (neighbouring k-blocks of one KV head share the q-blocks
-// they read), cut per XCD by cost.  An item's walk is the concatenation of
+// they read; KV head outer, batch entry next, as in the forward's order),
+// cut per XCD by cost.  An item's walk is the concatenation of
 // its group's transposed lists; walks longer than kv_chunk entries (twice the
 // mean, at least 64) are cut into chunks that run as separate workgroups and
 // write float32 partials, summed in chunk order by a reduction kernel, so a
@@ -285,7 +286,9 @@ void build_work_kv(Plan& P) {
   std::vector<Plan::KvDesc> pieces;
   P.kv_reduce.clear();
   int64_t partials = 0;
-  for (int64_t it = 0; it < items; ++it) {
+  for (int64_t l = 0; l < items; ++l) {
+    const int64_t j = l % nb, b = (l / nb) % B, hk = l / (nb * B);
+    const int64_t it = (b * Hkv + hk) * nb + j;
     const int64_t n = walk(it);
     if (n <= P.kv_chunk) {
       pieces.push_back({int32_t(it), 0, int32_t(n), -1});
@@ -336,11 +339,14 @@ void build_work(Plan& P) {
   } else {
     // Locality order: heads sharing a KV head and neighbouring q-blocks are
     // adjacent, so the workgroups running together on one XCD read the same
-    // K/V blocks through that XCD's L2.
+    // K/V blocks through that XCD's L2.  KV heads are the outer loop and
+    // batch entries the next, so every XCD's run holds all batch entries of
+    // its KV heads: entries of different lengths (a variable-length batch)
+    // load the XCDs evenly.
     std::vector<int32_t> loc;
     loc.reserve(items);
-    for (int64_t b = 0; b < B; ++b)
-      for (int64_t hk = 0; hk < H / group; ++hk)
+    for (int64_t hk = 0; hk < H / group; ++hk)
+      for (int64_t b = 0; b < B; ++b)
         for (int64_t i = 0; i < nb; ++i)
           for (int64_t g = 0; g < group; ++g) loc.push_back(int32_t((b * H + hk * group + g) * nb + i));
     P.work = xcd_slots(loc, cost);

@@ -130,9 +130,9 @@ def test_xcd_schedule_runs_are_local_and_balanced():
     for x in range(8):
         run = work[x::8]
         run = run[run >= 0]
-        i, h = run % nb, (run // nb) % H
-        # within a run: KV head major, then q-block, then the heads of the group
-        key = (h // group) * nb * group + i * group + h % group
+        i, h, b = run % nb, (run // nb) % H, run // (nb * H)
+        # within a run: KV head major, then batch entry, q-block, the heads of the group
+        key = (((h // group) * w.batch + b) * nb + i) * group + h % group
         assert np.all(np.diff(key) > 0)
         costs.append(int((lens[i] + 1).sum()))
     assert max(costs) - min(costs) <= lens.max() + 1
@@ -341,11 +341,15 @@ def test_kv_work_order_is_a_permutation(name):
     # every item is covered; only long walks (global-key columns) take several slots
     np.testing.assert_array_equal(np.unique(items), np.arange(w.batch * w.kv_heads * w.num_blocks))
     assert len(items) - len(np.unique(items)) < 0.05 * len(items)
-    # slot s runs on XCD s % 8: each XCD's items form one contiguous, ordered run of the item order
+    # slot s runs on XCD s % 8: each XCD's items form one contiguous, ordered
+    # run of the locality order (KV head, batch entry, k-block)
+    nb, B, Hkv = w.num_blocks, w.batch, w.kv_heads
     for x in range(8):
         run = work[x::8]
         run = run[run >= 0]
-        assert np.all(np.diff(run) >= 0) and np.all(np.diff(run) <= 1)
+        j, hk, b = run % nb, (run // nb) % Hkv, run // (nb * Hkv)
+        key = (hk * B + b) * nb + j
+        assert np.all(np.diff(key) >= 0) and np.all(np.diff(key) <= 1)
 
 
 def test_transposed_csr_errors():
@@ -477,3 +481,17 @@ def test_varlen_and_transposed_read_argument_errors():
                                           ctypes.byref(n)) == bsattn.ERR_INVALID_ARGUMENT
     assert L.bsa_plan_read_csr_transposed(None, 0, cp.ctypes.data_as(i32), None, None, 0,
                                           ctypes.byref(n)) == bsattn.ERR_INVALID_ARGUMENT
+
+
+def test_xcd_runs_hold_every_batch_entry():
+    """The XCD-local orders put KV heads outermost and batch entries next, so
+    each XCD's run holds all batch entries (variable-length batches stay
+    balanced across XCDs)."""
+    w = wl.WORKLOADS["gqa256k"].with_shape(name="b4", batch=4, heads=16, kv_heads=8, seq_len=8192)
+    p = host_plan(w, schedule=bsattn.SCHEDULE_XCD)
+    nb = w.num_blocks
+    for work, per_b in ((p.work(), nb * w.heads), (p.work_kv(), nb * w.kv_heads)):
+        for x in range(8):
+            run = work[x::8]
+            run = run[run >= 0]
+            assert set((run // per_b).tolist()) == set(range(w.batch)), f"XCD {x}"
