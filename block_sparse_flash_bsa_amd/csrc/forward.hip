@@ -251,14 +251,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   // u >= 4 V rows.
   auto dma_half_part = [&](int j, int hh, int u) {
     const int64_t row0 = int64_t(j) * kBN + hh * 64 + wave * 16;
-    if (kRagged && j == nbb - 1) {
-      // Last key block of the sequence: lane rows at or beyond Nb read row
-      // Nb - 1 (offsets from the block's first row, which is below Nb).
+    if (kRagged) {
+      // Rows relative to the tile's first row (below Nb), clamped to the
+      // last row of the sequence in its last block; one code path.
       const int64_t tile0 = int64_t(j) * kBN;
-      const int64_t rl = row0 + 4 * (u & 3) + lr;
-      const int64_t rc = rl < Nb ? rl : Nb - 1;
+      const int lim = j == nbb - 1 ? Nb - j * kBN - 1 : kBN - 1;
+      const int rl = hh * 64 + wave * 16 + 4 * (u & 3) + lr;
+      const int rc = rl < lim ? rl : lim;
       const uint32_t chunk = (u < 4 ? dko[u] : dvo) & 255u;
-      const uint32_t voff = uint32_t(rc - tile0) * 256u + chunk;
+      const uint32_t voff = uint32_t(rc) * 256u + chunk;
       if (u < 4)
         dma16(Kg + tile0 * (kD * 2), voff, Ka[hh] + wave * 16 * 256 + u * 1024);
       else
