@@ -170,73 +170,123 @@ __global__ __launch_bounds__(kRowThreads) void fill_rows(const uint8_t* __restri
 // The transposed CSR for the backward: the q-blocks i of each k-block column
 // (layout head * nb + j) with bitmap[hl][i][j] != 0 (and i >= j for a causal
 // layout), ascending, entry = (i << 1) | partial.  One workgroup per strip of
-// kStrip columns of one layout head: lane l of every wave owns column
-// j0 + l, so each wave reads kStrip consecutive bytes of a row per load, and
-// wave w owns the contiguous row chunk [w * chunk, (w + 1) * chunk).  The
-// count kernel adds the chunks' counts; the fill kernel recounts its chunk,
-// takes the counts of the chunks above it as its offset in the column's list
-// and writes its entries in row order, so every list comes out ascending.
+// kStrip * kVec columns of one layout head: lane l of every wave owns the kVec
+// columns j0 .. j0 + kVec - 1, j0 = strip start + kVec * l, and reads them
+// with one load per row (kVec = 4 when nb is a multiple of 4, so every row
+// of 4-byte groups is aligned; else 1), so each wave reads kStrip * kVec
+// consecutive bytes of a row per load; wave w owns the contiguous row chunk
+// [w * chunk, (w + 1) * chunk).  The count kernel adds the chunks' counts;
+// the fill kernel recounts its chunk, takes the counts of the chunks above it
+// as its offset in each column's list and writes its entries in row order,
+// so every list comes out ascending.
 constexpr int kStrip = 64;
 constexpr int kChunks = 16;
 constexpr int kStripThreads = kStrip * kChunks;
+constexpr int64_t kWideMinStrips = 256;   // 4-column lanes only with at least this many workgroups
 
 struct StripCursor {
-  const uint8_t* col;   // bitmap byte (row 0, this lane's column)
-  int j, i0, i1;        // column; rows [i0, i1) of this wave's chunk
+  const uint8_t* col;   // bitmap byte (row 0, this lane's first column)
+  int j0, i0, i1;       // first column; rows [i0, i1) of this wave's chunk
   bool valid;
 };
 
+template <int kVec>
+__device__ __forceinline__ int strips_of(int nb) {
+  return (nb + kStrip * kVec - 1) / (kStrip * kVec);
+}
+
+template <int kVec>
 __device__ __forceinline__ StripCursor strip_cursor(const uint8_t* bm, int nb, int causal) {
-  const int strips = (nb + kStrip - 1) / kStrip;
+  const int strips = strips_of<kVec>(nb);
   const int hl = blockIdx.x / strips, s = blockIdx.x % strips;
   const int lane = threadIdx.x % kStrip, w = threadIdx.x / kStrip;
   const int chunk = (nb + kChunks - 1) / kChunks;
   StripCursor c;
-  c.j = s * kStrip + lane;
-  c.valid = c.j < nb;
-  c.col = bm + size_t(hl) * nb * nb + (c.valid ? c.j : 0);
+  c.j0 = s * kStrip * kVec + lane * kVec;
+  c.valid = c.j0 < nb;                 // all kVec columns, as kVec divides nb
+  c.col = bm + size_t(hl) * nb * nb + (c.valid ? c.j0 : 0);
   c.i0 = min(nb, w * chunk);
   c.i1 = min(nb, c.i0 + chunk);
-  if (causal && c.i0 < c.j) c.i0 = min(c.j, c.i1);
+  // Under the causal cut, rows below the lane's first column hold none of its entries.
+  if (causal && c.i0 < c.j0) c.i0 = min(c.j0, c.i1);
   return c;
 }
 
-__device__ __forceinline__ int strip_count(const StripCursor& c, int nb) {
-  int n = 0;
-  if (c.valid)
-    for (int i = c.i0; i < c.i1; ++i) n += c.col[size_t(i) * nb] != 0;
-  return n;
+// The bytes of row i of the lane's columns (byte v of the result = column j0 + v).
+template <int kVec>
+__device__ __forceinline__ uint32_t strip_row(const StripCursor& c, int nb, int i) {
+  if constexpr (kVec == 4)
+    return *reinterpret_cast<const uint32_t*>(c.col + size_t(i) * nb);
+  else
+    return c.col[size_t(i) * nb];
 }
 
-__global__ __launch_bounds__(kStripThreads) void count_cols(const uint8_t* __restrict__ bm, int nb, int causal,
-                                                            int32_t* __restrict__ counts) {
-  __shared__ int part[kChunks][kStrip];
-  const StripCursor c = strip_cursor(bm, nb, causal);
-  const int lane = threadIdx.x % kStrip, w = threadIdx.x / kStrip;
-  part[w][lane] = strip_count(c, nb);
-  __syncthreads();
-  if (w == 0 && c.valid) {
-    int total = 0;
-    for (int x = 0; x < kChunks; ++x) total += part[x][lane];
-    const int strips = (nb + kStrip - 1) / kStrip;
-    counts[(blockIdx.x / strips) * nb + c.j] = total;
+template <int kVec>
+__device__ __forceinline__ bool strip_on(uint32_t x, int v, int i, int j0, int causal) {
+  return ((x >> (8 * v)) & 255u) != 0 && (!causal || i >= j0 + v);
+}
+
+template <int kVec>
+__device__ __forceinline__ void strip_count(const StripCursor& c, int nb, int causal, int (&n)[kVec]) {
+#pragma unroll
+  for (int v = 0; v < kVec; ++v) n[v] = 0;
+  if (!c.valid) return;
+  for (int i = c.i0; i < c.i1; ++i) {
+    const uint32_t x = strip_row<kVec>(c, nb, i);
+#pragma unroll
+    for (int v = 0; v < kVec; ++v) n[v] += strip_on<kVec>(x, v, i, c.j0, causal);
   }
 }
 
+template <int kVec>
+__global__ __launch_bounds__(kStripThreads) void count_cols(const uint8_t* __restrict__ bm, int nb, int causal,
+                                                            int32_t* __restrict__ counts) {
+  __shared__ int part[kChunks][kStrip * kVec];
+  const StripCursor c = strip_cursor<kVec>(bm, nb, causal);
+  const int lane = threadIdx.x % kStrip, w = threadIdx.x / kStrip;
+  int n[kVec];
+  strip_count<kVec>(c, nb, causal, n);
+#pragma unroll
+  for (int v = 0; v < kVec; ++v) part[w][lane * kVec + v] = n[v];
+  __syncthreads();
+  if (w == 0 && c.valid) {
+    const int hl = blockIdx.x / strips_of<kVec>(nb);
+#pragma unroll
+    for (int v = 0; v < kVec; ++v) {
+      int total = 0;
+      for (int x = 0; x < kChunks; ++x) total += part[x][lane * kVec + v];
+      counts[hl * nb + c.j0 + v] = total;
+    }
+  }
+}
+
+template <int kVec>
 __global__ __launch_bounds__(kStripThreads) void fill_cols(const uint8_t* __restrict__ bm, int nb, int causal,
                                                            const RowDesc* __restrict__ cols,
                                                            int32_t* __restrict__ entries) {
-  __shared__ int part[kChunks][kStrip];
-  const StripCursor c = strip_cursor(bm, nb, causal);
+  __shared__ int part[kChunks][kStrip * kVec];
+  const StripCursor c = strip_cursor<kVec>(bm, nb, causal);
   const int lane = threadIdx.x % kStrip, w = threadIdx.x / kStrip;
-  part[w][lane] = strip_count(c, nb);
+  int n[kVec];
+  strip_count<kVec>(c, nb, causal, n);
+#pragma unroll
+  for (int v = 0; v < kVec; ++v) part[w][lane * kVec + v] = n[v];
   __syncthreads();
   if (!c.valid) return;
-  const int strips = (nb + kStrip - 1) / kStrip;
-  int off = cols[(blockIdx.x / strips) * nb + c.j].start;
-  for (int x = 0; x < w; ++x) off += part[x][lane];
-  for (int i = c.i0; i < c.i1; ++i)
-    if (c.col[size_t(i) * nb] != 0) entries[off++] = (i << 1) | ((causal && i == c.j) ? 1 : 0);
+  const int hl = blockIdx.x / strips_of<kVec>(nb);
+  int off[kVec];
+#pragma unroll
+  for (int v = 0; v < kVec; ++v) {
+    off[v] = cols[hl * nb + c.j0 + v].start;
+    for (int x = 0; x < w; ++x) off[v] += part[x][lane * kVec + v];
+  }
+  for (int i = c.i0; i < c.i1; ++i) {
+    const uint32_t x = strip_row<kVec>(c, nb, i);
+#pragma unroll
+    for (int v = 0; v < kVec; ++v)
+      if (strip_on<kVec>(x, v, i, c.j0, causal))
+        entries[off[v]++] = (i << 1) | ((causal && i == c.j0 + v) ? 1 : 0);
+  }
 }
 
 }  // namespace
@@ -289,12 +339,25 @@ extern "C" bsa_status_t bsa_plan_set_bitmap(bsa_plan_t plan, const uint8_t* d_bi
   // The same entries per k-block column, for the backward's dK/dV walk.
   auto* d_cols = const_cast<RowDesc*>(plan->d_cols);
   auto* d_entries_t = const_cast<int32_t*>(plan->d_entries_t);
-  const unsigned strips = unsigned(plan->layout_heads) * unsigned((nb + kStrip - 1) / kStrip);
-  hipLaunchKernelGGL(count_cols, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal,
-                     plan->d_counts);
+  // 4-byte loads of 4 columns per lane when every row of the bitmap is 4-byte
+  // aligned and the wider strips still give a workgroup per CU.
+  const bool wide = nb % 4 == 0 && reinterpret_cast<uintptr_t>(d_bitmap) % 4 == 0 &&
+                    int64_t(plan->layout_heads) * ((nb + 4 * kStrip - 1) / (4 * kStrip)) >= kWideMinStrips;
+  const int vec = wide ? 4 : 1;
+  const unsigned strips = unsigned(plan->layout_heads) * unsigned((nb + kStrip * vec - 1) / (kStrip * vec));
+  if (vec == 4)
+    hipLaunchKernelGGL(count_cols<4>, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal,
+                       plan->d_counts);
+  else
+    hipLaunchKernelGGL(count_cols<1>, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal,
+                       plan->d_counts);
   scan(d_cols, nullptr);
-  hipLaunchKernelGGL(fill_cols, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal, d_cols,
-                     d_entries_t);
+  if (vec == 4)
+    hipLaunchKernelGGL(fill_cols<4>, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal, d_cols,
+                       d_entries_t);
+  else
+    hipLaunchKernelGGL(fill_cols<1>, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal, d_cols,
+                       d_entries_t);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(BSA_ERR_DEVICE, "planner launch failed: %s", hipGetErrorString(err));
   return BSA_OK;
