@@ -38,11 +38,13 @@
  * Only Guide You Need for Sparse Attention Kernels in Long-Context LLMs".
  *
  * Threading: calls on different plans may run concurrently; a plan may be
- * used by several streams at once (bsa_forward only reads it), except that
+ * used by several streams at once (the forwards only read it), except that
  * bsa_plan_set_bitmap rewrites a dynamic plan and must not overlap a forward
- * that uses it on another stream, and bsa_backward calls with one plan must
- * not overlap each other (they share the plan's partial-sum scratch).  The
- * last error string is thread-local.
+ * or backward that uses it on another stream (nor another set_bitmap: the
+ * plan's count and scan scratch is shared), and backward calls
+ * (bsa_backward, bsa_backward_varlen) with one plan must not overlap each
+ * other (they share the plan's partial-sum scratch).  The last error string
+ * is thread-local.
  */
 #ifndef BSATTN_H
 #define BSATTN_H
