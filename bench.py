@@ -257,9 +257,10 @@ def backward_context(names, steps=5):
 
 def lengths_context(steps=5):
     """Sequence lengths the block does not divide, and variable-length batches,
-    on the 128K window+global rule at B=4, H=32, N=32K: the whole-block kernel,
-    the ragged-tail kernel at N - 64, and bsa_forward_varlen at full and at
-    mixed lengths; TFLOP/s counts the active tiles of each entry's own length."""
+    on the 128K window+global rule at B=4, H=32, N=32K: the whole-block kernels,
+    the ragged-tail kernels at N - 64, and the variable-length forward and
+    backward at full and at mixed lengths; TFLOP/s counts the active tiles of
+    each entry's own length."""
     base = wl.WORKLOADS["winglobal128k"]
     lay = wl.layout_of(base)
     res = {}
@@ -285,18 +286,26 @@ def lengths_context(steps=5):
         w = base.with_shape(name=name, batch=4, seq_len=n)
         p = plan_for(w, lay)
         q, k, v = wl.make_qkv(w, "cuda")
+        do = wl.make_dout(w, "cuda")
         out = torch.empty_like(q)
         lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        delta = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
         ms = timed(lambda: bsattn.forward(q, k, v, p, out, lse))
-        res[name] = {"seq_len": n, "ms_per_forward": round(ms, 4), "tflops": rate(p.flops(), ms)}
+        bms = timed(lambda: bsattn.backward(q, k, v, out, lse, do, p, dq, dk, dv, delta))
+        # the backward's algorithmic work is 2.5x the forward's (5 GEMMs per tile against 2)
+        res[name] = {"seq_len": n, "ms_per_forward": round(ms, 4), "tflops": rate(p.flops(), ms),
+                     "ms_per_backward": round(bms, 4), "backward_tflops": rate(2.5 * p.flops(), bms)}
         if name == "whole_blocks":
             for lname, lens in (("varlen_full", [N] * 4), ("varlen_mixed", [N, 24000, 16000, 7000])):
                 sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
                 ms = timed(lambda: bsattn.forward_varlen(q, k, v, p, sl, out, lse))
+                bms = timed(lambda: bsattn.backward_varlen(q, k, v, out, lse, do, p, sl, dq, dk, dv, delta))
                 useful = sum(plan_for(base.with_shape(batch=1, seq_len=L), lay, host_only=True).flops()
                              for L in lens)
-                res[lname] = {"seq_lens": lens, "ms_per_forward": round(ms, 4), "tflops": rate(useful, ms)}
-        del q, k, v, out, lse, p
+                res[lname] = {"seq_lens": lens, "ms_per_forward": round(ms, 4), "tflops": rate(useful, ms),
+                              "ms_per_backward": round(bms, 4), "backward_tflops": rate(2.5 * useful, bms)}
+        del q, k, v, do, out, lse, dq, dk, dv, delta, p
         torch.cuda.empty_cache()
     log(f"[bench] lengths: {res}")
     return res
