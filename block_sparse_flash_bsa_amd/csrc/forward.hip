@@ -249,9 +249,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
                           uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)V1))};
   // Instruction u (0..7) of the 8 loads for half hh of tile j: u < 4 K rows,
   // u >= 4 V rows.
-  auto dma_half_part = [&](int j, int hh, int u) {
+  // clamp_c (compile time): the loads may reach rows at or beyond Nb, i.e.
+  // the entry ends inside block j; only the ragged instance uses it.
+  auto dma_half_part = [&](int j, int hh, int u, auto clamp_c) {
     const int64_t row0 = int64_t(j) * kBN + hh * 64 + wave * 16;
-    if (kRagged) {
+    if constexpr (kRagged && decltype(clamp_c)::value) {
       // Rows relative to the tile's first row (below Nb), clamped to the
       // last row of the sequence in its last block; one code path.
       const int64_t tile0 = int64_t(j) * kBN;
@@ -470,7 +472,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   // One CSR entry (two phases); the last one (no next tile to load) is peeled
   // off so the loop body issues its loads unconditionally.
   bf16x8 pq[4];
-  auto tile = [&](int e, auto next_c) {
+  // clamp_c: this tile's loads reach the entry's last block and the entry
+  // ends inside it (a uniform choice per tile, so the other tiles' loads take
+  // no address arithmetic).
+  auto tile = [&](int e, auto next_c, auto clamp_c) {
     constexpr bool has_next = decltype(next_c)::value;
     const int ent = ents[e0 + e];
     const int j = ent >> 1;
@@ -482,29 +487,41 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
     BSA_WAIT_BARRIER(0);                 // K half 0 of e and V half 1 of e-1 landed
     if (e > 0) pv_half(1, pq);
     qk_half(0, sq, [&](int u) {
-      if (u < 4) dma_half_part(j, 1, u);       // K half 1 of e
-      else dma_half_part(j, 0, u);             // V half 0 of e
+      if (u < 4) dma_half_part(j, 1, u, clamp_c);       // K half 1 of e
+      else dma_half_part(j, 0, u, clamp_c);             // V half 0 of e
     });
     softmax_half(sq, 0, j, partial, pq);
     BSA_WAIT_BARRIER(0);                 // K half 1 and V half 0 of e landed
     pv_half(0, pq);
     qk_half(1, sq, [&](int u) {
       if (u < 4) {
-        if constexpr (has_next) dma_half_part(jn, 0, u);   // K half 0 of e+1
+        if constexpr (has_next) dma_half_part(jn, 0, u, clamp_c);   // K half 0 of e+1
       } else {
-        dma_half_part(j, 1, u);                            // V half 1 of e
+        dma_half_part(j, 1, u, clamp_c);                            // V half 1 of e
       }
     });
     softmax_half(sq, 1, j, partial, pq);
   };
+  // The entry ends inside its last block (only then do loads need a clamp).
+  const bool ctail = kRagged && (Nb % kBN) != 0;
   if (ne > 0) {
     const int j0 = ents[e0] >> 1;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) dma_half_part(j0, 0, u);
+    for (int u = 0; u < 4; ++u) dma_half_part(j0, 0, u, std::true_type{});
   }
-  for (int e = 0; e + 1 < ne; ++e) tile(e, std::true_type{});
+  // Entries ascend and the walk ends at block nbb - 1, so only the last tile
+  // and the one before it (through its next entry) can reach that block:
+  // every earlier tile takes the unclamped loads.
+  if constexpr (kRagged) {
+    const int nfast = ctail && ne >= 2 && (ents[e0 + ne - 1] >> 1) == nbb - 1 ? ne - 2 : ne - 1;
+    int e = 0;
+    for (; e < nfast; ++e) tile(e, std::true_type{}, std::false_type{});
+    for (; e + 1 < ne; ++e) tile(e, std::true_type{}, std::true_type{});
+  } else {
+    for (int e = 0; e + 1 < ne; ++e) tile(e, std::true_type{}, std::false_type{});
+  }
   if (ne > 0) {
-    tile(ne - 1, std::false_type{});
+    tile(ne - 1, std::false_type{}, std::bool_constant<kRagged>{});
     BSA_WAIT_BARRIER(0);
     pv_half(1, pq);
   }
