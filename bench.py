@@ -68,23 +68,38 @@ def _cpu_init(path, lay, bs):
     """Worker start-up (spawned process): memory-map one head's Q/K/V."""
     os.environ["OMP_NUM_THREADS"] = "1"
     import oracle  # test infrastructure: only this baseline leg of the benchmark uses it
-    _CPU.update(oracle=oracle, lay=lay, bs=bs,
+    _CPU.update(oracle=oracle, lay=lay, bs=bs, h0=0,
                 q=np.load(path + "_q.npy", mmap_mode="r"), k=np.load(path + "_k.npy", mmap_mode="r"),
                 v=np.load(path + "_v.npy", mmap_mode="r"))
 
 
 def _cpu_worker(args):
-    """Run the oracle row by row on random queries for `seconds`; return (rows, elapsed)."""
+    """Run the oracle on random runs of 128 consecutive query rows (one
+    q-block) for `seconds`; return (rows, elapsed)."""
     seed, seconds = args
     d = _CPU
     N = d["q"].shape[2]
     rng = np.random.default_rng(seed)
     done, t0 = 0, time.perf_counter()
     while time.perf_counter() - t0 < seconds:
-        d["oracle"].forward(d["q"], d["k"], d["v"], d["lay"], d["bs"],
-                            rows=[(0, 0, int(rng.integers(0, N)))])
-        done += 1
+        q0 = int(rng.integers(0, N // 128)) * 128
+        q1 = min(N, q0 + 128)
+        d["oracle"].forward_query_range(d["q"][0, 0, q0:q1], d["k"][0, 0], d["v"][0, 0], d["lay"], d["bs"],
+                                        d["h0"], q0)
+        done += q1 - q0
     return done, time.perf_counter() - t0
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo (empty if unavailable)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
 
 
 def cpu_baseline(w, lay, q, k, v, flops, seconds=15.0):
@@ -92,7 +107,8 @@ def cpu_baseline(w, lay, q, k, v, flops, seconds=15.0):
 
     One head's Q/K/V (exact float32 copies of the bf16 inputs) is written to
     /tmp and memory-mapped by spawned worker processes (one thread each); each
-    worker evaluates random query rows for `seconds`.  The full-job time is
+    worker evaluates random q-blocks (128 consecutive query rows, the oracle's
+    query-range form of the definition) for `seconds`.  The full-job time is
     extrapolated from the measured rows per second."""
     import tempfile
     B, H, N = w.batch, w.heads, w.seq_len
@@ -106,8 +122,12 @@ def cpu_baseline(w, lay, q, k, v, flops, seconds=15.0):
     lay1 = dict(lay)
     if lay.get("bitmap") is not None:
         lay1["bitmap"] = np.asarray(lay["bitmap"][h0:h0 + 1])
-    cores = max(1, min(16, os.cpu_count() or 1))
+    host_cpus = os.cpu_count() or 1
+    cores = max(1, min(16, host_cpus))
     ctx = mp.get_context("spawn")
+    # One BLAS thread per worker: the spawned processes read these at import.
+    saved = {n: os.environ.get(n) for n in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS")}
+    os.environ.update(OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1")
     try:
         with ctx.Pool(cores, initializer=_cpu_init, initargs=(path, lay1, w.block)) as pool:
             pool.map(_cpu_worker, [(s, 0.5) for s in range(cores)])       # warm-up
@@ -118,6 +138,11 @@ def cpu_baseline(w, lay, q, k, v, flops, seconds=15.0):
                 log(f"[bench] cpu worker done: {r[0]} rows in {r[1]:.1f} s")
             wall = time.perf_counter() - t0
     finally:
+        for n, val in saved.items():
+            if val is None:
+                os.environ.pop(n, None)
+            else:
+                os.environ[n] = val
         for suffix in ("_q.npy", "_k.npy", "_v.npy"):
             if os.path.exists(path + suffix):
                 os.remove(path + suffix)
@@ -125,8 +150,10 @@ def cpu_baseline(w, lay, q, k, v, flops, seconds=15.0):
     rows = sum(r[0] for r in res)
     full_s = wall * (B * H * N) / rows
     return {"value": flops / full_s / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{rows} random query rows of head {h0} of {w.name}, evaluated one by one by "
-                      f"the float64 oracle in {cores} single-threaded processes over {wall:.1f} s; "
+            "host_cpu_count": host_cpus, "host_cpu_model": cpu_model(),
+            "sample": f"{rows} query rows (random q-blocks of 128 consecutive rows) of head {h0} of "
+                      f"{w.name}, evaluated by the float64 oracle's query-range form in {cores} "
+                      f"single-threaded processes over {wall:.1f} s (host: {host_cpus} CPUs); "
                       f"full-job time extrapolated to {B * H * N} rows = {full_s:.0f} s",
             "extrapolated_full_s": round(full_s, 1)}
 

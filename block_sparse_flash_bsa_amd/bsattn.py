@@ -316,18 +316,15 @@ def forward(q, k, v, p: Plan, out=None, lse=None):
     pr = p.problem
     B, H, Hk, N, D = pr.batch, pr.num_heads, pr.num_kv_heads, pr.seq_len, pr.head_dim
     dt = torch.bfloat16 if pr.dtype == BF16 else torch.float32
-    for name, t, shape in (("q", q, (B, H, N, D)), ("k", k, (B, Hk, N, D)), ("v", v, (B, Hk, N, D))):
-        if not t.is_cuda or t.dtype != dt or tuple(t.shape) != shape or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {dt} CUDA tensor of shape {shape}, got "
-                             f"{tuple(t.shape)} {t.dtype} on {t.device}")
+    if not q.is_cuda:
+        raise ValueError(f"q must be a CUDA tensor, got one on {q.device}")
     if out is None:
         out = torch.empty((B, H, N, D), dtype=dt, device=q.device)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    if tuple(out.shape) != (B, H, N, D) or out.dtype != dt or not out.is_contiguous() or not out.is_cuda:
-        raise ValueError("out has the wrong shape, dtype or layout")
-    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous() or not lse.is_cuda:
-        raise ValueError("lse must be a contiguous float32 CUDA tensor of shape (B, H, N)")
+    for name, t, shape, tdt in (("q", q, (B, H, N, D), dt), ("k", k, (B, Hk, N, D), dt), ("v", v, (B, Hk, N, D), dt),
+                                ("out", out, (B, H, N, D), dt), ("lse", lse, (B, H, N), torch.float32)):
+        _require(name, t, shape, tdt, q.device)
     with torch.cuda.device(q.device):
         stream = torch.cuda.current_stream().cuda_stream
         _check(lib().bsa_forward(q.data_ptr(), k.data_ptr(), v.data_ptr(), p.handle,
@@ -362,6 +359,8 @@ def _backward(q, k, v, out, lse, dout, p, seq_lens, dq, dk, dv, delta):
     B, H, Hk, N, D = pr.batch, pr.num_heads, pr.num_kv_heads, pr.seq_len, pr.head_dim
     dt = torch.bfloat16 if pr.dtype == BF16 else torch.float32
     qs, ks = (B, H, N, D), (B, Hk, N, D)
+    if not q.is_cuda:
+        raise ValueError(f"q must be a CUDA tensor, got one on {q.device}")
     dev = q.device
     if dq is None:
         dq = torch.empty(qs, dtype=dt, device=dev)
@@ -375,9 +374,7 @@ def _backward(q, k, v, out, lse, dout, p, seq_lens, dq, dk, dv, delta):
                                 ("lse", lse, (B, H, N), torch.float32), ("dout", dout, qs, dt),
                                 ("dq", dq, qs, dt), ("dk", dk, ks, dt), ("dv", dv, ks, dt),
                                 ("delta", delta, (B, H, N), torch.float32)):
-        if not t.is_cuda or t.dtype != tdt or tuple(t.shape) != shape or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous {tdt} CUDA tensor of shape {shape}, got "
-                             f"{tuple(t.shape)} {t.dtype} on {t.device}")
+        _require(name, t, shape, tdt, dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream().cuda_stream
         if seq_lens is None:
@@ -393,31 +390,35 @@ def _backward(q, k, v, out, lse, dout, p, seq_lens, dq, dk, dv, delta):
     return dq, dk, dv
 
 
+def _require(name, t, shape, dtype, device):
+    """Raise ValueError unless t is a contiguous CUDA tensor of this shape and
+    dtype on `device` (checked before any call into the library)."""
+    if (not t.is_cuda or t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous()
+            or t.device != device):
+        raise ValueError(f"{name} must be a contiguous {dtype} CUDA tensor of shape {tuple(shape)} on "
+                         f"{device}, got {tuple(t.shape)} {t.dtype} on {t.device}"
+                         f"{'' if t.is_contiguous() else ' (not contiguous)'}")
+
+
 def forward_varlen(q, k, v, p: Plan, seq_lens, out=None, lse=None):
     """bsa_forward_varlen on torch.cuda.current_stream(): batch entry b uses its
     first seq_lens[b] positions (seq_lens: int32 CUDA tensor [batch]); rows
     beyond come out as empty rows (O = 0, LSE = -inf).  Returns (out, lse)."""
     import torch
     pr = p.problem
-    B, H, N, D = pr.batch, pr.num_heads, pr.seq_len, pr.head_dim
-    if (not seq_lens.is_cuda or seq_lens.dtype != torch.int32 or tuple(seq_lens.shape) != (B,)
-            or not seq_lens.is_contiguous()):
-        raise ValueError(f"seq_lens must be a contiguous int32 CUDA tensor of shape ({B},)")
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError(f"{name} must be a contiguous CUDA tensor")
+    B, H, Hk, N, D = pr.batch, pr.num_heads, pr.num_kv_heads, pr.seq_len, pr.head_dim
+    if not q.is_cuda:
+        raise ValueError(f"q must be a CUDA tensor, got one on {q.device}")
+    dev = q.device
     if out is None:
-        out = torch.empty((B, H, N, D), dtype=q.dtype, device=q.device)
+        out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
     if lse is None:
-        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
-    Hk = pr.num_kv_heads
-    for name, t, shape in (("q", q, (B, H, N, D)), ("k", k, (B, Hk, N, D)), ("v", v, (B, Hk, N, D)),
-                           ("out", out, (B, H, N, D))):
-        if tuple(t.shape) != shape or t.dtype != torch.bfloat16:
-            raise ValueError(f"{name} must be bf16 of shape {shape}")
-    if tuple(lse.shape) != (B, H, N) or lse.dtype != torch.float32 or not lse.is_contiguous():
-        raise ValueError("lse must be a contiguous float32 CUDA tensor of shape (B, H, N)")
-    with torch.cuda.device(q.device):
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    for name, t, shape, tdt in (("q", q, (B, H, N, D), torch.bfloat16), ("k", k, (B, Hk, N, D), torch.bfloat16),
+                                ("v", v, (B, Hk, N, D), torch.bfloat16), ("seq_lens", seq_lens, (B,), torch.int32),
+                                ("out", out, (B, H, N, D), torch.bfloat16), ("lse", lse, (B, H, N), torch.float32)):
+        _require(name, t, shape, tdt, dev)
+    with torch.cuda.device(dev):
         stream = torch.cuda.current_stream().cuda_stream
         _check(lib().bsa_forward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), p.handle, seq_lens.data_ptr(),
                                         out.data_ptr(), lse.data_ptr(), c_void_p(stream)))

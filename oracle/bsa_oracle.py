@@ -32,6 +32,13 @@ What it computes (all arithmetic in float64 with numpy):
   algorithm.  An empty A(q) gives O = 0 and LSE = -inf (log of an empty sum).
   GQA: query head h reads KV head h // (H / Hkv).
 
+* `forward_query_range(Qr, Kh, Vh, layout, block_size, h, q0)` -- the same
+  definition for a run of consecutive queries of one head at once: masked
+  softmax attention over the union of their allowed keys, every other key
+  masked to -inf (so its weight is exactly 0).  It is what makes every-row
+  checks of full-size problems affordable; its pins compare it with the
+  per-query form and with library attention.
+
 * `backward(Q, K, V, dO, layout, block_size)` -- the gradients dQ, dK, dV of
   sum(dO * O) by the chain rule through the forward above, per query over its
   allowed keys (softmax Jacobian ds = p * (dp - sum p dp)); `backward_dq_rows`
@@ -113,15 +120,21 @@ def _intervals_tokens(layout, N: int, q: int):
     return [(a0, b0, 1), (a1, b1, 1), (max(a0, a1), min(b0, b1), -1)]
 
 
-def _block_active(layout, lh: int, i: int, j: int) -> bool:
-    """Block-level part of the predicate for block-unit specs and bitmaps."""
+def _blocks_active(layout, lh: int, i: int, js: np.ndarray) -> np.ndarray:
+    """Block-level part of the predicate for block-unit specs and bitmaps:
+    whether q-block i may see each key block in the int array js."""
+    js = np.asarray(js, dtype=np.int64)
     bm = layout.get("bitmap")
     if bm is not None:
-        return bool(np.asarray(bm)[lh, i, j])
+        return np.asarray(bm)[lh, i, js].astype(bool)
     wl = layout["window_left"]
     wr = layout["window_right"]
-    in_w = (wl < 0 or i - j <= wl) and (wr < 0 or j - i <= wr)
-    return in_w or j < layout["global_keys"] or i < layout["global_queries"]
+    in_w = np.ones(js.shape, dtype=bool)
+    if wl >= 0:
+        in_w &= (i - js) <= wl
+    if wr >= 0:
+        in_w &= (js - i) <= wr
+    return in_w | (js < layout["global_keys"]) | (i < layout["global_queries"])
 
 
 def allowed_keys(layout, N: int, bs: int, h: int, q: int) -> np.ndarray:
@@ -131,13 +144,11 @@ def allowed_keys(layout, N: int, bs: int, h: int, q: int) -> np.ndarray:
         if not parts:
             return np.zeros(0, dtype=np.int64)
         return np.unique(np.concatenate(parts)).astype(np.int64)
-    lh = _layout_head(layout, h)
     nb = -(-N // bs)                     # a last, shorter block when bs does not divide N
     i = q // bs
-    blocks = [j for j in range(nb) if _block_active(layout, lh, i, j)]
-    if not blocks:
-        return np.zeros(0, dtype=np.int64)
-    keys = np.concatenate([np.arange(j * bs, min((j + 1) * bs, N)) for j in blocks])
+    blocks = np.flatnonzero(_blocks_active(layout, _layout_head(layout, h), i, np.arange(nb)))
+    keys = (blocks[:, None] * bs + np.arange(bs)[None, :]).ravel()
+    keys = keys[keys < N]
     if layout["causal"]:
         keys = keys[keys <= q]
     return keys.astype(np.int64)
@@ -178,6 +189,12 @@ def attend_row(q_vec: np.ndarray, K_rows: np.ndarray, V_rows: np.ndarray,
     return o, float(m + math.log(l))
 
 
+def kv_head(h: int, group: int) -> int:
+    """KV head read by query head h when `group` consecutive query heads
+    share one KV head (GQA; a reading, since the pages do not treat GQA)."""
+    return h // group
+
+
 def forward(Q, K, V, layout, block_size: int, scale: Optional[float] = None,
             rows: Optional[Iterable[Tuple[int, int, int]]] = None):
     """Oracle forward.
@@ -202,7 +219,7 @@ def forward(Q, K, V, layout, block_size: int, scale: Optional[float] = None,
         L = np.full((B, H, N), -math.inf)
         for b in range(B):
             for h in range(H):
-                hk = h // group
+                hk = kv_head(h, group)
                 for q in range(N):
                     keys = allowed_keys(layout, N, block_size, h, q)
                     O[b, h, q], L[b, h, q] = attend_row(
@@ -212,10 +229,58 @@ def forward(Q, K, V, layout, block_size: int, scale: Optional[float] = None,
     O = np.zeros((len(rows), D))
     L = np.full(len(rows), -math.inf)
     for r, (b, h, q) in enumerate(rows):
-        hk = h // group
+        hk = kv_head(h, group)
         keys = allowed_keys(layout, N, block_size, h, q)
         O[r], L[r] = attend_row(_f64(Q[b, h, q]), _f64(K[b, hk][keys]),
                                 _f64(V[b, hk][keys]), scale)
+    return O, L
+
+
+def forward_query_range(Qr, Kh, Vh, layout, block_size: int, h: int, q0: int,
+                        scale: Optional[float] = None):
+    """The same definition for the consecutive queries q0 .. q0+R-1 of one head.
+
+    Qr: [R, D] the rows q0 .. q0+R-1 of query head h; Kh, Vh: [N, D] every
+    row of its KV head (any float dtype; only the rows used are upcast to
+    float64).  The queries are
+    taken together as masked softmax attention over C, the union of their
+    allowed key sets: S = scale * Q C^T, S[q, k] = -inf where k is not in
+    A(q), then the row-wise softmax, O = P V_C / l and LSE = m + ln l.  Every
+    key outside A(q) carries weight exactly 0, so each row equals its own
+    per-query definition (up to the order of the float64 sums).  This is the
+    naive masked formulation of "How Sparse Attention Kernels Actually Speed
+    Up Inference" (Sparse Attention Kernels vs Full Attention Performance)
+    restricted to the keys some row of the range may see.  A query with no
+    allowed key gets O = 0 and LSE = -inf.
+    Returns (O [R, D], LSE [R]) as float64.
+    """
+    R, D = int(Qr.shape[0]), int(Qr.shape[1])
+    N = int(Kh.shape[0])
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    per_row = [allowed_keys(layout, N, block_size, h, q) for q in range(q0, q0 + R)]
+    member = np.zeros(N, dtype=bool)
+    for ks in per_row:
+        member[ks] = True
+    C = np.flatnonzero(member)
+    O = np.zeros((R, D))
+    L = np.full(R, -math.inf)
+    if C.size == 0:
+        return O, L
+    col = np.full(N, -1, dtype=np.int64)
+    col[C] = np.arange(C.size)
+    M = np.zeros((R, C.size), dtype=bool)
+    for r, ks in enumerate(per_row):
+        M[r, col[ks]] = True
+    Kc, Vc = _f64(Kh[C]), _f64(Vh[C])
+    S = scale * (_f64(Qr) @ Kc.T)
+    S[~M] = -math.inf
+    m = S.max(axis=1)
+    ok = np.isfinite(m)
+    P = np.exp(S[ok] - m[ok, None])          # masked entries give exp(-inf) = 0
+    l = P.sum(axis=1)
+    O[ok] = (P @ Vc) / l[:, None]
+    L[ok] = m[ok] + np.log(l)
     return O, L
 
 
@@ -261,8 +326,9 @@ def _tile_counts_blocks(layout, N: int, bs: int, h: int, i: int) -> np.ndarray:
     lh = _layout_head(layout, h)
     counts = np.zeros(nb, dtype=np.int64)
     rows_i = min(bs, N - i * bs)                     # queries of block i
+    active = _blocks_active(layout, lh, i, np.arange(nb))
     for j in range(nb):
-        if not _block_active(layout, lh, i, j):
+        if not active[j]:
             continue
         cols_j = min(bs, N - j * bs)                 # keys of block j
         if not layout["causal"] or j < i:
@@ -387,7 +453,7 @@ def backward(Q, K, V, dO, layout, block_size: int, scale: Optional[float] = None
     dV = np.zeros_like(Vd)
     for b in range(B):
         for h in range(H):
-            hk = h // group
+            hk = kv_head(h, group)
             for q in range(N):
                 keys = allowed_keys(layout, N, block_size, h, q)
                 p, ds = grad_row(Qd[b, h, q], dOd[b, h, q], Kd[b, hk, keys], Vd[b, hk, keys], scale)
@@ -410,8 +476,9 @@ def backward_dq_rows(Q, K, V, dO, layout, block_size: int, rows, scale: Optional
     out = np.zeros((len(rows), D))
     for r, (b, h, q) in enumerate(rows):
         keys = allowed_keys(layout, N, block_size, h, q)
-        Kr = _f64(K[b, h // group][keys])
-        _, ds = grad_row(_f64(Q[b, h, q]), _f64(dO[b, h, q]), Kr, _f64(V[b, h // group][keys]), scale)
+        hk = kv_head(h, group)
+        Kr = _f64(K[b, hk][keys])
+        _, ds = grad_row(_f64(Q[b, h, q]), _f64(dO[b, h, q]), Kr, _f64(V[b, hk][keys]), scale)
         if keys.size:
             out[r] = scale * (ds @ Kr)
     return out

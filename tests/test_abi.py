@@ -495,3 +495,49 @@ def test_xcd_runs_hold_every_batch_entry():
             run = work[x::8]
             run = run[run >= 0]
             assert set((run // per_b).tolist()) == set(range(w.batch)), f"XCD {x}"
+
+
+# ------------------------------------------------ binding argument checks
+class _CudaStandIn:
+    """Duck-typed stand-in for a CUDA tensor (no GPU here): it only answers
+    the attributes the binding inspects before calling into the library."""
+
+    def __init__(self, shape, dtype, contiguous=True):
+        self.shape, self.dtype, self._c = tuple(shape), dtype, contiguous
+        self.is_cuda = True
+        self.device = torch.device("cuda", 0)
+
+    def is_contiguous(self):
+        return self._c
+
+    def data_ptr(self):
+        raise AssertionError("the binding reached the library call")
+
+
+def test_binding_rejects_bad_out_and_lse_before_any_launch():
+    w = wl.small_variant(wl.WORKLOADS["window16k"], 1024, heads=2, kv_heads=2)
+    p = host_plan(w)
+    B, H, N, D = w.batch, w.heads, w.seq_len, w.head_dim
+    bf = torch.bfloat16
+    q = _CudaStandIn((B, H, N, D), bf)
+    k = _CudaStandIn((B, H, N, D), bf)
+    v = _CudaStandIn((B, H, N, D), bf)
+    lens = _CudaStandIn((B,), torch.int32)
+    good_out = _CudaStandIn((B, H, N, D), bf)
+    good_lse = _CudaStandIn((B, H, N), torch.float32)
+    bad = {
+        "cpu out": (torch.empty((B, H, N, D), dtype=bf), good_lse),
+        "cpu lse": (good_out, torch.empty((B, H, N), dtype=torch.float32)),
+        "strided out": (_CudaStandIn((B, H, N, D), bf, contiguous=False), good_lse),
+        "strided lse": (good_out, _CudaStandIn((B, H, N), torch.float32, contiguous=False)),
+        "fp32 out": (_CudaStandIn((B, H, N, D), torch.float32), good_lse),
+    }
+    for what, (o, l) in bad.items():
+        with pytest.raises(ValueError):
+            bsattn.forward_varlen(q, k, v, p, lens, o, l)
+        with pytest.raises(ValueError):
+            bsattn.forward(q, k, v, p, o, l)
+    with pytest.raises(ValueError):       # lengths in host memory
+        bsattn.forward_varlen(q, k, v, p, torch.zeros(B, dtype=torch.int32), good_out, good_lse)
+    with pytest.raises(ValueError):       # q in host memory
+        bsattn.forward(torch.empty((B, H, N, D), dtype=bf), k, v, p, good_out, good_lse)
