@@ -35,7 +35,7 @@ EXPORTS = ("bsa_plan", "bsa_plan_host", "bsa_plan_destroy", "bsa_plan_csr", "bsa
            "bsa_plan_work", "bsa_plan_active_blocks", "bsa_plan_dynamic", "bsa_plan_set_bitmap",
            "bsa_plan_read_csr", "bsa_plan_read_csr_transposed", "bsa_forward",
            "bsa_plan_csr_transposed", "bsa_plan_work_kv",
-           "bsa_backward", "bsa_forward_varlen", "bsa_backward_varlen", "bsa_status_string", "bsa_last_error",
+           "bsa_backward", "bsa_backward_noalloc", "bsa_forward_varlen", "bsa_backward_varlen", "bsa_status_string", "bsa_last_error",
            "bsa_abi_version")
 
 
@@ -98,6 +98,7 @@ def lib():
                                           POINTER(POINTER(c_uint8)), POINTER(c_int64)]
     L.bsa_plan_work_kv.argtypes = [P, POINTER(POINTER(c_int32)), POINTER(c_int64)]
     L.bsa_backward.argtypes = [c_void_p] * 6 + [P] + [c_void_p] * 5
+    L.bsa_backward_noalloc.argtypes = [c_void_p] * 6 + [P] + [c_void_p] * 4
     L.bsa_forward_varlen.argtypes = [c_void_p, c_void_p, c_void_p, P, c_void_p, c_void_p, c_void_p, c_void_p]
     L.bsa_backward_varlen.argtypes = [c_void_p] * 6 + [P] + [c_void_p] * 6
     L.bsa_status_string.argtypes = [c_int32]
@@ -353,7 +354,15 @@ def backward_varlen(q, k, v, out, lse, dout, p: Plan, seq_lens, dq=None, dk=None
     return _backward(q, k, v, out, lse, dout, p, seq_lens, dq, dk, dv, delta)
 
 
-def _backward(q, k, v, out, lse, dout, p, seq_lens, dq, dk, dv, delta):
+def backward_noalloc(q, k, v, out, lse, dout, p: Plan, dq=None, dk=None, dv=None):
+    """bsa_backward_noalloc on torch.cuda.current_stream(): bsa_backward with
+    its workspace in the library's static per-GPU array (no device allocation
+    by the library; pass dq, dk and dv to allocate nothing at all).  Calls
+    that overlap on one GPU race.  Returns (dq, dk, dv)."""
+    return _backward(q, k, v, out, lse, dout, p, None, dq, dk, dv, None, noalloc=True)
+
+
+def _backward(q, k, v, out, lse, dout, p, seq_lens, dq, dk, dv, delta, noalloc=False):
     import torch
     pr = p.problem
     B, H, Hk, N, D = pr.batch, pr.num_heads, pr.num_kv_heads, pr.seq_len, pr.head_dim
@@ -368,16 +377,22 @@ def _backward(q, k, v, out, lse, dout, p, seq_lens, dq, dk, dv, delta):
         dk = torch.empty(ks, dtype=dt, device=dev)
     if dv is None:
         dv = torch.empty(ks, dtype=dt, device=dev)
-    if delta is None:
+    if delta is None and not noalloc:
         delta = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    for name, t, shape, tdt in (("q", q, qs, dt), ("k", k, ks, dt), ("v", v, ks, dt), ("out", out, qs, dt),
-                                ("lse", lse, (B, H, N), torch.float32), ("dout", dout, qs, dt),
-                                ("dq", dq, qs, dt), ("dk", dk, ks, dt), ("dv", dv, ks, dt),
-                                ("delta", delta, (B, H, N), torch.float32)):
+    checks = [("q", q, qs, dt), ("k", k, ks, dt), ("v", v, ks, dt), ("out", out, qs, dt),
+              ("lse", lse, (B, H, N), torch.float32), ("dout", dout, qs, dt),
+              ("dq", dq, qs, dt), ("dk", dk, ks, dt), ("dv", dv, ks, dt)]
+    if not noalloc:
+        checks.append(("delta", delta, (B, H, N), torch.float32))
+    for name, t, shape, tdt in checks:
         _require(name, t, shape, tdt, dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream().cuda_stream
-        if seq_lens is None:
+        if noalloc:
+            st = lib().bsa_backward_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                            lse.data_ptr(), dout.data_ptr(), p.handle, dq.data_ptr(),
+                                            dk.data_ptr(), dv.data_ptr(), c_void_p(stream))
+        elif seq_lens is None:
             st = lib().bsa_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                     dout.data_ptr(), p.handle, dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
                                     delta.data_ptr(), c_void_p(stream))

@@ -40,6 +40,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "internal.h"
 
@@ -1074,8 +1075,64 @@ bsa_status_t backward_impl(const void* q, const void* k, const void* v, const vo
   return BSA_OK;
 }
 
+// Workspace of bsa_backward_noalloc: Delta (one float per query row) in a
+// file-scope device array instead of a caller buffer, for callers that cannot
+// allocate (graph capture, allocation-free loops).  Each GPU the library runs
+// on holds its own copy for the life of the process.  Host code never uses
+// the array's name as an address: the per-device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr int64_t kScratchFloats = int64_t(16) << 20;   // 64 MiB: batch * heads * seq_len <= 16,777,216
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Address of `scratch` on device `dev` (the current device) into *out.
+bsa_status_t scratch_on(int dev, float** out) {
+  if (dev < 0 || dev >= kMaxScratchDevices)
+    return fail(BSA_ERR_UNSUPPORTED, "device ordinal %d is beyond the %d devices this entry point serves", dev,
+                kMaxScratchDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(BSA_ERR_DEVICE, "hipGetSymbolAddress of the backward workspace failed: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return BSA_OK;
+}
+
 }  // namespace
 }  // namespace bsa
+
+extern "C" bsa_status_t bsa_backward_noalloc(const void* q, const void* k, const void* v, const void* out,
+                                             const float* lse, const void* dout, bsa_plan_t plan, void* dq,
+                                             void* dk, void* dv, void* stream) {
+  using namespace bsa;
+  clear_error();
+  if (!plan) return fail(BSA_ERR_INVALID_ARGUMENT, "plan must not be NULL");
+  if (!plan->info.on_device)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "plan was built by bsa_plan_host and has no device copy");
+  const bsa_problem_t& pr = plan->prob;
+  const int64_t rows = int64_t(pr.batch) * pr.num_heads * pr.seq_len;
+  if (rows > kScratchFloats)
+    return fail(BSA_ERR_INVALID_ARGUMENT,
+                "batch * heads * seq_len = %lld exceeds the %lld rows of the static workspace; use bsa_backward",
+                (long long)rows, (long long)kScratchFloats);
+  if (plan->info.work_items == 0) return BSA_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(BSA_ERR_DEVICE, "hipGetDevice failed");
+  if (dev != plan->device)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "plan was built on device %d but device %d is current",
+                plan->device, dev);
+  float* delta = nullptr;
+  const bsa_status_t st = scratch_on(dev, &delta);
+  if (st != BSA_OK) return st;
+  return backward_impl(q, k, v, out, lse, dout, plan, nullptr, dq, dk, dv, delta, stream);
+}
 
 extern "C" bsa_status_t bsa_backward(const void* q, const void* k, const void* v, const void* out,
                                      const float* lse, const void* dout, bsa_plan_t plan, void* dq,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 3
+#define BSA_ABI_VERSION 4
 
 /* Status codes.  Every entry point that can fail returns one; no exception
  * crosses the ABI.  Out-parameters are written only on BSA_OK. */
@@ -340,6 +340,27 @@ bsa_status_t bsa_plan_work_kv(bsa_plan_t plan, const int32_t** work, int64_t* sl
 bsa_status_t bsa_backward(const void* q, const void* k, const void* v, const void* out,
                           const float* lse, const void* dout, bsa_plan_t plan, void* dq, void* dk,
                           void* dv, float* delta, void* stream);
+
+/* bsa_backward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving or training loops, harnesses that forbid
+ * hipMalloc.  It computes exactly what bsa_backward computes (the same
+ * kernels), but keeps Delta in a workspace of the library's own -- a static
+ * device array of 64 MiB per GPU, held until the process ends -- instead of a
+ * caller buffer, and calls no allocating routine.  The caller still passes
+ * every input and output; the plan (made beforehand) keeps the float32
+ * partial sums of split dK/dV walks as for bsa_backward.
+ *   Limit: batch * num_heads * seq_len <= 16,777,216 query rows.
+ *   Concurrency: every call on one GPU shares that GPU's workspace, so calls
+ *   that overlap on one GPU (other streams, other threads) race; serialise
+ *   them.  The workspace keeps the last call's contents, all of which the
+ *   next call overwrites before reading.
+ * Errors (before anything is launched): as bsa_backward, plus
+ * INVALID_ARGUMENT when the problem exceeds the limit and UNSUPPORTED on a
+ * device ordinal of 64 or more; DEVICE if the workspace address cannot be
+ * obtained on first use on a device. */
+bsa_status_t bsa_backward_noalloc(const void* q, const void* k, const void* v, const void* out,
+                                  const float* lse, const void* dout, bsa_plan_t plan, void* dq, void* dk,
+                                  void* dv, void* stream);
 
 /* Variable-length batch: the same forward, where batch entry b uses only its
  * first seq_lens[b] positions of the padded [batch][heads][seq_len][head_dim]
