@@ -34,6 +34,7 @@ struct bsa_plan {
   // units or a bitmap), so only the causal cut is applied inside a tile.
   int32_t causal = 0;
   int32_t token_rule = 0;
+  int32_t from_bitmap = 0;     // the layout was given as a block bitmap
   int64_t wl = -1, wr = -1, gk = 0, gq = 0;
   int32_t layout_heads = 1;
   int32_t nb = 0;

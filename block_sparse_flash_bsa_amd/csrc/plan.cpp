@@ -286,9 +286,20 @@ void build_work_kv(Plan& P) {
   std::vector<Plan::KvDesc> pieces;
   P.kv_reduce.clear();
   int64_t partials = 0;
+  // For a bitmap, each (batch entry, KV head)'s k-blocks are taken longest
+  // walk first, as the forward takes q-blocks (see build_work).
+  std::vector<int64_t> order;
+  order.reserve(items);
+  for (int64_t hk = 0; hk < Hkv; ++hk)
+    for (int64_t b = 0; b < B; ++b) {
+      const size_t first = order.size();
+      for (int64_t j = 0; j < nb; ++j) order.push_back((b * Hkv + hk) * nb + j);
+      if (P.from_bitmap)
+        std::stable_sort(order.begin() + first, order.end(),
+                         [&](int64_t x, int64_t y) { return walk(x) > walk(y); });
+    }
   for (int64_t l = 0; l < items; ++l) {
-    const int64_t j = l % nb, b = (l / nb) % B, hk = l / (nb * B);
-    const int64_t it = (b * Hkv + hk) * nb + j;
+    const int64_t it = order[l];
     const int64_t n = walk(it);
     if (n <= P.kv_chunk) {
       pieces.push_back({int32_t(it), 0, int32_t(n), -1});
@@ -343,12 +354,27 @@ void build_work(Plan& P) {
     // batch entries the next, so every XCD's run holds all batch entries of
     // its KV heads: entries of different lengths (a variable-length batch)
     // load the XCDs evenly.
+    // For a bitmap, neighbouring q-blocks share no more K/V blocks than any
+    // two others, so a head's q-blocks are taken longest row first instead:
+    // the workgroups that run together on an XCD then have rows of about the
+    // same length, start and end about together, and sweep the head's key
+    // blocks (in ascending order) at the same pace, so the blocks they read
+    // at a time stay few enough for the XCD's L2.
     std::vector<int32_t> loc;
     loc.reserve(items);
+    std::vector<int32_t> order(nb);
     for (int64_t hk = 0; hk < H / group; ++hk)
-      for (int64_t b = 0; b < B; ++b)
-        for (int64_t i = 0; i < nb; ++i)
+      for (int64_t b = 0; b < B; ++b) {
+        std::iota(order.begin(), order.end(), 0);
+        if (P.from_bitmap && !P.dynamic) {
+          const int64_t h0 = hk * group;
+          std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+            return cost((b * H + h0) * nb + x) > cost((b * H + h0) * nb + y);
+          });
+        }
+        for (int32_t i : order)
           for (int64_t g = 0; g < group; ++g) loc.push_back(int32_t((b * H + hk * group + g) * nb + i));
+      }
     P.work = xcd_slots(loc, cost);
   }
   P.info.work_items = items;
@@ -452,6 +478,7 @@ bsa_status_t make_plan(const bsa_problem_t* problem, const bsa_layout_t* layout,
     P->layout_heads = layout->bitmap ? layout->bitmap_heads : 1;
     P->causal = layout->causal;
     P->token_rule = (!layout->bitmap && layout->unit == BSA_UNIT_TOKENS) ? 1 : 0;
+    P->from_bitmap = layout->bitmap ? 1 : 0;
     if (P->token_rule) {
       P->wl = layout->window_left;
       P->wr = layout->window_right;

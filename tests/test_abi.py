@@ -138,6 +138,29 @@ def test_xcd_schedule_runs_are_local_and_balanced():
     assert max(costs) - min(costs) <= lens.max() + 1
 
 
+def test_xcd_schedule_takes_bitmap_rows_longest_first():
+    """For a bitmap layout each head's q-blocks run longest row first (ties in
+    q-block order), so the workgroups running together sweep the key blocks
+    at the same pace; heads stay contiguous per XCD run."""
+    w = wl.WORKLOADS["random32k"]
+    p = host_plan(w, schedule=bsattn.SCHEDULE_XCD)
+    work = p.work()
+    nb, H = w.num_blocks, w.heads
+    lens = [np.diff(p.csr(h)["row_ptr"]) for h in range(H)]
+    for x in range(8):
+        run = work[x::8]
+        run = run[run >= 0]
+        i, h, b = run % nb, (run // nb) % H, run // (nb * H)
+        grp = h * w.batch + b                  # head outer, batch entry next
+        assert np.all(np.diff(grp) >= 0)
+        for g in np.unique(grp):
+            ii = i[grp == g]
+            c = lens[g // w.batch][ii]
+            assert np.all(np.diff(c) <= 0)
+            ties = np.diff(c) == 0
+            assert np.all(np.diff(ii)[ties] > 0)
+
+
 def test_lpt_schedule_is_longest_first():
     w = wl.WORKLOADS["random32k"]
     p = host_plan(w, schedule=bsattn.SCHEDULE_LPT)
@@ -343,13 +366,30 @@ def test_kv_work_order_is_a_permutation(name):
     assert len(items) - len(np.unique(items)) < 0.05 * len(items)
     # slot s runs on XCD s % 8: each XCD's items form one contiguous, ordered
     # run of the locality order (KV head, batch entry, k-block)
-    nb, B, Hkv = w.num_blocks, w.batch, w.kv_heads
+    # (for a bitmap, each (KV head, batch entry)'s k-blocks go longest walk first)
+    nb, B, Hkv, group = w.num_blocks, w.batch, w.kv_heads, w.heads // w.kv_heads
+    lay = wl.layout_of(w)
+    if lay.get("bitmap") is not None:
+        col = p.csr_transposed
+        walk = np.zeros((B * Hkv * nb,), dtype=np.int64)
+        for it in range(len(walk)):
+            j, hk = it % nb, (it // nb) % Hkv
+            walk[it] = sum(int(np.diff(col(h)["col_ptr"])[j]) for h in range(hk * group, (hk + 1) * group))
+    seen = []
     for x in range(8):
         run = work[x::8]
         run = run[run >= 0]
         j, hk, b = run % nb, (run // nb) % Hkv, run // (nb * Hkv)
-        key = (hk * B + b) * nb + j
-        assert np.all(np.diff(key) >= 0) and np.all(np.diff(key) <= 1)
+        grp = hk * B + b
+        assert np.all(np.diff(grp) >= 0)
+        if lay.get("bitmap") is None:
+            key = grp * nb + j
+            assert np.all(np.diff(key) >= 0) and np.all(np.diff(key) <= 1)
+        else:
+            for g in np.unique(grp):
+                wk = walk[run[grp == g]]
+                assert np.all(np.diff(wk) <= 0), "k-blocks of a group must go longest walk first"
+        seen.append(run)
 
 
 def test_transposed_csr_errors():
