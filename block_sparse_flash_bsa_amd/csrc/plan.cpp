@@ -521,11 +521,9 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
       layout->global_queries != 0)
     return fail(BSA_ERR_INVALID_ARGUMENT,
                 "dynamic plan: window_left/right must be -1 and global_keys/queries 0 (the bitmap is the layout)");
-  if (problem->seq_len % problem->block_size != 0)
-    return fail(BSA_ERR_INVALID_ARGUMENT,
-                "dynamic plan: seq_len (%lld) must be a multiple of block_size (%d)",
-                (long long)problem->seq_len, problem->block_size);
-  const int64_t nb = problem->seq_len / problem->block_size;
+  // A seq_len the block does not divide ends in a shorter last block, as for
+  // static plans: its tiles are PARTIAL (the device planner flags them).
+  const int64_t nb = (problem->seq_len + problem->block_size - 1) / problem->block_size;
   const int64_t per_head = layout->causal ? nb * (nb + 1) / 2 : nb * nb;
   const int64_t cap = int64_t(layout->bitmap_heads) * per_head;
   if (cap > INT32_MAX)

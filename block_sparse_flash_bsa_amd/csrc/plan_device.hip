@@ -5,7 +5,8 @@
 // The CSR is the same as the host planner's for a bitmap layout: tile (i, j)
 // of layout head hl is an entry iff bitmap[hl][i][j] != 0 and, for a causal
 // layout, j <= i; the diagonal tile of a causal layout is PARTIAL (the
-// token-exact causal cut), every other entry FULL.  Entries are ascending in
+// token-exact causal cut), and so is every tile of a shorter last block (a
+// seq_len the block does not divide); every other entry is FULL.  Entries are ascending in
 // j.  Three steps: count the entries of each row, scan the counts into row
 // offsets (three small kernels), write each row's entries; then the same for
 // the k-block columns the backward walks.  The per-query-block lists follow step
@@ -142,7 +143,7 @@ __global__ __launch_bounds__(kScanBlock) void scan_apply(const int32_t* __restri
 
 // The entries of each row, ascending: entry = (j << 1) | partial.
 __global__ __launch_bounds__(kRowThreads) void fill_rows(const uint8_t* __restrict__ bm, int nb, int causal,
-                                                         const RowDesc* __restrict__ rows,
+                                                         int tail, const RowDesc* __restrict__ rows,
                                                          int32_t* __restrict__ entries) {
   __shared__ int wsum[kRowThreads / 64];
   const int row = blockIdx.x;
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(kRowThreads) void fill_rows(const uint8_t* __restri
     __syncthreads();
     int off = base;
     for (int w = 0; w < wave; ++w) off += wsum[w];
-    if (on) out[off + below] = (j << 1) | ((causal && j == i) ? 1 : 0);
+    if (on) out[off + below] = (j << 1) | (((causal && j == i) || i == tail || j == tail) ? 1 : 0);
     base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
     __syncthreads();
   }
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(kStripThreads) void count_cols(const uint8_t* __res
 
 template <int kVec>
 __global__ __launch_bounds__(kStripThreads) void fill_cols(const uint8_t* __restrict__ bm, int nb, int causal,
-                                                           const RowDesc* __restrict__ cols,
+                                                           int tail, const RowDesc* __restrict__ cols,
                                                            int32_t* __restrict__ entries) {
   __shared__ int part[kChunks][kStrip * kVec];
   const StripCursor c = strip_cursor<kVec>(bm, nb, causal);
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(kStripThreads) void fill_cols(const uint8_t* __rest
 #pragma unroll
     for (int v = 0; v < kVec; ++v)
       if (strip_on<kVec>(x, v, i, c.j0, causal))
-        entries[off[v]++] = (i << 1) | ((causal && i == c.j0 + v) ? 1 : 0);
+        entries[off[v]++] = (i << 1) | (((causal && i == c.j0 + v) || i == tail || c.j0 + v == tail) ? 1 : 0);
   }
 }
 
@@ -334,7 +335,10 @@ extern "C" bsa_status_t bsa_plan_set_bitmap(bsa_plan_t plan, const uint8_t* d_bi
                        plan->d_scan, nblk, out, nnz_out);
   };
   scan(d_rows, d_nnz);
-  hipLaunchKernelGGL(fill_rows, dim3(unsigned(rows)), dim3(kRowThreads), 0, s, d_bitmap, nb, plan->causal,
+  // The shorter last block of a seq_len the block does not divide: its tiles
+  // are PARTIAL (-1: every block whole).
+  const int tail = plan->prob.seq_len % plan->prob.block_size != 0 ? nb - 1 : -1;
+  hipLaunchKernelGGL(fill_rows, dim3(unsigned(rows)), dim3(kRowThreads), 0, s, d_bitmap, nb, plan->causal, tail,
                      d_rows, d_entries);
   // The same entries per k-block column, for the backward's dK/dV walk.
   auto* d_cols = const_cast<RowDesc*>(plan->d_cols);
@@ -353,11 +357,11 @@ extern "C" bsa_status_t bsa_plan_set_bitmap(bsa_plan_t plan, const uint8_t* d_bi
                        plan->d_counts);
   scan(d_cols, nullptr);
   if (vec == 4)
-    hipLaunchKernelGGL(fill_cols<4>, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal, d_cols,
-                       d_entries_t);
+    hipLaunchKernelGGL(fill_cols<4>, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal, tail,
+                       d_cols, d_entries_t);
   else
-    hipLaunchKernelGGL(fill_cols<1>, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal, d_cols,
-                       d_entries_t);
+    hipLaunchKernelGGL(fill_cols<1>, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal, tail,
+                       d_cols, d_entries_t);
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(BSA_ERR_DEVICE, "planner launch failed: %s", hipGetErrorString(err));
   return BSA_OK;

@@ -204,7 +204,9 @@ int64_t bsa_plan_active_blocks(bsa_plan_t plan);
  * are those of "Flash-MSA" on "The Only Guide You Need for Sparse Attention
  * Kernels in Long-Context LLMs".  The predicate is the bitmap branch of the
  * one above: tile (i, j) of layout head hl is active iff bitmap[hl][i][j] != 0
- * and (!causal || j <= i); it is PARTIAL iff causal and j == i.
+ * and (!causal || j <= i); it is PARTIAL iff causal and j == i, or i or j is
+ * the shorter last block of a seq_len that block_size does not divide
+ * (nb = ceil(seq_len / block_size) blocks per side, as for bsa_plan).
  * ------------------------------------------------------------------------- */
 
 /* Create a dynamic plan on the current HIP device.  layout->bitmap must be

@@ -309,11 +309,15 @@ def test_dynamic_plan_argument_errors():
             bsattn.ERR_INVALID_ARGUMENT
         assert bsattn.lib().bsa_last_error()
     assert L.bsa_plan_dynamic(ctypes.byref(pr), ctypes.byref(lay()), None) == bsattn.ERR_INVALID_ARGUMENT
-    # Dynamic plans need a sequence length the block divides (static plans do not).
+    # A sequence length the block does not divide passes the argument checks
+    # (a shorter last block, as for static plans): with no GPU the call gets as
+    # far as the device query.
     ragged = bsattn.make_problem(1, 2, 2, 1000, 64, 64, torch.float32)
-    assert L.bsa_plan_dynamic(ctypes.byref(ragged), ctypes.byref(lay()), ctypes.byref(h)) == \
-        bsattn.ERR_INVALID_ARGUMENT
-    assert b"multiple of block_size" in bsattn.lib().bsa_last_error()
+    st = L.bsa_plan_dynamic(ctypes.byref(ragged), ctypes.byref(lay()), ctypes.byref(h))
+    if st == bsattn.OK:
+        L.bsa_plan_destroy(h)
+    else:
+        assert st == bsattn.ERR_DEVICE, bsattn.lib().bsa_last_error()
     # Up to 2^31 - 1 possible entries (one int32 offset space).
     big = bsattn.make_problem(1, 32, 32, 16384 * 64, 64, 64, torch.float32)
     assert L.bsa_plan_dynamic(ctypes.byref(big), ctypes.byref(lay(heads=32)), ctypes.byref(h)) == \

@@ -47,18 +47,24 @@ def assert_same_csr(a, b, what):
         assert np.array_equal(np.asarray(a[key]), np.asarray(b[key])), f"{what}: {key} differs"
 
 
-@pytest.mark.parametrize("lh,H,nb,bs,density,causal", [
-    (1, 2, 37, 64, 0.3, False),
-    (1, 2, 37, 64, 0.3, True),
-    (4, 4, 64, 64, 0.15, True),
-    (16, 16, 256, 128, 0.10, False),
-    (2, 2, 130, 64, 0.2, True),
+@pytest.mark.parametrize("lh,H,nb,bs,density,causal,cut", [
+    (1, 2, 37, 64, 0.3, False, 0),
+    (1, 2, 37, 64, 0.3, True, 0),
+    (4, 4, 64, 64, 0.15, True, 0),
+    (16, 16, 256, 128, 0.10, False, 0),
+    (2, 2, 130, 64, 0.2, True, 0),
+    # seq_len = nb * bs - cut: a shorter last block, whose tiles are PARTIAL
+    (1, 2, 37, 64, 0.3, False, 63),
+    (2, 2, 37, 64, 0.3, True, 1),
+    (4, 4, 20, 128, 0.25, True, 100),
+    (16, 16, 256, 128, 0.10, False, 27),
 ])
-def test_device_csr_matches_host_plan_and_oracle(lh, H, nb, bs, density, causal):
+def test_device_csr_matches_host_plan_and_oracle(lh, H, nb, bs, density, causal, cut):
     bm = random_bitmap(lh, nb, density, seed=nb + lh)
     bm[0, 3, :] = 0                                  # an empty row (the diagonal too)
     bm[-1, nb - 2, :] = 1                            # a full row
-    N = nb * bs
+    bm[-1, :, nb - 1] = 1                            # a full last column (the short block when cut > 0)
+    N = nb * bs - cut
     lay = bitmap_layout(bm, causal)
     dtype = torch.float32 if bs == 64 else torch.bfloat16
     D = 64 if bs == 64 else 128
@@ -89,7 +95,10 @@ def test_device_csr_matches_host_plan_and_oracle(lh, H, nb, bs, density, causal)
         ht = hp.csr_transposed(h)
         assert all(np.array_equal(gt[key], ht[key]) for key in ("col_ptr", "row_idx", "flags"))
     assert int(nnz.item()) == total == hp.info["nnz"]
-    say(f"  lh={lh} nb={nb} causal={causal}: {total} entries identical, transposed lists too")
+    if cut:
+        flags = np.concatenate([np.asarray(dp.read_csr(h)["flags"]) for h in range(lh)])
+        assert flags.sum() > 0
+    say(f"  lh={lh} nb={nb} N={N} causal={causal}: {total} entries identical, transposed lists too")
 
 
 @pytest.mark.parametrize("lh,nb,causal", [(8, 1100, False), (8, 1100, True), (64, 1024, False), (64, 1024, True)])
@@ -210,3 +219,49 @@ def test_varlen_through_dynamic_plan_is_bitwise_the_static_one():
         for name, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), *res):
             assert torch.equal(a, b), f"causal={causal}: {name} differs"
         say(f"  causal={causal}: forward and backward bitwise equal")
+
+
+@pytest.mark.parametrize("dtype,seq_len,block,D", [(torch.bfloat16, 4000, 128, 128), (torch.float32, 1000, 64, 64)])
+def test_ragged_seq_len_through_dynamic_plan(dtype, seq_len, block, D):
+    """A seq_len the block does not divide: forward and backward through a
+    dynamic plan equal, bit for bit, the same calls through the host-built plan
+    of the same bitmap (the short last block's tiles PARTIAL in both), and the
+    oracle within the library tolerances on sampled rows, including the last
+    row and every row of the short block's first and last tokens."""
+    nb = -(-seq_len // block)
+    H, Hkv, B = 4, 2, 2
+    bm = random_bitmap(H, nb, 0.25, seed=seq_len)
+    bm[1, :, nb - 1] = 1                             # every q-block sees the short block
+    bm[2, nb - 1, :] = 1                             # the short block sees every key block
+    tol_o, tol_l = (2e-2, 1e-3) if dtype == torch.bfloat16 else (1e-5, 1e-5)
+    for causal in (False, True):
+        lay = bitmap_layout(bm, causal)
+        g = torch.Generator().manual_seed(seq_len + causal)
+        q, k, v, do = (torch.randn(B, h, seq_len, D, generator=g).to(dtype) for h in (H, Hkv, Hkv, H))
+        qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+        sp = bsattn.plan(B, H, Hkv, seq_len, D, block, dtype, lay)
+        dp = bsattn.plan_dynamic(B, H, Hkv, seq_len, D, block, dtype, causal, H)
+        assert dp.info["num_blocks"] == nb
+        dp.set_bitmap(torch.from_numpy(bm).cuda())
+        for h in range(H):
+            assert_same_csr(dp.read_csr(h), sp.csr(h), f"head {h}")
+        res = []
+        for p in (sp, dp):
+            o, l = bsattn.forward(qc, kc, vc, p)
+            res.append((o, l) + bsattn.backward(qc, kc, vc, o, l, doc, p))
+        torch.cuda.synchronize()
+        for name, a, b in zip(("O", "LSE", "dQ", "dK", "dV"), *res):
+            assert torch.equal(a, b), f"causal={causal}: {name} differs"
+        o, l = res[1][0], res[1][1]
+        tail = (nb - 1) * block
+        rows = [(b, h, qq) for b in range(B) for h in range(H)
+                for qq in (0, 1, block - 1, tail - 1, tail, seq_len - 2, seq_len - 1)]
+        O_ref, L_ref = oracle.forward(q, k, v, lay, block, rows=rows)
+        idx = tuple(torch.tensor(x) for x in zip(*rows))
+        eo = float(np.abs(o[idx].float().cpu().numpy() - O_ref).max())
+        fin = np.isfinite(L_ref)
+        el = float(np.abs(l[idx].cpu().numpy()[fin] - L_ref[fin]).max()) if fin.any() else 0.0
+        assert np.array_equal(np.isfinite(l[idx].cpu().numpy()), fin)
+        say(f"  {dtype} N={seq_len} causal={causal}: bitwise equal to the static plan; "
+            f"max|dO| {eo:.2e} max|dLSE| {el:.2e}")
+        assert eo <= tol_o and el <= tol_l
