@@ -232,6 +232,38 @@ def dynamic_plan_context():
                      "nnz_matches_host": int(nnz.item()) == hp.info["nnz"]}
         log(f"[bench] dynamic plan {name}: {res[name]}")
         del dbm, dp, hp
+    res["backward_long_columns"] = dynamic_backward_context()
+    return res
+
+
+def dynamic_backward_context(steps=5):
+    """The backward through a dynamic plan against the static plan of the same
+    bitmap, where key-block columns are dense (global key blocks read by every
+    q-block): B=1, H=32, Hkv=8, N=64K, causal, per-head Bernoulli(0.05) bitmap
+    with the diagonal and key blocks 0 and 1 on.  bsa_plan_set_bitmap cuts
+    the long dK/dV walks on the device, as the host planner does."""
+    w = wl.Workload("globalcols64k", 1, 32, 8, 65536, 128, 128, torch.bfloat16, 6, {})
+    nb = w.seq_len // w.block
+    g = torch.Generator(device="cuda").manual_seed(6)
+    bm = (torch.rand((w.heads, nb, nb), generator=g, device="cuda") < 0.05).to(torch.uint8)
+    bm[:, torch.arange(nb), torch.arange(nb)] = 1
+    bm[:, :, :2] = 1
+    lay = dict(causal=True, unit="blocks", window_left=-1, window_right=-1, global_keys=0, global_queries=0,
+               bitmap=bm.cpu().numpy())
+    sp = plan_for(w, lay)
+    dp = bsattn.plan_dynamic(w.batch, w.heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.dtype, True, w.heads)
+    dp.set_bitmap(bm)
+    q, k, v = wl.make_qkv(w, "cuda")
+    do = wl.make_dout(w, "cuda")
+    res = {"bitmap": [w.heads, nb, nb], "active_tiles": sp.info["active_blocks"]}
+    for name, p in (("static", sp), ("dynamic", dp)):
+        out, lse = bsattn.forward(q, k, v, p)
+        res[f"{name}_ms"] = round(float(np.mean(time_backward(p, q, k, v, out, lse, do, steps, 1))), 3)
+        res[f"{name}_split_columns"] = p.read_work_kv()[1]
+    res["dynamic_over_static"] = round(res["dynamic_ms"] / res["static_ms"], 3)
+    log(f"[bench] dynamic-plan backward with dense key-block columns: {res}")
+    del q, k, v, do, sp, dp, bm
+    torch.cuda.empty_cache()
     return res
 
 

@@ -66,6 +66,7 @@ struct BwdParams {
   const int32_t* kv_desc;     // dK/dV launch order: per slot {item (b * Hkv + hk) * nb + j,
                               // first and end entry of the group's walk, partial slot or -1}
   const int32_t* kv_reduce;   // per split column {item, first partial slot, count, 0}
+  const int32_t* kv_reduce_count;   // device count of kv_reduce entries (dynamic plans), else NULL
   float* kv_scratch;          // float32 partials [slot][dK, dV][128 keys][128]
   int64_t N;
   int32_t H, Hkv, group, nb, per_head_layout;
@@ -709,31 +710,35 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
 // ---------------------------------------------------------------------------
 // Split columns: dK = scale * sum of the chunks' partials, dV = their sum, in
 // chunk order (deterministic); kReduceParts workgroups per split column
-// (blockIdx.y), 4 values per thread.
+// (blockIdx.y), 4 values per thread.  A dynamic plan's list length is known
+// only on the device: its workgroups stride over the list by gridDim.x.
 // ---------------------------------------------------------------------------
 constexpr int kReduceParts = 2 * kB * kD / 4 / kThreads;   // 32
 
 __global__ __launch_bounds__(kThreads) void bwd_kv_reduce(BwdParams p) {
-  const int item = p.kv_reduce[4 * blockIdx.x];
-  const int first = p.kv_reduce[4 * blockIdx.x + 1];
-  const int count = p.kv_reduce[4 * blockIdx.x + 2];
-  const int j = item % p.nb;
-  const int bk = item / p.nb;
-  const int hk = bk % p.Hkv, b = bk / p.Hkv;
-  const int64_t row0 = (int64_t(b) * p.Hkv + hk) * p.N + int64_t(j) * kB;
+  const int splits = p.kv_reduce_count ? *p.kv_reduce_count : int(gridDim.x);
   const int v = blockIdx.y * kThreads + threadIdx.x;
   const int tensor = v / (kB * kD / 4);              // 0: dK, 1: dV
   const int e = 4 * (v % (kB * kD / 4));             // element (key * 128 + d) of the tile
-  if (int64_t(j) * kB + e / kD >= p.N) return;       // beyond a ragged sequence's end
-  f32x4 acc = f32x4{};
-  for (int c = 0; c < count; ++c)
-    acc += *reinterpret_cast<const f32x4*>(p.kv_scratch + (int64_t(first + c) * 2 + tensor) * kB * kD + e);
   const float mul = tensor == 0 ? p.scale : 1.f;
-  u32x2 pk;
-  pk[0] = uint32_t(bf16_bits(acc[0] * mul)) | (uint32_t(bf16_bits(acc[1] * mul)) << 16);
-  pk[1] = uint32_t(bf16_bits(acc[2] * mul)) | (uint32_t(bf16_bits(acc[3] * mul)) << 16);
-  uint16_t* const dst = (tensor == 0 ? p.dk : p.dv) + row0 * kD + e;
-  *reinterpret_cast<u32x2*>(dst) = pk;
+  for (int r = blockIdx.x; r < splits; r += gridDim.x) {
+    const int item = p.kv_reduce[4 * r];
+    const int first = p.kv_reduce[4 * r + 1];
+    const int count = p.kv_reduce[4 * r + 2];
+    const int j = item % p.nb;
+    const int bk = item / p.nb;
+    const int hk = bk % p.Hkv, b = bk / p.Hkv;
+    const int64_t row0 = (int64_t(b) * p.Hkv + hk) * p.N + int64_t(j) * kB;
+    if (int64_t(j) * kB + e / kD >= p.N) continue;    // beyond a ragged sequence's end
+    f32x4 acc = f32x4{};
+    for (int c = 0; c < count; ++c)
+      acc += *reinterpret_cast<const f32x4*>(p.kv_scratch + (int64_t(first + c) * 2 + tensor) * kB * kD + e);
+    u32x2 pk;
+    pk[0] = uint32_t(bf16_bits(acc[0] * mul)) | (uint32_t(bf16_bits(acc[1] * mul)) << 16);
+    pk[1] = uint32_t(bf16_bits(acc[2] * mul)) | (uint32_t(bf16_bits(acc[3] * mul)) << 16);
+    uint16_t* const dst = (tensor == 0 ? p.dk : p.dv) + row0 * kD + e;
+    *reinterpret_cast<u32x2*>(dst) = pk;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1006,6 +1011,7 @@ bsa_status_t backward_impl(const void* q, const void* k, const void* v, const vo
   prm.entries_t = plan->d_entries_t;
   prm.kv_desc = plan->d_work_kv;
   prm.kv_reduce = plan->d_kv_reduce;
+  prm.kv_reduce_count = plan->dynamic ? plan->d_kv_count : nullptr;
   prm.kv_scratch = plan->d_kv_scratch;
   prm.N = pr.seq_len;
   prm.N32 = int32_t(pr.seq_len);
@@ -1066,8 +1072,8 @@ bsa_status_t backward_impl(const void* q, const void* k, const void* v, const vo
       hipLaunchKernelGGL(bwd_dkdv_bf16_d128<false>, dim3(unsigned(plan->work_kv.size())), dim3(kThreads), 0, s, prm);
     err = hipGetLastError();
   }
-  if (err == hipSuccess && !plan->kv_reduce.empty()) {
-    hipLaunchKernelGGL(bwd_kv_reduce, dim3(unsigned(plan->kv_reduce.size()), kReduceParts), dim3(kThreads), 0, s,
+  if (err == hipSuccess && plan->kv_reduce_launch > 0) {
+    hipLaunchKernelGGL(bwd_kv_reduce, dim3(unsigned(plan->kv_reduce_launch), kReduceParts), dim3(kThreads), 0, s,
                        prm);
     err = hipGetLastError();
   }

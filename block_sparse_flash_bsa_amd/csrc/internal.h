@@ -62,6 +62,14 @@ struct bsa_plan {
   std::vector<KvDesc> kv_reduce;               // {item, first partial, count, 0}
   int32_t kv_chunk = 0;
   int64_t kv_partials = 0;
+  int64_t kv_reduce_launch = 0;                // workgroups (x) of the reduction launch
+  // Dynamic plans (bf16 backward): bsa_plan_set_bitmap cuts the long walks
+  // on the device, by the rule above.  The first kv_extra_slots launch slots
+  // take every chunk of a split column after its first (which keeps the
+  // column's own slot); at most kv_partials chunks exist at once (the chunk
+  // length doubles until they fit), and *d_kv_count is the number of split
+  // columns in d_kv_reduce.
+  int64_t kv_extra_slots = 0;
   // Device copy (bsa_plan and bsa_plan_dynamic).
   int device = -1;
   void* dev_mem = nullptr;
@@ -73,6 +81,11 @@ struct bsa_plan {
   const int32_t* d_work_kv = nullptr;          // [dK/dV launch slots] as int4 KvDesc
   const int32_t* d_kv_reduce = nullptr;        // [split columns] as int4 KvDesc
   float* d_kv_scratch = nullptr;               // [kv_partials][2][128][128] float32
+  const int32_t* d_kv_count = nullptr;         // dynamic: split columns written by set_bitmap
+  int32_t* d_kv_walk = nullptr;                // dynamic: [Hkv * nb] walk length of (hk, j)
+  int64_t* d_kv_pre = nullptr;                 // dynamic: [Hkv * nb] packed chunk prefixes
+  int32_t* d_kv_head = nullptr;                // dynamic: [8] chunk length and totals
+  const int32_t* d_kv_slot = nullptr;          // dynamic: [B * Hkv * nb] item -> slot after the extra ones
   void* dev_scratch = nullptr;                 // allocation behind d_kv_scratch
   // Dynamic plans: the CSR is written on the device by bsa_plan_set_bitmap;
   // d_counts is its per-row scratch [layout_heads * nb], d_scan the scan's

@@ -48,6 +48,9 @@ bool kernel_supported(int32_t dtype, int32_t head_dim, int32_t block_size) {
 namespace {
 
 constexpr int kNumXcd = 8;  // MI355X: 8 XCDs; workgroup w is dispatched to XCD w % 8
+// A dynamic plan keeps float32 partial dK/dV tiles (128 KiB each) for at most
+// this many chunks of split walks: 128 MiB.
+constexpr int64_t kDynamicPartials = 1024;
 
 struct TokenRule {
   bool causal;
@@ -323,6 +326,7 @@ void build_work_kv(Plan& P) {
       P.kv_desc[s] = pieces[slots[s]];
       P.work_kv[s] = pieces[slots[s]].item;
     }
+  P.kv_reduce_launch = int64_t(P.kv_reduce.size());
 }
 
 // Launch order.  Item id = (b * H + h) * nb + i; cost = row length + 1.
@@ -531,6 +535,7 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
                 (long long)cap);
   Plan* P = new (std::nothrow) Plan();
   if (!P) return fail(BSA_ERR_OUT_OF_MEMORY, "host allocation of the plan failed");
+  std::vector<int32_t> slot_of;   // dK/dV item -> its slot after the extra ones
   try {
     P->prob = *problem;
     if (P->prob.scale == 0.f) P->prob.scale = 1.0f / std::sqrt(float(problem->head_dim));
@@ -541,15 +546,29 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
     P->dynamic = 1;
     P->entry_capacity = cap;
     build_work(*P);
-    // dK/dV launch order: every (b, KV head, k-block) walks its whole column
-    // (lengths are only known on the device, so nothing is split).
+    // dK/dV launch order: one slot per (b, KV head, k-block), locality runs
+    // per XCD with equal item counts.  For the bf16 backward, kv_extra_slots
+    // slots (whole rounds of the XCD count, so every item keeps its XCD) go
+    // before them for the chunks bsa_plan_set_bitmap cuts from long walks;
+    // until then every walk is whole (and empty).
     const int64_t kv_items = int64_t(problem->batch) * problem->num_kv_heads * nb;
     std::vector<int32_t> loc(static_cast<size_t>(kv_items));
     std::iota(loc.begin(), loc.end(), 0);
-    P->work_kv = loc.empty() ? loc : xcd_slots(loc, [](int64_t) { return int64_t(1); });
+    const std::vector<int32_t> order = loc.empty() ? loc : xcd_slots(loc, [](int64_t) { return int64_t(1); });
+    const bool split = problem->dtype == BSA_BF16 && problem->head_dim == 128 && problem->block_size == 128;
+    if (split && kv_items > 0) {
+      P->kv_partials = std::min<int64_t>(kv_items, kDynamicPartials);
+      P->kv_extra_slots = (P->kv_partials + kNumXcd - 1) / kNumXcd * kNumXcd;
+      P->kv_reduce_launch = std::min<int64_t>(std::max<int64_t>(P->kv_partials / 2, 1), 64);
+    }
+    P->work_kv.assign(static_cast<size_t>(P->kv_extra_slots), -1);
+    P->work_kv.insert(P->work_kv.end(), order.begin(), order.end());
     P->kv_desc.assign(P->work_kv.size(), {-1, 0, 0, -1});
     for (size_t s = 0; s < P->work_kv.size(); ++s)
       if (P->work_kv[s] >= 0) P->kv_desc[s] = {P->work_kv[s], 0, INT32_MAX, -1};
+    slot_of.assign(static_cast<size_t>(kv_items), -1);
+    for (size_t s = 0; s < order.size(); ++s)
+      if (order[s] >= 0) slot_of[static_cast<size_t>(order[s])] = int32_t(s);
   } catch (const std::bad_alloc&) {
     delete P;
     return fail(BSA_ERR_OUT_OF_MEMORY, "host allocation while building the plan failed");
@@ -563,8 +582,11 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
     return fail(BSA_ERR_DEVICE, "hipGetDevice failed: no usable HIP device");
   }
   // [rows | counts | entries | work | transposed rows | transposed entries |
-  // dK/dV work | scan block sums], each part 256-byte aligned.
+  // dK/dV work | scan block sums | walk splitting: item slots, walks, chunk
+  // prefixes, split columns, header], each part 256-byte aligned.
   const size_t rows = size_t(P->layout_heads) * P->nb;
+  const bool split = P->kv_extra_slots > 0;
+  const size_t kv_cols = split ? size_t(problem->num_kv_heads) * P->nb : 0;
   auto up = [](size_t x) { return (x + 255) & ~size_t(255); };
   const size_t off_counts = up(rows * sizeof(bsa::RowDesc));
   const size_t off_entries = off_counts + up(rows * sizeof(int32_t));
@@ -573,7 +595,12 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
   const size_t off_entries_t = off_cols + up(rows * sizeof(bsa::RowDesc));
   const size_t off_work_kv = off_entries_t + up(size_t(cap) * sizeof(int32_t));
   const size_t off_scan = off_work_kv + up(P->kv_desc.size() * sizeof(Plan::KvDesc));
-  const size_t bytes = off_scan + ((rows + 1023) / 1024 + 1) * sizeof(int64_t);
+  const size_t off_slot = off_scan + up(((rows + 1023) / 1024 + 1) * sizeof(int64_t));
+  const size_t off_walk = off_slot + up((split ? slot_of.size() : 0) * sizeof(int32_t));
+  const size_t off_pre = off_walk + up(kv_cols * sizeof(int32_t));
+  const size_t off_reduce = off_pre + up(kv_cols * sizeof(int64_t));
+  const size_t off_head = off_reduce + up(size_t(P->kv_partials) * sizeof(Plan::KvDesc));
+  const size_t bytes = off_head + 8 * sizeof(int32_t);
   hipError_t err = hipMalloc(&P->dev_mem, bytes);
   if (err != hipSuccess) {
     P->dev_mem = nullptr;
@@ -591,6 +618,23 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
   if (err == hipSuccess && !P->kv_desc.empty())
     err = hipMemcpy(base + off_work_kv, P->kv_desc.data(), P->kv_desc.size() * sizeof(Plan::KvDesc),
                     hipMemcpyHostToDevice);
+  // No split column until the first bitmap arrives.
+  if (err == hipSuccess) err = hipMemset(base + off_head, 0, 8 * sizeof(int32_t));
+  if (err == hipSuccess && split)
+    err = hipMemcpy(base + off_slot, slot_of.data(), slot_of.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (err == hipSuccess && split) {
+    // float32 partial dK and dV of every chunk of a split column.
+    const size_t sbytes = size_t(P->kv_partials) * 2 * 128 * 128 * sizeof(float);
+    err = hipMalloc(&P->dev_scratch, sbytes);
+    if (err != hipSuccess) {
+      P->dev_scratch = nullptr;
+      (void)hipFree(P->dev_mem);
+      delete P;
+      return fail(err == hipErrorOutOfMemory ? BSA_ERR_OUT_OF_MEMORY : BSA_ERR_DEVICE,
+                  "hipMalloc(%zu) for the backward's partial sums failed: %s", sbytes, hipGetErrorString(err));
+    }
+    P->d_kv_scratch = static_cast<float*>(P->dev_scratch);
+  }
   if (err != hipSuccess) {
     (void)hipFree(P->dev_mem);
     delete P;
@@ -604,7 +648,14 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
   P->d_entries_t = reinterpret_cast<const int32_t*>(base + off_entries_t);
   P->d_work_kv = reinterpret_cast<const int32_t*>(base + off_work_kv);
   P->d_scan = reinterpret_cast<int64_t*>(base + off_scan);
-  P->d_kv_reduce = nullptr;
+  P->d_kv_reduce = reinterpret_cast<const int32_t*>(base + off_reduce);
+  P->d_kv_head = reinterpret_cast<int32_t*>(base + off_head);
+  P->d_kv_count = P->d_kv_head + 4;
+  if (split) {
+    P->d_kv_slot = reinterpret_cast<const int32_t*>(base + off_slot);
+    P->d_kv_walk = reinterpret_cast<int32_t*>(base + off_walk);
+    P->d_kv_pre = reinterpret_cast<int64_t*>(base + off_pre);
+  }
   P->info.on_device = 1;
   *out = P;
   return BSA_OK;

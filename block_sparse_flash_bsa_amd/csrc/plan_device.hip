@@ -290,6 +290,122 @@ __global__ __launch_bounds__(kStripThreads) void fill_cols(const uint8_t* __rest
   }
 }
 
+// ---------------------------------------------------------------------------
+// Cutting long dK/dV walks (bf16 backward of a dynamic plan).  The walk of
+// item (b, hk, j) is the transposed lists of column j of the KV group's
+// query heads, one after another: walk[hk * nb + j] entries, the same for
+// every batch entry.  As the host planner does for static plans, a walk
+// longer than the chunk length C = max(64, 2 * mean walk) becomes
+// k = ceil(L / C) chunks [c * L / k, (c + 1) * L / k); here C doubles until
+// the chunks fit the plan's partial-tile and slot budgets.  One workgroup
+// finds C and, per column, the exclusive prefixes of the extra chunks
+// (beyond each split column's first), the partial tiles and the split
+// columns, packed 21 bits each (the budgets keep every sum below 2^20); a
+// wide kernel then writes the launch descriptors and the reduction list.
+// ---------------------------------------------------------------------------
+constexpr int kPackBits = 21;
+constexpr long long kPackMask = (1ll << kPackBits) - 1;
+constexpr int kWriteThreads = 256;
+
+__device__ __forceinline__ long long split_pack(long long L, long long chunk) {
+  if (L <= chunk) return 0;
+  const long long k = (L + chunk - 1) / chunk;
+  return (k - 1) | (k << kPackBits) | (1ll << (2 * kPackBits));
+}
+
+// head: [0] chunk length, [1] extra chunks, [2] partial tiles, [3] split
+// columns (each per batch entry), [4] split columns in all.
+__global__ __launch_bounds__(kScanBlock) void kv_split_plan(const RowDesc* __restrict__ cols, int nb, int n,
+                                                            int group, int per_head, int batch,
+                                                            long long max_extra, long long max_parts,
+                                                            int32_t* __restrict__ walk, int64_t* __restrict__ pre,
+                                                            int32_t* __restrict__ head) {
+  __shared__ long long wsum[kScanWaves];
+  // Thread t owns the contiguous columns [x0, x1) and reads back only what it wrote.
+  const int per = (n + kScanBlock - 1) / kScanBlock;
+  const int x0 = min(n, int(threadIdx.x) * per), x1 = min(n, x0 + per);
+  long long mine = 0;
+  for (int x = x0; x < x1; ++x) {
+    const int hk = x / nb, j = x - hk * nb;
+    int L = 0;
+    for (int g = 0; g < group; ++g) L += cols[(per_head ? hk * group + g : 0) * nb + j].count;
+    walk[x] = L;
+    mine += L;
+  }
+  long long total;
+  block_scan(mine, wsum, total);
+  __syncthreads();
+  long long chunk = n > 0 ? 2 * ((total + n - 1) / n) : 0;
+  if (chunk < 64) chunk = 64;
+  for (;;) {
+    // Extra chunks (low 32 bits) and partial tiles (high 32 bits) at this chunk length.
+    long long ep = 0;
+    for (int x = x0; x < x1; ++x) {
+      const long long L = walk[x];
+      if (L > chunk) {
+        const long long k = (L + chunk - 1) / chunk;
+        ep += (k - 1) + (k << 32);
+      }
+    }
+    long long sum;
+    block_scan(ep, wsum, sum);
+    __syncthreads();
+    if ((sum & 0xffffffffll) * batch <= max_extra && (sum >> 32) * batch <= max_parts) break;
+    chunk *= 2;
+  }
+  long long packed = 0;
+  for (int x = x0; x < x1; ++x) packed += split_pack(walk[x], chunk);
+  long long all;
+  long long run = block_scan(packed, wsum, all) - packed;
+  for (int x = x0; x < x1; ++x) {
+    pre[x] = run;
+    run += split_pack(walk[x], chunk);
+  }
+  if (threadIdx.x == 0) {
+    head[0] = int32_t(chunk < 0x7fffffffll ? chunk : 0x7fffffffll);
+    head[1] = int32_t(all & kPackMask);
+    head[2] = int32_t((all >> kPackBits) & kPackMask);
+    head[3] = int32_t((all >> (2 * kPackBits)) & kPackMask);
+    head[4] = batch * head[3];
+  }
+}
+
+// One thread per item t = b * n + hk * nb + j (and per extra slot): the
+// item's own slot runs its whole walk or its first chunk; the other chunks go
+// to the extra slots, the split column to the reduction list; extra slots
+// left over are idle.
+__global__ __launch_bounds__(kWriteThreads) void kv_split_write(const int32_t* __restrict__ walk,
+                                                                const int64_t* __restrict__ pre,
+                                                                const int32_t* __restrict__ head,
+                                                                const int32_t* __restrict__ slot_of, int n,
+                                                                int64_t items, int64_t extra_slots,
+                                                                int4* __restrict__ desc, int4* __restrict__ reduce) {
+  const int64_t t = int64_t(blockIdx.x) * kWriteThreads + threadIdx.x;
+  const int chunk = head[0], e_b = head[1], p_b = head[2], s_b = head[3];
+  const int64_t b = t / n;
+  if (t >= (items / n) * e_b && t < extra_slots) desc[t] = make_int4(-1, 0, 0, -1);
+  if (t >= items) return;
+  const int x = int(t - b * n);
+  const int L = walk[x];
+  const int s = slot_of[t];
+  if (s < 0) return;
+  int4* own = desc + extra_slots + s;
+  if (L <= chunk) {
+    *own = make_int4(int(t), 0, L, -1);
+    return;
+  }
+  const long long pk = pre[x];
+  const int e0 = int(pk & kPackMask), p0 = int((pk >> kPackBits) & kPackMask);
+  const int r0 = int((pk >> (2 * kPackBits)) & kPackMask);
+  const int k = (L + chunk - 1) / chunk;
+  const int pb = int(b * p_b + p0);
+  *own = make_int4(int(t), 0, L / k, pb);
+  int4* ex = desc + b * e_b + e0 - 1;    // chunk c >= 1 at ex[c]
+  for (int c = 1; c < k; ++c)
+    ex[c] = make_int4(int(t), int(int64_t(c) * L / k), int(int64_t(c + 1) * L / k), pb + c);
+  reduce[b * s_b + r0] = make_int4(int(t), pb, k, 0);
+}
+
 }  // namespace
 }  // namespace bsa
 
@@ -362,6 +478,21 @@ extern "C" bsa_status_t bsa_plan_set_bitmap(bsa_plan_t plan, const uint8_t* d_bi
   else
     hipLaunchKernelGGL(fill_cols<1>, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal, tail,
                        d_cols, d_entries_t);
+  if (plan->kv_extra_slots > 0) {
+    // The dK/dV launch descriptors for the new walk lengths.
+    const int hkv = plan->prob.num_kv_heads, group = plan->prob.num_heads / hkv;
+    const int n = hkv * nb;
+    const int64_t items = int64_t(plan->prob.batch) * n;
+    hipLaunchKernelGGL(kv_split_plan, dim3(1), dim3(kScanBlock), 0, s, d_cols, nb, n, group,
+                       plan->layout_heads > 1 ? 1 : 0, plan->prob.batch, (long long)plan->kv_extra_slots,
+                       (long long)plan->kv_partials, plan->d_kv_walk, plan->d_kv_pre, plan->d_kv_head);
+    const int64_t cover = items > plan->kv_extra_slots ? items : plan->kv_extra_slots;
+    hipLaunchKernelGGL(kv_split_write, dim3(unsigned((cover + kWriteThreads - 1) / kWriteThreads)),
+                       dim3(kWriteThreads), 0, s, plan->d_kv_walk, plan->d_kv_pre, plan->d_kv_head,
+                       plan->d_kv_slot, n, items, plan->kv_extra_slots,
+                       reinterpret_cast<int4*>(const_cast<int32_t*>(plan->d_work_kv)),
+                       reinterpret_cast<int4*>(const_cast<int32_t*>(plan->d_kv_reduce)));
+  }
   const hipError_t err = hipGetLastError();
   if (err != hipSuccess) return fail(BSA_ERR_DEVICE, "planner launch failed: %s", hipGetErrorString(err));
   return BSA_OK;
@@ -421,4 +552,26 @@ extern "C" bsa_status_t bsa_plan_read_csr_transposed(bsa_plan_t plan, int32_t la
   bsa::clear_error();
   return bsa::read_device_csr(plan, plan ? plan->d_cols : nullptr, plan ? plan->d_entries_t : nullptr,
                               layout_head, col_ptr, row_idx, flags, capacity, nnz);
+}
+
+extern "C" bsa_status_t bsa_plan_read_work_kv(bsa_plan_t plan, int32_t* desc, int64_t capacity, int64_t* slots,
+                                              int64_t* splits) {
+  using namespace bsa;
+  clear_error();
+  if (!plan || !slots || !splits || (capacity > 0 && !desc))
+    return fail(BSA_ERR_INVALID_ARGUMENT, "NULL argument to bsa_plan_read_work_kv");
+  if (!plan->info.on_device)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "plan was built by bsa_plan_host and has no device copy");
+  const int64_t n = int64_t(plan->kv_desc.size());
+  if (capacity < n)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "capacity %lld is below the plan's %lld dK/dV slots",
+                (long long)capacity, (long long)n);
+  int32_t count = int32_t(plan->kv_reduce.size());
+  if (hipDeviceSynchronize() != hipSuccess ||
+      (n && hipMemcpy(desc, plan->d_work_kv, size_t(n) * 4 * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) ||
+      (plan->dynamic && hipMemcpy(&count, plan->d_kv_count, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess))
+    return fail(BSA_ERR_DEVICE, "reading the dK/dV launch order failed: %s", hipGetErrorString(hipGetLastError()));
+  *slots = n;
+  *splits = count;
+  return BSA_OK;
 }

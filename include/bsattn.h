@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 4
+#define BSA_ABI_VERSION 5
 
 /* Status codes.  Every entry point that can fail returns one; no exception
  * crosses the ABI.  Out-parameters are written only on BSA_OK. */
@@ -214,7 +214,9 @@ int64_t bsa_plan_active_blocks(bsa_plan_t plan);
  * bitmaps that bsa_plan_set_bitmap will take; layout->causal applies; the
  * window and global fields must be -1 and 0 (unit is ignored).  Device memory
  * for the largest possible CSR is allocated here (bitmap_heads * nb * nb
- * four-byte entries, nb * (nb + 1) / 2 per head when causal) together with a
+ * four-byte entries, nb * (nb + 1) / 2 per head when causal; for the bf16
+ * backward also min(batch * num_kv_heads * nb, 1024) float32 partial dK/dV
+ * tiles of 128 KiB for the chunks of long walks) together with a
  * fixed launch order of every (b, h, q-block) item, locality runs per XCD as
  * in BSA_SCHEDULE_XCD but with equal item counts (row lengths are not known
  * on the host), and the same for the backward's transposed lists and its
@@ -307,12 +309,29 @@ bsa_status_t bsa_plan_csr_transposed(bsa_plan_t plan, int32_t layout_head, const
 /* Launch order of the dK/dV kernel: slot s runs item work[s] =
  * (b * num_kv_heads + hk) * nb + j, or -1 for an idle slot.  An item whose
  * walk (the transposed lists of its group's query heads, one after another)
- * is longer than twice the mean, such as the k-block of a global key, is cut
- * into chunks that occupy several slots; their float32 partial sums live in
- * plan-owned device scratch and a reduction kernel adds them in chunk order.
- * Dynamic plans never split (their column lengths live on the device).
- * Plan-owned.  Errors: INVALID_ARGUMENT for NULL pointers. */
+ * is longer than the chunk length C = max(64, 2 * mean walk), such as the
+ * k-block of a global key, is cut into k = ceil(walk / C) chunks that occupy
+ * several slots; their float32 partial sums live in plan-owned device scratch
+ * and a reduction kernel adds them in chunk order.  For a dynamic plan's bf16
+ * backward the cut is made on the device by bsa_plan_set_bitmap, by the same
+ * rule (so the results equal a static plan's of the same bitmap bit for bit),
+ * except that C doubles while the chunks would exceed the plan's budget of
+ * min(items, 1024) partial tiles of 128 KiB; its first slots (that budget,
+ * rounded up to a multiple of 8) are reserved for those chunks and show here
+ * as idle, the other slots as the items' fixed order.  Plan-owned.
+ * Errors: INVALID_ARGUMENT for NULL pointers. */
 bsa_status_t bsa_plan_work_kv(bsa_plan_t plan, const int32_t** work, int64_t* slots);
+
+/* The dK/dV launch descriptors as the device holds them (synchronous: waits
+ * for the device): desc [slots][4] int32 = {item, first walk entry, end
+ * entry, partial tile or -1 for a whole walk}, item -1 for an idle slot;
+ * *splits = the number of split columns the reduction sums.  For a dynamic
+ * plan these are what the last bsa_plan_set_bitmap wrote.  capacity is the
+ * room in desc, in slots (bsa_plan_work_kv gives the count).
+ * Errors: INVALID_ARGUMENT for NULL pointers, a host-only plan or too small a
+ * capacity; DEVICE if the copy fails. */
+bsa_status_t bsa_plan_read_work_kv(bsa_plan_t plan, int32_t* desc, int64_t capacity, int64_t* slots,
+                                   int64_t* splits);
 
 /* Run the backward pass asynchronously on `stream` (a hipStream_t; NULL =
  * the default stream) of the plan's device.

@@ -265,3 +265,116 @@ def test_ragged_seq_len_through_dynamic_plan(dtype, seq_len, block, D):
         say(f"  {dtype} N={seq_len} causal={causal}: bitwise equal to the static plan; "
             f"max|dO| {eo:.2e} max|dLSE| {el:.2e}")
         assert eo <= tol_o and el <= tol_l
+
+
+def chunks_of(desc):
+    """The launch descriptors as a sorted list of (item, begin, end, split?),
+    independent of slot positions and partial-tile numbering."""
+    return sorted((int(a), int(b), int(c), int(p >= 0)) for a, b, c, p in desc if a >= 0)
+
+
+def grads(p, q, k, v, do):
+    o, l = bsattn.forward(q, k, v, p)
+    g = bsattn.backward(q, k, v, o, l, do, p)
+    torch.cuda.synchronize()
+    return (o, l) + g
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dynamic_plan_splits_long_walks_like_the_static_plan(causal):
+    """Full bitmap columns (a global key block read by every q-block): the
+    device cuts their dK/dV walks by the host planner's rule, so the
+    descriptors hold the same chunks, the backward equals the static plan's
+    bit for bit and matches the oracle on every element; a second bitmap with
+    no long column leaves no chunk behind."""
+    B, H, Hkv, N, bs = 1, 8, 1, 4096, 128
+    nb = N // bs
+    bm = random_bitmap(H, nb, 0.05, seed=21)
+    bm[:, :, 0] = 1
+    bm[:, :, 5] = 1
+    bm[0, :, 20] = 1
+    g = torch.Generator().manual_seed(5 + causal)
+    q, do = (torch.randn(B, H, N, 128, generator=g).to(torch.bfloat16) for _ in range(2))
+    k, v = (torch.randn(B, Hkv, N, 128, generator=g).to(torch.bfloat16) for _ in range(2))
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    dp = bsattn.plan_dynamic(B, H, Hkv, N, 128, bs, torch.bfloat16, causal, H)
+    for step, bmap in (("long columns", bm), ("no long column", random_bitmap(H, nb, 0.05, seed=22))):
+        lay = bitmap_layout(bmap, causal)
+        sp = bsattn.plan(B, H, Hkv, N, 128, bs, torch.bfloat16, lay)
+        dp.set_bitmap(torch.from_numpy(bmap).cuda())
+        ds, nd = dp.read_work_kv()
+        ss, ns = sp.read_work_kv()
+        assert chunks_of(ds) == chunks_of(ss) and nd == ns, step
+        if step == "long columns":
+            assert ns > 0, "expected the full columns' walks to be split"
+        else:
+            assert ns == 0 and all(d[3] < 0 for d in ds if d[0] >= 0)
+        a, b = grads(sp, qc, kc, vc, doc), grads(dp, qc, kc, vc, doc)
+        for name, x, y in zip(("O", "LSE", "dQ", "dK", "dV"), a, b):
+            assert torch.equal(x, y), f"{step}: {name} differs from the static plan"
+        say(f"  causal={causal} {step}: {ns} split columns, bitwise equal to the static plan")
+    # Oracle, every element, for the bitmap with the long columns.
+    lay = bitmap_layout(bm, causal)
+    dp.set_bitmap(torch.from_numpy(bm).cuda())
+    _, _, dq, dk, dv = grads(dp, qc, kc, vc, doc)
+    rq, rk, rv = oracle.backward(q, k, v, do, lay, bs)
+    for name, got, ref in (("dQ", dq, rq), ("dK", dk, rk), ("dV", dv, rv)):
+        got = got.double().cpu().numpy()
+        err, scale = float(np.abs(got - ref).max()), float(np.abs(ref).max())
+        say(f"  {name}: max|err| {err:.3e} (max|ref| {scale:.3e})")
+        assert err <= 1e-2 * scale
+
+
+def test_dynamic_split_budget_doubles_the_chunk():
+    """More chunks than the plan's partial-tile budget (1024 tiles; 18 batch
+    entries x 30 long columns x 2 chunks = 1080): the device doubles the chunk
+    length, here until no walk is split, while the static plan splits all 540
+    columns; the gradients still match the oracle on sampled keys of long and
+    short columns and the static plan's within bf16 rounding."""
+    B, H, Hkv, nb, bs = 18, 4, 1, 72, 128
+    N = nb * bs
+    bm = np.zeros((1, nb, nb), np.uint8)
+    for j in range(30):                              # 30 columns of 36 q-blocks each
+        bm[0, (j + np.arange(36)) % nb, j] = 1
+    bm[0, np.arange(nb), np.arange(nb)] = 1          # the diagonal: no empty row
+    lay = bitmap_layout(bm, False)
+    sp = bsattn.plan(B, H, Hkv, N, 128, bs, torch.bfloat16, lay)
+    dp = bsattn.plan_dynamic(B, H, Hkv, N, 128, bs, torch.bfloat16, False, 1)
+    dp.set_bitmap(torch.from_numpy(bm).cuda())
+    ds, nd = dp.read_work_kv()
+    ss, ns = sp.read_work_kv()
+    say(f"  static plan: {ns} split columns; dynamic plan: {nd}")
+    assert ns == 30 * B and nd == 0
+    assert all(p < 0 for a, _, _, p in ds if a >= 0)
+    g = torch.Generator().manual_seed(9)
+    q, do = (torch.randn(B, H, N, 128, generator=g).to(torch.bfloat16) for _ in range(2))
+    k, v = (torch.randn(B, Hkv, N, 128, generator=g).to(torch.bfloat16) for _ in range(2))
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    a, b = grads(sp, qc, kc, vc, doc), grads(dp, qc, kc, vc, doc)
+    for name, x, y in zip(("O", "LSE", "dQ"), a[:3], b[:3]):
+        assert torch.equal(x, y), name
+    for name, x, y in zip(("dK", "dV"), a[3:], b[3:]):
+        err, scale = float((x.float() - y.float()).abs().max()), float(y.float().abs().max())
+        say(f"  {name}: max|dynamic - static| {err:.3e} (max {scale:.3e})")
+        assert err <= 2 ** -7 * scale
+    # Host float64 copies of the batch entries the sampled keys sit in.
+    keys = [(17, 0, 29 * bs + 77), (7, 0, 50 * bs + 3)]   # a long and a short column
+    sel = sorted({kb for kb, _, _ in keys})
+    f64 = {name: {kb: t[kb].double().numpy() for kb in sel} for name, t in (("q", q), ("k", k), ("v", v), ("do", do))}
+
+    class View:
+        """[b, h] / [b, h, q] indexing over the per-batch-entry host copies."""
+        def __init__(self, part, shape):
+            self.part, self.shape = part, shape
+
+        def __getitem__(self, idx):
+            return self.part[idx[0]][idx[1:]]
+
+    views = [View(f64[name], t.shape) for name, t in (("q", q), ("k", k), ("v", v), ("do", do))]
+    for key in keys:
+        rk, rv = oracle.backward_dkv_keys(*views, lay, bs, [key])
+        for name, got, ref in (("dK", b[3][key], rk[0]), ("dV", b[4][key], rv[0])):
+            got = got.double().cpu().numpy()
+            err, scale = float(np.abs(got - ref).max()), float(np.abs(ref).max())
+            say(f"  {name} at key {key}: max|err| {err:.3e} (max|ref| {scale:.3e})")
+            assert err <= 1e-2 * scale
