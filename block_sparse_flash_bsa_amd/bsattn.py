@@ -434,16 +434,17 @@ def forward_varlen(q, k, v, p: Plan, seq_lens, out=None, lse=None):
     import torch
     pr = p.problem
     B, H, Hk, N, D = pr.batch, pr.num_heads, pr.num_kv_heads, pr.seq_len, pr.head_dim
+    dt = torch.bfloat16 if pr.dtype == BF16 else torch.float32
     if not q.is_cuda:
         raise ValueError(f"q must be a CUDA tensor, got one on {q.device}")
     dev = q.device
     if out is None:
-        out = torch.empty((B, H, N, D), dtype=torch.bfloat16, device=dev)
+        out = torch.empty((B, H, N, D), dtype=dt, device=dev)
     if lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
-    for name, t, shape, tdt in (("q", q, (B, H, N, D), torch.bfloat16), ("k", k, (B, Hk, N, D), torch.bfloat16),
-                                ("v", v, (B, Hk, N, D), torch.bfloat16), ("seq_lens", seq_lens, (B,), torch.int32),
-                                ("out", out, (B, H, N, D), torch.bfloat16), ("lse", lse, (B, H, N), torch.float32)):
+    for name, t, shape, tdt in (("q", q, (B, H, N, D), dt), ("k", k, (B, Hk, N, D), dt),
+                                ("v", v, (B, Hk, N, D), dt), ("seq_lens", seq_lens, (B,), torch.int32),
+                                ("out", out, (B, H, N, D), dt), ("lse", lse, (B, H, N), torch.float32)):
         _require(name, t, shape, tdt, dev)
     with torch.cuda.device(dev):
         stream = torch.cuda.current_stream().cuda_stream

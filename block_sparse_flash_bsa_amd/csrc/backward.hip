@@ -794,8 +794,16 @@ __global__ __launch_bounds__(BS * kF32Lanes) void bwd_dq_f32(BwdParams p) {
   const int t = threadIdx.x;
   const int r = t / kF32Lanes, sl = t % kF32Lanes;
   const int qg = i * BS + r;
+  // The entry's length and block count: the walk is the prefix of the
+  // ascending CSR row below block nbb, tiles of a shorter last block are
+  // masked token by token, and rows at or beyond Nb load row Nb - 1.
+  const int Nb = entry_length(p, b);
+  const int nbb = (Nb + BS - 1) / BS;
+  const bool short_tail = Nb % BS != 0;
+  int ne = i >= nbb ? 0 : row.count;
+  while (ne > 0 && (p.entries[row.start + ne - 1] >> 1) >= nbb) --ne;
   const int64_t hb = (int64_t(b) * p.H + h) * p.N;
-  const int64_t qld = hb + (qg < p.N ? qg : p.N - 1);     // rows beyond a ragged end load row N - 1
+  const int64_t qld = hb + (qg < Nb ? qg : (Nb > 0 ? Nb - 1 : 0));
   const float* fq = reinterpret_cast<const float*>(p.q);
   const float* fdo = reinterpret_cast<const float*>(p.dout);
   const float* Kb = reinterpret_cast<const float*>(p.k) + (int64_t(b) * p.Hkv + hk) * p.N * D;
@@ -811,15 +819,15 @@ __global__ __launch_bounds__(BS * kF32Lanes) void bwd_dq_f32(BwdParams p) {
   const float lse2 = lse == -INFINITY ? 0.f : lse * kLog2e;   // empty rows: every score is masked
   const float dlt = p.delta[qld];
 
-  for (int e = 0; e < row.count; ++e) {
+  for (int e = 0; e < ne; ++e) {
     const int ent = p.entries[row.start + e];
     const int j = ent >> 1;
-    const bool partial = ent & 1;
+    const bool partial = (ent & 1) || (short_tail && (j == nbb - 1 || i == nbb - 1));
     for (int st = 0; st < BS / KT; ++st) {
       const int k0 = j * BS + st * KT;
       __syncthreads();
       for (int x = t; x < KT * D / 4; x += NT) {
-        const int64_t kr = k0 + x / (D / 4) < p.N ? k0 + x / (D / 4) : p.N - 1;
+        const int64_t kr = k0 + x / (D / 4) < Nb ? k0 + x / (D / 4) : Nb - 1;
         const int64_t src = kr * D + (x % (D / 4)) * 4;
         reinterpret_cast<float4*>(Ks)[x] = *reinterpret_cast<const float4*>(Kb + src);
         reinterpret_cast<float4*>(Vs)[x] = *reinterpret_cast<const float4*>(Vb + src);
@@ -836,7 +844,7 @@ __global__ __launch_bounds__(BS * kF32Lanes) void bwd_dq_f32(BwdParams p) {
         }
         a = quad_sum(a);
         c = quad_sum(c);
-        const float pr = (partial && !pair_ok(p, qg, k0 + kk, p.N32)) ? 0.f : __builtin_amdgcn_exp2f(fmaf(a, p.sl2, -lse2));
+        const float pr = (partial && !pair_ok(p, qg, k0 + kk, Nb)) ? 0.f : __builtin_amdgcn_exp2f(fmaf(a, p.sl2, -lse2));
         const float ds = pr * (c - dlt);
 #pragma unroll
         for (int d = 0; d < DL; ++d) acc[d] = fmaf(ds, kr[d], acc[d]);
@@ -867,8 +875,13 @@ __global__ __launch_bounds__(BS * kF32Lanes) void bwd_dkdv_f32(BwdParams p) {
   const int t = threadIdx.x;
   const int r = t / kF32Lanes, sl = t % kF32Lanes;
   const int kg = j * BS + r;
+  // As in dQ: a k-block at or beyond block nbb has no walk, each list stops
+  // below block nbb, and rows at or beyond Nb load row Nb - 1.
+  const int Nb = entry_length(p, b);
+  const int nbb = (Nb + BS - 1) / BS;
+  const bool short_tail = Nb % BS != 0;
   const int64_t kvb = (int64_t(b) * p.Hkv + hk) * p.N;
-  const int64_t kld = kvb + (kg < p.N ? kg : p.N - 1);
+  const int64_t kld = kvb + (kg < Nb ? kg : (Nb > 0 ? Nb - 1 : 0));
   const float* fk = reinterpret_cast<const float*>(p.k);
   const float* fv = reinterpret_cast<const float*>(p.v);
   float kv[DL], vv[DL], dk[DL], dv[DL];
@@ -879,7 +892,7 @@ __global__ __launch_bounds__(BS * kF32Lanes) void bwd_dkdv_f32(BwdParams p) {
     dk[d] = 0.f;
     dv[d] = 0.f;
   }
-  for (int g = 0; g < p.group; ++g) {
+  for (int g = 0; g < (j < nbb ? p.group : 0); ++g) {
     const int h = hk * p.group + g;
     const RowDesc col = p.cols[(p.per_head_layout ? h : 0) * p.nb + j];
     const int64_t hb = (int64_t(b) * p.H + h) * p.N;
@@ -888,18 +901,19 @@ __global__ __launch_bounds__(BS * kF32Lanes) void bwd_dkdv_f32(BwdParams p) {
     for (int e = 0; e < col.count; ++e) {
       const int ent = p.entries_t[col.start + e];
       const int i = ent >> 1;
-      const bool partial = ent & 1;
+      if (i >= nbb) break;                        // the lists ascend in q-block
+      const bool partial = (ent & 1) || (short_tail && (j == nbb - 1 || i == nbb - 1));
       for (int st = 0; st < BS / QT; ++st) {
         const int q0 = i * BS + st * QT;
         __syncthreads();
         for (int x = t; x < QT * D / 4; x += NT) {
-          const int64_t qr = q0 + x / (D / 4) < p.N ? q0 + x / (D / 4) : p.N - 1;
+          const int64_t qr = q0 + x / (D / 4) < Nb ? q0 + x / (D / 4) : Nb - 1;
           const int64_t src = qr * D + (x % (D / 4)) * 4;
           reinterpret_cast<float4*>(Qs)[x] = *reinterpret_cast<const float4*>(Qb + src);
           reinterpret_cast<float4*>(dOs)[x] = *reinterpret_cast<const float4*>(dOb + src);
         }
         for (int x = t; x < QT; x += NT) {
-          const int64_t qr = hb + (q0 + x < p.N ? q0 + x : p.N - 1);
+          const int64_t qr = hb + (q0 + x < Nb ? q0 + x : Nb - 1);
           const float l = p.lse[qr];
           Ls[x] = l == -INFINITY ? 0.f : l * kLog2e;
           Dls[x] = p.delta[qr];
@@ -917,7 +931,7 @@ __global__ __launch_bounds__(BS * kF32Lanes) void bwd_dkdv_f32(BwdParams p) {
           a = quad_sum(a);
           c = quad_sum(c);
           const float pr =
-              (partial && !pair_ok(p, q0 + qq, kg, p.N32)) ? 0.f : __builtin_amdgcn_exp2f(fmaf(a, p.sl2, -Ls[qq]));
+              (partial && !pair_ok(p, q0 + qq, kg, Nb)) ? 0.f : __builtin_amdgcn_exp2f(fmaf(a, p.sl2, -Ls[qq]));
           const float ds = pr * (c - Dls[qq]);
 #pragma unroll
           for (int d = 0; d < DL; ++d) {
@@ -1154,9 +1168,6 @@ extern "C" bsa_status_t bsa_backward_varlen(const void* q, const void* k, const 
   using namespace bsa;
   clear_error();
   if (!plan) return fail(BSA_ERR_INVALID_ARGUMENT, "plan must not be NULL");
-  const bsa_problem_t& pr = plan->prob;
-  if (!(pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128))
-    return fail(BSA_ERR_UNSUPPORTED, "bsa_backward_varlen has kernels for bf16, head_dim 128, block 128 only");
   if (plan->info.work_items == 0) return BSA_OK;
   if (!seq_lens) return fail(BSA_ERR_INVALID_ARGUMENT, "seq_lens must not be NULL");
   hipPointerAttribute_t attr{};

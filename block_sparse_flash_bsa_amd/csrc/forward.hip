@@ -577,8 +577,21 @@ __global__ __launch_bounds__(BS * kF32Lanes) void fwd_f32(FwdParams p) {
   const int r = t / kF32Lanes, sl = t % kF32Lanes;
   const int64_t q0 = int64_t(i) * BS;
   const int64_t qg = q0 + r;
+  // This entry's length Nb (seq_lens[b] clamped to [0, N] in a variable-length
+  // batch, else N) and block count; the walk is the prefix of the ascending
+  // CSR row below block nbb (none for a q-block at or beyond it), and the
+  // tiles of a shorter last block are masked token by token.
+  int64_t Nb = p.N;
+  if (p.seq_lens) {
+    const int64_t x = p.seq_lens[b];
+    Nb = x < 0 ? 0 : (x > Nb ? Nb : x);
+  }
+  const int64_t nbb = (Nb + BS - 1) / BS;
+  const bool short_tail = Nb % BS != 0;
+  int ne = i >= nbb ? 0 : row.count;
+  while (ne > 0 && (p.entries[row.start + ne - 1] >> 1) >= nbb) --ne;
 
-  const int64_t qld = qg < p.N ? qg : p.N - 1;   // rows beyond a ragged end load row N - 1
+  const int64_t qld = qg < Nb ? qg : (Nb > 0 ? Nb - 1 : 0);   // rows at or beyond Nb load row Nb - 1
   const float* Qp = static_cast<const float*>(p.q) + ((int64_t(b) * p.H + h) * p.N + qld) * D + sl * DL;
   const float* Kb = static_cast<const float*>(p.k) + (int64_t(b) * p.Hkv + hk) * p.N * D;
   const float* Vb = static_cast<const float*>(p.v) + (int64_t(b) * p.Hkv + hk) * p.N * D;
@@ -591,16 +604,16 @@ __global__ __launch_bounds__(BS * kF32Lanes) void fwd_f32(FwdParams p) {
   float m = -INFINITY, l = 0.f;
   const float c = p.sl2;
 
-  for (int e = 0; e < row.count; ++e) {
+  for (int e = 0; e < ne; ++e) {
     const int ent = p.entries[row.start + e];
     const int j = ent >> 1;
-    const bool partial = ent & 1;
+    const bool partial = (ent & 1) || (short_tail && (j == nbb - 1 || i == nbb - 1));
     for (int st = 0; st < BS / KT; ++st) {
       const int64_t k0 = int64_t(j) * BS + st * KT;
       __syncthreads();
       for (int x = t; x < KT * D / 4; x += NT) {
-        // Keys beyond a ragged end load row N - 1; the mask removes them.
-        const int64_t kr = k0 + x / (D / 4) < p.N ? k0 + x / (D / 4) : p.N - 1;
+        // Keys at or beyond Nb load row Nb - 1; the mask removes them.
+        const int64_t kr = k0 + x / (D / 4) < Nb ? k0 + x / (D / 4) : Nb - 1;
         const int64_t src = kr * D + (x % (D / 4)) * 4;
         reinterpret_cast<float4*>(Ks)[x] = *reinterpret_cast<const float4*>(Kb + src);
         reinterpret_cast<float4*>(Vs)[x] = *reinterpret_cast<const float4*>(Vb + src);
@@ -616,7 +629,8 @@ __global__ __launch_bounds__(BS * kF32Lanes) void fwd_f32(FwdParams p) {
           for (int d = 0; d < DL; ++d) a = fmaf(qv[d], kr[d], a);
 #pragma unroll
           for (int w = 1; w < kF32Lanes; w *= 2) a += __shfl_xor(a, w);
-          s[kk] = (partial && !allowed(p, qg, k0 + kc + kk)) ? -INFINITY : a * c;
+          const int64_t kk_g = k0 + kc + kk;
+          s[kk] = (partial && (kk_g >= Nb || qg >= Nb || !allowed(p, qg, kk_g))) ? -INFINITY : a * c;
         }
         float mx = m;
 #pragma unroll
@@ -640,7 +654,7 @@ __global__ __launch_bounds__(BS * kF32Lanes) void fwd_f32(FwdParams p) {
       }
     }
   }
-  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const float inv = l > 0.f ? 1.f / l : 0.f;     // rows at or beyond Nb: O = 0, LSE = -inf
   if (qg >= p.N) return;                          // beyond a ragged sequence's end
   float* Op = static_cast<float*>(p.o) + ((int64_t(b) * p.H + h) * p.N + qg) * D + sl * DL;
 #pragma unroll
@@ -766,9 +780,6 @@ extern "C" bsa_status_t bsa_forward_varlen(const void* q, const void* k, const v
   using namespace bsa;
   clear_error();
   if (!plan) return fail(BSA_ERR_INVALID_ARGUMENT, "plan must not be NULL");
-  const bsa_problem_t& pr = plan->prob;
-  if (!(pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128))
-    return fail(BSA_ERR_UNSUPPORTED, "bsa_forward_varlen has a kernel for bf16, head_dim 128, block 128 only");
   if (plan->info.work_items == 0) return BSA_OK;
   if (!seq_lens) return fail(BSA_ERR_INVALID_ARGUMENT, "seq_lens must not be NULL");
   hipPointerAttribute_t attr{};

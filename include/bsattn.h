@@ -396,8 +396,9 @@ bsa_status_t bsa_backward_noalloc(const void* q, const void* k, const void* v, c
  * variable-length sequences in production kernels, "Sparse Attention
  * Kernels vs Full Attention Performance").
  *   seq_lens: device int32 [batch]; values are clamped to [0, seq_len].
- * Other arguments as bsa_forward.  Supported: bf16, head_dim 128, block 128
- * (static or dynamic plans); otherwise UNSUPPORTED.
+ * Other arguments as bsa_forward.  Every kernel of bsa_forward has a
+ * variable-length form (bf16 128/128 on MFMA; float32 with head_dim and block
+ * 64 or 128), for static and dynamic plans.
  * Errors: as bsa_forward, plus INVALID_ARGUMENT for a NULL seq_lens or one
  * that is not device memory of the plan's device. */
 bsa_status_t bsa_forward_varlen(const void* q, const void* k, const void* v, bsa_plan_t plan,
@@ -413,8 +414,9 @@ bsa_status_t bsa_forward_varlen(const void* q, const void* k, const void* v, bsa
  * padded rows of delta hold <dO, O> of whatever the padding holds.
  *   seq_lens: device int32 [batch]; values are clamped to [0, seq_len]; the
  *             same array that produced out and lse.
- * Other arguments as bsa_backward.  Supported: bf16, head_dim 128, block 128
- * (static or dynamic plans); otherwise UNSUPPORTED.
+ * Other arguments as bsa_backward.  Every kernel of bsa_backward has a
+ * variable-length form (bf16 128/128; float32 with head_dim and block 64 or
+ * 128), for static and dynamic plans.
  * Errors: as bsa_backward, plus INVALID_ARGUMENT for a NULL seq_lens or one
  * that is not device memory of the plan's device. */
 bsa_status_t bsa_backward_varlen(const void* q, const void* k, const void* v, const void* out,

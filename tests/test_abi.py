@@ -507,16 +507,15 @@ def test_varlen_and_transposed_read_argument_errors():
     assert L.bsa_forward_varlen(one, one, one, None, one, one, one, None) == bsattn.ERR_INVALID_ARGUMENT
     assert L.bsa_backward_varlen(one, one, one, one, one, one, None, one, one, one, one, one, None) == \
         bsattn.ERR_INVALID_ARGUMENT
+    # Both dtypes have variable-length kernels; a NULL seq_lens is refused first.
     f32 = bsattn.plan(1, 2, 2, 1024, 64, 64, torch.float32, spec(False, "blocks", 1, 1), host_only=True)
-    assert L.bsa_forward_varlen(one, one, one, f32.handle, one, one, one, None) == bsattn.ERR_UNSUPPORTED
-    assert L.bsa_backward_varlen(one, one, one, one, one, one, f32.handle, one, one, one, one, one, None) == \
-        bsattn.ERR_UNSUPPORTED
     bf = bsattn.plan(2, 2, 2, 1024, 128, 128, torch.bfloat16, spec(True, "tokens", 300), host_only=True)
-    assert L.bsa_forward_varlen(one, one, one, bf.handle, None, one, one, None) == bsattn.ERR_INVALID_ARGUMENT
-    assert b"seq_lens" in L.bsa_last_error()
-    assert L.bsa_backward_varlen(one, one, one, one, one, one, bf.handle, None, one, one, one, one, None) == \
-        bsattn.ERR_INVALID_ARGUMENT
-    assert b"seq_lens" in L.bsa_last_error()
+    for pl in (f32, bf):
+        assert L.bsa_forward_varlen(one, one, one, pl.handle, None, one, one, None) == bsattn.ERR_INVALID_ARGUMENT
+        assert b"seq_lens" in L.bsa_last_error()
+        assert L.bsa_backward_varlen(one, one, one, one, one, one, pl.handle, None, one, one, one, one, None) == \
+            bsattn.ERR_INVALID_ARGUMENT
+        assert b"seq_lens" in L.bsa_last_error()
     # The transposed lists of a static plan are read with bsa_plan_csr_transposed, not from the device.
     cp = np.zeros(9, np.int32)
     n = ctypes.c_int64()

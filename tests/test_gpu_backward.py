@@ -513,15 +513,57 @@ def test_backward_varlen_full_lengths_equal_plain_backward(N):
         assert torch.equal(a, b)
 
 
+@pytest.mark.parametrize("D,BS,kind", [(64, 64, "window"), (128, 128, "bitmap"), (64, 128, "bitmap"),
+                                       (128, 64, "window")])
+def test_backward_varlen_parity_f32(D, BS, kind):
+    """The float32 kernels' variable-length backward: each entry's gradients
+    match the oracle's on the trimmed sequence (max abs error <= 1e-5 *
+    max(1, max|reference|)), rows beyond the length are zero, and the NaN
+    padding of Q, K, V and dO is never read."""
+    N, lens = 1000, [1000, 640, 2 * BS, 0]
+    w = wl.WORKLOADS["tiny_f32"].with_shape(name=f"bwd-varlen-f32-{kind}", batch=4, heads=4, kv_heads=2,
+                                            seq_len=N, head_dim=D, block=BS)
+    nb = -(-N // BS)
+    if kind == "window":
+        lay = dict(causal=True, unit="tokens", window_left=200, window_right=0, global_keys=3,
+                   global_queries=0, bitmap=None)
+    else:
+        bm = np.random.default_rng(BS + D).random((4, nb, nb)) < 0.4
+        bm[:, np.arange(nb), np.arange(nb)] = True
+        lay = dict(causal=False, unit="blocks", window_left=-1, window_right=-1, global_keys=0,
+                   global_queries=0, bitmap=torch.from_numpy(bm))
+    say(f"[bwd-varlen-f32] D={D} block={BS} {kind} N={N} lens={lens}")
+    q, k, v = wl.make_qkv(w, "cpu")
+    do = wl.make_dout(w, "cpu")
+    for b, L in enumerate(lens):
+        for t in (q, k, v, do):
+            t[b, :, L:] = float("nan")
+    p = gpu_plan(w, lay)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    out, lse = bsattn.forward_varlen(qc, kc, vc, p, sl)
+    dq, dk, dv = bsattn.backward_varlen(qc, kc, vc, out, lse, doc, p, sl)
+    torch.cuda.synchronize()
+    dq, dk, dv = (x.double().cpu().numpy() for x in (dq, dk, dv))
+    for b, L in enumerate(lens):
+        for name, g in (("dQ", dq), ("dK", dk), ("dV", dv)):
+            assert np.all(g[b, :, L:] == 0), f"entry {b}: {name} rows beyond {L} not zero"
+        if L == 0:
+            continue
+        ly = dict(lay)
+        if ly["bitmap"] is not None:
+            nbl = -(-L // BS)
+            ly["bitmap"] = ly["bitmap"][:, :nbl, :nbl]
+        sl_b = (slice(b, b + 1), slice(None), slice(0, L))
+        rq, rk, rv = oracle.backward(q[sl_b], k[sl_b], v[sl_b], do[sl_b], ly, BS)
+        for name, g, r in (("dQ", dq[sl_b], rq), ("dK", dk[sl_b], rk), ("dV", dv[sl_b], rv)):
+            err = float(np.abs(g - r).max())
+            tol = F32_TOL * max(1.0, float(np.abs(r).max()))
+            say(f"  entry {b} (L={L}) {name}: max|err| = {err:.3e} (tol {tol:.1e})")
+            assert err <= tol, f"entry {b} {name}: {err} > {tol}"
+
+
 def test_backward_varlen_rejects_bad_arguments():
-    w = wl.WORKLOADS["tiny_f32"]
-    p = gpu_plan(w, wl.layout_of(w))
-    x = wl.make_qkv(w, "cpu")[0].cuda()
-    lens = torch.full((1,), 1024, dtype=torch.int32, device="cuda")
-    ptr = x.data_ptr()
-    st = bsattn.lib().bsa_backward_varlen(ptr, ptr, ptr, ptr, ptr, ptr, p.handle, lens.data_ptr(), ptr, ptr, ptr,
-                                          ptr, None)
-    assert st == bsattn.ERR_UNSUPPORTED                     # fp32: no variable-length kernels
     wb = wl.small_variant(wl.WORKLOADS["window16k"], 1024, heads=2, kv_heads=2)
     pb = gpu_plan(wb, wl.layout_of(wb))
     y = wl.make_qkv(wb, "cpu")[0].cuda()

@@ -447,14 +447,45 @@ def test_forward_varlen_full_lengths_equal_plain_forward(Nmax):
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("D,BS,kind", [(64, 64, "window"), (128, 128, "bitmap"), (64, 128, "window"),
+                                       (128, 64, "bitmap")])
+def test_forward_varlen_parity_f32(D, BS, kind):
+    """The float32 kernels' variable-length form: a ragged maximum length
+    (1000) and entries that end inside a block, on a block edge and at 0;
+    rows below each length match the oracle on the trimmed sequence within
+    1e-5, rows beyond are empty, NaN padding is never read."""
+    Nmax, lens = 1000, [1000, 640, 2 * BS, 0]
+    w = wl.WORKLOADS["tiny_f32"].with_shape(name=f"varlen-f32-{kind}", batch=4, heads=4, kv_heads=2, seq_len=Nmax,
+                                            head_dim=D, block=BS)
+    nb = -(-Nmax // BS)
+    if kind == "window":
+        lay = dict(causal=True, unit="tokens", window_left=200, window_right=0, global_keys=3,
+                   global_queries=0, bitmap=None)
+    else:
+        bm = np.random.default_rng(BS + D).random((4, nb, nb)) < 0.4
+        bm[:, np.arange(nb), np.arange(nb)] = True
+        lay = dict(causal=False, unit="blocks", window_left=-1, window_right=-1, global_keys=0,
+                   global_queries=0, bitmap=torch.from_numpy(bm))
+    say(f"[varlen-f32] D={D} block={BS} {kind} Nmax={Nmax} lens={lens}")
+    q, k, v = varlen_inputs(w, lens)
+    p = gpu_plan(w, lay)
+    out, lse = bsattn.forward_varlen(q.cuda(), k.cuda(), v.cuda(), p,
+                                     torch.tensor(lens, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    for b, L in enumerate(lens):
+        assert np.all(out[b, :, L:] == 0) and np.all(lse[b, :, L:] == -np.inf), f"entry {b}: rows beyond {L}"
+        if L == 0:
+            continue
+        ly = dict(lay)
+        if ly["bitmap"] is not None:
+            nbl = -(-L // BS)
+            ly["bitmap"] = ly["bitmap"][:, :nbl, :nbl]
+        O_ref, L_ref = oracle.forward(q[b:b + 1, :, :L], k[b:b + 1, :, :L], v[b:b + 1, :, :L], ly, BS)
+        check(out[b:b + 1, :, :L], lse[b:b + 1, :, :L], O_ref, L_ref, torch.float32, f"entry {b} (L={L})")
+
+
 def test_forward_varlen_rejects_bad_arguments():
-    w = wl.WORKLOADS["tiny_f32"]
-    p = gpu_plan(w, wl.layout_of(w))
-    q = wl.make_qkv(w, "cpu")[0].cuda()
-    lens = torch.full((1,), 1024, dtype=torch.int32, device="cuda")
-    st = bsattn.lib().bsa_forward_varlen(q.data_ptr(), q.data_ptr(), q.data_ptr(), p.handle, lens.data_ptr(),
-                                         q.data_ptr(), q.data_ptr(), None)
-    assert st == bsattn.ERR_UNSUPPORTED                     # fp32: no variable-length kernel
     wb = wl.small_variant(wl.WORKLOADS["window16k"], 1024, heads=2, kv_heads=2)
     pb = gpu_plan(wb, wl.layout_of(wb))
     qb, kb, vb = (x.cuda() for x in wl.make_qkv(wb, "cpu"))
