@@ -298,7 +298,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   float l_part = 0.f;        // this lane's share of the row sum
   const float c = p.sl2;
   float cv;                  // c in a VGPR (see exp_pass)
+  uint32_t span_v;           // mspan in a VGPR (the mask compares read only VGPRs)
   __asm__("v_mov_b32 %0, %1" : "=v"(cv) : "s"(c));
+  __asm__("v_mov_b32 %0, %1" : "=v"(span_v) : "s"(p.mspan));
   const bool q_global = qg < p.gq32;
 
   // S^T for the 64 keys of half hh: two 32x32 tiles; lane holds row r32,
@@ -337,6 +339,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
     const int k0 = j * kBN + hh * 64;                            // first key of the half
     const int dq = int(qg) - k0;                                 // q - k at offset 0
     const uint32_t dql = uint32_t(dq) - uint32_t(p.mlo);
+    // Every key of the half allowed for every row of the wave: no mask.
+    if (__all(dql >= 63u && dql <= p.mspan) && !(kRagged && (j == nbb - 1 || i == nbb - 1))) return;
     if (p.token_rule && (k0 < p.gk32 || __any(q_global))) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -353,7 +357,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int ko = t * 32 + 8 * (r >> 2) + 4 * hf + (r & 3);
-          sq[t][r] = dql - uint32_t(ko) <= p.mspan ? sq[t][r] : -INFINITY;
+          sq[t][r] = dql - uint32_t(ko) <= span_v ? sq[t][r] : -INFINITY;
         }
     }
     if (kRagged && (j == nbb - 1 || i == nbb - 1)) {
@@ -430,7 +434,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
     const float msub = (m_use == -INFINITY) ? 0.f : m_use;
     exp_pass(sq, -msub, pq, ls);
     l_part = fmaf(l_part, alpha, (ls[0] + ls[1]) + (ls[2] + ls[3]));
-    if (moved) {
+    // Rows whose reference was -inf have O = 0 still (every P so far was 0):
+    // no rescale unless some row of the wave had a finite one.
+    if (moved && __any(m_ref != -INFINITY)) {
       __asm__ volatile("");
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
@@ -532,10 +538,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   }
 
   // Epilogue: O = acc / l (0 for an empty row), LSE = ln2 * (m_ref + log2 l).
+  // Each wave stages its 32 x 128 block of O (bf16) in 8 KB of the K buffers,
+  // which no wave reads after the last barrier (and which no load fills when
+  // the walk is empty), then writes whole 256-byte rows: 16 bytes per lane,
+  // four rows per store, instead of 16-byte pieces of 32 rows per store.
+  // 16-byte chunk c of row r sits at chunk c ^ (r & 15), so both passes are
+  // free of bank conflicts; each wave reads back only what it wrote.
   const float l = sum_with_partner(l_part);
   const float inv = l > 0.f ? 1.f / l : 0.f;
-  if (kRagged && qg >= p.N) return;              // beyond a ragged sequence's end
-  uint16_t* Op = static_cast<uint16_t*>(p.o) + ((int64_t(b) * p.H + h) * p.N + qg) * kD;
+  lds_u8* const stage = ((wave >> 1) ? K3[1] : K3[0]) + (wave & 1) * (32 * 256);
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
@@ -543,8 +554,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
       u32x2 pk;
       pk[0] = uint32_t(bf16_bits(o[dt][4 * g + 0] * inv)) | (uint32_t(bf16_bits(o[dt][4 * g + 1] * inv)) << 16);
       pk[1] = uint32_t(bf16_bits(o[dt][4 * g + 2] * inv)) | (uint32_t(bf16_bits(o[dt][4 * g + 3] * inv)) << 16);
-      *reinterpret_cast<u32x2*>(Op + dt * 32 + 8 * g + 4 * hf) = pk;
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+          stage + r32 * 256 + 16 * ((4 * dt + g) ^ (r32 & 15)) + 8 * hf) = pk;
     }
+  __asm__ volatile("" ::: "memory");
+  const int sr = lane >> 4, sc = lane & 15;      // row within a group of 4, 16-byte chunk
+  uint16_t* const Ow = static_cast<uint16_t*>(p.o) + ((int64_t(b) * p.H + h) * p.N + int64_t(i) * kBM + wave * 32) * kD;
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int r = 4 * s + sr;
+    const u32x4 val = *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(stage + r * 256 + 16 * (sc ^ (r & 15)));
+    if (!kRagged || int64_t(i) * kBM + wave * 32 + r < p.N)   // no row beyond a ragged sequence's end
+      *reinterpret_cast<u32x4*>(Ow + r * kD + 8 * sc) = val;
+  }
+  if (kRagged && qg >= p.N) return;
   if (hf == 0)
     p.lse[(int64_t(b) * p.H + h) * p.N + qg] = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
 }
