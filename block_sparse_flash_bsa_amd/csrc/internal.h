@@ -1,6 +1,7 @@
 // Internal definitions shared by the host planner and the forward launcher.
 #pragma once
 
+#include <atomic>
 #include <cstdint>
 #include <string>
 #include <vector>
@@ -43,6 +44,18 @@ struct bsa_plan {
   std::vector<std::vector<uint8_t>> flags;     // [layout_heads][nnz_h]
   std::vector<int32_t> work;                   // [launch slots], -1 = idle
   bsa_plan_info_t info{};
+  // Forward launch (bf16 kernel, XCD schedule): slots [0, fwd_static_slots)
+  // of `work` run one workgroup each; the rest of XCD x's run (rows beyond,
+  // fwd_tail_len[x] items) is a queue that 8 * fwd_dyn_per_xcd further
+  // workgroups drain, each from its own XCD's queue first and then from the
+  // fullest one, so XCDs that run faster take over the end of slower ones.
+  // d_fwd_sched: [8] queue lengths, then kFwdCounterSets sets of 16 int32
+  // (8 queue counters and a done counter), one set per call in turn.
+  int64_t fwd_static_slots = 0;
+  int64_t fwd_dyn_per_xcd = 0;
+  int32_t fwd_tail_len[8] = {};
+  int32_t* d_fwd_sched = nullptr;
+  std::atomic<uint32_t> fwd_calls{0};
   // Backward: the CSR transposed (per k-block, the ascending q-blocks whose
   // lists hold it, same flags) and the launch order of the dK/dV kernel,
   // items (b * Hkv + hk) * nb + j.  Static plans only.
@@ -97,6 +110,8 @@ struct bsa_plan {
 };
 
 namespace bsa {
+constexpr int kFwdCounterSets = 64;          // calls of one plan that may run at once
+constexpr size_t kFwdSchedBytes = (16 + 16 * kFwdCounterSets) * sizeof(int32_t);
 // The C function bsa_plan() hides the struct tag in C++; use this alias.
 using Plan = struct ::bsa_plan;
 }  // namespace bsa

@@ -329,6 +329,37 @@ void build_work_kv(Plan& P) {
   P.kv_reduce_launch = int64_t(P.kv_reduce.size());
 }
 
+// The forward's queue tail (see Plan): XCDs of one chip run the same work
+// at speeds a few percent apart, and the launch ends with the slowest, so the
+// last eighth of every XCD's rows is left to workgroups that take items as
+// they free up, from any XCD's queue.  A quarter as many again as the queue
+// rows run per XCD, so a fast XCD can take over that much of the others'
+// ends.  Claiming an item costs a round trip to memory or two, so only
+// launches of long rows (at least kTailMinTiles tiles on average; row lengths
+// of a dynamic plan are unknown here) have a queue.
+constexpr int64_t kTailMinRows = 16;
+constexpr int64_t kTailMinTiles = 16;
+void build_tail(Plan& P, int64_t total_cost) {
+  P.fwd_static_slots = int64_t(P.work.size());
+  P.fwd_dyn_per_xcd = 0;
+  for (int32_t& t : P.fwd_tail_len) t = 0;
+  const int64_t rows = int64_t(P.work.size()) / kNumXcd;
+  const int64_t items = P.info.work_items;
+  if (P.dynamic || items == 0 || total_cost - items < kTailMinTiles * items) return;
+  if (int64_t(P.work.size()) % kNumXcd != 0 || rows < kTailMinRows) return;
+  const int64_t tail_rows = (rows + 7) / 8;
+  const int64_t cut = rows - tail_rows;
+  // xcd_slots fills each XCD's rows from the first: its items end at its
+  // first idle slot.
+  for (int x = 0; x < kNumXcd; ++x) {
+    int64_t len = 0;
+    while (len < rows && P.work[size_t(len * kNumXcd + x)] >= 0) ++len;
+    P.fwd_tail_len[x] = int32_t(std::max<int64_t>(0, len - cut));
+  }
+  P.fwd_static_slots = cut * kNumXcd;
+  P.fwd_dyn_per_xcd = tail_rows + (tail_rows + 3) / 4;
+}
+
 // Launch order.  Item id = (b * H + h) * nb + i; cost = row length + 1.
 void build_work(Plan& P) {
   const int64_t B = P.prob.batch, H = P.prob.num_heads, nb = P.nb;
@@ -380,6 +411,10 @@ void build_work(Plan& P) {
           for (int64_t g = 0; g < group; ++g) loc.push_back(int32_t((b * H + hk * group + g) * nb + i));
       }
     P.work = xcd_slots(loc, cost);
+    P.info.work_items = items;
+    int64_t total_cost = 0;
+    for (int32_t it : loc) total_cost += cost(it);
+    build_tail(P, total_cost);
   }
   P.info.work_items = items;
   P.info.launch_slots = int64_t(P.work.size());
@@ -400,8 +435,10 @@ bsa_status_t upload(Plan& P) {
   const size_t off_entries_t = up(off_cols + rows * sizeof(bsa::RowDesc));
   const size_t off_work_kv = up(off_entries_t + nnz * sizeof(int32_t));
   const size_t off_kv_reduce = up(off_work_kv + slots_kv * sizeof(Plan::KvDesc));
-  const size_t bytes = off_kv_reduce + P.kv_reduce.size() * sizeof(Plan::KvDesc) + 16;
+  const size_t off_sched = up(off_kv_reduce + P.kv_reduce.size() * sizeof(Plan::KvDesc) + 16);
+  const size_t bytes = off_sched + bsa::kFwdSchedBytes;
   std::vector<unsigned char> host(bytes, 0);
+  std::memcpy(host.data() + off_sched, P.fwd_tail_len, sizeof(P.fwd_tail_len));   // counters start at 0
   auto* rd = reinterpret_cast<bsa::RowDesc*>(host.data());
   auto* en = reinterpret_cast<int32_t*>(host.data() + off_entries);
   int32_t start = 0;
@@ -450,6 +487,7 @@ bsa_status_t upload(Plan& P) {
   P.d_entries_t = reinterpret_cast<const int32_t*>(base + off_entries_t);
   P.d_work_kv = reinterpret_cast<const int32_t*>(base + off_work_kv);
   P.d_kv_reduce = reinterpret_cast<const int32_t*>(base + off_kv_reduce);
+  P.d_fwd_sched = reinterpret_cast<int32_t*>(base + off_sched);
   if (P.kv_partials > 0 && P.prob.dtype == BSA_BF16 && P.prob.head_dim == 128 && P.prob.block_size == 128) {
     // float32 partial dK and dV of every chunk of a split column.
     const size_t sbytes = size_t(P.kv_partials) * 2 * 128 * 128 * sizeof(float);
@@ -600,7 +638,8 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
   const size_t off_pre = off_walk + up(kv_cols * sizeof(int32_t));
   const size_t off_reduce = off_pre + up(kv_cols * sizeof(int64_t));
   const size_t off_head = off_reduce + up(size_t(P->kv_partials) * sizeof(Plan::KvDesc));
-  const size_t bytes = off_head + 8 * sizeof(int32_t);
+  const size_t off_sched = off_head + up(8 * sizeof(int32_t));
+  const size_t bytes = off_sched + bsa::kFwdSchedBytes;
   hipError_t err = hipMalloc(&P->dev_mem, bytes);
   if (err != hipSuccess) {
     P->dev_mem = nullptr;
@@ -620,6 +659,10 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
                     hipMemcpyHostToDevice);
   // No split column until the first bitmap arrives.
   if (err == hipSuccess) err = hipMemset(base + off_head, 0, 8 * sizeof(int32_t));
+  // The forward's queue lengths; its counters start at 0.
+  if (err == hipSuccess) err = hipMemset(base + off_sched, 0, bsa::kFwdSchedBytes);
+  if (err == hipSuccess)
+    err = hipMemcpy(base + off_sched, P->fwd_tail_len, sizeof(P->fwd_tail_len), hipMemcpyHostToDevice);
   if (err == hipSuccess && split)
     err = hipMemcpy(base + off_slot, slot_of.data(), slot_of.size() * sizeof(int32_t), hipMemcpyHostToDevice);
   if (err == hipSuccess && split) {
@@ -650,6 +693,7 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
   P->d_scan = reinterpret_cast<int64_t*>(base + off_scan);
   P->d_kv_reduce = reinterpret_cast<const int32_t*>(base + off_reduce);
   P->d_kv_head = reinterpret_cast<int32_t*>(base + off_head);
+  P->d_fwd_sched = reinterpret_cast<int32_t*>(base + off_sched);
   P->d_kv_count = P->d_kv_head + 4;
   if (split) {
     P->d_kv_slot = reinterpret_cast<const int32_t*>(base + off_slot);

@@ -261,6 +261,37 @@ def test_schedules_give_identical_results():
         assert torch.equal(o, outs[0][0]) and torch.equal(l, outs[0][1])
 
 
+def test_queue_tail_over_many_calls():
+    """The launch's queue tail (the last eighth of each XCD's rows, drained by
+    workgroups of any XCD through counters that the call's last queue
+    workgroup clears): 140 calls of one plan, more than twice round the 64
+    counter sets, each into NaN-poisoned outputs, give bit for bit the first
+    call's results, which equal the results of the LPT order (no queue) and
+    the oracle's on sampled rows; two streams alternate."""
+    w = wl.small_variant(wl.WORKLOADS["winglobal128k"], 16384, heads=8, kv_heads=8)
+    lay = wl.layout_of(w)
+    q, k, v = (x.cuda() for x in wl.make_qkv(w, "cpu"))
+    p = gpu_plan(w, lay)
+    assert len(p.work()) // 8 >= 16                   # rows enough for a queue tail
+    ref = run(gpu_plan(w, lay, schedule=2), q, k, v)  # LPT order: one workgroup per slot
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
+    for call in range(140):
+        st = streams[call % 2]
+        st.wait_stream(streams[(call + 1) % 2])
+        with torch.cuda.stream(st):
+            out.fill_(float("nan"))
+            lse.fill_(float("nan"))
+            bsattn.forward(q, k, v, p, out, lse)
+        st.synchronize()
+        assert torch.equal(out, ref[0]) and torch.equal(lse, ref[1]), f"call {call}"
+    rows = [(0, h, qq) for h in (0, 7) for qq in (0, 511, 8191, 16383)]
+    O_ref, L_ref = oracle.forward(q.cpu(), k.cpu(), v.cpu(), lay, w.block, rows=rows)
+    idx = tuple(torch.tensor(x) for x in zip(*rows))
+    check(out[idx].float().cpu().numpy(), lse[idx].cpu().numpy(), O_ref, L_ref, w.dtype, "sampled rows")
+
+
 def test_non_default_stream():
     q, k, v = (x.cuda() for x in small_case(N=2048))
     lay = spec(True, "tokens", 300, 0, gk=3)
