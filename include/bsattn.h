@@ -274,6 +274,14 @@ bsa_status_t bsa_plan_read_csr_transposed(bsa_plan_t plan, int32_t layout_head, 
  *         of exp(scaled scores) over the allowed keys; -inf for empty rows
  * All buffers are caller-owned; out and lse must not alias the inputs.  Every
  * element of out and lse is written.  Nothing is allocated or freed.
+ * Launch: one workgroup per slot of the plan's order (bsa_plan_work); for the
+ * bf16 kernel on a static plan of the XCD order whose rows average 16 tiles
+ * or more, the last eighth of each XCD's rows is instead a queue that extra
+ * workgroups drain, claiming from any XCD's queue as they free up (XCDs of
+ * one chip run a few percent apart).  Its claim counters are plan memory, in
+ * 64 sets that successive calls take in turn (each call's last workgroup
+ * clears its set): calls with one plan may run concurrently, on any streams,
+ * up to 64 at a time.  Results do not depend on which workgroup runs an item.
  * Errors (returned before anything is launched): INVALID_ARGUMENT for NULL
  * pointers, a host-only plan, or a plan made on another device; DEVICE if
  * the launch fails.  Faults during execution surface at the caller's next
