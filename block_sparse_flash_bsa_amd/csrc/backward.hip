@@ -43,6 +43,7 @@
 #include <mutex>
 
 #include "internal.h"
+#include "queue.h"
 
 namespace bsa {
 namespace {
@@ -80,6 +81,9 @@ struct BwdParams {
   // Variable-length batch (bsa_backward_varlen): device int32 [batch], entry b
   // uses its first seq_lens[b] positions; nullptr otherwise.
   const int32_t* seq_lens;
+  // Launches of the bf16 tile kernels: slots run by one workgroup each, then
+  // queue workgroups (queue.h); lq_dq over `work`, lq_kv over kv_desc.
+  LaunchQueue lq_dq, lq_kv;
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -300,8 +304,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
   const uint32_t Va[2] = {uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)V0)),
                           uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)V1))};
 
-  const int item = p.work[blockIdx.x];
-  if (item < 0) return;
+  __shared__ int s_slot;
+  int done;
+  const int slot = queue_slot(p.lq_dq, &s_slot, done);
+  const int item = slot >= 0 ? p.work[slot] : -1;
+  if (item < 0) {
+    queue_release(p.lq_dq, done);
+    return;
+  }
   const int i = item % p.nb;
   const int bh = item / p.nb;
   const int h = bh % p.H, b = bh / p.H;
@@ -451,6 +461,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
       ent = ent_n;
     }
   }
+  queue_release(p.lq_dq, done);
   if (!kRagged || qg < p.N) store_row(p.dq + qrow * kD, acc, p.scale, hf);
 }
 
@@ -482,11 +493,17 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
   const uint32_t dOa[2] = {uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)dO0)),
                            uint32_t(reinterpret_cast<uintptr_t>((lds_u8*)dO1))};
 
-  const int item = p.kv_desc[4 * blockIdx.x];
-  if (item < 0) return;
-  const int walk_begin = p.kv_desc[4 * blockIdx.x + 1];
-  const int walk_end = p.kv_desc[4 * blockIdx.x + 2];
-  const int partial_slot = p.kv_desc[4 * blockIdx.x + 3];
+  __shared__ int s_slot;
+  int done;
+  const int slot = queue_slot(p.lq_kv, &s_slot, done);
+  const int item = slot >= 0 ? p.kv_desc[4 * slot] : -1;
+  if (item < 0) {
+    queue_release(p.lq_kv, done);
+    return;
+  }
+  const int walk_begin = p.kv_desc[4 * slot + 1];
+  const int walk_end = p.kv_desc[4 * slot + 2];
+  const int partial_slot = p.kv_desc[4 * slot + 3];
   const int j = item % p.nb;
   const int bk = item / p.nb;
   const int hk = bk % p.Hkv, b = bk / p.Hkv;
@@ -686,6 +703,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
       have = have_next;
     }
   }
+  queue_release(p.lq_kv, done);
   if (partial_slot < 0) {
     if (!kRagged || kg < p.N) {
       store_row(p.dk + krow * kD, dk, p.scale, hf);
@@ -1067,6 +1085,10 @@ bsa_status_t backward_impl(const void* q, const void* k, const void* v, const vo
     return BSA_OK;
   }
   const bool ragged = pr.seq_len % kB != 0 || seq_lens;
+  prm.lq_dq = launch_queue(*plan, 0);
+  prm.lq_kv = launch_queue(*plan, 1);
+  const unsigned grid_dq = unsigned(int64_t(prm.lq_dq.static_slots) + prm.lq_dq.dyn_total);
+  const unsigned grid_kv = unsigned(int64_t(prm.lq_kv.static_slots) + prm.lq_kv.dyn_total);
   const int64_t rows = int64_t(pr.batch) * pr.num_heads * pr.seq_len;
   const int64_t rows_per_block = kThreads / 16;
   hipLaunchKernelGGL(bwd_delta_bf16, dim3(unsigned((rows + rows_per_block - 1) / rows_per_block)), dim3(kThreads),
@@ -1074,16 +1096,16 @@ bsa_status_t backward_impl(const void* q, const void* k, const void* v, const vo
   hipError_t err = hipGetLastError();
   if (err == hipSuccess) {
     if (ragged)
-      hipLaunchKernelGGL(bwd_dq_bf16_d128<true>, dim3(unsigned(plan->info.launch_slots)), dim3(kThreads), 0, s, prm);
+      hipLaunchKernelGGL(bwd_dq_bf16_d128<true>, dim3(grid_dq), dim3(kThreads), 0, s, prm);
     else
-      hipLaunchKernelGGL(bwd_dq_bf16_d128<false>, dim3(unsigned(plan->info.launch_slots)), dim3(kThreads), 0, s, prm);
+      hipLaunchKernelGGL(bwd_dq_bf16_d128<false>, dim3(grid_dq), dim3(kThreads), 0, s, prm);
     err = hipGetLastError();
   }
   if (err == hipSuccess && !plan->work_kv.empty()) {
     if (ragged)
-      hipLaunchKernelGGL(bwd_dkdv_bf16_d128<true>, dim3(unsigned(plan->work_kv.size())), dim3(kThreads), 0, s, prm);
+      hipLaunchKernelGGL(bwd_dkdv_bf16_d128<true>, dim3(grid_kv), dim3(kThreads), 0, s, prm);
     else
-      hipLaunchKernelGGL(bwd_dkdv_bf16_d128<false>, dim3(unsigned(plan->work_kv.size())), dim3(kThreads), 0, s, prm);
+      hipLaunchKernelGGL(bwd_dkdv_bf16_d128<false>, dim3(grid_kv), dim3(kThreads), 0, s, prm);
     err = hipGetLastError();
   }
   if (err == hipSuccess && plan->kv_reduce_launch > 0) {

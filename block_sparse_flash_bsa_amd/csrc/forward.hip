@@ -41,6 +41,7 @@
 #include <type_traits>
 
 #include "internal.h"
+#include "queue.h"
 
 namespace bsa {
 namespace {
@@ -69,12 +70,9 @@ struct FwdParams {
   // Variable-length batch (bsa_forward_varlen): device int32 [batch], entry b
   // uses its first seq_lens[b] positions; nullptr otherwise.
   const int32_t* seq_lens;
-  // Launch of the bf16 kernel: workgroups below static_slots run work[slot];
-  // the dyn_total after them take items from the XCD queues (tail_pop):
-  // queue x holds work[static_slots + 8 t + x] for t < tail_len[x].
-  int32_t static_slots, dyn_total;
-  const int32_t* tail_len;   // device [8]
-  int32_t* cnt;              // device [9]: the call's queue counters and done counter
+  // Launch of the bf16 kernel: slots of `work` run by one workgroup each,
+  // then queue workgroups (queue.h).
+  LaunchQueue lq;
 };
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -89,53 +87,6 @@ __device__ __forceinline__ bool allowed(const FwdParams& p, int64_t q, int64_t k
   if (!p.token_rule) return true;
   const bool in_w = (p.wl < 0 || q - k <= p.wl) && (p.wr < 0 || k - q <= p.wr);
   return in_w || k < p.gk || q < p.gq;
-}
-
-// Wave 0 of a queue workgroup: the next item of its own XCD's queue or, when
-// that is empty, of the queue with the most items left (so an XCD that runs
-// ahead takes over the end of a slower one); -1 when every queue is empty.
-// After the claim on its own queue, lanes 0..7 read the 8 counters and lane 0
-// claims with one atomic add; a claim that comes too late leaves that queue
-// seen empty, so at most 8 fail before an item is claimed or every queue is
-// seen empty.  Every counter access is a
-// system-scope atomic, which bypasses the XCDs' own L2 caches, so all XCDs
-// see one counter.  The result is wave-uniform.
-__device__ int tail_pop(const FwdParams& p) {
-  const int lane = threadIdx.x & 63;
-  const int x = blockIdx.x & 7;
-  // Own queue first, with one atomic add (usually enough).
-  int t0 = 0;
-  if (lane == 0) t0 = __hip_atomic_fetch_add(p.cnt + x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  t0 = __shfl(t0, 0);
-  if (t0 < p.tail_len[x]) return p.work[p.static_slots + 8 * t0 + x];
-  for (int tries = 0; tries <= 8; ++tries) {
-    int rem = -1, who = lane;
-    if (lane < 8) {
-      const int q = (x + lane) & 7;
-      rem = p.tail_len[q] - __hip_atomic_load(p.cnt + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    }
-    if (__shfl(rem, 0) <= 0) {
-      // The fullest queue (lowest lane on ties); lanes 0..7 reduce among themselves.
-#pragma unroll
-      for (int off = 4; off >= 1; off >>= 1) {
-        const int orem = __shfl_xor(rem, off), owho = __shfl_xor(who, off);
-        if (orem > rem || (orem == rem && owho < who)) {
-          rem = orem;
-          who = owho;
-        }
-      }
-    } else {
-      who = 0;
-    }
-    const int pick = __shfl(who, 0);
-    if (__shfl(rem, 0) <= 0) return -1;
-    const int q = (x + pick) & 7;
-    int t = 0;
-    if (lane == 0) t = __hip_atomic_fetch_add(p.cnt + q, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-    t = __shfl(t, 0);
-    if (t < p.tail_len[q]) return p.work[p.static_slots + 8 * t + q];
-  }
-  return -1;
 }
 
 __device__ __forceinline__ void decode(const FwdParams& p, int item, int& b, int& h, int& i) {
@@ -249,34 +200,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   __shared__ __attribute__((aligned(1024))) unsigned char K1[kHalfBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char V0[kHalfBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char V1[kHalfBytes];
-  __shared__ int s_item;
+  __shared__ int s_slot;
 
-  // The item: the slot's own, or one claimed from the queues; a queue
-  // workgroup also counts itself done, and the last to do so clears the
-  // call's counters (every claim is made by then) for the call that next
-  // uses them.
-  const bool queued = int(blockIdx.x) >= p.static_slots;
-  int done = 0;
-  int item;
-  if (!queued) {
-    item = p.work[blockIdx.x];
-  } else {
-    if (threadIdx.x < 64) {
-      const int it = tail_pop(p);
-      if (threadIdx.x == 0) {
-        s_item = it;
-        done = __hip_atomic_fetch_add(p.cnt + 8, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-      }
-    }
-    __syncthreads();
-    item = __builtin_amdgcn_readfirstlane(s_item);   // the same in every lane
-  }
-  auto clear_counters = [&]() {
-    if (queued && threadIdx.x == 0 && done == p.dyn_total - 1)
-      for (int x = 0; x < 9; ++x) __hip_atomic_store(p.cnt + x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
-  };
+  // The slot: the workgroup's own, or one claimed from the queues.
+  int done;
+  const int slot = queue_slot(p.lq, &s_slot, done);
+  const int item = slot >= 0 ? p.work[slot] : -1;
   if (item < 0) {
-    clear_counters();
+    queue_release(p.lq, done);
     return;
   }
   int b, h, i;
@@ -647,7 +578,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
     if (!kRagged || int64_t(i) * kBM + wave * 32 + r < p.N)   // no row beyond a ragged sequence's end
       *reinterpret_cast<u32x4*>(Ow + r * kD + 8 * sc) = val;
   }
-  clear_counters();
+  queue_release(p.lq, done);
   if (kRagged && qg >= p.N) return;
   if (hf == 0)
     p.lse[(int64_t(b) * p.H + h) * p.N + qg] = l > 0.f ? (m_ref + log2f(l)) * kLn2 : -INFINITY;
@@ -850,20 +781,9 @@ bsa_status_t forward_impl(const void* q, const void* k, const void* v, bsa_plan_
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t err = hipSuccess;
-  prm.static_slots = int32_t(slots);
-  prm.dyn_total = 0;
-  prm.tail_len = plan->d_fwd_sched;
-  prm.cnt = nullptr;
+  prm.lq = launch_queue(*plan, 0);
   if (pr.dtype == BSA_BF16 && pr.head_dim == 128 && pr.block_size == 128) {
-    int64_t grid = slots;
-    if (plan->fwd_dyn_per_xcd > 0) {
-      // This call's counter set (calls take the sets in turn).
-      const uint32_t set = plan->fwd_calls.fetch_add(1, std::memory_order_relaxed) % kFwdCounterSets;
-      prm.static_slots = int32_t(plan->fwd_static_slots);
-      prm.dyn_total = int32_t(8 * plan->fwd_dyn_per_xcd);
-      prm.cnt = plan->d_fwd_sched + 16 + 16 * set;
-      grid = plan->fwd_static_slots + prm.dyn_total;
-    }
+    const int64_t grid = int64_t(prm.lq.static_slots) + prm.lq.dyn_total;
     if (pr.seq_len % kBN != 0 || seq_lens)
       hipLaunchKernelGGL(fwd_bf16_d128<true>, dim3(unsigned(grid)), dim3(kThreads), 0, s, prm, prm.entries);
     else

@@ -44,18 +44,18 @@ struct bsa_plan {
   std::vector<std::vector<uint8_t>> flags;     // [layout_heads][nnz_h]
   std::vector<int32_t> work;                   // [launch slots], -1 = idle
   bsa_plan_info_t info{};
-  // Forward launch (bf16 kernel, XCD schedule): slots [0, fwd_static_slots)
-  // of `work` run one workgroup each; the rest of XCD x's run (rows beyond,
-  // fwd_tail_len[x] items) is a queue that 8 * fwd_dyn_per_xcd further
-  // workgroups drain, each from its own XCD's queue first and then from the
-  // fullest one, so XCDs that run faster take over the end of slower ones.
-  // d_fwd_sched: [8] queue lengths, then kFwdCounterSets sets of 16 int32
-  // (8 queue counters and a done counter), one set per call in turn.
-  int64_t fwd_static_slots = 0;
-  int64_t fwd_dyn_per_xcd = 0;
-  int32_t fwd_tail_len[8] = {};
-  int32_t* d_fwd_sched = nullptr;
-  std::atomic<uint32_t> fwd_calls{0};
+  // Launch queues (queue.h) of the bf16 tile kernels: [0] the forward and
+  // dQ over `work`, [1] dK/dV over the descriptors.  Slots [0,
+  // queue_static[k]) run one workgroup each; the rest of XCD x's run
+  // (queue_tail[k][x] slots) is a queue that 8 * queue_dyn_per_xcd[k]
+  // further workgroups drain.  d_queue: [16] queue lengths ([0..7] launch 0,
+  // [8..15] launch 1), then kQueueCounterSets sets of 16 int32 (8 queue
+  // counters and a done counter), one set per launch in turn.
+  int64_t queue_static[2] = {0, 0};
+  int64_t queue_dyn_per_xcd[2] = {0, 0};
+  int32_t queue_tail[2][8] = {};
+  int32_t* d_queue = nullptr;
+  std::atomic<uint32_t> queue_launches{0};
   // Backward: the CSR transposed (per k-block, the ascending q-blocks whose
   // lists hold it, same flags) and the launch order of the dK/dV kernel,
   // items (b * Hkv + hk) * nb + j.  Static plans only.
@@ -110,8 +110,8 @@ struct bsa_plan {
 };
 
 namespace bsa {
-constexpr int kFwdCounterSets = 64;          // calls of one plan that may run at once
-constexpr size_t kFwdSchedBytes = (16 + 16 * kFwdCounterSets) * sizeof(int32_t);
+constexpr int kQueueCounterSets = 64;        // queued launches of one plan that may run at once
+constexpr size_t kQueueBytes = (16 + 16 * kQueueCounterSets) * sizeof(int32_t);
 // The C function bsa_plan() hides the struct tag in C++; use this alias.
 using Plan = struct ::bsa_plan;
 }  // namespace bsa

@@ -234,6 +234,37 @@ std::vector<int32_t> xcd_slots(const std::vector<int32_t>& loc, Cost cost) {
   return slots;
 }
 
+// Launch queue k of the bf16 tile kernels (queue.h): XCDs of one chip run
+// the same work at speeds a few percent apart, and the launch ends with the
+// slowest, so the last eighth of every XCD's rows of `slots` is left to
+// workgroups that take slots as they free up, from any XCD's queue.  A
+// quarter as many again as the queue rows run per XCD, so a fast XCD can
+// take over that much of the others' ends.  Claiming a slot costs a round
+// trip to memory or two, so only launches whose items average at least
+// kQueueMinTiles tiles have a queue (row lengths of a dynamic plan are not
+// known here: its launches keep one workgroup per slot).
+constexpr int64_t kQueueMinRows = 16;
+constexpr int64_t kQueueMinTiles = 16;
+void build_queue(Plan& P, int k, const std::vector<int32_t>& slots, int64_t items, int64_t tiles) {
+  P.queue_static[k] = int64_t(slots.size());
+  P.queue_dyn_per_xcd[k] = 0;
+  for (int32_t& t : P.queue_tail[k]) t = 0;
+  const int64_t rows = int64_t(slots.size()) / kNumXcd;
+  if (P.dynamic || items == 0 || tiles < kQueueMinTiles * items) return;
+  if (int64_t(slots.size()) % kNumXcd != 0 || rows < kQueueMinRows) return;
+  const int64_t tail_rows = (rows + 7) / 8;
+  const int64_t cut = rows - tail_rows;
+  // xcd_slots fills each XCD's rows from the first: its slots end at its
+  // first idle one.
+  for (int x = 0; x < kNumXcd; ++x) {
+    int64_t len = 0;
+    while (len < rows && slots[size_t(len * kNumXcd + x)] >= 0) ++len;
+    P.queue_tail[k][x] = int32_t(std::max<int64_t>(0, len - cut));
+  }
+  P.queue_static[k] = cut * kNumXcd;
+  P.queue_dyn_per_xcd[k] = tail_rows + (tail_rows + 3) / 4;
+}
+
 // The CSR transposed: for each layout head and k-block j, the ascending
 // q-blocks i whose lists hold j, with the entry's flag.  The dK/dV part of
 // the backward walks these lists.
@@ -327,37 +358,9 @@ void build_work_kv(Plan& P) {
       P.work_kv[s] = pieces[slots[s]].item;
     }
   P.kv_reduce_launch = int64_t(P.kv_reduce.size());
-}
-
-// The forward's queue tail (see Plan): XCDs of one chip run the same work
-// at speeds a few percent apart, and the launch ends with the slowest, so the
-// last eighth of every XCD's rows is left to workgroups that take items as
-// they free up, from any XCD's queue.  A quarter as many again as the queue
-// rows run per XCD, so a fast XCD can take over that much of the others'
-// ends.  Claiming an item costs a round trip to memory or two, so only
-// launches of long rows (at least kTailMinTiles tiles on average; row lengths
-// of a dynamic plan are unknown here) have a queue.
-constexpr int64_t kTailMinRows = 16;
-constexpr int64_t kTailMinTiles = 16;
-void build_tail(Plan& P, int64_t total_cost) {
-  P.fwd_static_slots = int64_t(P.work.size());
-  P.fwd_dyn_per_xcd = 0;
-  for (int32_t& t : P.fwd_tail_len) t = 0;
-  const int64_t rows = int64_t(P.work.size()) / kNumXcd;
-  const int64_t items = P.info.work_items;
-  if (P.dynamic || items == 0 || total_cost - items < kTailMinTiles * items) return;
-  if (int64_t(P.work.size()) % kNumXcd != 0 || rows < kTailMinRows) return;
-  const int64_t tail_rows = (rows + 7) / 8;
-  const int64_t cut = rows - tail_rows;
-  // xcd_slots fills each XCD's rows from the first: its items end at its
-  // first idle slot.
-  for (int x = 0; x < kNumXcd; ++x) {
-    int64_t len = 0;
-    while (len < rows && P.work[size_t(len * kNumXcd + x)] >= 0) ++len;
-    P.fwd_tail_len[x] = int32_t(std::max<int64_t>(0, len - cut));
-  }
-  P.fwd_static_slots = cut * kNumXcd;
-  P.fwd_dyn_per_xcd = tail_rows + (tail_rows + 3) / 4;
+  int64_t walked = 0;
+  for (const auto& d : pieces) walked += d.end - d.begin;
+  build_queue(P, 1, P.work_kv, int64_t(pieces.size()), walked);
 }
 
 // Launch order.  Item id = (b * H + h) * nb + i; cost = row length + 1.
@@ -372,6 +375,8 @@ void build_work(Plan& P) {
     return int64_t(rp[i + 1] - rp[i]) + 1;
   };
   P.work.clear();
+  P.queue_static[0] = 0;
+  P.queue_dyn_per_xcd[0] = 0;
   int schedule = P.prob.schedule == BSA_SCHEDULE_DEFAULT ? BSA_SCHEDULE_XCD : P.prob.schedule;
   if (schedule == BSA_SCHEDULE_ROWMAJOR || items == 0) {
     P.work.resize(items);
@@ -411,11 +416,11 @@ void build_work(Plan& P) {
           for (int64_t g = 0; g < group; ++g) loc.push_back(int32_t((b * H + hk * group + g) * nb + i));
       }
     P.work = xcd_slots(loc, cost);
-    P.info.work_items = items;
-    int64_t total_cost = 0;
-    for (int32_t it : loc) total_cost += cost(it);
-    build_tail(P, total_cost);
+    int64_t tiles = 0;
+    for (int32_t it : loc) tiles += cost(it) - 1;
+    build_queue(P, 0, P.work, items, tiles);
   }
+  if (P.queue_dyn_per_xcd[0] == 0) P.queue_static[0] = int64_t(P.work.size());
   P.info.work_items = items;
   P.info.launch_slots = int64_t(P.work.size());
 }
@@ -435,10 +440,10 @@ bsa_status_t upload(Plan& P) {
   const size_t off_entries_t = up(off_cols + rows * sizeof(bsa::RowDesc));
   const size_t off_work_kv = up(off_entries_t + nnz * sizeof(int32_t));
   const size_t off_kv_reduce = up(off_work_kv + slots_kv * sizeof(Plan::KvDesc));
-  const size_t off_sched = up(off_kv_reduce + P.kv_reduce.size() * sizeof(Plan::KvDesc) + 16);
-  const size_t bytes = off_sched + bsa::kFwdSchedBytes;
+  const size_t off_queue = up(off_kv_reduce + P.kv_reduce.size() * sizeof(Plan::KvDesc) + 16);
+  const size_t bytes = off_queue + bsa::kQueueBytes;
   std::vector<unsigned char> host(bytes, 0);
-  std::memcpy(host.data() + off_sched, P.fwd_tail_len, sizeof(P.fwd_tail_len));   // counters start at 0
+  std::memcpy(host.data() + off_queue, P.queue_tail, sizeof(P.queue_tail));   // counters start at 0
   auto* rd = reinterpret_cast<bsa::RowDesc*>(host.data());
   auto* en = reinterpret_cast<int32_t*>(host.data() + off_entries);
   int32_t start = 0;
@@ -487,7 +492,7 @@ bsa_status_t upload(Plan& P) {
   P.d_entries_t = reinterpret_cast<const int32_t*>(base + off_entries_t);
   P.d_work_kv = reinterpret_cast<const int32_t*>(base + off_work_kv);
   P.d_kv_reduce = reinterpret_cast<const int32_t*>(base + off_kv_reduce);
-  P.d_fwd_sched = reinterpret_cast<int32_t*>(base + off_sched);
+  P.d_queue = reinterpret_cast<int32_t*>(base + off_queue);
   if (P.kv_partials > 0 && P.prob.dtype == BSA_BF16 && P.prob.head_dim == 128 && P.prob.block_size == 128) {
     // float32 partial dK and dV of every chunk of a split column.
     const size_t sbytes = size_t(P.kv_partials) * 2 * 128 * 128 * sizeof(float);
@@ -604,6 +609,8 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
     P->kv_desc.assign(P->work_kv.size(), {-1, 0, 0, -1});
     for (size_t s = 0; s < P->work_kv.size(); ++s)
       if (P->work_kv[s] >= 0) P->kv_desc[s] = {P->work_kv[s], 0, INT32_MAX, -1};
+    P->queue_static[1] = int64_t(P->work_kv.size());   // no launch queue (lengths unknown here)
+    P->queue_dyn_per_xcd[1] = 0;
     slot_of.assign(static_cast<size_t>(kv_items), -1);
     for (size_t s = 0; s < order.size(); ++s)
       if (order[s] >= 0) slot_of[static_cast<size_t>(order[s])] = int32_t(s);
@@ -638,8 +645,8 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
   const size_t off_pre = off_walk + up(kv_cols * sizeof(int32_t));
   const size_t off_reduce = off_pre + up(kv_cols * sizeof(int64_t));
   const size_t off_head = off_reduce + up(size_t(P->kv_partials) * sizeof(Plan::KvDesc));
-  const size_t off_sched = off_head + up(8 * sizeof(int32_t));
-  const size_t bytes = off_sched + bsa::kFwdSchedBytes;
+  const size_t off_queue = off_head + up(8 * sizeof(int32_t));
+  const size_t bytes = off_queue + bsa::kQueueBytes;
   hipError_t err = hipMalloc(&P->dev_mem, bytes);
   if (err != hipSuccess) {
     P->dev_mem = nullptr;
@@ -659,10 +666,8 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
                     hipMemcpyHostToDevice);
   // No split column until the first bitmap arrives.
   if (err == hipSuccess) err = hipMemset(base + off_head, 0, 8 * sizeof(int32_t));
-  // The forward's queue lengths; its counters start at 0.
-  if (err == hipSuccess) err = hipMemset(base + off_sched, 0, bsa::kFwdSchedBytes);
-  if (err == hipSuccess)
-    err = hipMemcpy(base + off_sched, P->fwd_tail_len, sizeof(P->fwd_tail_len), hipMemcpyHostToDevice);
+  // Launch queues: a dynamic plan has none (lengths 0; counters unused).
+  if (err == hipSuccess) err = hipMemset(base + off_queue, 0, bsa::kQueueBytes);
   if (err == hipSuccess && split)
     err = hipMemcpy(base + off_slot, slot_of.data(), slot_of.size() * sizeof(int32_t), hipMemcpyHostToDevice);
   if (err == hipSuccess && split) {
@@ -693,7 +698,7 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
   P->d_scan = reinterpret_cast<int64_t*>(base + off_scan);
   P->d_kv_reduce = reinterpret_cast<const int32_t*>(base + off_reduce);
   P->d_kv_head = reinterpret_cast<int32_t*>(base + off_head);
-  P->d_fwd_sched = reinterpret_cast<int32_t*>(base + off_sched);
+  P->d_queue = reinterpret_cast<int32_t*>(base + off_queue);
   P->d_kv_count = P->d_kv_head + 4;
   if (split) {
     P->d_kv_slot = reinterpret_cast<const int32_t*>(base + off_slot);
