@@ -279,9 +279,11 @@ bsa_status_t bsa_plan_read_csr_transposed(bsa_plan_t plan, int32_t layout_head, 
  * or more, the last eighth of each XCD's rows is instead a queue that extra
  * workgroups drain, claiming from any XCD's queue as they free up (XCDs of
  * one chip run a few percent apart).  Its claim counters are plan memory, in
- * 64 sets that successive calls take in turn (each call's last workgroup
- * clears its set): calls with one plan may run concurrently, on any streams,
- * up to 64 at a time.  Results do not depend on which workgroup runs an item.
+ * 64 sets that successive queued launches take in turn (each launch's last
+ * workgroup clears its set): calls with one plan may run concurrently, on any
+ * streams, as long as at most 64 queued launches (a forward is one, a
+ * backward two) are in flight at once.  Results do not depend on which
+ * workgroup runs an item.
  * Errors (returned before anything is launched): INVALID_ARGUMENT for NULL
  * pointers, a host-only plan, or a plan made on another device; DEVICE if
  * the launch fails.  Faults during execution surface at the caller's next
@@ -355,7 +357,10 @@ bsa_status_t bsa_plan_read_work_kv(bsa_plan_t plan, int32_t* desc, int64_t capac
  * q-block, walking its CSR row), dK/dV (one workgroup per KV head and
  * k-block, walking its transposed list over the group's query heads, or per
  * chunk of a long walk) and, if the plan split any walk, the reduction of
- * the chunks' partial sums.  Every
+ * the chunks' partial sums.  The bf16 dQ and dK/dV launches of a static
+ * plan whose walks average 16 tiles or more end in launch queues as the
+ * forward does (see bsa_forward), each taking one of the plan's 64 counter
+ * sets.  Every
  * element of dq, dk, dv and delta is written (zero rows where nothing
  * attends).  Outputs must not alias inputs or each other.  Nothing is
  * allocated or freed.
