@@ -5,10 +5,10 @@ package.  The product package never imports it.
 """
 from .bsa_oracle import (FULL, PARTIAL, allowed_count, allowed_keys, allowed_queries,
                          attend_row, backward, backward_dkv_keys, backward_dq_rows,
-                         forward, forward_query_range, grad_row, kv_head, plan,
+                         forward, forward_query_range, grad_row, kv_head, lse_merge, plan,
                          tile_counts)
 
 __all__ = ["FULL", "PARTIAL", "allowed_count", "allowed_keys", "allowed_queries",
            "attend_row", "backward", "backward_dkv_keys", "backward_dq_rows",
-           "forward", "forward_query_range", "grad_row", "kv_head", "plan",
+           "forward", "forward_query_range", "grad_row", "kv_head", "lse_merge", "plan",
            "tile_counts"]

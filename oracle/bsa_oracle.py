@@ -46,6 +46,16 @@ What it computes (all arithmetic in float64 with numpy):
   problems, the latter through `allowed_queries`, the predicate evaluated
   for every query at a fixed key.
 
+* `lse_merge(O_parts, L_parts)` -- partial results over disjoint key sets of
+  the same queries combined into the result over their union: the softmax
+  over A_1 U A_2 splits into the two partial softmaxes weighted by their
+  normalisers, so LSE = ln(sum_p e^{L_p}) and O = sum_p e^{L_p} O_p / e^{LSE}
+  (the online-softmax combination of local and remote partial attention in
+  "How Do Sparse Attention Kernels Work in GPU Clusters?"); parts with L = -inf
+  (no key) carry no weight, and a row empty in every part stays O = 0,
+  LSE = -inf.  Its pins merge the oracle's own partial results over split
+  layouts and compare with the oracle over the union.
+
 * `plan(layout, N, bs)` -- the per-query-block list of key blocks (step three
   of "How Does Flash-MSA Sparse Attention Work?": a query block fetches only
   its active key blocks; a mask given as block indices in "The Architecture
@@ -508,3 +518,25 @@ def backward_dkv_keys(Q, K, V, dO, layout, block_size: int, keys, scale: Optiona
                 dK[r] += scale * ds[pos] * qv
                 dV[r] += p[pos] * dov
     return dK, dV
+
+
+# --------------------------------------------------------------------------
+# Merging partial results over disjoint key sets
+# --------------------------------------------------------------------------
+def lse_merge(O_parts, L_parts):
+    """Combine P partial results of the same query rows over disjoint key
+    sets: O_parts [P, ..., D], L_parts [P, ...] (natural-log LSE, -inf for a
+    part with no key).  Returns (O, LSE) over the union, in float64:
+    LSE = ln(sum_p e^{L_p}), O = sum_p e^{L_p - LSE} O_p; rows with every
+    L_p = -inf give O = 0 and LSE = -inf."""
+    O = np.asarray(O_parts, dtype=np.float64)
+    L = np.asarray(L_parts, dtype=np.float64)
+    m = L.max(axis=0)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    w = np.exp(L - m_safe[None])                       # e^{-inf} = 0 for empty parts
+    s = w.sum(axis=0)
+    lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, s)))
+    out = (w[..., None] * O).sum(axis=0) / np.where(empty, 1.0, s)[..., None]
+    out[empty] = 0.0
+    return out, lse
