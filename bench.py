@@ -267,6 +267,37 @@ def dynamic_backward_context(steps=5):
     return res
 
 
+def merge_context(steps=20):
+    """bsa_lse_merge of two partial results of the 128K workload's output shape
+    (bf16 O [32, 131072, 128] and fp32 LSE per part): an HBM-bound kernel that
+    reads each part once and writes the result once; GB/s against 8 TB/s."""
+    P, rows, D = 2, 32 * 131072, 128
+    g = torch.Generator(device="cuda").manual_seed(9)
+    O = torch.randn((P, rows, D), generator=g, device="cuda").to(torch.bfloat16)
+    L = torch.randn((P, rows), generator=g, device="cuda")
+    out = torch.empty((rows, D), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty(rows, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        bsattn.lse_merge(O, L, out, lse)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        bsattn.lse_merge(O, L, out, lse)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    nbytes = (P + 1) * rows * (D * 2 + 4)
+    res = {"parts": P, "rows": rows, "head_dim": D, "ms": round(ms, 4), "bytes": nbytes,
+           "gb_per_s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+           "frac_of_hbm_peak": round(nbytes / (ms * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)}
+    log(f"[bench] lse_merge: {res}")
+    del O, L, out, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def time_backward(p, q, k, v, out, lse, do, steps, warmup):
     """Warm up, then time `steps` backwards (three launches each) with a HIP
     event pair around each on the launch stream; returns the per-step ms."""
@@ -533,6 +564,7 @@ def main():
         del q, k, v, out, lse
         torch.cuda.empty_cache()
         ctx["dynamic_plan"] = dynamic_plan_context()
+        ctx["lse_merge"] = merge_context()
         ctx["lengths"] = lengths_context()
         ctx["backward"] = backward_context(["tiny_f32", "window16k", "random32k", "winglobal128k", "gqa256k"])
         result["context"] = ctx

@@ -35,7 +35,8 @@ EXPORTS = ("bsa_plan", "bsa_plan_host", "bsa_plan_destroy", "bsa_plan_csr", "bsa
            "bsa_plan_work", "bsa_plan_active_blocks", "bsa_plan_dynamic", "bsa_plan_set_bitmap",
            "bsa_plan_read_csr", "bsa_plan_read_csr_transposed", "bsa_forward",
            "bsa_plan_csr_transposed", "bsa_plan_work_kv", "bsa_plan_read_work_kv",
-           "bsa_backward", "bsa_backward_noalloc", "bsa_forward_varlen", "bsa_backward_varlen", "bsa_status_string", "bsa_last_error",
+           "bsa_backward", "bsa_backward_noalloc", "bsa_forward_varlen", "bsa_backward_varlen", "bsa_lse_merge",
+           "bsa_status_string", "bsa_last_error",
            "bsa_abi_version")
 
 
@@ -102,6 +103,8 @@ def lib():
     L.bsa_backward_noalloc.argtypes = [c_void_p] * 6 + [P] + [c_void_p] * 4
     L.bsa_forward_varlen.argtypes = [c_void_p, c_void_p, c_void_p, P, c_void_p, c_void_p, c_void_p, c_void_p]
     L.bsa_backward_varlen.argtypes = [c_void_p] * 6 + [P] + [c_void_p] * 6
+    L.bsa_lse_merge.argtypes = [c_int32, c_int64, c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p,
+                                c_void_p]
     L.bsa_status_string.argtypes = [c_int32]
     L.bsa_status_string.restype = c_char_p
     L.bsa_last_error.argtypes = []
@@ -110,7 +113,7 @@ def lib():
     for name in ("bsa_plan", "bsa_plan_host", "bsa_plan_csr", "bsa_plan_get_info", "bsa_plan_work",
                  "bsa_plan_dynamic", "bsa_plan_set_bitmap", "bsa_plan_read_csr", "bsa_plan_read_csr_transposed",
                  "bsa_forward", "bsa_plan_csr_transposed", "bsa_plan_work_kv", "bsa_plan_read_work_kv", "bsa_backward", "bsa_forward_varlen",
-                 "bsa_backward_varlen"):
+                 "bsa_backward_varlen", "bsa_lse_merge"):
         getattr(L, name).restype = c_int32
     _lib = L
     return L
@@ -450,4 +453,36 @@ def forward_varlen(q, k, v, p: Plan, seq_lens, out=None, lse=None):
         stream = torch.cuda.current_stream().cuda_stream
         _check(lib().bsa_forward_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), p.handle, seq_lens.data_ptr(),
                                         out.data_ptr(), lse.data_ptr(), c_void_p(stream)))
+    return out, lse
+
+
+def lse_merge(o_parts, lse_parts, out=None, lse=None):
+    """bsa_lse_merge on torch.cuda.current_stream(): o_parts [P, ..., D] (bf16
+    or float32) and lse_parts [P, ...] (float32) of P partial results over
+    disjoint key sets of the same rows; returns (out [..., D], lse [...])."""
+    import torch
+    if o_parts.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"o_parts must be bfloat16 or float32, got {o_parts.dtype}")
+    if not o_parts.is_cuda:
+        raise ValueError(f"o_parts must be a CUDA tensor, got one on {o_parts.device}")
+    P, D = int(o_parts.shape[0]), int(o_parts.shape[-1])
+    row_shape = tuple(o_parts.shape[1:-1])
+    dev = o_parts.device
+    if out is None:
+        out = torch.empty(row_shape + (D,), dtype=o_parts.dtype, device=dev)
+    if lse is None:
+        lse = torch.empty(row_shape, dtype=torch.float32, device=dev)
+    for name, t, shape, tdt in (("o_parts", o_parts, tuple(o_parts.shape), o_parts.dtype),
+                                ("lse_parts", lse_parts, (P,) + row_shape, torch.float32),
+                                ("out", out, row_shape + (D,), o_parts.dtype),
+                                ("lse", lse, row_shape, torch.float32)):
+        _require(name, t, shape, tdt, dev)
+    rows = 1
+    for x in row_shape:
+        rows *= int(x)
+    with torch.cuda.device(dev):
+        stream = torch.cuda.current_stream().cuda_stream
+        _check(lib().bsa_lse_merge(P, rows, D, BF16 if o_parts.dtype == torch.bfloat16 else F32,
+                                   o_parts.data_ptr(), lse_parts.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                   c_void_p(stream)))
     return out, lse

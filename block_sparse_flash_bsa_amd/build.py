@@ -22,7 +22,7 @@ PROBE_LIB = os.path.join(PKG, "libbsattn_probe.so")   # benchmark's MFMA-rate pr
 ARCH = os.environ.get("BSA_OFFLOAD_ARCH", "gfx950")
 ROCM_INCLUDE = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include")
 
-SOURCES = ["plan.cpp", "plan_device.hip", "forward.hip", "backward.hip"]
+SOURCES = ["plan.cpp", "plan_device.hip", "forward.hip", "backward.hip", "merge.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", CSRC]
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 5
+#define BSA_ABI_VERSION 6
 
 /* Status codes.  Every entry point that can fail returns one; no exception
  * crosses the ABI.  Out-parameters are written only on BSA_OK. */
@@ -435,6 +435,33 @@ bsa_status_t bsa_forward_varlen(const void* q, const void* k, const void* v, bsa
 bsa_status_t bsa_backward_varlen(const void* q, const void* k, const void* v, const void* out,
                                  const float* lse, const void* dout, bsa_plan_t plan, const int32_t* seq_lens,
                                  void* dq, void* dk, void* dv, float* delta, void* stream);
+
+/* Merge P partial attention results of the same R query rows over disjoint
+ * key sets into the result over their union.  Softmax attention over
+ * A_1 U ... U A_P is the partial softmaxes weighted by their normalisers, so
+ * per row, with m = max_p L_p:
+ *   lse_out = m + ln sum_p e^{L_p - m},
+ *   out     = sum_p e^{L_p - m} O_p / sum_p e^{L_p - m};
+ * a part with L_p = -inf (no key) carries no weight, and a row empty in every
+ * part gets out = 0, lse_out = -inf.  This is the online-softmax combination
+ * of local and remote partial attention in "How Do Sparse Attention Kernels
+ * Work in GPU Clusters?" (its distributed forward): what rows split into key
+ * ranges, or attention sharded by keys, need afterwards.  Asynchronous on
+ * `stream` (NULL = default stream) of the current device; float32 arithmetic.
+ *   parts    : P >= 1
+ *   rows     : R >= 0 query rows (batch * heads * seq_len for forward outputs)
+ *   head_dim : D, with D * element size a multiple of 16 bytes
+ *   dtype    : BSA_BF16 or BSA_F32, of o_parts and out
+ *   o_parts  : device, [P][R][D] contiguous (the parts' O, stacked)
+ *   lse_parts: device, float32 [P][R] (the parts' LSE, natural log)
+ *   out      : device, [R][D] dtype (bf16 rounded to nearest even)
+ *   lse_out  : device, float32 [R]
+ * out and lse_out must not alias the inputs.  Nothing is allocated.
+ * Errors (before anything is launched): INVALID_ARGUMENT for P < 1, R < 0, a
+ * bad dtype or head_dim, NULL pointers (R > 0), or pointers that are not
+ * device memory of the current device; DEVICE if the launch fails. */
+bsa_status_t bsa_lse_merge(int32_t parts, int64_t rows, int32_t head_dim, int32_t dtype, const void* o_parts,
+                           const float* lse_parts, void* out, float* lse_out, void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* bsa_status_string(bsa_status_t status);

@@ -499,6 +499,25 @@ def test_probe_library_exports_its_header():
     assert L.bsa_probe_mfma(0, 1, None, None) == 1          # argument errors return before any HIP call
 
 
+def test_lse_merge_argument_errors():
+    """Errors bsa_lse_merge reports before touching the device; zero rows is
+    a no-op."""
+    L = bsattn.lib()
+    one = ctypes.c_void_p(1)
+    for args, what in (((0, 10, 128, bsattn.BF16), b"parts"), ((2, -1, 128, bsattn.BF16), b"rows"),
+                       ((2, 10, 128, 7), b"dtype"), ((2, 10, 4, bsattn.BF16), b"head_dim"),
+                       ((2, 10, 2, bsattn.F32), b"head_dim")):
+        assert L.bsa_lse_merge(*args, one, one, one, one, None) == bsattn.ERR_INVALID_ARGUMENT
+        assert what in L.bsa_last_error()
+    assert L.bsa_lse_merge(2, 10, 128, bsattn.BF16, None, one, one, one, None) == bsattn.ERR_INVALID_ARGUMENT
+    assert L.bsa_lse_merge(2, 0, 128, bsattn.BF16, None, None, None, None, None) == bsattn.OK
+    # host memory is refused (or, with no GPU, the device query fails first)
+    host = np.zeros(4096, np.float32)
+    st = L.bsa_lse_merge(1, 4, 128, bsattn.F32, host.ctypes.data, host.ctypes.data, host.ctypes.data,
+                         host.ctypes.data, None)
+    assert st in (bsattn.ERR_INVALID_ARGUMENT, bsattn.ERR_DEVICE)
+
+
 def test_varlen_and_transposed_read_argument_errors():
     """Errors the variable-length entry points and the transposed-list read
     report before touching the device."""

@@ -302,6 +302,35 @@ def test_backward_deterministic_and_overwrites():
     assert not torch.isnan(delta).any()
 
 
+def test_backward_launch_queues_over_many_calls():
+    """The dQ and dK/dV launch queues (the last eighth of each XCD's rows
+    drained by workgroups of any XCD, counters taken per launch in turn from
+    the plan's 64 sets): 45 forward + backward calls of one plan (135 queued
+    launches, twice round the sets) on two alternating streams, each into
+    NaN-poisoned gradients, give bit for bit the gradients of the LPT order,
+    whose launches have no queue."""
+    w = wl.small_variant(wl.WORKLOADS["winglobal128k"], 16384, heads=8, kv_heads=8)
+    lay = wl.layout_of(w)
+    q, k, v = (x.cuda() for x in wl.make_qkv(w, "cpu"))
+    do = wl.make_dout(w, "cuda")
+    p = gpu_plan(w, lay)
+    assert len(p.work()) // 8 >= 16 and len(p.work_kv()) // 8 >= 16
+    ref = fwd_bwd(gpu_plan(w, lay, schedule=2), q, k, v, do)
+    grads = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+    streams = [torch.cuda.current_stream(), torch.cuda.Stream()]
+    for call in range(45):
+        st = streams[call % 2]
+        st.wait_stream(streams[(call + 1) % 2])
+        with torch.cuda.stream(st):
+            for g in grads:
+                g.fill_(float("nan"))
+            out, lse = bsattn.forward(q, k, v, p)
+            bsattn.backward(q, k, v, out, lse, do, p, *grads)
+        st.synchronize()
+        for name, a, b in zip(("dQ", "dK", "dV"), grads, ref):
+            assert torch.equal(a, b), f"call {call}: {name} differs"
+
+
 def test_backward_custom_scale_stream_and_empty_problems():
     """A non-default scale (enters P and the scale of dQ, dK), a non-default
     stream, and problems with no work items (returns at once)."""
