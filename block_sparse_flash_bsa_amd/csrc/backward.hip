@@ -195,6 +195,37 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
+// Store a wave's 32-column x 128-row transposed accumulator (acc[dt] row
+// 32 dt + 8 (r / 4) + 4 hf + r % 4 of this lane's column, column r32) as 32
+// bf16 rows of 128 values at dst0 (row r32 at dst0 + 128 r32), times mul;
+// only the first nvalid rows are written.  The block is staged in 8 KB of
+// LDS that no wave reads any more (16-byte chunk c of row r at c ^ (r & 15):
+// no bank conflicts either way), then written as whole 256-byte rows, 16
+// bytes per lane and four rows per store, instead of 16-byte pieces of 32
+// rows per store.  The wave reads back only what it wrote.
+__device__ __forceinline__ void store_block(uint16_t* dst0, const f32x16 (&acc)[4], float mul, int r32, int hf,
+                                            int lane, lds_u8* stage, int nvalid) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x2 pk;
+      pk[0] = uint32_t(bf16_bits(acc[dt][4 * g + 0] * mul)) | (uint32_t(bf16_bits(acc[dt][4 * g + 1] * mul)) << 16);
+      pk[1] = uint32_t(bf16_bits(acc[dt][4 * g + 2] * mul)) | (uint32_t(bf16_bits(acc[dt][4 * g + 3] * mul)) << 16);
+      *reinterpret_cast<__attribute__((address_space(3))) u32x2*>(
+          stage + r32 * 256 + 16 * ((4 * dt + g) ^ (r32 & 15)) + 8 * hf) = pk;
+    }
+  __asm__ volatile("" ::: "memory");
+  const int sr = lane >> 4, sc = lane & 15;      // row within a group of 4, 16-byte chunk
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    const int r = 4 * s + sr;
+    const u32x4 val = *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(stage + r * 256 + 16 * (sc ^ (r & 15)));
+    if (r < nvalid) *reinterpret_cast<u32x4*>(dst0 + int64_t(r) * kD + 8 * sc) = val;
+  }
+  __asm__ volatile("" ::: "memory");
+}
+
 // Store a 32-column x 128-row transposed accumulator (acc[dt] row
 // 32 dt + 8 (r / 4) + 4 hf + r % 4 of this lane's column) as one bf16 row of
 // 128 values at `dst`, times `mul`.
@@ -462,7 +493,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
     }
   }
   queue_release(p.lq_dq, done);
-  if (!kRagged || qg < p.N) store_row(p.dq + qrow * kD, acc, p.scale, hf);
+  // Every wave is past its last LDS read: the wave's 8 KB buffer stages dQ.
+  BSA_WAIT_BARRIER(0);
+  {
+    const int row0 = i * kB + wave * 32;
+    const int nvalid = kRagged ? (p.N32 - row0 < 0 ? 0 : (p.N32 - row0 > 32 ? 32 : p.N32 - row0)) : 32;
+    lds_u8* const stage = wave == 0 ? Kb[0] : wave == 1 ? Kb[1] : wave == 2 ? Vb[0] : Vb[1];
+    store_block(p.dq + (qrow - r32) * kD, acc, p.scale, r32, hf, lane, stage, nvalid);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -705,10 +743,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_bf16_d128(BwdParams p) {
   }
   queue_release(p.lq_kv, done);
   if (partial_slot < 0) {
-    if (!kRagged || kg < p.N) {
-      store_row(p.dk + krow * kD, dk, p.scale, hf);
-      store_row(p.dv + krow * kD, dv, 1.f, hf);
-    }
+    // Every wave is past its last LDS read: 8 KB of the V block per wave
+    // stages dK, then dV.
+    BSA_WAIT_BARRIER(0);
+    const int row0 = j * kB + wave * 32;
+    const int nvalid = kRagged ? (p.N32 - row0 < 0 ? 0 : (p.N32 - row0 > 32 ? 32 : p.N32 - row0)) : 32;
+    lds_u8* const stage = Vs + wave * (32 * 256);
+    store_block(p.dk + (krow - r32) * kD, dk, p.scale, r32, hf, lane, stage, nvalid);
+    store_block(p.dv + (krow - r32) * kD, dv, 1.f, r32, hf, lane, stage, nvalid);
   } else {
     // One chunk of a split column: float32 partial sums, unscaled.
     float* const part = p.kv_scratch + int64_t(partial_slot) * 2 * kB * kD + (wave * 32 + r32) * kD;
