@@ -158,16 +158,37 @@ def cpu_baseline(w, lay, q, k, v, flops, seconds=15.0):
             "extrapolated_full_s": round(full_s, 1)}
 
 
+# Sources a kernel's code is compiled from: its own file and the headers it
+# includes.  A counter summary records their combined SHA-256.
+KERNEL_SOURCES = {
+    "forward": ("forward.hip", "queue.h", "internal.h"),
+    "backward": ("backward.hip", "queue.h", "internal.h"),
+}
+
+
+def sources_sha256(kind):
+    """SHA-256 over the concatenated sources of one kernel family (None when one is missing)."""
+    import hashlib
+    here = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        path = os.path.join(here, "block_sparse_flash_bsa_amd", "csrc", name)
+        if not os.path.exists(path):
+            return None
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def recorded_traffic(kernel, workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE, each scaled by its plain-copy calibration).
     None when there is no summary for this kernel and workload, or when the
-    kernel source changed since the counters were taken."""
-    import hashlib
+    kernel's sources changed since the counters were taken."""
     here = os.path.dirname(os.path.abspath(__file__))
     path = os.path.join(here, "profiles", f"{kernel}_{workload}_hbm.txt")
-    src = os.path.join(here, "block_sparse_flash_bsa_amd", "csrc", "forward.hip")
-    if not os.path.exists(path) or not os.path.exists(src):
+    sha = sources_sha256("forward")
+    if not os.path.exists(path) or sha is None:
         return None
     rec = {}
     with open(path) as f:
@@ -175,9 +196,7 @@ def recorded_traffic(kernel, workload):
             if not line.startswith("#") and ":" in line:
                 key, val = line.split(":", 1)
                 rec[key.strip()] = val.strip()
-    with open(src, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if rec.get("forward_hip_sha256") != sha or "traffic_bytes_per_launch" not in rec:
+    if rec.get("forward_sources_sha256") != sha or "traffic_bytes_per_launch" not in rec:
         return None
     return int(rec["traffic_bytes_per_launch"])
 
