@@ -15,10 +15,11 @@
 // and K and turned into weights with the saved LSE.
 //
 // Kernels:
-//   bwd_delta_bf16     Delta_q per row (HBM-bound, 16 lanes per row).
-//   bwd_dq_bf16_d128   one workgroup per (b, h, q-block), walking the
-//                      forward's CSR row: S^T and dP^T = V dO^T on MFMA,
-//                      dS^T in registers, dQ^T += K^T dS^T.
+//   bwd_dq_bf16_d128   one workgroup per (b, h, q-block): first Delta_q of
+//                      its rows from O and dO (written for the dK/dV
+//                      kernel), then a walk of the forward's CSR row: S^T
+//                      and dP^T = V dO^T on MFMA, dS^T in registers,
+//                      dQ^T += K^T dS^T.
 //   bwd_dkdv_bf16_d128 one workgroup per (b, KV head, k-block), walking the
 //                      transposed CSR over every query head of the GQA group:
 //                      S and dP = dO V^T on MFMA, P and dS in registers,
@@ -195,6 +196,14 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
   return __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
 }
 
+// Sum of x over lanes l and l ^ 32 (v_permlane32_swap: one result holds the
+// lane's own value, the other its partner's).
+__device__ __forceinline__ float sum_with_partner(float x) {
+  const uint32_t b = __float_as_uint(x);
+  const auto sw = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 // Store a wave's 32-column x 128-row transposed accumulator (acc[dt] row
 // 32 dt + 8 (r / 4) + 4 hf + r % 4 of this lane's column, column r32) as 32
 // bf16 rows of 128 values at dst0 (row r32 at dst0 + 128 r32), times mul;
@@ -224,44 +233,6 @@ __device__ __forceinline__ void store_block(uint16_t* dst0, const f32x16 (&acc)[
     if (r < nvalid) *reinterpret_cast<u32x4*>(dst0 + int64_t(r) * kD + 8 * sc) = val;
   }
   __asm__ volatile("" ::: "memory");
-}
-
-// Store a 32-column x 128-row transposed accumulator (acc[dt] row
-// 32 dt + 8 (r / 4) + 4 hf + r % 4 of this lane's column) as one bf16 row of
-// 128 values at `dst`, times `mul`.
-__device__ __forceinline__ void store_row(uint16_t* dst, const f32x16 (&acc)[4], float mul, int hf) {
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x2 pk;
-      pk[0] = uint32_t(bf16_bits(acc[dt][4 * g + 0] * mul)) | (uint32_t(bf16_bits(acc[dt][4 * g + 1] * mul)) << 16);
-      pk[1] = uint32_t(bf16_bits(acc[dt][4 * g + 2] * mul)) | (uint32_t(bf16_bits(acc[dt][4 * g + 3] * mul)) << 16);
-      *reinterpret_cast<u32x2*>(dst + dt * 32 + 8 * g + 4 * hf) = pk;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Delta_q = <dO_q, O_q> in float32: 16 lanes per 128-element row.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(kThreads) void bwd_delta_bf16(const uint16_t* __restrict__ o,
-                                                         const uint16_t* __restrict__ dout,
-                                                         float* __restrict__ delta, int64_t rows) {
-  const int64_t row = int64_t(blockIdx.x) * (kThreads / 16) + (threadIdx.x >> 4);
-  const int c = threadIdx.x & 15;
-  float s = 0.f;
-  if (row < rows) {
-    const u32x4 a = *reinterpret_cast<const u32x4*>(o + row * kD + c * 8);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(dout + row * kD + c * 8);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      s = fmaf(__uint_as_float(a[u] << 16), __uint_as_float(b[u] << 16), s);
-      s = fmaf(__uint_as_float(a[u] & 0xffff0000u), __uint_as_float(b[u] & 0xffff0000u), s);
-    }
-  }
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) s += __shfl_xor(s, m);
-  if (c == 0 && row < rows) delta[row] = s;
 }
 
 // Wait until at most N of this wave's vector-memory operations are pending,
@@ -311,7 +282,12 @@ __device__ __forceinline__ uint32_t cols_base(int lane, int s) {
 // ---------------------------------------------------------------------------
 // dQ: one workgroup per (b, h, q-block); wave w owns query rows 32w .. +31
 // and walks the forward's CSR row in steps of 32 keys.  Q^T and dO^T stay in
-// registers as B operands, the row's LSE and Delta in one register each.  K
+// registers as B operands, the row's LSE and Delta in one register each.
+// Delta_q = <dO_q, O_q> is formed first, from O loaded in dO's register
+// layout (each lane holds half of its row, lanes l and l ^ 32 the two
+// halves), and written to p.delta for the dK/dV kernel, which runs after
+// this one on the same stream; every launch slot of the plan is one q-block,
+// so every row is written (0 for rows at or beyond the entry's length).  K
 // rows (read row-wise for S^T and transposed for dQ^T) and V rows (row-wise
 // for dP^T) of a step are double-buffered and filled by direct HBM->LDS
 // loads issued a step ahead, interleaved with the S^T/dP^T MFMAs; one
@@ -369,18 +345,35 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_bf16_d128(BwdParams p) {
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) acc[dt] = f32x16{};
 
-  if (ne > 0) {
-    // Q^T and dO^T as B operands: lane (row r32, half hf) holds d = 16c + 8hf .. +7.
-    bf16x8 qf[8], df[8];
+  // dO^T as a B operand: lane (row r32, half hf) holds d = 16c + 8hf .. +7;
+  // O in the same layout gives Delta (float32 products of the bf16 values).
+  bf16x8 df[8];
+  float dlt;
+  {
+    bf16x8 of[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      qf[c] = *reinterpret_cast<const bf16x8*>(p.q + qrow_ld * kD + c * 16 + hf * 8);
       df[c] = *reinterpret_cast<const bf16x8*>(p.dout + qrow_ld * kD + c * 16 + hf * 8);
+      of[c] = *reinterpret_cast<const bf16x8*>(p.o + qrow_ld * kD + c * 16 + hf * 8);
     }
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        part[e & 3] = fmaf(static_cast<float>(of[c][e]), static_cast<float>(df[c][e]), part[e & 3]);
+    dlt = sum_with_partner((part[0] + part[1]) + (part[2] + part[3]));
+    if (hf == 0 && (!kRagged || qg < p.N32)) p.delta[qrow] = kRagged && qg >= Nb ? 0.f : dlt;
+  }
+
+  if (ne > 0) {
+    // Q^T as a B operand, in dO's layout.
+    bf16x8 qf[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(p.q + qrow_ld * kD + c * 16 + hf * 8);
     const float lse = p.lse[qrow_ld];
     // An empty row (LSE = -inf) has every score masked in every tile it meets.
     const float lse2 = lse == -INFINITY ? 0.f : lse * kLog2e;
-    const float dlt = p.delta[qrow_ld];
     // Complete these loads before the first HBM->LDS load, so the pending
     // counts the barriers wait on only see those.
     __asm__ volatile("s_waitcnt vmcnt(0)" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]),
@@ -822,11 +815,14 @@ __device__ __forceinline__ float quad_sum(float a) {
 // Delta_q = <dO_q, O_q> for float32 rows of D values, 16 lanes per row.
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_delta_f32(const float* __restrict__ o, const float* __restrict__ dout,
-                                                        float* __restrict__ delta, int64_t rows) {
+                                                        float* __restrict__ delta, int64_t rows, BwdParams p) {
   const int64_t row = int64_t(blockIdx.x) * (kThreads / 16) + (threadIdx.x >> 4);
   const int c = threadIdx.x & 15;
   float s = 0.f;
-  if (row < rows) {
+  // Rows at or beyond their entry's length (variable-length batches) are
+  // padding: not read, and their Delta is 0.
+  const bool inside = row < rows && (!p.seq_lens || row % p.N < entry_length(p, int(row / p.N / p.H)));
+  if (inside) {
 #pragma unroll
     for (int d = c; d < D; d += 16) s = fmaf(o[row * D + d], dout[row * D + d], s);
   }
@@ -1030,7 +1026,7 @@ hipError_t launch_f32_backward(const BwdParams& prm, const Plan& plan, hipStream
   const int64_t rows_per_block = kThreads / 16;
   hipLaunchKernelGGL(bwd_delta_f32<D>, dim3(unsigned((rows + rows_per_block - 1) / rows_per_block)), dim3(kThreads),
                      0, s, static_cast<const float*>(static_cast<const void*>(prm.o)),
-                     static_cast<const float*>(static_cast<const void*>(prm.dout)), prm.delta, rows);
+                     static_cast<const float*>(static_cast<const void*>(prm.dout)), prm.delta, rows, prm);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL((bwd_dq_f32<D, BS>), dim3(unsigned(plan.info.launch_slots)), dim3(BS * kF32Lanes), smem_dq, s,
@@ -1131,18 +1127,11 @@ bsa_status_t backward_impl(const void* q, const void* k, const void* v, const vo
   prm.lq_kv = launch_queue(*plan, 1);
   const unsigned grid_dq = unsigned(int64_t(prm.lq_dq.static_slots) + prm.lq_dq.dyn_total);
   const unsigned grid_kv = unsigned(int64_t(prm.lq_kv.static_slots) + prm.lq_kv.dyn_total);
-  const int64_t rows = int64_t(pr.batch) * pr.num_heads * pr.seq_len;
-  const int64_t rows_per_block = kThreads / 16;
-  hipLaunchKernelGGL(bwd_delta_bf16, dim3(unsigned((rows + rows_per_block - 1) / rows_per_block)), dim3(kThreads),
-                     0, s, prm.o, prm.dout, prm.delta, rows);
+  if (ragged)
+    hipLaunchKernelGGL(bwd_dq_bf16_d128<true>, dim3(grid_dq), dim3(kThreads), 0, s, prm);
+  else
+    hipLaunchKernelGGL(bwd_dq_bf16_d128<false>, dim3(grid_dq), dim3(kThreads), 0, s, prm);
   hipError_t err = hipGetLastError();
-  if (err == hipSuccess) {
-    if (ragged)
-      hipLaunchKernelGGL(bwd_dq_bf16_d128<true>, dim3(grid_dq), dim3(kThreads), 0, s, prm);
-    else
-      hipLaunchKernelGGL(bwd_dq_bf16_d128<false>, dim3(grid_dq), dim3(kThreads), 0, s, prm);
-    err = hipGetLastError();
-  }
   if (err == hipSuccess && !plan->work_kv.empty()) {
     if (ragged)
       hipLaunchKernelGGL(bwd_dkdv_bf16_d128<true>, dim3(grid_kv), dim3(kThreads), 0, s, prm);

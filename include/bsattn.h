@@ -353,8 +353,10 @@ bsa_status_t bsa_plan_read_work_kv(bsa_plan_t plan, int32_t* desc, int64_t capac
  *   delta   : device, float32 [batch][num_heads][seq_len]: caller-owned
  *             workspace; receives Delta_q = <dO_q, O_q> (computed from the
  *             rounded out), which the dK/dV kernel reads
- * Kernels run in order on the stream: Delta, dQ (one workgroup per
- * q-block, walking its CSR row), dK/dV (one workgroup per KV head and
+ * Kernels run in order on the stream: dQ (one workgroup per q-block: it
+ * first forms Delta for the block's rows and writes it to delta, then walks
+ * the block's CSR row; the float32 path forms Delta in a kernel of its own
+ * before dQ), dK/dV (one workgroup per KV head and
  * k-block, walking its transposed list over the group's query heads, or per
  * chunk of a long walk) and, if the plan split any walk, the reduction of
  * the chunks' partial sums.  The bf16 dQ and dK/dV launches of a static
@@ -422,9 +424,9 @@ bsa_status_t bsa_forward_varlen(const void* q, const void* k, const void* v, bsa
  * the ones of a sequence of seq_lens[b] positions under the same layout
  * (the dQ walks stop at the entry's last block, the dK/dV walks skip q-blocks
  * beyond it, and its last partial block is masked token by token).  Rows of
- * dq, dk and dv at or beyond seq_lens[b] are written as zeros.  Padding of
- * q, k, v, out, lse and dout is never read, so it may hold anything; the
- * padded rows of delta hold <dO, O> of whatever the padding holds.
+ * dq, dk, dv and delta at or beyond seq_lens[b] are written as zeros.
+ * Padding of q, k, v, out, lse and dout is never read, so it may hold
+ * anything.
  *   seq_lens: device int32 [batch]; values are clamped to [0, seq_len]; the
  *             same array that produced out and lse.
  * Other arguments as bsa_backward.  Every kernel of bsa_backward has a

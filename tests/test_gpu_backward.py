@@ -302,6 +302,59 @@ def test_backward_deterministic_and_overwrites():
     assert not torch.isnan(delta).any()
 
 
+@pytest.mark.parametrize("kind", ["plain", "ragged", "varlen", "varlen_f32"])
+def test_delta_workspace_is_row_dot_of_dout_and_out(kind):
+    """The dQ kernel forms Delta_q = <dO_q, O_q> for its own rows and writes it
+    to the caller's workspace before the dK/dV kernel reads it: every row of
+    a NaN-poisoned workspace comes back as the float64 dot of the bf16 O and
+    dO rows, to float32 rounding of 128 products, and rows at or beyond a
+    batch entry's length (whose padding holds NaN) as 0."""
+    if kind == "plain":
+        w = SMALL["gqa256k"]
+        lay, lens = wl.layout_of(w), None
+    elif kind == "ragged":
+        w = wl.WORKLOADS["gqa256k"].with_shape(name="delta-ragged", batch=1, heads=4, kv_heads=2, seq_len=1000)
+        lay, lens = wl.layout_of(w), None
+    else:
+        w, lay, lens = _varlen_case("window")
+        if kind == "varlen_f32":
+            w = w.with_shape(name="varlen-f32", dtype=torch.float32, head_dim=64, block=64)
+    say(f"[delta] {kind} B={w.batch} H={w.heads}/{w.kv_heads} N={w.seq_len} lens={lens}")
+    q, k, v = wl.make_qkv(w, "cpu")
+    do = wl.make_dout(w, "cpu")
+    if lens is not None:
+        for b, L in enumerate(lens):
+            for t in (q, k, v, do):
+                t[b, :, L:] = float("nan")
+    p = gpu_plan(w, lay)
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    delta = torch.full((w.batch, w.heads, w.seq_len), float("nan"), device="cuda")
+    if lens is None:
+        out, lse = bsattn.forward(qc, kc, vc, p)
+        bsattn.backward(qc, kc, vc, out, lse, doc, p, delta=delta)
+    else:
+        sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+        out, lse = bsattn.forward_varlen(qc, kc, vc, p, sl)
+        bsattn.backward_varlen(qc, kc, vc, out, lse, doc, p, sl, delta=delta)
+    torch.cuda.synchronize()
+    got = delta.cpu().double().numpy()
+    o64 = out.cpu().double().numpy()
+    d64 = do.double().numpy()
+    valid = np.ones(got.shape, dtype=bool)
+    if lens is not None:
+        for b, L in enumerate(lens):
+            valid[b, :, L:] = False
+            d64[b, :, L:] = 0.0
+    ref = np.einsum("bhnd,bhnd->bhn", o64, d64)
+    mag = np.einsum("bhnd,bhnd->bhn", np.abs(o64), np.abs(d64))
+    assert not np.isnan(got).any(), "unwritten or NaN rows of Delta"
+    assert np.all(got[~valid] == 0.0), "rows beyond an entry's length are not 0"
+    err = np.abs(got - ref)[valid]
+    bound = (1e-5 * mag + 1e-30)[valid]
+    say(f"  max|err| = {err.max():.3e}, worst err/bound = {(err / bound).max():.3f}")
+    assert np.all(err <= bound)
+
+
 def test_backward_launch_queues_over_many_calls():
     """The dQ and dK/dV launch queues (the last eighth of each XCD's rows
     drained by workgroups of any XCD, counters taken per launch in turn from
