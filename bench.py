@@ -249,8 +249,25 @@ def dynamic_plan_context():
                      "host_plan_ms": round(host_ms, 2),
                      "device_plan_us": round(e0.elapsed_time(e1) * 1e3 / 20, 1),
                      "nnz_matches_host": int(nnz.item()) == hp.info["nnz"]}
+        # The forward through each plan (same bitmap, same inputs), alternating.
+        q, k, v = wl.make_qkv(cw, "cuda")
+        out, lse = bsattn.forward(q, k, v, hp)
+        ms = {"static": [], "dynamic": []}
+        for _ in range(3):
+            for kind, pl in (("static", hp), ("dynamic", dp)):
+                bsattn.forward(q, k, v, pl, out, lse)
+                torch.cuda.synchronize()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(5):
+                    bsattn.forward(q, k, v, pl, out, lse)
+                b.record()
+                torch.cuda.synchronize()
+                ms[kind].append(a.elapsed_time(b) / 5)
+        res[name]["forward_static_ms"] = round(float(np.median(ms["static"])), 4)
+        res[name]["forward_dynamic_ms"] = round(float(np.median(ms["dynamic"])), 4)
         log(f"[bench] dynamic plan {name}: {res[name]}")
-        del dbm, dp, hp
+        del dbm, dp, hp, q, k, v, out, lse
     res["backward_long_columns"] = dynamic_backward_context()
     return res
 
