@@ -394,19 +394,21 @@ void build_work(Plan& P) {
     // batch entries the next, so every XCD's run holds all batch entries of
     // its KV heads: entries of different lengths (a variable-length batch)
     // load the XCDs evenly.
-    // For a bitmap, neighbouring q-blocks share no more K/V blocks than any
-    // two others, so a head's q-blocks are taken longest row first instead:
-    // the workgroups that run together on an XCD then have rows of about the
-    // same length, start and end about together, and sweep the head's key
-    // blocks (in ascending order) at the same pace, so the blocks they read
-    // at a time stay few enough for the XCD's L2.
+    // For a bitmap without the causal cut, neighbouring q-blocks share no
+    // more K/V blocks than any two others, so a head's q-blocks are taken
+    // longest row first instead: the workgroups that run together on an XCD
+    // then have rows of about the same length, start and end about together,
+    // and sweep the head's key blocks (in ascending order) at the same pace,
+    // so the blocks they read at a time stay few enough for the XCD's L2.
+    // Under the causal cut a row's length already grows with its q-block,
+    // and the ascending order measured faster.
     std::vector<int32_t> loc;
     loc.reserve(items);
     std::vector<int32_t> order(nb);
     for (int64_t hk = 0; hk < H / group; ++hk)
       for (int64_t b = 0; b < B; ++b) {
         std::iota(order.begin(), order.end(), 0);
-        if (P.from_bitmap && !P.dynamic) {
+        if (P.from_bitmap && !P.dynamic && !P.causal) {
           const int64_t h0 = hk * group;
           std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
             return cost((b * H + h0) * nb + x) > cost((b * H + h0) * nb + y);
