@@ -34,7 +34,7 @@ SCHEDULE_DEFAULT, SCHEDULE_XCD, SCHEDULE_LPT, SCHEDULE_ROWMAJOR = 0, 1, 2, 3
 EXPORTS = ("bsa_plan", "bsa_plan_host", "bsa_plan_destroy", "bsa_plan_csr", "bsa_plan_get_info",
            "bsa_plan_work", "bsa_plan_active_blocks", "bsa_plan_dynamic", "bsa_plan_set_bitmap",
            "bsa_plan_read_csr", "bsa_plan_read_csr_transposed", "bsa_forward",
-           "bsa_plan_csr_transposed", "bsa_plan_work_kv", "bsa_plan_read_work_kv",
+           "bsa_plan_csr_transposed", "bsa_plan_work_kv", "bsa_plan_read_work", "bsa_plan_read_work_kv",
            "bsa_backward", "bsa_backward_noalloc", "bsa_forward_varlen", "bsa_backward_varlen", "bsa_lse_merge",
            "bsa_status_string", "bsa_last_error",
            "bsa_abi_version")
@@ -98,6 +98,7 @@ def lib():
     L.bsa_plan_csr_transposed.argtypes = [P, c_int32, POINTER(POINTER(c_int32)), POINTER(POINTER(c_int32)),
                                           POINTER(POINTER(c_uint8)), POINTER(c_int64)]
     L.bsa_plan_work_kv.argtypes = [P, POINTER(POINTER(c_int32)), POINTER(c_int64)]
+    L.bsa_plan_read_work.argtypes = [P, c_void_p, c_int64, POINTER(c_int64)]
     L.bsa_plan_read_work_kv.argtypes = [P, c_void_p, c_int64, POINTER(c_int64), POINTER(c_int64)]
     L.bsa_backward.argtypes = [c_void_p] * 6 + [P] + [c_void_p] * 5
     L.bsa_backward_noalloc.argtypes = [c_void_p] * 6 + [P] + [c_void_p] * 4
@@ -112,7 +113,7 @@ def lib():
     L.bsa_abi_version.restype = c_int32
     for name in ("bsa_plan", "bsa_plan_host", "bsa_plan_csr", "bsa_plan_get_info", "bsa_plan_work",
                  "bsa_plan_dynamic", "bsa_plan_set_bitmap", "bsa_plan_read_csr", "bsa_plan_read_csr_transposed",
-                 "bsa_forward", "bsa_plan_csr_transposed", "bsa_plan_work_kv", "bsa_plan_read_work_kv", "bsa_backward", "bsa_forward_varlen",
+                 "bsa_forward", "bsa_plan_csr_transposed", "bsa_plan_work_kv", "bsa_plan_read_work", "bsa_plan_read_work_kv", "bsa_backward", "bsa_forward_varlen",
                  "bsa_backward_varlen", "bsa_lse_merge"):
         getattr(L, name).restype = c_int32
     _lib = L
@@ -256,6 +257,15 @@ class Plan:
         n = c_int64()
         _check(lib().bsa_plan_work_kv(self.handle, ctypes.byref(w), ctypes.byref(n)))
         return np.ctypeslib.as_array(w, (n.value,)).copy() if n.value else np.zeros(0, np.int32)
+
+    def read_work(self):
+        """bsa_plan_read_work: the forward's launch order as the device holds it
+        (for a dynamic plan, as the last set_bitmap left it)."""
+        n = len(self.work())
+        w = np.zeros(max(n, 1), np.int32)
+        slots = c_int64()
+        _check(lib().bsa_plan_read_work(self.handle, w.ctypes.data, n, ctypes.byref(slots)))
+        return w[:slots.value]
 
     def read_work_kv(self):
         """bsa_plan_read_work_kv: the dK/dV launch descriptors on the device, an

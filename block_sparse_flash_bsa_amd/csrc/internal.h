@@ -107,6 +107,13 @@ struct bsa_plan {
   int64_t entry_capacity = 0;
   int32_t* d_counts = nullptr;
   int64_t* d_scan = nullptr;
+  // Dynamic plans without the causal cut: bsa_plan_set_bitmap reorders each
+  // (KV head, batch entry) run of the launch order longest row first, as
+  // build_work does for a static bitmap plan.  d_work_base is the order at
+  // creation (q-blocks ascending), d_order [Hkv * nb] the q-blocks of each
+  // KV head's run by descending row length; d_work is rewritten from both.
+  const int32_t* d_work_base = nullptr;
+  int32_t* d_order = nullptr;
 };
 
 namespace bsa {

@@ -648,7 +648,13 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
   const size_t off_reduce = off_pre + up(kv_cols * sizeof(int64_t));
   const size_t off_head = off_reduce + up(size_t(P->kv_partials) * sizeof(Plan::KvDesc));
   const size_t off_queue = off_head + up(8 * sizeof(int32_t));
-  const size_t bytes = off_queue + bsa::kQueueBytes;
+  // Without the causal cut the launch order is re-sorted per bitmap (longest
+  // row first): the order at creation and the per-KV-head q-block order.
+  const bool reorder = !P->causal && !P->work.empty() &&
+                       (P->prob.schedule == BSA_SCHEDULE_DEFAULT || P->prob.schedule == BSA_SCHEDULE_XCD);
+  const size_t off_work_base = off_queue + up(bsa::kQueueBytes);
+  const size_t off_order = off_work_base + up((reorder ? P->work.size() : 0) * sizeof(int32_t));
+  const size_t bytes = off_order + (reorder ? size_t(problem->num_kv_heads) * P->nb * sizeof(int32_t) : 0);
   hipError_t err = hipMalloc(&P->dev_mem, bytes);
   if (err != hipSuccess) {
     P->dev_mem = nullptr;
@@ -657,12 +663,14 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
                 "hipMalloc(%zu) for the dynamic plan failed: %s", bytes, hipGetErrorString(err));
   }
   auto* base = static_cast<unsigned char*>(P->dev_mem);
-  // Empty rows and columns until the first bitmap arrives; the launch orders
-  // never change.
+  // Empty rows and columns until the first bitmap arrives; the dK/dV order
+  // never changes, the forward's only as above.
   err = hipMemset(base, 0, off_counts);
   if (err == hipSuccess) err = hipMemset(base + off_cols, 0, rows * sizeof(bsa::RowDesc));
   if (err == hipSuccess && !P->work.empty())
     err = hipMemcpy(base + off_work, P->work.data(), P->work.size() * sizeof(int32_t), hipMemcpyHostToDevice);
+  if (err == hipSuccess && reorder)
+    err = hipMemcpy(base + off_work_base, P->work.data(), P->work.size() * sizeof(int32_t), hipMemcpyHostToDevice);
   if (err == hipSuccess && !P->kv_desc.empty())
     err = hipMemcpy(base + off_work_kv, P->kv_desc.data(), P->kv_desc.size() * sizeof(Plan::KvDesc),
                     hipMemcpyHostToDevice);
@@ -702,6 +710,10 @@ bsa_status_t make_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layo
   P->d_kv_head = reinterpret_cast<int32_t*>(base + off_head);
   P->d_queue = reinterpret_cast<int32_t*>(base + off_queue);
   P->d_kv_count = P->d_kv_head + 4;
+  if (reorder) {
+    P->d_work_base = reinterpret_cast<const int32_t*>(base + off_work_base);
+    P->d_order = reinterpret_cast<int32_t*>(base + off_order);
+  }
   if (split) {
     P->d_kv_slot = reinterpret_cast<const int32_t*>(base + off_slot);
     P->d_kv_walk = reinterpret_cast<int32_t*>(base + off_walk);

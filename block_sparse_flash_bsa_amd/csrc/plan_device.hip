@@ -406,6 +406,72 @@ __global__ __launch_bounds__(kWriteThreads) void kv_split_write(const int32_t* _
   reduce[b * s_b + r0] = make_int4(int(t), pb, k, 0);
 }
 
+// Launch order of a dynamic plan without the causal cut, longest row first
+// within each (KV head, batch entry) run, as the host planner orders the
+// q-blocks of a static bitmap plan (the workgroups that run together on an
+// XCD then have rows of about the same length and sweep the key blocks at
+// the same pace).  order_rows: one workgroup per KV head ranks the q-blocks
+// of its group's first query head's layout by descending row length, a
+// counting sort over kOrderBuckets buckets (lengths from kOrderBuckets - 1 up
+// share the last); the order inside a bucket is whatever the atomics give,
+// which changes only which slot runs a q-block, not what it computes.
+constexpr int kOrderThreads = 256;
+constexpr int kOrderBuckets = 1024;
+__global__ __launch_bounds__(kOrderThreads) void order_rows(const RowDesc* __restrict__ rows, int nb, int group,
+                                                            int per_head, int32_t* __restrict__ order) {
+  __shared__ int hist[kOrderBuckets];
+  __shared__ int part[kOrderThreads];
+  const int hk = blockIdx.x;
+  const RowDesc* r = rows + size_t(per_head ? hk * group : 0) * nb;
+  for (int x = threadIdx.x; x < kOrderBuckets; x += kOrderThreads) hist[x] = 0;
+  __syncthreads();
+  auto key = [](int c) { return kOrderBuckets - 1 - (c < kOrderBuckets - 1 ? c : kOrderBuckets - 1); };
+  for (int i = threadIdx.x; i < nb; i += kOrderThreads) atomicAdd(&hist[key(r[i].count)], 1);
+  __syncthreads();
+  // Exclusive scan of the buckets: each thread sums its 4, the 256 partial
+  // sums are scanned in place, then each thread writes its 4 offsets.
+  constexpr int kPer = kOrderBuckets / kOrderThreads;
+  const int t = threadIdx.x;
+  int local = 0;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) local += hist[t * kPer + u];
+  part[t] = local;
+  __syncthreads();
+  for (int off = 1; off < kOrderThreads; off <<= 1) {
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - local;
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int c = hist[t * kPer + u];
+    hist[t * kPer + u] = run;
+    run += c;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < nb; i += kOrderThreads) order[size_t(hk) * nb + atomicAdd(&hist[key(r[i].count)], 1)] = i;
+}
+
+// work[s] = work_base[s] with its q-block i replaced by the i-th of its KV
+// head's order (idle slots stay idle).
+__global__ __launch_bounds__(kOrderThreads) void reorder_work(const int32_t* __restrict__ base, int64_t slots,
+                                                              int nb, int H, int group,
+                                                              const int32_t* __restrict__ order,
+                                                              int32_t* __restrict__ work) {
+  const int64_t s = int64_t(blockIdx.x) * kOrderThreads + threadIdx.x;
+  if (s >= slots) return;
+  const int32_t item = base[s];
+  if (item < 0) {
+    work[s] = -1;
+    return;
+  }
+  const int i = item % nb, bh = item / nb;
+  const int hk = (bh % H) / group;
+  work[s] = bh * nb + order[size_t(hk) * nb + i];
+}
+
 }  // namespace
 }  // namespace bsa
 
@@ -456,6 +522,16 @@ extern "C" bsa_status_t bsa_plan_set_bitmap(bsa_plan_t plan, const uint8_t* d_bi
   const int tail = plan->prob.seq_len % plan->prob.block_size != 0 ? nb - 1 : -1;
   hipLaunchKernelGGL(fill_rows, dim3(unsigned(rows)), dim3(kRowThreads), 0, s, d_bitmap, nb, plan->causal, tail,
                      d_rows, d_entries);
+  if (plan->d_work_base) {
+    // Longest row first within each (KV head, batch entry) run of the order.
+    const int hkv = plan->prob.num_kv_heads, group = plan->prob.num_heads / hkv;
+    const int64_t slots = int64_t(plan->work.size());
+    hipLaunchKernelGGL(order_rows, dim3(unsigned(hkv)), dim3(kOrderThreads), 0, s, d_rows, nb, group,
+                       plan->layout_heads > 1 ? 1 : 0, plan->d_order);
+    hipLaunchKernelGGL(reorder_work, dim3(unsigned((slots + kOrderThreads - 1) / kOrderThreads)),
+                       dim3(kOrderThreads), 0, s, plan->d_work_base, slots, nb, plan->prob.num_heads, group,
+                       plan->d_order, const_cast<int32_t*>(plan->d_work));
+  }
   // The same entries per k-block column, for the backward's dK/dV walk.
   auto* d_cols = const_cast<RowDesc*>(plan->d_cols);
   auto* d_entries_t = const_cast<int32_t*>(plan->d_entries_t);
@@ -552,6 +628,23 @@ extern "C" bsa_status_t bsa_plan_read_csr_transposed(bsa_plan_t plan, int32_t la
   bsa::clear_error();
   return bsa::read_device_csr(plan, plan ? plan->d_cols : nullptr, plan ? plan->d_entries_t : nullptr,
                               layout_head, col_ptr, row_idx, flags, capacity, nnz);
+}
+
+extern "C" bsa_status_t bsa_plan_read_work(bsa_plan_t plan, int32_t* work, int64_t capacity, int64_t* slots) {
+  using namespace bsa;
+  clear_error();
+  if (!plan || !slots || (capacity > 0 && !work)) return fail(BSA_ERR_INVALID_ARGUMENT, "NULL argument to bsa_plan_read_work");
+  if (!plan->info.on_device)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "plan was built by bsa_plan_host and has no device copy");
+  const int64_t n = int64_t(plan->work.size());
+  if (capacity < n)
+    return fail(BSA_ERR_INVALID_ARGUMENT, "capacity %lld is below the plan's %lld launch slots", (long long)capacity,
+                (long long)n);
+  if (hipDeviceSynchronize() != hipSuccess ||
+      (n && hipMemcpy(work, plan->d_work, size_t(n) * sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess))
+    return fail(BSA_ERR_DEVICE, "reading the launch order failed: %s", hipGetErrorString(hipGetLastError()));
+  *slots = n;
+  return BSA_OK;
 }
 
 extern "C" bsa_status_t bsa_plan_read_work_kv(bsa_plan_t plan, int32_t* desc, int64_t capacity, int64_t* slots,

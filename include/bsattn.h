@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define BSA_ABI_VERSION 6
+#define BSA_ABI_VERSION 7
 
 /* Status codes.  Every entry point that can fail returns one; no exception
  * crosses the ABI.  Out-parameters are written only on BSA_OK. */
@@ -224,8 +224,8 @@ int64_t bsa_plan_active_blocks(bsa_plan_t plan);
  * forward writes O = 0 and LSE = -inf.  Count fields of bsa_plan_info_t that
  * depend on the bitmap (nnz, nnz_partial, active_blocks, allowed_pairs,
  * max_row_entries) are -1 and bsa_plan_active_blocks returns -1;
- * bsa_plan_work returns the fixed launch order, bsa_plan_csr fails with
- * INVALID_ARGUMENT (bsa_plan_read_csr copies the device CSR back).
+ * bsa_plan_work returns the launch order at creation, bsa_plan_csr fails
+ * with INVALID_ARGUMENT (bsa_plan_read_csr copies the device CSR back).
  * Errors: INVALID_ARGUMENT, UNSUPPORTED, OUT_OF_MEMORY, DEVICE, as bsa_plan. */
 bsa_status_t bsa_plan_dynamic(const bsa_problem_t* problem, const bsa_layout_t* layout,
                               bsa_plan_t* out_plan);
@@ -238,9 +238,14 @@ bsa_status_t bsa_plan_dynamic(const bsa_problem_t* problem, const bsa_layout_t* 
  * same stream (or after synchronisation) uses the new CSR.  If d_nnz is not
  * NULL it is a device pointer to one int64_t that receives the total number
  * of entries over all layout heads (multiply by batch, and by num_heads when
- * bitmap_heads == 1, for the tiles one forward computes).  The bitmap is read
- * only during the call's kernels; the caller keeps ownership.  Nothing is
- * allocated.
+ * bitmap_heads == 1, for the tiles one forward computes).  For a plan without
+ * the causal cut on the default (XCD) schedule it also re-sorts the launch
+ * order: within each (KV head, batch entry) run, q-blocks go longest row
+ * first (row lengths of the group's first query head's layout, bucketed, in
+ * no fixed order within a bucket), as bsa_plan orders the q-blocks of a
+ * static bitmap plan; results do not depend on the order
+ * (bsa_plan_read_work copies it back).  The bitmap is read only during the
+ * call's kernels; the caller keeps ownership.  Nothing is allocated.
  * Errors (before anything is launched): INVALID_ARGUMENT for a NULL plan or
  * bitmap, a plan that is not dynamic, a bitmap or plan on another device, or
  * a bitmap pointer that is not device memory; DEVICE if a launch fails. */
@@ -331,6 +336,15 @@ bsa_status_t bsa_plan_csr_transposed(bsa_plan_t plan, int32_t layout_head, const
  * as idle, the other slots as the items' fixed order.  Plan-owned.
  * Errors: INVALID_ARGUMENT for NULL pointers. */
 bsa_status_t bsa_plan_work_kv(bsa_plan_t plan, const int32_t** work, int64_t* slots);
+
+/* The forward's (and dQ's) launch order as the device holds it
+ * (synchronous: waits for the device): work [slots] in the format of
+ * bsa_plan_work.  For a dynamic plan this is the order the last
+ * bsa_plan_set_bitmap left (see there).  capacity is the room in work, in
+ * slots (bsa_plan_work gives the count).
+ * Errors: INVALID_ARGUMENT for NULL pointers, a host-only plan or too small a
+ * capacity; DEVICE if the copy fails. */
+bsa_status_t bsa_plan_read_work(bsa_plan_t plan, int32_t* work, int64_t capacity, int64_t* slots);
 
 /* The dK/dV launch descriptors as the device holds them (synchronous: waits
  * for the device): desc [slots][4] int32 = {item, first walk entry, end

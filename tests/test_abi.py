@@ -603,3 +603,17 @@ def test_binding_rejects_bad_out_and_lse_before_any_launch():
         bsattn.forward_varlen(q, k, v, p, torch.zeros(B, dtype=torch.int32), good_out, good_lse)
     with pytest.raises(ValueError):       # q in host memory
         bsattn.forward(torch.empty((B, H, N, D), dtype=bf), k, v, p, good_out, good_lse)
+
+
+def test_read_work_argument_errors():
+    """bsa_plan_read_work refuses NULL arguments and host-only plans before any
+    device call."""
+    L = bsattn.lib()
+    hp = bsattn.plan(1, 2, 2, 1024, 128, 128, torch.bfloat16, spec(True, "tokens", 300), host_only=True)
+    w = np.zeros(64, np.int32)
+    n = ctypes.c_int64()
+    assert L.bsa_plan_read_work(None, w.ctypes.data, 64, ctypes.byref(n)) == bsattn.ERR_INVALID_ARGUMENT
+    assert L.bsa_plan_read_work(hp.handle, w.ctypes.data, 64, None) == bsattn.ERR_INVALID_ARGUMENT
+    assert L.bsa_plan_read_work(hp.handle, None, 64, ctypes.byref(n)) == bsattn.ERR_INVALID_ARGUMENT
+    assert L.bsa_plan_read_work(hp.handle, w.ctypes.data, 64, ctypes.byref(n)) == bsattn.ERR_INVALID_ARGUMENT
+    assert b"bsa_plan_host" in L.bsa_last_error()

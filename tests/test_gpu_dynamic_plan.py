@@ -151,6 +151,63 @@ def test_forward_through_dynamic_plan_is_bitwise_the_static_one():
         assert np.array_equal(np.isfinite(l2[idx].cpu().numpy()), fin)
 
 
+@pytest.mark.parametrize("lh", [1, 4])
+def test_dynamic_order_is_longest_row_first(lh):
+    """bsa_plan_set_bitmap re-sorts the launch order of a dynamic plan without
+    the causal cut: every slot keeps its (b, h) (so its XCD run), the q-blocks
+    of each (b, h) appear once each, and along each (KV head, batch entry) run
+    of the order at creation the row lengths of the group's first head come
+    non-increasing; a causal plan keeps its order; the forward through the
+    re-sorted plan into NaN-poisoned outputs equals the static plan's bit for
+    bit."""
+    B, H, Hkv, nb, bs = 2, 4, 2, 64, 128
+    group = H // Hkv
+    rng = np.random.default_rng(21 + lh)
+    dens = rng.random((lh, nb, 1)) * 0.5          # rows of very different lengths
+    bm = (rng.random((lh, nb, nb)) < dens).astype(np.uint8)
+    bm[:, np.arange(nb), np.arange(nb)] = 1
+    w = wl.WORKLOADS["random32k"].with_shape(name="order", batch=B, heads=H, kv_heads=Hkv, seq_len=nb * bs)
+    for causal in (False, True):
+        dp = bsattn.plan_dynamic(B, H, Hkv, nb * bs, 128, bs, torch.bfloat16, causal, lh)
+        base = dp.work()
+        dp.set_bitmap(torch.from_numpy(bm).cuda())
+        got = dp.read_work()
+        assert got.shape == base.shape
+        assert np.array_equal(got < 0, base < 0)
+        live = base >= 0
+        if causal:
+            assert np.array_equal(got, base), "a causal dynamic plan keeps its order"
+            continue
+        assert np.array_equal(got[live] // nb, base[live] // nb), "a slot changed its (b, h)"
+        for bh in range(B * H):
+            qs = np.sort(got[live][got[live] // nb == bh] % nb)
+            assert np.array_equal(qs, np.arange(nb)), f"(b, h) {bh}: q-blocks not a permutation"
+        # Position of each slot in the order at creation: (KV head, batch entry,
+        # q-block, group member), outer to inner.
+        it = base[live]
+        i0, bh0 = it % nb, it // nb
+        h0, b0 = bh0 % H, bh0 // H
+        pos = ((h0 // group * B + b0) * nb + i0) * group + h0 % group
+        srt = np.argsort(pos)
+        new_i = (got[live] % nb)[srt]
+        hk_s = (h0 // group)[srt]
+        b_s = b0[srt]
+        lens = bm.sum(axis=2).astype(np.int64)       # [lh, nb] row lengths (no causal cut)
+        for hk in range(Hkv):
+            head = hk * group if lh > 1 else 0
+            for b in range(B):
+                seq = np.minimum(lens[head][new_i[(hk_s == hk) & (b_s == b)]], 1023)
+                assert np.all(np.diff(seq) <= 0), f"run (hk {hk}, b {b}) not longest first"
+        q, k, v = (x.cuda() for x in wl.make_qkv(w, "cpu"))
+        sp = bsattn.plan(B, H, Hkv, nb * bs, 128, bs, torch.bfloat16, bitmap_layout(bm, False))
+        o1, l1 = bsattn.forward(q, k, v, sp)
+        o2 = torch.full_like(o1, float("nan"))
+        l2 = torch.full_like(l1, float("nan"))
+        bsattn.forward(q, k, v, dp, o2, l2)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
 def test_new_bitmap_replaces_the_old_one():
     nb, bs, H = 48, 64, 2
     dp = bsattn.plan_dynamic(1, H, H, nb * bs, 64, bs, torch.float32, False, 1)
