@@ -806,9 +806,12 @@ __global__ __launch_bounds__(kThreads) void bwd_kv_reduce(BwdParams p) {
 // ---------------------------------------------------------------------------
 constexpr int kF32Lanes = 4;
 
+// Sum over the kF32Lanes (4) lanes of each aligned lane quad: butterfly
+// exchanges with lanes l ^ 1 and l ^ 2 through DPP quad permutations, which
+// move values between lanes inside the VALU instead of through LDS.
 __device__ __forceinline__ float quad_sum(float a) {
-#pragma unroll
-  for (int w = 1; w < kF32Lanes; w *= 2) a += __shfl_xor(a, w);
+  a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false));
+  a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0x4E, 0xF, 0xF, false));
   return a;
 }
 
@@ -890,8 +893,13 @@ __global__ __launch_bounds__(BS * kF32Lanes) void bwd_dq_f32(BwdParams p) {
       }
       __syncthreads();
       for (int kk = 0; kk < KT; ++kk) {
-        const float* kr = Ks + kk * D + sl * DL;
-        const float* vr = Vs + kk * D + sl * DL;
+        // This lane's slices of the key's K and V rows, 16 bytes per LDS read.
+        float kr[DL], vr[DL];
+#pragma unroll
+        for (int d4 = 0; d4 < DL / 4; ++d4) {
+          *reinterpret_cast<float4*>(kr + 4 * d4) = reinterpret_cast<const float4*>(Ks + kk * D + sl * DL)[d4];
+          *reinterpret_cast<float4*>(vr + 4 * d4) = reinterpret_cast<const float4*>(Vs + kk * D + sl * DL)[d4];
+        }
         float a = 0.f, c = 0.f;
 #pragma unroll
         for (int d = 0; d < DL; ++d) {
@@ -976,8 +984,13 @@ __global__ __launch_bounds__(BS * kF32Lanes) void bwd_dkdv_f32(BwdParams p) {
         }
         __syncthreads();
         for (int qq = 0; qq < QT; ++qq) {
-          const float* qr = Qs + qq * D + sl * DL;
-          const float* dr = dOs + qq * D + sl * DL;
+          // This lane's slices of the query's Q and dO rows, 16 bytes per LDS read.
+          float qr[DL], dr[DL];
+#pragma unroll
+          for (int d4 = 0; d4 < DL / 4; ++d4) {
+            *reinterpret_cast<float4*>(qr + 4 * d4) = reinterpret_cast<const float4*>(Qs + qq * D + sl * DL)[d4];
+            *reinterpret_cast<float4*>(dr + 4 * d4) = reinterpret_cast<const float4*>(dOs + qq * D + sl * DL)[d4];
+          }
           float a = 0.f, c = 0.f;
 #pragma unroll
           for (int d = 0; d < DL; ++d) {

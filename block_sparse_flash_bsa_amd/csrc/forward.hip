@@ -592,6 +592,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
 // 64-key stages.
 // ---------------------------------------------------------------------------
 constexpr int kF32Lanes = 4;   // lanes per query row
+static_assert(kF32Lanes == 4, "quad_sum reduces over lane quads");
+
+// Sum over the kF32Lanes (4) lanes of each aligned lane quad: butterfly
+// exchanges with lanes l ^ 1 and l ^ 2 through DPP quad permutations, which
+// move values between lanes inside the VALU instead of through LDS.
+__device__ __forceinline__ float quad_sum(float a) {
+  a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0xB1, 0xF, 0xF, false));
+  a += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, a), 0x4E, 0xF, 0xF, false));
+  return a;
+}
 
 template <int D, int BS>
 __global__ __launch_bounds__(BS * kF32Lanes) void fwd_f32(FwdParams p) {
@@ -658,12 +668,17 @@ __global__ __launch_bounds__(BS * kF32Lanes) void fwd_f32(FwdParams p) {
         float s[16];
 #pragma unroll
         for (int kk = 0; kk < 16; ++kk) {
-          const float* kr = Ks + (kc + kk) * D + sl * DL;
+          const float4* kr = reinterpret_cast<const float4*>(Ks + (kc + kk) * D + sl * DL);   // 16-byte aligned
           float a = 0.f;
 #pragma unroll
-          for (int d = 0; d < DL; ++d) a = fmaf(qv[d], kr[d], a);
-#pragma unroll
-          for (int w = 1; w < kF32Lanes; w *= 2) a += __shfl_xor(a, w);
+          for (int d4 = 0; d4 < DL / 4; ++d4) {
+            const float4 kx = kr[d4];
+            a = fmaf(qv[4 * d4], kx.x, a);
+            a = fmaf(qv[4 * d4 + 1], kx.y, a);
+            a = fmaf(qv[4 * d4 + 2], kx.z, a);
+            a = fmaf(qv[4 * d4 + 3], kx.w, a);
+          }
+          a = quad_sum(a);
           const int64_t kk_g = k0 + kc + kk;
           s[kk] = (partial && (kk_g >= Nb || qg >= Nb || !allowed(p, qg, kk_g))) ? -INFINITY : a * c;
         }
@@ -682,9 +697,15 @@ __global__ __launch_bounds__(BS * kF32Lanes) void fwd_f32(FwdParams p) {
         for (int kk = 0; kk < 16; ++kk) {
           const float pv = __builtin_amdgcn_exp2f(s[kk] - msub);
           l += pv;
-          const float* vr = Vs + (kc + kk) * D + sl * DL;
+          const float4* vr = reinterpret_cast<const float4*>(Vs + (kc + kk) * D + sl * DL);
 #pragma unroll
-          for (int d = 0; d < DL; ++d) acc[d] = fmaf(pv, vr[d], acc[d]);
+          for (int d4 = 0; d4 < DL / 4; ++d4) {
+            const float4 vx = vr[d4];
+            acc[4 * d4] = fmaf(pv, vx.x, acc[4 * d4]);
+            acc[4 * d4 + 1] = fmaf(pv, vx.y, acc[4 * d4 + 1]);
+            acc[4 * d4 + 2] = fmaf(pv, vx.z, acc[4 * d4 + 2]);
+            acc[4 * d4 + 3] = fmaf(pv, vx.w, acc[4 * d4 + 3]);
+          }
         }
       }
     }
