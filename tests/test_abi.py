@@ -161,6 +161,44 @@ def test_xcd_schedule_takes_bitmap_rows_longest_first():
             assert np.all(np.diff(ii)[ties] > 0)
 
 
+def test_xcd_schedule_of_bitmaps_cuts_runs_by_item_count():
+    """A bitmap plan's XCD runs hold equal item counts, so whole (head, batch
+    entry) runs sit on one XCD when they divide evenly (the random 32K layout:
+    32 runs over 8 XCDs, 4 each)."""
+    w = wl.WORKLOADS["random32k"]
+    p = host_plan(w, schedule=bsattn.SCHEDULE_XCD)
+    work = p.work()
+    nb, H = w.num_blocks, w.heads
+    counts, owners = [], {}
+    for x in range(8):
+        run = work[x::8]
+        run = run[run >= 0]
+        counts.append(len(run))
+        for g in np.unique((run // (nb * H)) + w.batch * ((run // nb) % H)):
+            owners.setdefault(int(g), set()).add(x)
+    assert max(counts) - min(counts) <= 1
+    assert all(len(v) == 1 for v in owners.values()), "a (head, batch entry) run spans two XCDs"
+
+
+def test_xcd_schedule_keeps_causal_bitmap_rows_ascending():
+    """Under the causal cut a bitmap plan keeps each head's q-blocks in
+    ascending order (a row's length grows with its q-block anyway)."""
+    nb, H, B = 64, 4, 2
+    rng = np.random.default_rng(4)
+    bm = (rng.random((H, nb, nb)) < 0.3).astype(np.uint8)
+    bm[:, np.arange(nb), np.arange(nb)] = 1
+    lay = dict(causal=True, unit="blocks", window_left=-1, window_right=-1, global_keys=0, global_queries=0,
+               bitmap=bm)
+    p = bsattn.plan(B, H, H, nb * 128, 128, 128, torch.bfloat16, lay, host_only=True)
+    work = p.work()
+    for x in range(8):
+        run = work[x::8]
+        run = run[run >= 0]
+        i, grp = run % nb, run // nb
+        for g in np.unique(grp):
+            assert np.all(np.diff(i[grp == g]) > 0)
+
+
 def test_lpt_schedule_is_longest_first():
     w = wl.WORKLOADS["random32k"]
     p = host_plan(w, schedule=bsattn.SCHEDULE_LPT)
