@@ -90,7 +90,7 @@ typedef int32_t bsa_status_t;
  *     every tile touching that block is PARTIAL.  The FAQ of "The Only Guide
  *     You Need for Sparse Attention Kernels in Long-Context LLMs" answers the
  *     variable-length question by padding to the block size; this does that
- *     padding inside the kernels.  Dynamic plans need a multiple of the block.
+ *     padding inside the kernels, for static and dynamic plans alike.
  *   block_size: layout block = kernel tile height and width.
  *   Supported (dtype, head_dim, block_size):
  *     BSA_BF16: (128, 128)                    -- MFMA kernel
