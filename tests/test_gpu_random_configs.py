@@ -117,3 +117,64 @@ def test_random_problem_against_oracle(case):
         err = float(np.abs(g - r).max())
         say(f"  {name}: max|err| {err:.2e}, {err / scale:.2e} of max|ref|")
         assert err <= rel * scale, f"{name}: {err} > {rel} * {scale}"
+
+
+VARLEN_CASES = 24
+
+
+@pytest.mark.parametrize("case", range(VARLEN_CASES))
+def test_random_variable_length_batch_against_oracle(case):
+    """The same draws as a padded batch of 2 to 4 entries with random lengths
+    (0 to N): each entry's rows match the oracle on its trimmed sequence,
+    rows beyond its length are empty (O = 0, LSE = -inf) and their gradients
+    zero, and NaN padding of the inputs is never read."""
+    w, lay = draw(1000 + case)
+    rng = np.random.default_rng(9000 + case)
+    w = w.with_shape(batch=int(rng.integers(2, 5)))
+    lens = [int(x) for x in rng.integers(0, w.seq_len + 1, size=w.batch)]
+    lens[int(rng.integers(0, w.batch))] = w.seq_len          # one entry at full length
+    say(f"[random varlen {case}] {describe(w, lay)} lens={lens}")
+    q, k, v = wl.make_qkv(w, "cpu")
+    do = wl.make_dout(w, "cpu")
+    for b, L in enumerate(lens):
+        for t in (q, k, v, do):
+            t[b, :, L:] = float("nan")
+    p = bsattn.plan(w.batch, w.heads, w.kv_heads, w.seq_len, w.head_dim, w.block, w.dtype, lay)
+    sl = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    qc, kc, vc, doc = q.cuda(), k.cuda(), v.cuda(), do.cuda()
+    out, lse = bsattn.forward_varlen(qc, kc, vc, p, sl)
+    backward = case % 2 == 0
+    if backward:
+        dq, dk, dv = bsattn.backward_varlen(qc, kc, vc, out, lse, doc, p, sl)
+    torch.cuda.synchronize()
+    O = out.float().cpu().numpy().astype(np.float64)
+    L_ = lse.cpu().numpy().astype(np.float64)
+    to, tl = (2e-2, 1e-3) if w.dtype == torch.bfloat16 else (1e-5, 1e-5)
+    rel = 1e-2 if w.dtype == torch.bfloat16 else 1e-5
+    grads = tuple(x.float().cpu().numpy().astype(np.float64) for x in (dq, dk, dv)) if backward else ()
+    for b, L in enumerate(lens):
+        assert np.all(O[b, :, L:] == 0) and np.all(L_[b, :, L:] == -np.inf), f"entry {b}: rows beyond {L}"
+        for g in grads:
+            assert np.all(g[b, :, L:] == 0), f"entry {b}: gradient rows beyond {L}"
+        if L == 0:
+            continue
+        ly = dict(lay)
+        if ly.get("bitmap") is not None:
+            nbl = -(-L // w.block)
+            ly["bitmap"] = ly["bitmap"][:, :nbl, :nbl]
+        sb = (slice(b, b + 1), slice(None), slice(0, L))
+        O_ref, L_ref = oracle.forward(q[sb], k[sb], v[sb], ly, w.block)
+        fin = np.isfinite(L_ref)
+        Ob, Lb = O[sb], L_[sb]
+        assert np.array_equal(np.isfinite(Lb), fin), f"entry {b}: empty-row pattern differs"
+        eo = float(np.abs(Ob - O_ref).max())
+        el = float(np.abs(Lb[fin] - L_ref[fin]).max()) if fin.any() else 0.0
+        say(f"  entry {b} (L={L}): max|dO| {eo:.2e}, max|dLSE| {el:.2e}")
+        assert eo <= to and el <= tl
+        if backward:
+            ref = oracle.backward(q[sb], k[sb], v[sb], do[sb], ly, w.block)
+            for name, g, r in zip(("dQ", "dK", "dV"), grads, ref):
+                amax = float(np.abs(r).max())
+                scale = max(amax, 1e-30) if w.dtype == torch.bfloat16 else max(amax, 1.0)
+                err = float(np.abs(g[sb] - r).max())
+                assert err <= rel * scale, f"entry {b} {name}: {err} > {rel} * {scale}"
