@@ -178,3 +178,43 @@ def test_random_variable_length_batch_against_oracle(case):
                 scale = max(amax, 1e-30) if w.dtype == torch.bfloat16 else max(amax, 1.0)
                 err = float(np.abs(g[sb] - r).max())
                 assert err <= rel * scale, f"entry {b} {name}: {err} > {rel} * {scale}"
+
+
+DYNAMIC_CASES = 16
+
+
+@pytest.mark.parametrize("case", range(DYNAMIC_CASES))
+def test_random_dynamic_plan_equals_static(case):
+    """Random bitmaps through a dynamic plan (CSR, transposed lists, split
+    walks and launch order built on the device) give, bit for bit, the
+    forward and backward of the static plan of the same bitmap."""
+    rng = np.random.default_rng(11000 + case)
+    bf16 = rng.random() < 0.7
+    D, bs = (128, 128) if bf16 else (int(rng.choice([64, 128])), int(rng.choice([64, 128])))
+    Hkv = int(rng.integers(1, 3))
+    H = Hkv * int(rng.choice([1, 2, 4]))
+    B = int(rng.integers(1, 3))
+    N = int(rng.integers(bs, 8 * bs + 1))
+    nb = -(-N // bs)
+    causal = bool(rng.random() < 0.5)
+    lh = int(rng.choice([1, H]))
+    bm = (rng.random((lh, nb, nb)) < rng.uniform(0.05, 0.5)).astype(np.uint8)
+    if rng.random() < 0.5:
+        bm[:, :, int(rng.integers(0, nb))] = 1            # a dense key-block column
+    w = wl.Workload(f"dyn-{case}", B, H, Hkv, N, D, bs, torch.bfloat16 if bf16 else torch.float32, 300 + case, {})
+    lay = dict(causal=causal, unit="blocks", window_left=-1, window_right=-1, global_keys=0, global_queries=0,
+               bitmap=bm)
+    say(f"[random dynamic {case}] {describe(w, lay)}")
+    q, k, v = (x.cuda() for x in wl.make_qkv(w, "cpu"))
+    do = wl.make_dout(w, "cuda")
+    sp = bsattn.plan(B, H, Hkv, N, D, bs, w.dtype, lay)
+    dp = bsattn.plan_dynamic(B, H, Hkv, N, D, bs, w.dtype, causal, lh)
+    dp.set_bitmap(torch.from_numpy(bm).cuda())
+    o1, l1 = bsattn.forward(q, k, v, sp)
+    o2, l2 = bsattn.forward(q, k, v, dp)
+    g1 = bsattn.backward(q, k, v, o1, l1, do, sp)
+    g2 = bsattn.backward(q, k, v, o2, l2, do, dp)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "forward differs"
+    for name, a, b in zip(("dQ", "dK", "dV"), g1, g2):
+        assert torch.equal(a, b), f"{name} differs"
