@@ -143,7 +143,9 @@ __device__ __forceinline__ uint16_t bf16_bits(float x) {
 // SIMD interleaves two independent waves whose matrix and softmax phases
 // overlap.  K and V are each held as two 16 KB halves (keys 0-63 and 64-127
 // of the current tile), all filled by direct HBM->LDS loads
-// (global_load_lds_dwordx4; no staging registers, no LDS stores).  A tile is
+// (global_load_lds_dwordx4; no staging registers, no LDS stores); the item's
+// Q tile arrives the same way, through the K and V buffers of half 1, before
+// the first tile.  A tile is
 // processed in two 64-key halves, each after one workgroup barrier:
 //   barrier 1: K and V half 0 of tile e have landed, and every wave is done
 //     with half 1 of tile e-1: load K and V half 1 of tile e, then S^T,
@@ -228,22 +230,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   const int qrow = wave * 32 + r32;                       // row within the q-block
   const int64_t qg = int64_t(i) * kBM + qrow;             // global query index
 
-  const int64_t qld = kRagged && qg >= Nb ? (Nb > 0 ? Nb - 1 : 0) : qg;   // row to load Q from
-  const uint16_t* __restrict__ Qp =
-      static_cast<const uint16_t*>(p.q) + ((int64_t(b) * p.H + h) * p.N + qld) * kD;
   const unsigned char* Kg =
       reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.k) + (int64_t(b) * p.Hkv + hk) * p.N * kD);
   const unsigned char* Vg =
       reinterpret_cast<const unsigned char*>(static_cast<const uint16_t*>(p.v) + (int64_t(b) * p.Hkv + hk) * p.N * kD);
 
-  // Q^T operand: lane (row r32, half hf) holds d = 16c + 8hf .. +7 for c = 0..7.
+  // Q^T operand: lane (row r32, half hf) holds d = 16c + 8hf .. +7 for c = 0..7
+  // (read from LDS before the first tile, below).
   bf16x8 qf[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) qf[c] = *reinterpret_cast<const bf16x8*>(Qp + c * 16 + hf * 8);
-  // Complete the Q loads before the first HBM->LDS load, so the counts of
-  // pending loads below only see those.
-  __asm__ volatile("s_waitcnt vmcnt(0)" ::"v"(qf[0]), "v"(qf[1]), "v"(qf[2]), "v"(qf[3]), "v"(qf[4]),
-                   "v"(qf[5]), "v"(qf[6]), "v"(qf[7]) : "memory");
 
   // HBM->LDS loads of one 64-key half of K or V tile j: wave w fills rows
   // 16w .. 16w+15 of the half, 4 rows (1 KB) per instruction; lane L writes
@@ -527,9 +521,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_d128(FwdParams p, const 
   // The entry ends inside its last block (only then do loads need a clamp).
   const bool ctail = kRagged && (Nb % kBN) != 0;
   if (ne > 0) {
+    // Q arrives by HBM->LDS loads as well, into K1 (rows 0-63 of the q-block)
+    // and V1 (rows 64-127) with K's swizzle, issued together with K half 0 of
+    // the first tile; after one barrier each wave reads its Q^T operand from
+    // there.  The first tile's barrier then orders those reads before the
+    // loads of half 1 into K1 and V1.  Rows at or beyond Nb (kRagged) load
+    // row Nb - 1.
+    {
+      const int64_t R0 = int64_t(i) * kBM + wave * 32;          // the wave's first row
+      const int64_t last = kRagged ? (Nb > 0 ? Nb - 1 : 0) : R0 + 31;
+      const int64_t Rb = R0 < last ? R0 : last;
+      const unsigned char* Qg = reinterpret_cast<const unsigned char*>(
+          static_cast<const uint16_t*>(p.q) + ((int64_t(b) * p.H + h) * p.N + Rb) * kD);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        int64_t src = R0 + 4 * u + lr;
+        if (kRagged) src = src < last ? src : last;
+        const uint32_t voff = uint32_t(src - Rb) * 256u + 16u * (lc ^ ((4 * u + lr) & 15));
+        dma16(Qg, voff, ((wave >> 1) ? Va[1] : Ka[1]) + (wave & 1) * (32 * 256) + u * 1024);
+      }
+    }
     const int j0 = ents[e0] >> 1;
 #pragma unroll
     for (int u = 0; u < 4; ++u) dma_half_part(j0, 0, u, std::true_type{});
+    BSA_WAIT_BARRIER(0);
+    lds_u8* const qs = ((wave >> 1) ? V3[1] : K3[1]) + (wave & 1) * (32 * 256) + r32 * 256;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      qf[c] = *reinterpret_cast<__attribute__((address_space(3))) bf16x8*>(qs + 16 * ((2 * c + hf) ^ (r32 & 15)));
   }
   // Entries ascend and the walk ends at block nbb - 1, so only the last tile
   // and the one before it (through its next entry) can reach that block:
