@@ -293,28 +293,43 @@ def test_empty_rows_have_no_entries():
     assert p.info["nnz"] == 0
 
 
-@pytest.mark.parametrize("source,symbol", [
+BF16_TILE_KERNELS = [
     ("forward.hip", "_ZN3bsa12_GLOBAL__N_113fwd_bf16_d128ILb0EEEvNS0_9FwdParamsEPKi"),
     ("forward.hip", "_ZN3bsa12_GLOBAL__N_113fwd_bf16_d128ILb1EEEvNS0_9FwdParamsEPKi"),
     ("backward.hip", "_ZN3bsa12_GLOBAL__N_118bwd_dkdv_bf16_d128ILb0EEEvNS0_9BwdParamsE"),
     ("backward.hip", "_ZN3bsa12_GLOBAL__N_118bwd_dkdv_bf16_d128ILb1EEEvNS0_9BwdParamsE"),
     ("backward.hip", "_ZN3bsa12_GLOBAL__N_116bwd_dq_bf16_d128ILb0EEEvNS0_9BwdParamsE"),
-    ("backward.hip", "_ZN3bsa12_GLOBAL__N_116bwd_dq_bf16_d128ILb1EEEvNS0_9BwdParamsE")])
-def test_bf16_kernel_m0_only_set_for_lds_loads(tmp_path, source, symbol):
+    ("backward.hip", "_ZN3bsa12_GLOBAL__N_116bwd_dq_bf16_d128ILb1EEEvNS0_9BwdParamsE")]
+
+_ASM = {}
+
+
+def _device_asm(source):
+    """gfx950 assembly of one HIP source, compiled once per test session
+    (hipcc cross-compiles without a GPU)."""
+    if source not in _ASM:
+        import subprocess
+        import tempfile
+        from block_sparse_flash_bsa_amd import build as bld
+        src = os.path.join(ROOT, "block_sparse_flash_bsa_amd", "csrc", source)
+        out = os.path.join(tempfile.mkdtemp(prefix="bsa_asm_"), source + ".s")
+        cmd = [bld.hipcc(), "-x", "hip", *bld.HIP_FLAGS, "-O3", "-std=c++17", "--cuda-device-only", "-S",
+               "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "block_sparse_flash_bsa_amd", "csrc"),
+               src, "-o", out]
+        subprocess.run(cmd, check=True, capture_output=True)
+        with open(out) as f:
+            _ASM[source] = f.read()
+    return _ASM[source]
+
+
+@pytest.mark.parametrize("source,symbol", BF16_TILE_KERNELS)
+def test_bf16_kernel_m0_only_set_for_lds_loads(source, symbol):
     """The bf16 forward and dK/dV kernels write M0 in inline assembly right
     before each HBM->LDS load; the compiler treats M0 as reserved and does not
     honour it as a clobber, so its own code must never rely on M0 across those
-    loads.  Compile the kernel to gfx950 assembly (works without a GPU) and
-    check that every M0 access in it is one of those load sequences."""
-    import subprocess
-    from block_sparse_flash_bsa_amd import build as bld
-    src = os.path.join(ROOT, "block_sparse_flash_bsa_amd", "csrc", source)
-    out = tmp_path / (source + ".s")
-    cmd = [bld.hipcc(), "-x", "hip", *bld.HIP_FLAGS, "-O3", "-std=c++17", "--cuda-device-only", "-S",
-           "-I", os.path.join(ROOT, "include"), "-I", os.path.join(ROOT, "block_sparse_flash_bsa_amd", "csrc"),
-           src, "-o", str(out)]
-    subprocess.run(cmd, check=True, capture_output=True)
-    asm = out.read_text()
+    loads.  Check on the kernel's gfx950 assembly that every M0 access in it
+    is one of those load sequences."""
+    asm = _device_asm(source)
     start = asm.index(symbol + ":")
     body = [l.strip() for l in asm[start:asm.index(".Lfunc_end", start)].splitlines()]
     body = [l for l in body if l and not l.startswith(";")]
@@ -323,6 +338,28 @@ def test_bf16_kernel_m0_only_set_for_lds_loads(tmp_path, source, symbol):
     for k in uses:
         assert body[k].startswith("s_mov_b32 m0, s"), body[k]
         assert body[k + 1].startswith("s_nop") and body[k + 2].startswith("global_load_lds_dwordx4"), body[k:k + 3]
+
+
+@pytest.mark.parametrize("source,symbol", BF16_TILE_KERNELS)
+def test_bf16_kernel_fits_two_workgroups_per_cu(source, symbol):
+    """Every bf16 tile kernel runs two 4-wave workgroups per CU, so that each
+    SIMD interleaves two independent waves: at most half of the CU's 160 KB
+    of LDS per workgroup and at most 256 registers (arithmetic plus
+    accumulation) per wave, from the kernel metadata of its gfx950 build.
+    The forward kernels and the whole-block backward kernels (the benchmark
+    paths) spill no vector registers and use no scratch memory (a few scalar
+    registers may be parked in vector-register lanes)."""
+    import yaml
+    asm = _device_asm(source)
+    meta = asm[asm.index(".amdgpu_metadata") + len(".amdgpu_metadata"):asm.index(".end_amdgpu_metadata")]
+    meta = meta[meta.index("---"):meta.rindex("...") + 3]        # the YAML document
+    kernels = {k[".name"]: k for k in yaml.safe_load(meta)["amdhsa.kernels"]}
+    k = kernels[symbol]
+    assert k[".max_flat_workgroup_size"] == 256
+    assert k[".group_segment_fixed_size"] <= 160 * 1024 // 2, k[".group_segment_fixed_size"]
+    assert k[".vgpr_count"] + k.get(".agpr_count", 0) <= 256, (k[".vgpr_count"], k.get(".agpr_count"))
+    if source == "forward.hip" or "ILb0E" in symbol:
+        assert k[".vgpr_spill_count"] == 0 and k[".private_segment_fixed_size"] == 0
 
 
 # ------------------------------------------------------------ dynamic plans
