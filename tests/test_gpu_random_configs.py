@@ -22,7 +22,7 @@ from block_sparse_flash_bsa_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
 
-CASES = 64
+CASES = 192
 
 
 def say(*a):
@@ -119,7 +119,7 @@ def test_random_problem_against_oracle(case):
         assert err <= rel * scale, f"{name}: {err} > {rel} * {scale}"
 
 
-VARLEN_CASES = 24
+VARLEN_CASES = 64
 
 
 @pytest.mark.parametrize("case", range(VARLEN_CASES))
@@ -180,7 +180,7 @@ def test_random_variable_length_batch_against_oracle(case):
                 assert err <= rel * scale, f"entry {b} {name}: {err} > {rel} * {scale}"
 
 
-DYNAMIC_CASES = 16
+DYNAMIC_CASES = 48
 
 
 @pytest.mark.parametrize("case", range(DYNAMIC_CASES))
