@@ -26,32 +26,53 @@
 namespace bsa {
 namespace {
 
-constexpr int kRowThreads = 256;    // threads per row (4 waves)
+// Rows: one wave per row (layout head * nb + i), four rows per workgroup.
+// With kVec = 16 (nb and the bitmap's address multiples of 16, so every row
+// is 16-byte aligned) lane L reads bytes [16 L, 16 L + 16) of each 1 KB
+// stretch of its row with one load; with kVec = 1 it reads byte L of each
+// 64-byte stretch.  Only the bytes below the row's last column (the diagonal
+// under the causal cut) count.
+constexpr int kRowThreads = 256;
+constexpr int kRowWaves = kRowThreads / 64;
 
-// Sum of v over the workgroup (blockDim.x == kRowThreads); all threads get it.
-__device__ __forceinline__ int block_sum(int v, int* red) {
+// Bit v set iff byte v of the kVec bytes at p is nonzero, for v < lim (the
+// bytes at or beyond lim are not read when kVec is 1, and are read but
+// dropped when kVec is 16; the caller keeps all 16 inside the row).
+template <int kVec>
+__device__ __forceinline__ uint32_t nonzero_bits(const uint8_t* p, int lim) {
+  if (lim <= 0) return 0;
+  if constexpr (kVec == 1) {
+    return p[0] != 0 ? 1u : 0u;
+  } else {
+    const uint4 x = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+    uint32_t bits = 0;
 #pragma unroll
-  for (int w = 32; w >= 1; w >>= 1) v += __shfl_xor(v, w);
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
-  __syncthreads();
-  const int total = red[0] + red[1] + red[2] + red[3];
-  __syncthreads();
-  return total;
+    for (int k = 0; k < 4; ++k) {
+      // Bit 7 of each byte: set iff the byte is nonzero (its low 7 bits
+      // carry into bit 7 when any is set, or bit 7 is set already).
+      const uint32_t hi = (((w[k] & 0x7F7F7F7Fu) + 0x7F7F7F7Fu) | w[k]) & 0x80808080u;
+      bits |= (((hi >> 7) & 1u) | ((hi >> 14) & 2u) | ((hi >> 21) & 4u) | ((hi >> 28) & 8u)) << (4 * k);
+    }
+    return lim >= 16 ? bits : bits & ((1u << lim) - 1u);
+  }
 }
 
-// counts[row] = entries of row (layout head * nb + i).
-__global__ __launch_bounds__(kRowThreads) void count_rows(const uint8_t* __restrict__ bm, int nb, int causal,
-                                                          int32_t* __restrict__ counts) {
-  __shared__ int red[kRowThreads / 64];
-  const int row = blockIdx.x;
+// counts[row] = entries of row.
+template <int kVec>
+__global__ __launch_bounds__(kRowThreads) void count_rows(const uint8_t* __restrict__ bm, int nb, int nrows,
+                                                          int causal, int32_t* __restrict__ counts) {
+  const int row = blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+  if (row >= nrows) return;                          // whole waves
+  const int lane = threadIdx.x & 63;
   const int i = row % nb;
   const int jend = causal ? i + 1 : nb;
   const uint8_t* r = bm + size_t(row) * nb;
   int c = 0;
-  for (int j = threadIdx.x; j < jend; j += kRowThreads) c += r[j] != 0;
-  const int total = block_sum(c, red);
-  if (threadIdx.x == 0) counts[row] = total;
+  for (int j0 = lane * kVec; j0 < jend; j0 += 64 * kVec) c += __popc(nonzero_bits<kVec>(r + j0, jend - j0));
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) c += __shfl_xor(c, w);
+  if (lane == 0) counts[row] = c;
 }
 
 // rows[x] = {exclusive prefix of counts, counts[x]} over all n rows, and
@@ -141,30 +162,38 @@ __global__ __launch_bounds__(kScanBlock) void scan_apply(const int32_t* __restri
   if (d_nnz && blockIdx.x == 0 && threadIdx.x == 0) *d_nnz = sums[nblk];
 }
 
-// The entries of each row, ascending: entry = (j << 1) | partial.
-__global__ __launch_bounds__(kRowThreads) void fill_rows(const uint8_t* __restrict__ bm, int nb, int causal,
-                                                         int tail, const RowDesc* __restrict__ rows,
+// The entries of each row, ascending: entry = (j << 1) | partial.  Each
+// stretch of the row: every lane's count, their exclusive prefix over the
+// wave, and each lane writes its entries from there in column order.
+template <int kVec>
+__global__ __launch_bounds__(kRowThreads) void fill_rows(const uint8_t* __restrict__ bm, int nb, int nrows,
+                                                         int causal, int tail, const RowDesc* __restrict__ rows,
                                                          int32_t* __restrict__ entries) {
-  __shared__ int wsum[kRowThreads / 64];
-  const int row = blockIdx.x;
+  const int row = blockIdx.x * kRowWaves + (threadIdx.x >> 6);
+  if (row >= nrows) return;                          // whole waves
+  const int lane = threadIdx.x & 63;
   const int i = row % nb;
   const int jend = causal ? i + 1 : nb;
   const uint8_t* r = bm + size_t(row) * nb;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int32_t* out = entries + rows[row].start;
   int base = 0;
-  for (int j0 = 0; j0 < jend; j0 += kRowThreads) {
-    const int j = j0 + threadIdx.x;
-    const bool on = j < jend && r[j] != 0;
-    const uint64_t m = __ballot(on);
-    const int below = __popcll(m & ((uint64_t(1) << lane) - 1));
-    if (lane == 0) wsum[wave] = __popcll(m);
-    __syncthreads();
-    int off = base;
-    for (int w = 0; w < wave; ++w) off += wsum[w];
-    if (on) out[off + below] = (j << 1) | (((causal && j == i) || i == tail || j == tail) ? 1 : 0);
-    base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-    __syncthreads();
+  for (int p0 = 0; p0 < jend; p0 += 64 * kVec) {     // wave-uniform
+    const int j0 = p0 + lane * kVec;
+    uint32_t bits = j0 < jend ? nonzero_bits<kVec>(r + j0, jend - j0) : 0u;
+    const int c = __popc(bits);
+    int inc = c;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(inc, d);
+      if (lane >= d) inc += y;
+    }
+    int pos = base + inc - c;
+    while (bits) {
+      const int j = j0 + __builtin_ctz(bits);
+      bits &= bits - 1u;
+      out[pos++] = (j << 1) | (((causal && j == i) || i == tail || j == tail) ? 1 : 0);
+    }
+    base += __shfl(inc, 63);
   }
 }
 
@@ -297,7 +326,8 @@ __global__ __launch_bounds__(kStripThreads) void fill_cols(const uint8_t* __rest
 // every batch entry.  As the host planner does for static plans, a walk
 // longer than the chunk length C = max(64, 2 * mean walk) becomes
 // k = ceil(L / C) chunks [c * L / k, (c + 1) * L / k); here C doubles until
-// the chunks fit the plan's partial-tile and slot budgets.  One workgroup
+// the chunks fit the plan's partial-tile and slot budgets.  A wide kernel
+// sums each column's walk over the group's lists; one workgroup then
 // finds C and, per column, the exclusive prefixes of the extra chunks
 // (beyond each split column's first), the partial tiles and the split
 // columns, packed 21 bits each (the budgets keep every sum below 2^20); a
@@ -313,25 +343,28 @@ __device__ __forceinline__ long long split_pack(long long L, long long chunk) {
   return (k - 1) | (k << kPackBits) | (1ll << (2 * kPackBits));
 }
 
+// walk[x] for every column x = hk * nb + j: one thread each.
+__global__ __launch_bounds__(kWriteThreads) void kv_walks(const RowDesc* __restrict__ cols, int nb, int n,
+                                                          int group, int per_head, int32_t* __restrict__ walk) {
+  const int x = blockIdx.x * kWriteThreads + threadIdx.x;
+  if (x >= n) return;
+  const int hk = x / nb, j = x - hk * nb;
+  int L = 0;
+  for (int g = 0; g < group; ++g) L += cols[(per_head ? hk * group + g : 0) * nb + j].count;
+  walk[x] = L;
+}
+
 // head: [0] chunk length, [1] extra chunks, [2] partial tiles, [3] split
 // columns (each per batch entry), [4] split columns in all.
-__global__ __launch_bounds__(kScanBlock) void kv_split_plan(const RowDesc* __restrict__ cols, int nb, int n,
-                                                            int group, int per_head, int batch,
-                                                            long long max_extra, long long max_parts,
-                                                            int32_t* __restrict__ walk, int64_t* __restrict__ pre,
-                                                            int32_t* __restrict__ head) {
+__global__ __launch_bounds__(kScanBlock) void kv_split_plan(int n, int batch, long long max_extra,
+                                                            long long max_parts, const int32_t* __restrict__ walk,
+                                                            int64_t* __restrict__ pre, int32_t* __restrict__ head) {
   __shared__ long long wsum[kScanWaves];
-  // Thread t owns the contiguous columns [x0, x1) and reads back only what it wrote.
+  // Thread t owns the contiguous columns [x0, x1).
   const int per = (n + kScanBlock - 1) / kScanBlock;
   const int x0 = min(n, int(threadIdx.x) * per), x1 = min(n, x0 + per);
   long long mine = 0;
-  for (int x = x0; x < x1; ++x) {
-    const int hk = x / nb, j = x - hk * nb;
-    int L = 0;
-    for (int g = 0; g < group; ++g) L += cols[(per_head ? hk * group + g : 0) * nb + j].count;
-    walk[x] = L;
-    mine += L;
-  }
+  for (int x = x0; x < x1; ++x) mine += walk[x];
   long long total;
   block_scan(mine, wsum, total);
   __syncthreads();
@@ -502,8 +535,15 @@ extern "C" bsa_status_t bsa_plan_set_bitmap(bsa_plan_t plan, const uint8_t* d_bi
   hipStream_t s = static_cast<hipStream_t>(stream);
   auto* d_rows = const_cast<RowDesc*>(plan->d_rows);
   auto* d_entries = const_cast<int32_t*>(plan->d_entries);
-  hipLaunchKernelGGL(count_rows, dim3(unsigned(rows)), dim3(kRowThreads), 0, s, d_bitmap, nb, plan->causal,
-                     plan->d_counts);
+  // 16-byte loads when every row of the bitmap is 16-byte aligned.
+  const bool rows16 = nb % 16 == 0 && reinterpret_cast<uintptr_t>(d_bitmap) % 16 == 0;
+  const unsigned row_groups = unsigned((rows + kRowWaves - 1) / kRowWaves);
+  if (rows16)
+    hipLaunchKernelGGL(count_rows<16>, dim3(row_groups), dim3(kRowThreads), 0, s, d_bitmap, nb, rows,
+                       plan->causal, plan->d_counts);
+  else
+    hipLaunchKernelGGL(count_rows<1>, dim3(row_groups), dim3(kRowThreads), 0, s, d_bitmap, nb, rows,
+                       plan->causal, plan->d_counts);
   const int nblk = (rows + kScanBlock - 1) / kScanBlock;
   auto scan = [&](RowDesc* out, int64_t* nnz_out) {
     if (nblk <= kSmallScanBlocks) {
@@ -520,8 +560,12 @@ extern "C" bsa_status_t bsa_plan_set_bitmap(bsa_plan_t plan, const uint8_t* d_bi
   // The shorter last block of a seq_len the block does not divide: its tiles
   // are PARTIAL (-1: every block whole).
   const int tail = plan->prob.seq_len % plan->prob.block_size != 0 ? nb - 1 : -1;
-  hipLaunchKernelGGL(fill_rows, dim3(unsigned(rows)), dim3(kRowThreads), 0, s, d_bitmap, nb, plan->causal, tail,
-                     d_rows, d_entries);
+  if (rows16)
+    hipLaunchKernelGGL(fill_rows<16>, dim3(row_groups), dim3(kRowThreads), 0, s, d_bitmap, nb, rows,
+                       plan->causal, tail, d_rows, d_entries);
+  else
+    hipLaunchKernelGGL(fill_rows<1>, dim3(row_groups), dim3(kRowThreads), 0, s, d_bitmap, nb, rows,
+                       plan->causal, tail, d_rows, d_entries);
   if (plan->d_work_base) {
     // Longest row first within each (KV head, batch entry) run of the order.
     const int hkv = plan->prob.num_kv_heads, group = plan->prob.num_heads / hkv;
@@ -559,9 +603,11 @@ extern "C" bsa_status_t bsa_plan_set_bitmap(bsa_plan_t plan, const uint8_t* d_bi
     const int hkv = plan->prob.num_kv_heads, group = plan->prob.num_heads / hkv;
     const int n = hkv * nb;
     const int64_t items = int64_t(plan->prob.batch) * n;
-    hipLaunchKernelGGL(kv_split_plan, dim3(1), dim3(kScanBlock), 0, s, d_cols, nb, n, group,
-                       plan->layout_heads > 1 ? 1 : 0, plan->prob.batch, (long long)plan->kv_extra_slots,
-                       (long long)plan->kv_partials, plan->d_kv_walk, plan->d_kv_pre, plan->d_kv_head);
+    hipLaunchKernelGGL(kv_walks, dim3(unsigned((n + kWriteThreads - 1) / kWriteThreads)), dim3(kWriteThreads), 0,
+                       s, d_cols, nb, n, group, plan->layout_heads > 1 ? 1 : 0, plan->d_kv_walk);
+    hipLaunchKernelGGL(kv_split_plan, dim3(1), dim3(kScanBlock), 0, s, n, plan->prob.batch,
+                       (long long)plan->kv_extra_slots, (long long)plan->kv_partials, plan->d_kv_walk,
+                       plan->d_kv_pre, plan->d_kv_head);
     const int64_t cover = items > plan->kv_extra_slots ? items : plan->kv_extra_slots;
     hipLaunchKernelGGL(kv_split_write, dim3(unsigned((cover + kWriteThreads - 1) / kWriteThreads)),
                        dim3(kWriteThreads), 0, s, plan->d_kv_walk, plan->d_kv_pre, plan->d_kv_head,
