@@ -205,14 +205,16 @@ __global__ __launch_bounds__(kRowThreads) void fill_rows(const uint8_t* __restri
 // with one load per row (kVec = 4 when nb is a multiple of 4, so every row
 // of 4-byte groups is aligned; else 1), so each wave reads kStrip * kVec
 // consecutive bytes of a row per load; wave w owns the contiguous row chunk
-// [w * chunk, (w + 1) * chunk).  The count kernel adds the chunks' counts;
+// [w * chunk, (w + 1) * chunk), loading kRowBatch rows at a time before it
+// uses them (so each lane has that many loads in flight).  The count kernel adds the chunks' counts;
 // the fill kernel recounts its chunk, takes the counts of the chunks above it
 // as its offset in each column's list and writes its entries in row order,
 // so every list comes out ascending.
 constexpr int kStrip = 64;
 constexpr int kChunks = 16;
 constexpr int kStripThreads = kStrip * kChunks;
-constexpr int64_t kWideMinStrips = 256;   // 4-column lanes only with at least this many workgroups
+constexpr int64_t kWideMinStrips = 256;
+constexpr int kRowBatch = 8;              // rows loaded together per lane   // 4-column lanes only with at least this many workgroups
 
 struct StripCursor {
   const uint8_t* col;   // bitmap byte (row 0, this lane's first column)
@@ -261,10 +263,14 @@ __device__ __forceinline__ void strip_count(const StripCursor& c, int nb, int ca
 #pragma unroll
   for (int v = 0; v < kVec; ++v) n[v] = 0;
   if (!c.valid) return;
-  for (int i = c.i0; i < c.i1; ++i) {
-    const uint32_t x = strip_row<kVec>(c, nb, i);
+  for (int i = c.i0; i < c.i1; i += kRowBatch) {
+    uint32_t x[kRowBatch];
 #pragma unroll
-    for (int v = 0; v < kVec; ++v) n[v] += strip_on<kVec>(x, v, i, c.j0, causal);
+    for (int u = 0; u < kRowBatch; ++u) x[u] = i + u < c.i1 ? strip_row<kVec>(c, nb, i + u) : 0u;
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u)
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) n[v] += strip_on<kVec>(x[u], v, i + u, c.j0, causal);
   }
 }
 
@@ -310,12 +316,18 @@ __global__ __launch_bounds__(kStripThreads) void fill_cols(const uint8_t* __rest
     off[v] = cols[hl * nb + c.j0 + v].start;
     for (int x = 0; x < w; ++x) off[v] += part[x][lane * kVec + v];
   }
-  for (int i = c.i0; i < c.i1; ++i) {
-    const uint32_t x = strip_row<kVec>(c, nb, i);
+  for (int i0 = c.i0; i0 < c.i1; i0 += kRowBatch) {
+    uint32_t x[kRowBatch];
 #pragma unroll
-    for (int v = 0; v < kVec; ++v)
-      if (strip_on<kVec>(x, v, i, c.j0, causal))
-        entries[off[v]++] = (i << 1) | (((causal && i == c.j0 + v) || i == tail || c.j0 + v == tail) ? 1 : 0);
+    for (int u = 0; u < kRowBatch; ++u) x[u] = i0 + u < c.i1 ? strip_row<kVec>(c, nb, i0 + u) : 0u;
+#pragma unroll
+    for (int u = 0; u < kRowBatch; ++u) {
+      const int i = i0 + u;
+#pragma unroll
+      for (int v = 0; v < kVec; ++v)
+        if (strip_on<kVec>(x[u], v, i, c.j0, causal))
+          entries[off[v]++] = (i << 1) | (((causal && i == c.j0 + v) || i == tail || c.j0 + v == tail) ? 1 : 0);
+    }
   }
 }
 
@@ -360,11 +372,9 @@ __global__ __launch_bounds__(kScanBlock) void kv_split_plan(int n, int batch, lo
                                                             long long max_parts, const int32_t* __restrict__ walk,
                                                             int64_t* __restrict__ pre, int32_t* __restrict__ head) {
   __shared__ long long wsum[kScanWaves];
-  // Thread t owns the contiguous columns [x0, x1).
-  const int per = (n + kScanBlock - 1) / kScanBlock;
-  const int x0 = min(n, int(threadIdx.x) * per), x1 = min(n, x0 + per);
+  // Sums run over columns x = t, t + kScanBlock, ... (coalesced reads).
   long long mine = 0;
-  for (int x = x0; x < x1; ++x) mine += walk[x];
+  for (int x = threadIdx.x; x < n; x += kScanBlock) mine += walk[x];
   long long total;
   block_scan(mine, wsum, total);
   __syncthreads();
@@ -373,7 +383,7 @@ __global__ __launch_bounds__(kScanBlock) void kv_split_plan(int n, int batch, lo
   for (;;) {
     // Extra chunks (low 32 bits) and partial tiles (high 32 bits) at this chunk length.
     long long ep = 0;
-    for (int x = x0; x < x1; ++x) {
+    for (int x = threadIdx.x; x < n; x += kScanBlock) {
       const long long L = walk[x];
       if (L > chunk) {
         const long long k = (L + chunk - 1) / chunk;
@@ -386,13 +396,16 @@ __global__ __launch_bounds__(kScanBlock) void kv_split_plan(int n, int batch, lo
     if ((sum & 0xffffffffll) * batch <= max_extra && (sum >> 32) * batch <= max_parts) break;
     chunk *= 2;
   }
-  long long packed = 0;
-  for (int x = x0; x < x1; ++x) packed += split_pack(walk[x], chunk);
-  long long all;
-  long long run = block_scan(packed, wsum, all) - packed;
-  for (int x = x0; x < x1; ++x) {
-    pre[x] = run;
-    run += split_pack(walk[x], chunk);
+  // Exclusive prefix of the packed counts in column order, kScanBlock columns at a time.
+  long long all = 0;
+  for (int c0 = 0; c0 < n; c0 += kScanBlock) {
+    const int x = c0 + threadIdx.x;
+    const long long v = x < n ? split_pack(walk[x], chunk) : 0;
+    long long part;
+    const long long inc = block_scan(v, wsum, part);
+    __syncthreads();                                   // wsum is reused by the next block of columns
+    if (x < n) pre[x] = all + inc - v;
+    all += part;
   }
   if (threadIdx.x == 0) {
     head[0] = int32_t(chunk < 0x7fffffffll ? chunk : 0x7fffffffll);
