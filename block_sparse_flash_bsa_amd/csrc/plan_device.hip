@@ -296,7 +296,13 @@ __global__ __launch_bounds__(kStripThreads) void count_cols(const uint8_t* __res
   }
 }
 
-template <int kVec>
+// kMasks: the wave's chunk has at most kMaskBatches * kRowBatch rows (nb at
+// most kChunks times that), and the count pass keeps, per batch of
+// kRowBatch rows, the lane's entry bits (bit u * kVec + v: row i0 + u,
+// column j0 + v) in registers, so the write pass reads no bitmap byte again.
+constexpr int kMaskBatches = 16;
+
+template <int kVec, bool kMasks>
 __global__ __launch_bounds__(kStripThreads) void fill_cols(const uint8_t* __restrict__ bm, int nb, int causal,
                                                            int tail, const RowDesc* __restrict__ cols,
                                                            int32_t* __restrict__ entries) {
@@ -304,7 +310,37 @@ __global__ __launch_bounds__(kStripThreads) void fill_cols(const uint8_t* __rest
   const StripCursor c = strip_cursor<kVec>(bm, nb, causal);
   const int lane = threadIdx.x % kStrip, w = threadIdx.x / kStrip;
   int n[kVec];
-  strip_count<kVec>(c, nb, causal, n);
+  uint32_t mk[kMasks ? kMaskBatches : 1];
+  if constexpr (kMasks) {
+    static_assert(kVec * kRowBatch <= 32, "one word of entry bits per batch");
+#pragma unroll
+    for (int v = 0; v < kVec; ++v) n[v] = 0;
+#pragma unroll
+    for (int bb = 0; bb < kMaskBatches; ++bb) {
+      const int i0 = c.i0 + bb * kRowBatch;
+      uint32_t m = 0;
+      if (c.valid && i0 < c.i1) {
+        uint32_t x[kRowBatch];
+#pragma unroll
+        for (int u = 0; u < kRowBatch; ++u) x[u] = i0 + u < c.i1 ? strip_row<kVec>(c, nb, i0 + u) : 0u;
+#pragma unroll
+        for (int u = 0; u < kRowBatch; ++u)
+#pragma unroll
+          for (int v = 0; v < kVec; ++v)
+            if (strip_on<kVec>(x[u], v, i0 + u, c.j0, causal)) m |= 1u << (u * kVec + v);
+      }
+      mk[bb] = m;
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) {
+        uint32_t col = 0;
+#pragma unroll
+        for (int u = 0; u < kRowBatch; ++u) col |= 1u << (u * kVec + v);
+        n[v] += __popc(m & col);
+      }
+    }
+  } else {
+    strip_count<kVec>(c, nb, causal, n);
+  }
 #pragma unroll
   for (int v = 0; v < kVec; ++v) part[w][lane * kVec + v] = n[v];
   __syncthreads();
@@ -316,17 +352,30 @@ __global__ __launch_bounds__(kStripThreads) void fill_cols(const uint8_t* __rest
     off[v] = cols[hl * nb + c.j0 + v].start;
     for (int x = 0; x < w; ++x) off[v] += part[x][lane * kVec + v];
   }
-  for (int i0 = c.i0; i0 < c.i1; i0 += kRowBatch) {
-    uint32_t x[kRowBatch];
+  auto put = [&](int i, int v) {
+    entries[off[v]++] = (i << 1) | (((causal && i == c.j0 + v) || i == tail || c.j0 + v == tail) ? 1 : 0);
+  };
+  if constexpr (kMasks) {
 #pragma unroll
-    for (int u = 0; u < kRowBatch; ++u) x[u] = i0 + u < c.i1 ? strip_row<kVec>(c, nb, i0 + u) : 0u;
+    for (int bb = 0; bb < kMaskBatches; ++bb) {
+      const uint32_t m = mk[bb];
+      if (m == 0) continue;
 #pragma unroll
-    for (int u = 0; u < kRowBatch; ++u) {
-      const int i = i0 + u;
+      for (int u = 0; u < kRowBatch; ++u)
 #pragma unroll
-      for (int v = 0; v < kVec; ++v)
-        if (strip_on<kVec>(x[u], v, i, c.j0, causal))
-          entries[off[v]++] = (i << 1) | (((causal && i == c.j0 + v) || i == tail || c.j0 + v == tail) ? 1 : 0);
+        for (int v = 0; v < kVec; ++v)
+          if ((m >> (u * kVec + v)) & 1u) put(c.i0 + bb * kRowBatch + u, v);
+    }
+  } else {
+    for (int i0 = c.i0; i0 < c.i1; i0 += kRowBatch) {
+      uint32_t x[kRowBatch];
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u) x[u] = i0 + u < c.i1 ? strip_row<kVec>(c, nb, i0 + u) : 0u;
+#pragma unroll
+      for (int u = 0; u < kRowBatch; ++u)
+#pragma unroll
+        for (int v = 0; v < kVec; ++v)
+          if (strip_on<kVec>(x[u], v, i0 + u, c.j0, causal)) put(i0 + u, v);
     }
   }
 }
@@ -605,12 +654,21 @@ extern "C" bsa_status_t bsa_plan_set_bitmap(bsa_plan_t plan, const uint8_t* d_bi
     hipLaunchKernelGGL(count_cols<1>, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal,
                        plan->d_counts);
   scan(d_cols, nullptr);
-  if (vec == 4)
-    hipLaunchKernelGGL(fill_cols<4>, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal, tail,
-                       d_cols, d_entries_t);
+  // Entry bits kept in registers between the fill kernel's two passes when
+  // each wave's chunk of rows fits them.
+  const bool masks = (nb + kChunks - 1) / kChunks <= kMaskBatches * kRowBatch;
+  if (vec == 4 && masks)
+    hipLaunchKernelGGL((fill_cols<4, true>), dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal,
+                       tail, d_cols, d_entries_t);
+  else if (vec == 4)
+    hipLaunchKernelGGL((fill_cols<4, false>), dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal,
+                       tail, d_cols, d_entries_t);
+  else if (masks)
+    hipLaunchKernelGGL((fill_cols<1, true>), dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal,
+                       tail, d_cols, d_entries_t);
   else
-    hipLaunchKernelGGL(fill_cols<1>, dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal, tail,
-                       d_cols, d_entries_t);
+    hipLaunchKernelGGL((fill_cols<1, false>), dim3(strips), dim3(kStripThreads), 0, s, d_bitmap, nb, plan->causal,
+                       tail, d_cols, d_entries_t);
   if (plan->kv_extra_slots > 0) {
     // The dK/dV launch descriptors for the new walk lengths.
     const int hkv = plan->prob.num_kv_heads, group = plan->prob.num_heads / hkv;
