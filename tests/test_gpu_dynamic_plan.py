@@ -101,12 +101,16 @@ def test_device_csr_matches_host_plan_and_oracle(lh, H, nb, bs, density, causal,
     say(f"  lh={lh} nb={nb} N={N} causal={causal}: {total} entries identical, transposed lists too")
 
 
-@pytest.mark.parametrize("lh,nb,causal", [(8, 1100, False), (8, 1100, True), (64, 1024, False), (64, 1024, True)])
+@pytest.mark.parametrize("lh,nb,causal", [(8, 1100, False), (8, 1100, True), (64, 1024, False), (64, 1024, True),
+                                           (6, 2100, False), (32, 2052, True)])
 def test_device_csr_many_rows_matches_host_plan(lh, nb, causal):
     """More rows than the one-workgroup scan takes (8 x 1100 and 64 x 1024
     rows): the blocked three-kernel scan gives the host planner's CSR and
     transposed lists bit for bit; 64 x 1024 also takes the column kernels'
-    4-byte loads (256 strips of 256 columns)."""
+    4-byte loads (256 strips of 256 columns).  With nb above 2048 a wave's
+    chunk of rows exceeds what the column fill keeps in registers, so it
+    reads its strip again: one byte per lane (6 x 2100) and four (32 x 2052,
+    288 strips)."""
     bs = 64
     bm = random_bitmap(lh, nb, 0.01, seed=17)
     bm[2, 700, :] = 1                                # a full row
